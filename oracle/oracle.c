@@ -1,0 +1,228 @@
+/*
+ * q4gsw oracle: a plain, slow, obviously correct CPU model of the 4-bit
+ * group-symmetric weight-quantized linear layer, in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or helper with the GPU library, and it includes no HIP header.
+ *
+ * What it computes (sources are the pages' own text):
+ *
+ *   dequant(W[n,k]) = (code[n,k] - 8) * scale[k / group_size, n]
+ *       The dequantisation formula is given in the "Solution" part of the body of
+ *       the pull request "[ExecuTorch][Vulkan] Add et_vk.linear_q4gsw_backward
+ *       kernel (4-bit input-grad)"; its "Key changes" part gives the scale
+ *       shape [num_groups, N].  The pages leave the scale's row index open; the
+ *       plainest reading consistent with that shape (groups are contiguous runs
+ *       of group_size along K) is k / group_size, integer division.
+ *
+ *   forward      y[m,n]  = sum_k x[m,k] * dequant(W[n,k])         (y = x . W^T)
+ *       The forward is the linear_q4gsw op named on all three pages; the same
+ *       pull request states its backward as the adjoint below, which fixes the
+ *       forward as y = x . dequant(W)^T.
+ *
+ *   input grad   dx[m,k] = sum_n d_out[m,n] * dequant(W[n,k])     (contract N)
+ *       Opening summary of the same Vulkan pull request body (the input
+ *       gradient of the frozen 4-bit base, contracting over N).
+ *
+ *   QKV          three forwards of one activation with three weights, three
+ *       distinct outputs: body of "[ExecuTorch][WebGPU] Replace broad QKV
+ *       fusion with BK64 kernel" (the QKV paragraph).  It is composed in the
+ *       Python wrapper from three calls of oracle_linear_fwd.
+ *
+ * Every input element is widened exactly to double: fp16 and bf16 are decoded
+ * from their IEEE bit fields here.  Every product is exact in fp64 (at most
+ * 24 + 3 + 24 significant bits); sums run with the contraction index
+ * ascending, so the only rounding is the fp64 summation.  The normaliser
+ * R = sum |activation| * |dequant(W)| over the same contraction is returned
+ * beside every result; GPU results are judged against tol * R.
+ *
+ * Threads split the output elements only, so every sum keeps its order and the
+ * results are bitwise identical for any thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+
+enum {
+    ORACLE_OK = 0,
+    ORACLE_E_ARG = 1,        /* bad size, dtype or group size */
+    ORACLE_E_CODE = 2,       /* a code outside 0..15 */
+};
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int exponent = (h >> 10) & 0x1f;
+    int fraction = h & 0x3ff;
+    double magnitude;
+    if (exponent == 0) {
+        magnitude = ldexp((double)fraction, -24);               /* subnormal or zero */
+    } else if (exponent == 31) {
+        magnitude = fraction ? NAN : INFINITY;
+    } else {
+        magnitude = ldexp((double)(fraction | 0x400), exponent - 25);
+    }
+    return sign ? -magnitude : magnitude;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32: 1 sign, 8 exponent (bias 127), 7 fraction. */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int exponent = (b >> 7) & 0xff;
+    int fraction = b & 0x7f;
+    double magnitude;
+    if (exponent == 0) {
+        magnitude = ldexp((double)fraction, -133);
+    } else if (exponent == 255) {
+        magnitude = fraction ? NAN : INFINITY;
+    } else {
+        magnitude = ldexp((double)(fraction | 0x80), exponent - 134);
+    }
+    return sign ? -magnitude : magnitude;
+}
+
+/* IEEE binary32 read as bits: 1 sign, 8 exponent (bias 127), 23 fraction. */
+double oracle_f32_to_f64(uint32_t u)
+{
+    int sign = (u >> 31) & 1;
+    int exponent = (u >> 23) & 0xff;
+    uint32_t fraction = u & 0x7fffffu;
+    double magnitude;
+    if (exponent == 0) {
+        magnitude = ldexp((double)fraction, -149);
+    } else if (exponent == 255) {
+        magnitude = fraction ? NAN : INFINITY;
+    } else {
+        magnitude = ldexp((double)(fraction | 0x800000u), exponent - 150);
+    }
+    return sign ? -magnitude : magnitude;
+}
+
+static double element(const void *base, int dtype, int64_t index)
+{
+    if (dtype == ORACLE_F32) {
+        uint32_t u;
+        memcpy(&u, (const char *)base + 4 * index, 4);
+        return oracle_f32_to_f64(u);
+    }
+    uint16_t h;
+    memcpy(&h, (const char *)base + 2 * index, 2);
+    return dtype == ORACLE_F16 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);
+}
+
+/* dequant(W[n,k]) = (code - 8) * scale[k / group_size, n]; scales are [K/group_size, N]. */
+double oracle_dequant(const uint8_t *codes, const void *scales, int scale_dtype,
+                      int64_t N, int64_t K, int64_t group_size, int64_t n, int64_t k)
+{
+    int code = codes[n * K + k];
+    int64_t group = k / group_size;
+    return (double)(code - 8) * element(scales, scale_dtype, group * N + n);
+}
+
+static int check_args(int act_dtype, int scale_dtype, int64_t M, int64_t N, int64_t K,
+                      int64_t group_size, const uint8_t *codes)
+{
+    if (M < 0 || N < 0 || K < 0 || group_size <= 0 || K % group_size != 0)
+        return ORACLE_E_ARG;
+    if (act_dtype < ORACLE_F32 || act_dtype > ORACLE_BF16)
+        return ORACLE_E_ARG;
+    if (scale_dtype != ORACLE_F32 && scale_dtype != ORACLE_F16)
+        return ORACLE_E_ARG;
+    for (int64_t i = 0; i < N * K; ++i)
+        if (codes[i] > 15)
+            return ORACLE_E_CODE;
+    return ORACLE_OK;
+}
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* y[m,n] = sum_k x[m,k] * dequant(W[n,k]); r[m,n] = sum_k |x[m,k]| * |dequant(W[n,k])|.
+ * x is [M,K] row-major in act_dtype; codes [N,K]; y and r (r may be NULL) are [M,N]. */
+int oracle_linear_fwd(const void *x, int act_dtype, int64_t M,
+                      const uint8_t *codes, const void *scales, int scale_dtype,
+                      int64_t N, int64_t K, int64_t group_size,
+                      double *y, double *r, int nthreads)
+{
+    int status = check_args(act_dtype, scale_dtype, M, N, K, group_size, codes);
+    if (status != ORACLE_OK)
+        return status;
+    set_threads(nthreads);
+    int64_t outputs = M * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < outputs; ++o) {
+        int64_t m = o / N, n = o % N;
+        double sum = 0.0, norm = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = element(x, act_dtype, m * K + k);
+            double w = oracle_dequant(codes, scales, scale_dtype, N, K, group_size, n, k);
+            sum += a * w;
+            norm += fabs(a) * fabs(w);
+        }
+        y[o] = sum;
+        if (r)
+            r[o] = norm;
+    }
+    return ORACLE_OK;
+}
+
+/* dx[m,k] = sum_n d_out[m,n] * dequant(W[n,k]); r[m,k] = sum_n |d_out[m,n]| * |dequant(W[n,k])|.
+ * d_out is [M,N] row-major in act_dtype; codes [N,K]; dx and r (r may be NULL) are [M,K]. */
+int oracle_linear_bwd_input(const void *d_out, int act_dtype, int64_t M,
+                            const uint8_t *codes, const void *scales, int scale_dtype,
+                            int64_t N, int64_t K, int64_t group_size,
+                            double *dx, double *r, int nthreads)
+{
+    int status = check_args(act_dtype, scale_dtype, M, N, K, group_size, codes);
+    if (status != ORACLE_OK)
+        return status;
+    set_threads(nthreads);
+    int64_t outputs = M * K;
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < outputs; ++o) {
+        int64_t m = o / K, k = o % K;
+        double sum = 0.0, norm = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double g = element(d_out, act_dtype, m * N + n);
+            double w = oracle_dequant(codes, scales, scale_dtype, N, K, group_size, n, k);
+            sum += g * w;
+            norm += fabs(g) * fabs(w);
+        }
+        dx[o] = sum;
+        if (r)
+            r[o] = norm;
+    }
+    return ORACLE_OK;
+}
+
+/* The number of OpenMP threads a parallel region would use after set_threads(nthreads). */
+int oracle_threads(int nthreads)
+{
+    set_threads(nthreads);
+#ifdef _OPENMP
+    int used = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+    }
+    return used;
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,149 @@
+"""ctypes front end of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.
+
+Inputs are CPU tensors from ``synthetic_inputs`` (activations in f32/f16/bf16,
+codes uint8 [N, K], scales f16/f32 [K/group_size, N]).  Their raw bytes are handed
+to the C code, which decodes every element to double itself.  Results are numpy
+float64 arrays: the output and the normaliser R = sum |activation|*|dequant(W)|.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import build as _build
+
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(t: torch.Tensor) -> int:
+    assert t.device.type == "cpu" and t.is_contiguous()
+    return t.data_ptr()
+
+
+class Oracle:
+    """One loaded copy of the oracle library (the default one, or a test build of it)."""
+
+    def __init__(self, path: str):
+        handle = ctypes.CDLL(path)
+        i64, vp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        for name in ("oracle_linear_fwd", "oracle_linear_bwd_input"):
+            fn = getattr(handle, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [vp, ip, i64, vp, vp, ip, i64, i64, i64, vp, vp, ip]
+        handle.oracle_dequant.restype = ctypes.c_double
+        handle.oracle_dequant.argtypes = [vp, vp, ip, i64, i64, i64, i64, i64]
+        handle.oracle_f16_to_f64.restype = ctypes.c_double
+        handle.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        handle.oracle_bf16_to_f64.restype = ctypes.c_double
+        handle.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        handle.oracle_f32_to_f64.restype = ctypes.c_double
+        handle.oracle_f32_to_f64.argtypes = [ctypes.c_uint32]
+        handle.oracle_threads.restype = ctypes.c_int
+        handle.oracle_threads.argtypes = [ctypes.c_int]
+        self.lib = handle
+        self.path = path
+
+    def _run(self, fn_name: str, act: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+             group_size: int, out_rows: int, out_cols: int, threads: int) -> Tuple[np.ndarray, np.ndarray]:
+        act = act.contiguous()
+        codes = codes.contiguous()
+        scales = scales.contiguous()
+        N, K = codes.shape
+        out = np.zeros((out_rows, out_cols), dtype=np.float64)
+        norm = np.zeros((out_rows, out_cols), dtype=np.float64)
+        status = getattr(self.lib, fn_name)(
+            _ptr(act), _DTYPE_CODE[act.dtype], act.shape[0], _ptr(codes), _ptr(scales),
+            _DTYPE_CODE[scales.dtype], N, K, group_size,
+            out.ctypes.data, norm.ctypes.data, threads)
+        if status != 0:
+            raise OracleError(f"{fn_name} returned {status}")
+        return out, norm
+
+    def linear_fwd(self, x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, group_size: int,
+                   threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """y = x . dequant(W)^T and its normaliser, both [M, N] float64."""
+        N, K = codes.shape
+        if x.dim() != 2 or x.shape[1] != K:
+            raise OracleError("x must be [M, K]")
+        return self._run("oracle_linear_fwd", x, codes, scales, group_size, x.shape[0], N, threads)
+
+    def linear_bwd_input(self, d_out: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                         group_size: int, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """d_x = d_out . dequant(W) (contracting over N) and its normaliser, both [M, K] float64."""
+        N, K = codes.shape
+        if d_out.dim() != 2 or d_out.shape[1] != N:
+            raise OracleError("d_out must be [M, N]")
+        return self._run("oracle_linear_bwd_input", d_out, codes, scales, group_size,
+                         d_out.shape[0], K, threads)
+
+    def qkv(self, x: torch.Tensor, weights: Sequence, threads: int = 0) -> List[Tuple[np.ndarray, np.ndarray]]:
+        """Three forwards of one activation: [(q, R_q), (k, R_k), (v, R_v)].
+
+        ``weights`` holds three objects with ``codes``, ``scales`` and ``group_size``
+        sharing K and group_size (the fused projection triple)."""
+        if len(weights) != 3:
+            raise OracleError("qkv takes three weights")
+        K = weights[0].codes.shape[1]
+        gs = weights[0].group_size
+        for w in weights:
+            if w.codes.shape[1] != K or w.group_size != gs:
+                raise OracleError("q, k and v weights must share K and group_size")
+        return [self.linear_fwd(x, w.codes, w.scales, w.group_size, threads) for w in weights]
+
+    def dequant(self, codes: torch.Tensor, scales: torch.Tensor, group_size: int, n: int, k: int) -> float:
+        """One element of dequant(W), as the oracle computes it."""
+        codes = codes.contiguous()
+        scales = scales.contiguous()
+        N, K = codes.shape
+        return self.lib.oracle_dequant(_ptr(codes), _ptr(scales), _DTYPE_CODE[scales.dtype], N, K,
+                                       group_size, n, k)
+
+    def f16_to_f64(self, bits: int) -> float:
+        return self.lib.oracle_f16_to_f64(bits)
+
+    def bf16_to_f64(self, bits: int) -> float:
+        return self.lib.oracle_bf16_to_f64(bits)
+
+    def f32_to_f64(self, bits: int) -> float:
+        return self.lib.oracle_f32_to_f64(bits)
+
+    def threads_used(self, threads: int = 0) -> int:
+        """OpenMP threads a call with ``threads`` would use (0 = the runtime default)."""
+        return self.lib.oracle_threads(threads)
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (built on first use when missing or stale)."""
+    global _default
+    if _default is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        _default = Oracle(path)
+    return _default
+
+
+def linear_fwd(x, codes, scales, group_size, threads=0):
+    return default().linear_fwd(x, codes, scales, group_size, threads)
+
+
+def linear_bwd_input(d_out, codes, scales, group_size, threads=0):
+    return default().linear_bwd_input(d_out, codes, scales, group_size, threads)
+
+
+def qkv(x, weights, threads=0):
+    return default().qkv(x, weights, threads)

@@ -1,0 +1,289 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` takes a loaded ``oracle.oracle.Oracle`` and raises AssertionError if
+the oracle disagrees with the fact it pins.  test_oracle.py runs them on the real
+oracle; test_oracle_mutants.py runs them on copies of oracle.c with one planted
+mistake each and checks that some pin fails.
+
+The facts:
+  * hand-worked examples (tests/golden) of the definition on the pages;
+  * the code -> value table of the dequantisation formula (tests/golden);
+  * IEEE decoding of every fp16 / bf16 bit pattern, against numpy and torch;
+  * pure-Python brute force on tiny inputs (same summation order: bitwise);
+  * numpy fp64 matmul of an explicitly dequantised matrix (<= 1e-12 R);
+  * code 8 contributes exactly zero; outputs are linear in the scales;
+  * the adjoint identity <d_out, fwd(x)> = <bwd(d_out), x>;
+  * one-hot closed forms that read back every code and scale address;
+  * QKV equals three forwards; thread-count invariance; R >= |y| with equality
+    when every term has one sign.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+
+import numpy as np
+import torch
+
+from synthetic_inputs import DTYPES, Weight, draw_activation, draw_codes, draw_scales
+from tests.conftest import ROOT, load_golden
+
+ACT_DTYPES = ("f32", "f16", "bf16")
+SCALE_DTYPES = ("f32", "f16")
+
+
+def _t(rows, dtype):
+    return torch.tensor(rows, dtype=torch.float64).to(DTYPES[dtype]).contiguous()
+
+
+def _case(seed, M, N, K, gs, act="f32", sdt="f32", s_lo=0.005, s_hi=0.02, sigma=1.0):
+    g = torch.Generator().manual_seed(seed)
+    x = draw_activation(g, M, K, act, sigma)
+    d_out = draw_activation(g, M, N, act, sigma)
+    codes = draw_codes(g, N, K)
+    scales = draw_scales(g, K // gs, N, sdt, s_lo, s_hi)
+    return x, d_out, codes, scales
+
+
+def _dense(codes, scales, gs):
+    """Explicit dequantised [N, K] float64 matrix built with numpy (a library route)."""
+    c = codes.numpy().astype(np.float64) - 8.0
+    s = scales.to(torch.float64).numpy()            # [G, N]
+    return c * np.repeat(s.T, gs, axis=1)           # [N, K]
+
+
+# ---------------------------------------------------------------------------------------------
+def pin_worked_example(o):
+    g = load_golden("worked_example_4x2.txt")
+    gs = int(g["group_size"])
+    codes = torch.tensor(g["codes"], dtype=torch.uint8)
+    for act, sdt in itertools.product(ACT_DTYPES, SCALE_DTYPES):
+        scales = _t(g["scales"], sdt)
+        y, ry = o.linear_fwd(_t(g["x"], act), codes, scales, gs)
+        assert np.array_equal(y, np.array(g["y"])), (act, sdt, y)
+        assert np.array_equal(ry, np.array(g["y_norm"])), (act, sdt, ry)
+        dx, rdx = o.linear_bwd_input(_t(g["d_out"], act), codes, scales, gs)
+        assert np.array_equal(dx, np.array(g["d_x"])), (act, sdt, dx)
+        assert np.array_equal(rdx, np.array(g["d_x_norm"])), (act, sdt, rdx)
+
+
+def pin_code_table(o):
+    pairs = []
+    with open(os.path.join(ROOT, "tests", "golden", "dequant_codes.txt")) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                pairs.append((int(c), float(v)))
+    assert len(pairs) == 16
+    codes = torch.tensor([[c for c, _ in pairs]], dtype=torch.uint8)     # N=1, K=16
+    for sdt in SCALE_DTYPES:
+        scales = torch.ones(1, 1, dtype=DTYPES[sdt])                      # gs = 16, one group
+        for k, (_, v) in enumerate(pairs):
+            assert o.dequant(codes, scales, 16, 0, k) == v
+        half = torch.full((1, 1), 0.5, dtype=DTYPES[sdt])
+        for k, (_, v) in enumerate(pairs):
+            assert o.dequant(codes, half, 16, 0, k) == v * 0.5
+
+
+def pin_decoders(o):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref16 = bits.view(np.float16).astype(np.float64)
+    refbf = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    for b in range(0, 65536, 1):
+        v = o.f16_to_f64(b)
+        r = ref16[b]
+        assert (v == r) or (math.isnan(v) and math.isnan(r)), ("f16", b, v, r)
+        v = o.bf16_to_f64(b)
+        r = refbf[b]
+        assert (v == r) or (math.isnan(v) and math.isnan(r)), ("bf16", b, v, r)
+    rng = np.random.default_rng(1)
+    specials = np.array([0, 1, 0x7FFFFF, 0x800000, 0x3F800000, 0x7F7FFFFF, 0x7F800000,
+                         0x80000001, 0xFF800000, 0x00400000], dtype=np.uint32)
+    sample = np.concatenate([specials, rng.integers(0, 2**32, 4000, dtype=np.uint64).astype(np.uint32)])
+    with np.errstate(invalid="ignore"):
+        ref32 = sample.view(np.float32).astype(np.float64)
+    for b, r in zip(sample.tolist(), ref32.tolist()):
+        v = o.f32_to_f64(b)
+        assert (v == r) or (math.isnan(v) and math.isnan(r)), ("f32", b, v, r)
+
+
+def pin_brute_force(o):
+    """Pure-Python loops on tiny inputs; k (resp. n) ascending, so equality is bitwise."""
+    seed = 10
+    for (M, N, K, gs) in [(1, 1, 8, 8), (2, 3, 8, 2), (3, 5, 12, 4), (2, 4, 16, 1), (1, 3, 24, 8),
+                          (4, 2, 6, 3)]:
+        for act, sdt in [("f32", "f32"), ("f16", "f16"), ("bf16", "f16"), ("f32", "f16")]:
+            seed += 1
+            x, d_out, codes, scales = _case(seed, M, N, K, gs, act, sdt)
+            xs, ds = x.tolist(), d_out.tolist()
+            cs, ss = codes.tolist(), scales.tolist()
+            D = [[(cs[n][k] - 8) * ss[k // gs][n] for k in range(K)] for n in range(N)]
+            y, ry = o.linear_fwd(x, codes, scales, gs)
+            dx, rdx = o.linear_bwd_input(d_out, codes, scales, gs)
+            for m in range(M):
+                for n in range(N):
+                    acc = 0.0
+                    nrm = 0.0
+                    for k in range(K):
+                        acc += xs[m][k] * D[n][k]
+                        nrm += abs(xs[m][k]) * abs(D[n][k])
+                    assert y[m, n] == acc and ry[m, n] == nrm, (M, N, K, gs, act, sdt, m, n)
+                for k in range(K):
+                    acc = 0.0
+                    nrm = 0.0
+                    for n in range(N):
+                        acc += ds[m][n] * D[n][k]
+                        nrm += abs(ds[m][n]) * abs(D[n][k])
+                    assert dx[m, k] == acc and rdx[m, k] == nrm, (M, N, K, gs, act, sdt, m, k)
+
+
+def pin_numpy_matmul(o):
+    for seed, (M, N, K, gs, act, sdt) in enumerate([(7, 33, 96, 32, "f16", "f16"),
+                                                    (5, 40, 128, 16, "bf16", "f16"),
+                                                    (3, 24, 64, 64, "f32", "f32")]):
+        x, d_out, codes, scales = _case(100 + seed, M, N, K, gs, act, sdt)
+        D = _dense(codes, scales, gs)
+        xd = x.to(torch.float64).numpy()
+        dd = d_out.to(torch.float64).numpy()
+        y, ry = o.linear_fwd(x, codes, scales, gs)
+        assert np.all(np.abs(y - xd @ D.T) <= 1e-12 * ry + 1e-300)
+        assert np.allclose(ry, np.abs(xd) @ np.abs(D).T, rtol=1e-12, atol=0)
+        dx, rdx = o.linear_bwd_input(d_out, codes, scales, gs)
+        assert np.all(np.abs(dx - dd @ D) <= 1e-12 * rdx + 1e-300)
+        assert np.allclose(rdx, np.abs(dd) @ np.abs(D), rtol=1e-12, atol=0)
+
+
+def pin_code8_zero(o):
+    x, d_out, codes, scales = _case(200, 3, 6, 32, 8, "f32", "f16")
+    eights = torch.full_like(codes, 8)
+    y, ry = o.linear_fwd(x, eights, scales, 8)
+    assert np.all(y == 0) and np.all(ry == 0)
+    dx, rdx = o.linear_bwd_input(d_out, eights, scales, 8)
+    assert np.all(dx == 0) and np.all(rdx == 0)
+    # a column of code 8 makes y blind to that activation column
+    c2 = codes.clone()
+    c2[:, 5] = 8
+    y0, _ = o.linear_fwd(x, c2, scales, 8)
+    x2 = x.clone()
+    x2[:, 5] = 1000.0
+    y1, _ = o.linear_fwd(x2, c2, scales, 8)
+    assert np.array_equal(y0, y1)
+    # a row of code 8 makes d_x blind to that output-gradient column
+    c3 = codes.clone()
+    c3[2, :] = 8
+    dx0, _ = o.linear_bwd_input(d_out, c3, scales, 8)
+    d2 = d_out.clone()
+    d2[:, 2] = -777.0
+    dx1, _ = o.linear_bwd_input(d2, c3, scales, 8)
+    assert np.array_equal(dx0, dx1)
+    # and a code other than 8 is not blind
+    y2, _ = o.linear_fwd(x2, codes, scales, 8)
+    assert not np.array_equal(y2, o.linear_fwd(x, codes, scales, 8)[0])
+
+
+def pin_scale_linearity(o):
+    x, d_out, codes, scales = _case(300, 4, 8, 64, 16, "bf16", "f16")
+    y, ry = o.linear_fwd(x, codes, scales, 16)
+    dx, rdx = o.linear_bwd_input(d_out, codes, scales, 16)
+    for p in (2.0, 0.5, 8.0):
+        s2 = (scales.to(torch.float64) * p).to(scales.dtype)
+        y2, ry2 = o.linear_fwd(x, codes, s2, 16)
+        assert np.array_equal(y2, y * p) and np.array_equal(ry2, ry * p)
+        dx2, rdx2 = o.linear_bwd_input(d_out, codes, s2, 16)
+        assert np.array_equal(dx2, dx * p) and np.array_equal(rdx2, rdx * p)
+    # additivity: s = s_a + s_b with both parts exact in fp32
+    sa = (scales.to(torch.float32) * 0.75).contiguous()
+    sb = (scales.to(torch.float32) * 0.25).contiguous()
+    s_sum = (sa + sb).contiguous()
+    ya, ra = o.linear_fwd(x, codes, sa, 16)
+    yb, _ = o.linear_fwd(x, codes, sb, 16)
+    ys, rs = o.linear_fwd(x, codes, s_sum, 16)
+    assert np.all(np.abs(ys - (ya + yb)) <= 1e-12 * rs)
+
+
+def pin_adjoint(o):
+    for seed, (M, N, K, gs, act) in enumerate([(3, 40, 64, 16, "f32"), (6, 17, 48, 8, "f16"),
+                                               (2, 64, 32, 32, "bf16")]):
+        x, d_out, codes, scales = _case(400 + seed, M, N, K, gs, act, "f16")
+        y, ry = o.linear_fwd(x, codes, scales, gs)
+        dx, _ = o.linear_bwd_input(d_out, codes, scales, gs)
+        xd = x.to(torch.float64).numpy()
+        dd = d_out.to(torch.float64).numpy()
+        lhs = float(np.sum(dd * y))
+        rhs = float(np.sum(dx * xd))
+        T = float(np.sum(np.abs(dd) * ry))
+        assert abs(lhs - rhs) <= 1e-12 * T, (lhs, rhs, T)
+
+
+def pin_one_hot(o):
+    """x = identity reads back every dequantised element: y[m, n] = (code[n, m] - 8) * scale."""
+    N, K, gs = 12, 48, 8
+    g = torch.Generator().manual_seed(500)
+    codes = draw_codes(g, N, K)
+    eye = torch.eye(K, dtype=torch.float32)
+    ones = torch.ones(K // gs, N, dtype=torch.float16)
+    y, _ = o.linear_fwd(eye, codes, ones, gs)
+    assert np.array_equal(y, (codes.numpy().astype(np.float64) - 8).T)
+    # distinct power-of-two scale per (group, n): pins the scale's row and column index
+    expo = torch.tensor([[((gi * N + n) % 13) - 6 for n in range(N)] for gi in range(K // gs)],
+                        dtype=torch.float64)
+    pscales = torch.pow(2.0, expo).to(torch.float16)
+    y, _ = o.linear_fwd(eye, codes, pscales, gs)
+    for m in range(K):
+        for n in range(N):
+            want = (int(codes[n, m]) - 8) * 2.0 ** (((m // gs) * N + n) % 13 - 6)
+            assert y[m, n] == want, (m, n, y[m, n], want)
+    # one-hot output gradients read back rows: d_x[m, k] = dequant(W[m, k])
+    eyeN = torch.eye(N, dtype=torch.bfloat16)
+    dx, _ = o.linear_bwd_input(eyeN, codes, pscales, gs)
+    for m in range(N):
+        for k in range(K):
+            want = (int(codes[m, k]) - 8) * 2.0 ** (((k // gs) * N + m) % 13 - 6)
+            assert dx[m, k] == want, (m, k, dx[m, k], want)
+
+
+def pin_qkv(o):
+    g = torch.Generator().manual_seed(600)
+    x = draw_activation(g, 5, 64, "f16")
+    ws = [Weight(draw_codes(g, n, 64), draw_scales(g, 2, n, "f16", 0.002, 0.02), 32) for n in (32, 8, 8)]
+    outs = o.qkv(x, ws)
+    for (yo, ro), w in zip(outs, ws):
+        y, r = o.linear_fwd(x, w.codes, w.scales, 32)
+        assert np.array_equal(yo, y) and np.array_equal(ro, r)
+    # the triple equals one forward over the row-stacked weight
+    cat_codes = torch.cat([w.codes for w in ws], dim=0)
+    cat_scales = torch.cat([w.scales for w in ws], dim=1).contiguous()
+    y, _ = o.linear_fwd(x, cat_codes, cat_scales, 32)
+    assert np.array_equal(np.concatenate([yo for yo, _ in outs], axis=1), y)
+
+
+def pin_threads(o):
+    x, d_out, codes, scales = _case(700, 9, 37, 64, 16, "f16", "f16")
+    a = o.linear_fwd(x, codes, scales, 16, threads=1)
+    b = o.linear_fwd(x, codes, scales, 16, threads=3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    a = o.linear_bwd_input(d_out, codes, scales, 16, threads=1)
+    b = o.linear_bwd_input(d_out, codes, scales, 16, threads=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def pin_normaliser(o):
+    x, d_out, codes, scales = _case(800, 4, 10, 32, 8, "f32", "f32")
+    y, ry = o.linear_fwd(x, codes, scales, 8)
+    assert np.all(ry >= np.abs(y))
+    dx, rdx = o.linear_bwd_input(d_out, codes, scales, 8)
+    assert np.all(rdx >= np.abs(dx))
+    # one sign everywhere: x >= 0, code >= 8, scale > 0 gives R == y exactly
+    xp = x.abs().contiguous()
+    cp = (codes % 8 + 8).to(torch.uint8).contiguous()
+    y, ry = o.linear_fwd(xp, cp, scales, 8)
+    assert np.array_equal(y, ry)
+    dp = d_out.abs().contiguous()
+    dx, rdx = o.linear_bwd_input(dp, cp, scales, 8)
+    assert np.array_equal(dx, rdx)
+
+
+PINS = [pin_worked_example, pin_code_table, pin_decoders, pin_brute_force, pin_numpy_matmul,
+        pin_code8_zero, pin_scale_linearity, pin_adjoint, pin_one_hot, pin_qkv, pin_threads,
+        pin_normaliser]

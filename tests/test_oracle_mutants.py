@@ -1,0 +1,50 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case copies oracle.c, plants one mistake in the copy (a dropped term, a wrong
+sign, offset or index, a transposed operand, a broken IEEE decode), builds it with
+gcc on the CPU and checks that at least one pin of tests/oracle_pins.py fails on
+it.  The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+from oracle import build as oracle_build
+from oracle.oracle import Oracle
+from tests import oracle_pins
+
+MUTANTS = {
+    "zero_point_7": ("(double)(code - 8)", "(double)(code - 7)"),
+    "sign_flip": ("(double)(code - 8)", "(double)(8 - code)"),
+    "scale_transposed": ("group * N + n", "n * (K / group_size) + group"),
+    "group_modulo": ("int64_t group = k / group_size;", "int64_t group = k % (K / group_size);"),
+    "fwd_k_reversed": ("element(x, act_dtype, m * K + k)", "element(x, act_dtype, m * K + (K - 1 - k))"),
+    "bwd_n_reversed": ("element(d_out, act_dtype, m * N + n)", "element(d_out, act_dtype, m * N + (N - 1 - n))"),
+    "fwd_first_term_dropped": ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 1; k < K; ++k) {"),
+    "bwd_first_term_dropped": ("for (int64_t n = 0; n < N; ++n) {", "for (int64_t n = 1; n < N; ++n) {"),
+    "fwd_norm_signed": ("norm += fabs(a) * fabs(w);", "norm += a * w;"),
+    "bwd_norm_signed": ("norm += fabs(g) * fabs(w);", "norm += fabs(g) * w;"),
+    "f16_exponent_bias": ("exponent - 25", "exponent - 24"),
+    "f16_subnormal": ("ldexp((double)fraction, -24)", "ldexp((double)fraction, -25)"),
+    "bf16_hidden_bit": ("(fraction | 0x80)", "(fraction | 0x100)"),
+    "f32_exponent_bias": ("exponent - 150", "exponent - 149"),
+    "threads_reorder": ("int64_t m = o / N, n = o % N;", "int64_t m = o % M, n = o / M;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle_build.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutant_src = tmp_path / "oracle_mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle_build.build(src=str(mutant_src), out=str(tmp_path / f"liboracle_{name}.so"))
+    o = Oracle(lib)
+    failed = []
+    for pin in oracle_pins.PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
