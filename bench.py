@@ -1,0 +1,261 @@
+"""Benchmark of the q4gsw hot path on one MI355X.
+
+One step = one pass of every op of the Llama-3.2-1B-shaped q4gsw suite, each on its own
+seeded synthetic inputs already resident in HBM:
+  decode   forward       M=1,   K=2048, N=8192, gs=32,  fp16 x, fp16 scales
+  prefill  forward       M=512, K=8192, N=2048, gs=128, bf16 x, fp16 scales
+  qkv      fused QKV     M in {128, 508, 512}, K=2048, N=2048+512+512, gs=32, fp16 x
+  bwd      input grad    M=512, N=8192, K=2048, gs=128, fp32 d_out ~ N(0, 0.1)
+Outputs are fp32.  Several copies of every weight and activation are rotated so the
+working set exceeds the 256 MB Infinity Cache and the weight stream comes from HBM.
+
+Prints one JSON line: whole-step TFLOP/s, per-op TFLOP/s and weight GB/s with their
+roofline fractions, the roofline object of the dominant op (HIP-event timing on the
+launch stream) and the fp64 CPU oracle timed on a bounded sample of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense fp16 / bf16 MFMA
+MALL_BYTES = 256 << 20
+METRIC = "q4gsw linear TFLOP/s + weight GB/s (decode, prefill, QKV, bwd) vs roofline"
+QKV_MS = (128, 508, 512)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--ops", default="decode,prefill,qkv,bwd", help="comma-separated subset of the step")
+    p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=32, help="rows per M=512 op in the oracle sample")
+    return p.parse_args()
+
+
+class Op:
+    """One op of the step: its inputs (several rotated copies), flops and algorithmic bytes."""
+
+    def __init__(self, name, kind, case, q, sets):
+        import torch
+        self.name, self.kind, self.case = name, kind, case
+        ws = case.weights
+        self.M = case.M
+        N = sum(w.N for w in ws)
+        K = ws[0].K
+        self.flops = 2.0 * self.M * N * K
+        act = case.x if case.x is not None else case.d_out
+        w_bytes = sum(w.N * w.K / 2 + w.scales.numel() * w.scales.element_size() for w in ws)
+        self.weight_bytes = w_bytes
+        out_elems = self.M * (K if kind == "bwd" else N)
+        self.bytes = w_bytes + act.numel() * act.element_size() + 4.0 * out_elems
+        self.sets = []
+        for s in range(sets):
+            pw = [q.pack(w.codes.cuda(), w.scales.cuda(), w.group_size) for w in ws]
+            a = act.cuda()
+            if kind == "bwd":
+                outs = (torch.empty(self.M, K, dtype=torch.float32, device="cuda"),)
+            else:
+                outs = tuple(torch.empty(self.M, w.N, dtype=torch.float32, device="cuda") for w in ws)
+            self.sets.append((pw, a, outs))
+        pw0 = self.sets[0][0]
+        if kind == "qkv":
+            need = q.qkv_workspace_bytes(pw0[0], pw0[1], pw0[2], self.M, act.dtype)
+            self.route = q.route(q.OP_QKV, pw0[0], self.M, act.dtype)
+        elif kind == "bwd":
+            need = q.workspace_bytes(q.OP_BWD_INPUT, pw0[0], self.M, act.dtype)
+            self.route = q.route(q.OP_BWD_INPUT, pw0[0], self.M, act.dtype)
+        else:
+            need = q.workspace_bytes(q.OP_FWD, pw0[0], self.M, act.dtype)
+            self.route = q.route(q.OP_FWD, pw0[0], self.M, act.dtype)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.set_bytes = sum(p.buffer.numel() for p in pw0) + act.numel() * act.element_size()
+        self.bound = "hbm" if self.flops / self.bytes < MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+
+    def run(self, q, i):
+        pw, a, outs = self.sets[i % len(self.sets)]
+        if self.kind == "qkv":
+            q.qkv_fused(pw[0], pw[1], pw[2], a, outs=outs, workspace=self.ws)
+        elif self.kind == "bwd":
+            q.linear_bwd_input(pw[0], a, out=outs[0], workspace=self.ws)
+        else:
+            q.linear_fwd(pw[0], a, out=outs[0], workspace=self.ws)
+
+
+def build_ops(q, names, rotate):
+    from synthetic_inputs import make_workload
+    specs = []
+    for n in names:
+        if n == "decode":
+            specs.append(("decode", "fwd", make_workload("decode")))
+        elif n == "prefill":
+            specs.append(("prefill", "fwd", make_workload("prefill")))
+        elif n == "qkv":
+            for M in QKV_MS:
+                specs.append((f"qkv_m{M}", "qkv", make_workload("qkv", M=M)))
+        elif n == "bwd":
+            specs.append(("bwd", "bwd", make_workload("bwd")))
+        else:
+            raise SystemExit(f"unknown op {n}")
+    if rotate <= 0:
+        one = 0
+        for _, kind, case in specs:
+            act = case.x if case.x is not None else case.d_out
+            one += sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights)
+            one += act.numel() * act.element_size()
+        rotate = max(2, int(MALL_BYTES * 1.5 // one) + 1)
+    return [Op(n, k, c, q, rotate) for n, k, c in specs], rotate
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_group_quantized_q4gsw_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(op_name, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(op_name)
+    if not ent or ent.get("src_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(ops, rows_per_op):
+    """The fp64 oracle (as it stands) on a bounded sample of the step: the first rows of each op."""
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
+    used = O.default().threads_used(threads)
+    flops = 0.0
+    parts = []
+    t0 = time.perf_counter()
+    for op in ops:
+        c = op.case
+        rows = min(op.M, rows_per_op)
+        if op.kind == "bwd":
+            d = c.d_out[:rows].contiguous()
+            O.linear_bwd_input(d, c.w.codes, c.w.scales, c.w.group_size, threads=threads)
+            flops += 2.0 * rows * c.w.N * c.w.K
+        else:
+            x = c.x[:rows].contiguous()
+            for w in c.weights:
+                O.linear_fwd(x, w.codes, w.scales, w.group_size, threads=threads)
+                flops += 2.0 * rows * w.N * w.K
+        parts.append(f"{op.name}:{rows}/{op.M} rows")
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": "fp64 oracle on the first rows of each op (" + ", ".join(parts) +
+                      f"); {flops / 1e9:.2f} GFLOP in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_group_quantized_q4gsw_amd as q
+    torch.cuda.set_device(0)
+    names = [n.strip() for n in args.ops.split(",") if n.strip()]
+    ops, rotate = build_ops(q, names, args.rotate)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        for op in ops:
+            op.run(q, i)
+    torch.cuda.synchronize()
+
+    ev = {op.name: [] for op in ops}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        for op in ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            op.run(q, args.warmup + i)
+            b.record()
+            ev[op.name].append((a, b))
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    per_op = {}
+    total_flops = 0.0
+    for op in ops:
+        ms = sum(a.elapsed_time(b) for a, b in ev[op.name]) / args.steps
+        s = ms / 1e3
+        tflops = op.flops / s / 1e12
+        gbs = op.bytes / s / 1e9
+        wgbs = op.weight_bytes / s / 1e9
+        frac = gbs / HBM_PEAK_GBS if op.bound == "hbm" else tflops / MFMA_PEAK_TFLOPS
+        per_op[op.name] = {"ms": round(ms, 5), "tflops": round(tflops, 2), "weight_gbs": round(wgbs, 1),
+                           "alg_gbs": round(gbs, 1), "bound": op.bound, "roofline_frac": round(frac, 4),
+                           "route": op.route, "M": op.M}
+        total_flops += op.flops
+
+    dom = max(ops, key=lambda o: per_op[o.name]["ms"])
+    d = per_op[dom.name]
+    src = source_hash()
+    if dom.bound == "hbm":
+        roof = {"bound": "hbm", "achieved": d["alg_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(d["alg_gbs"] / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(d["tflops"] / MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = traffic_for(dom.name, src)
+    roof["op"] = dom.name
+    roof["route"] = dom.route
+    roof["per_launch_ms"] = d["ms"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(total_flops / (ms_step / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4 weights; f16/bf16 MFMA (f32 x: bf16 hi+lo); f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "llama-3.2-1b q4gsw step: " + ", ".join(
+            f"{o.name} M{o.M} route={o.route}" for o in ops), "ops": names, "rotated_sets": rotate,
+            "wall_s": round(wall, 3), "src_hash": src},
+        "per_op": per_op,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(ops, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

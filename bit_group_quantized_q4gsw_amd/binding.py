@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libq4gsw.so (include/q4gsw.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory (output and workspace
+tensors) and the current HIP stream.  There is no CPU fallback: importing the
+package without the built library raises.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4gsw.so")
+
+F32, F16, BF16 = 0, 1, 2
+OP_FWD, OP_BWD_INPUT, OP_QKV = 0, 1, 2
+ROUTES = {
+    "none": 0, "generic": 1, "gemv": 2, "gemm_fold": 3, "gemm_group": 4, "gemm_split": 5,
+    "bwd_gemv": 6, "bwd_fold": 7, "bwd_split": 8, "qkv_fused": 9,
+}
+FLAG_FOLD_F16 = 1
+_TORCH_DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+
+class Q4gswError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class WeightDesc(ctypes.Structure):
+    """Mirror of struct q4gsw_weight."""
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+        ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("group_size", ctypes.c_int64),
+        ("n_pad", ctypes.c_int64), ("k_pad", ctypes.c_int64), ("g_pad", ctypes.c_int64),
+        ("scale_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("data", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
+        ("nibble_offset", ctypes.c_uint64), ("scale_offset", ctypes.c_uint64),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with bit_group_quantized_q4gsw_amd/build.py "
+                              "(or __graft_entry__.build()); there is no CPU fallback")
+        h = ctypes.CDLL(LIB_PATH)
+        i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+        pw = ctypes.POINTER(WeightDesc)
+        sigs = {
+            "q4gsw_packed_bytes": [i64, i64, i64, i32, ctypes.POINTER(u64)],
+            "q4gsw_pack": [vp, vp, i32, i64, i64, i64, vp, u64, vp, pw],
+            "q4gsw_unpack": [pw, vp, vp, vp],
+            "q4gsw_workspace_bytes": [i32, pw, i64, i32, ctypes.POINTER(u64)],
+            "q4gsw_qkv_workspace_bytes": [pw, pw, pw, i64, i32, ctypes.POINTER(u64)],
+            "q4gsw_linear_fwd": [pw, vp, i32, i64, vp, vp, u64, vp],
+            "q4gsw_linear_bwd_input": [pw, vp, i32, i64, vp, vp, u64, vp],
+            "q4gsw_qkv_fused": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, vp],
+            "q4gsw_route": [i32, pw, i64, i32],
+        }
+        for name, args in sigs.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int32
+        h.q4gsw_route_name.argtypes = [i32]
+        h.q4gsw_route_name.restype = ctypes.c_char_p
+        h.q4gsw_status_str.argtypes = [i32]
+        h.q4gsw_status_str.restype = ctypes.c_char_p
+        h.q4gsw_force_route.argtypes = [i32]
+        h.q4gsw_force_route.restype = None
+        h.q4gsw_layout_version.argtypes = []
+        h.q4gsw_layout_version.restype = ctypes.c_uint32
+        h.q4gsw_build_info.argtypes = []
+        h.q4gsw_build_info.restype = ctypes.c_char_p
+        _lib = h
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().q4gsw_status_str(status).decode()
+
+
+def route_name(route: int) -> str:
+    return lib().q4gsw_route_name(route).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise Q4gswError(status, what)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.contiguous()
+
+
+class PackedWeight:
+    """A packed q4gsw weight: the descriptor plus the device buffer it points into."""
+
+    def __init__(self, desc: WeightDesc, buffer: torch.Tensor):
+        self.desc = desc
+        self.buffer = buffer
+
+    @property
+    def N(self) -> int:
+        return self.desc.N
+
+    @property
+    def K(self) -> int:
+        return self.desc.K
+
+    @property
+    def group_size(self) -> int:
+        return self.desc.group_size
+
+    @property
+    def foldable(self) -> bool:
+        return bool(self.desc.flags & FLAG_FOLD_F16)
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def packed_bytes(N: int, K: int, group_size: int, scale_dtype: torch.dtype) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().q4gsw_packed_bytes(N, K, group_size, _TORCH_DTYPE[scale_dtype], ctypes.byref(out)),
+           "q4gsw_packed_bytes")
+    return out.value
+
+
+def pack(codes: torch.Tensor, scales: torch.Tensor, group_size: int) -> PackedWeight:
+    """codes uint8 [N, K] (0..15) and scales [K/group_size, N] (fp16/fp32), both on the GPU."""
+    codes = _dev(codes, "codes")
+    scales = _dev(scales, "scales")
+    if codes.dtype != torch.uint8 or codes.dim() != 2:
+        raise ValueError("codes must be uint8 [N, K]")
+    N, K = codes.shape
+    if scales.dtype not in (torch.float16, torch.float32):
+        raise ValueError("scales must be fp16 or fp32")
+    if group_size < 1 or K % group_size or tuple(scales.shape) != (K // group_size, N):
+        raise ValueError("scales must be [K / group_size, N]")
+    nbytes = packed_bytes(N, K, group_size, scales.dtype)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    desc = WeightDesc()
+    _check(lib().q4gsw_pack(codes.data_ptr(), scales.data_ptr(), _TORCH_DTYPE[scales.dtype], N, K, group_size,
+                            buf.data_ptr(), nbytes, _stream(), ctypes.byref(desc)), "q4gsw_pack")
+    return PackedWeight(desc, buf)
+
+
+def unpack(w: PackedWeight) -> Tuple[torch.Tensor, torch.Tensor]:
+    dev = w.buffer.device
+    codes = torch.empty(w.N, w.K, dtype=torch.uint8, device=dev)
+    sdt = torch.float16 if w.desc.scale_dtype == F16 else torch.float32
+    scales = torch.empty(w.K // w.group_size, w.N, dtype=sdt, device=dev)
+    _check(lib().q4gsw_unpack(w.ref(), codes.data_ptr(), scales.data_ptr(), _stream()), "q4gsw_unpack")
+    return codes, scales
+
+
+def _workspace(nbytes: int, device) -> Tuple[Optional[torch.Tensor], int, int]:
+    if nbytes == 0:
+        return None, 0, 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.data_ptr(), nbytes
+
+
+def workspace_bytes(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().q4gsw_workspace_bytes(op, w.ref(), M, _TORCH_DTYPE[dtype], ctypes.byref(out)),
+           "q4gsw_workspace_bytes")
+    return out.value
+
+
+def linear_fwd(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M, N] fp32 = x [M, K] . dequant(W)^T."""
+    x = _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    y = out if out is not None else torch.empty(M, w.N, dtype=torch.float32, device=x.device)
+    need = workspace_bytes(OP_FWD, w, M, x.dtype)
+    if workspace is not None and workspace.numel() >= need:
+        ws, wp, wb = workspace, workspace.data_ptr(), workspace.numel()
+    else:
+        ws, wp, wb = _workspace(need, x.device)
+    _check(lib().q4gsw_linear_fwd(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), wp, wb,
+                                  _stream()), "q4gsw_linear_fwd")
+    return y
+
+
+def linear_bwd_input(w: PackedWeight, d_out: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """d_x [M, K] fp32 = d_out [M, N] . dequant(W), contracting over N."""
+    d_out = _dev(d_out, "d_out")
+    if d_out.dim() != 2 or d_out.shape[1] != w.N:
+        raise ValueError("d_out must be [M, N]")
+    M = d_out.shape[0]
+    dx = out if out is not None else torch.empty(M, w.K, dtype=torch.float32, device=d_out.device)
+    need = workspace_bytes(OP_BWD_INPUT, w, M, d_out.dtype)
+    if workspace is not None and workspace.numel() >= need:
+        ws, wp, wb = workspace, workspace.data_ptr(), workspace.numel()
+    else:
+        ws, wp, wb = _workspace(need, d_out.device)
+    _check(lib().q4gsw_linear_bwd_input(w.ref(), d_out.data_ptr(), _TORCH_DTYPE[d_out.dtype], M, dx.data_ptr(),
+                                        wp, wb, _stream()), "q4gsw_linear_bwd_input")
+    return dx
+
+
+def qkv_workspace_bytes(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, M: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().q4gsw_qkv_workspace_bytes(wq.ref(), wk.ref(), wv.ref(), M, _TORCH_DTYPE[dtype],
+                                           ctypes.byref(out)), "q4gsw_qkv_workspace_bytes")
+    return out.value
+
+
+def qkv_fused(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, x: torch.Tensor,
+              outs: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(q, k, v) fp32 = x . dequant(Wq)^T, x . dequant(Wk)^T, x . dequant(Wv)^T in one call."""
+    x = _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != wq.K:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    if outs is None:
+        outs = tuple(torch.empty(M, w.N, dtype=torch.float32, device=x.device) for w in (wq, wk, wv))
+    need = qkv_workspace_bytes(wq, wk, wv, M, x.dtype)
+    if workspace is not None and workspace.numel() >= need:
+        ws, wp, wb = workspace, workspace.data_ptr(), workspace.numel()
+    else:
+        ws, wp, wb = _workspace(need, x.device)
+    q, k, v = outs
+    _check(lib().q4gsw_qkv_fused(wq.ref(), wk.ref(), wv.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M,
+                                 q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, wb, _stream()), "q4gsw_qkv_fused")
+    return q, k, v
+
+
+def route(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> str:
+    return route_name(lib().q4gsw_route(op, w.ref(), M, _TORCH_DTYPE[dtype]))
+
+
+@contextlib.contextmanager
+def forced_route(name: str):
+    """Force every call inside the block onto one route family (tests and benchmarks)."""
+    lib().q4gsw_force_route(ROUTES[name])
+    try:
+        yield
+    finally:
+        lib().q4gsw_force_route(0)
+
+
+def build_info() -> str:
+    return lib().q4gsw_build_info().decode()

@@ -1,0 +1,465 @@
+// C-ABI front end of the q4gsw library: validation, route selection and launches.
+//
+// Validation runs on the host before any HIP call, so every error path can be
+// exercised without a GPU.  Route selection follows the pages' pattern of a
+// geometry predicate with a fallback to the ordinary route (WebGPU BK64 QKV PR
+// body) and of route attestation for test harnesses (the WebGPU SDPA routing PR
+// body in the same stack): q4gsw_route reports the route a call takes.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/q4gsw.h"
+#include "internal.h"
+
+using namespace q4gsw;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxM = int64_t(1) << 23;
+
+std::atomic<int32_t> g_forced_route{Q4GSW_ROUTE_NONE};
+
+int esize(int32_t dt) { return dt == Q4GSW_F32 ? 4 : 2; }
+bool act_dtype_ok(int32_t dt) { return dt == Q4GSW_F32 || dt == Q4GSW_F16 || dt == Q4GSW_BF16; }
+bool scale_dtype_ok(int32_t dt) { return dt == Q4GSW_F32 || dt == Q4GSW_F16; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+Range range_of(const void* p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+q4gsw_status check_desc(const q4gsw_weight* w) {
+    if (!w) return Q4GSW_E_NULL;
+    if (w->magic != Q4GSW_MAGIC || w->version != Q4GSW_LAYOUT_VERSION) return Q4GSW_E_DESC;
+    if (w->N < 1 || w->K < 1 || w->N > kMaxDim || w->K > kMaxDim || w->group_size < 1 ||
+        w->K % w->group_size != 0)
+        return Q4GSW_E_DESC;
+    if (!scale_dtype_ok(w->scale_dtype)) return Q4GSW_E_DESC;
+    const Layout L = make_layout(w->N, w->K, w->group_size, esize(w->scale_dtype));
+    if (w->n_pad != L.n_pad || w->k_pad != L.k_pad || w->g_pad != L.g_pad || w->nibble_offset != L.nibble_offset ||
+        w->scale_offset != L.scale_offset || w->bytes < L.total)
+        return Q4GSW_E_DESC;
+    if (!w->data) return Q4GSW_E_NULL;
+    return Q4GSW_OK;
+}
+
+WView view_of(const q4gsw_weight* w) {
+    WView v;
+    v.nib = static_cast<const uint8_t*>(w->data) + w->nibble_offset;
+    v.scales = static_cast<const uint8_t*>(w->data) + w->scale_offset;
+    v.scale_f16 = w->scale_dtype == Q4GSW_F16;
+    v.N = w->N;
+    v.K = w->K;
+    v.gs = w->group_size;
+    v.n_pad = w->n_pad;
+    v.k_pad = w->k_pad;
+    v.g_pad = w->g_pad;
+    return v;
+}
+
+bool fold_ok(const q4gsw_weight* w) { return (w->flags & Q4GSW_FLAG_FOLD_F16) != 0; }
+
+enum Kind { kGeneric, kSmallM, kMfma };
+
+Kind route_kind(int32_t route) {
+    switch (route) {
+        case Q4GSW_ROUTE_GENERIC: return kGeneric;
+        case Q4GSW_ROUTE_GEMV:
+        case Q4GSW_ROUTE_BWD_GEMV: return kSmallM;
+        default: return kMfma;
+    }
+}
+
+// Route of a forward (or QKV) call; Q4GSW_ROUTE_NONE with *err set when a forced route cannot serve it.
+int32_t pick_fwd(const q4gsw_weight* w, int64_t M, int32_t dt, bool qkv, q4gsw_status* err) {
+    const WView v = view_of(w);
+    const bool small_ok = M <= 8 && w->group_size % 8 == 0;
+    const bool mfma_ok = gemm_fwd_supported(v, dt, fold_ok(w));
+    auto mfma_route = [&]() -> int32_t {
+        if (qkv) return Q4GSW_ROUTE_QKV_FUSED;
+        if (dt == Q4GSW_F32) return Q4GSW_ROUTE_GEMM_SPLIT;
+        if (dt == Q4GSW_F16 && w->scale_dtype == Q4GSW_F16 && fold_ok(w)) return Q4GSW_ROUTE_GEMM_FOLD;
+        return Q4GSW_ROUTE_GEMM_GROUP;
+    };
+    *err = Q4GSW_OK;
+    const int32_t forced = g_forced_route.load(std::memory_order_relaxed);
+    if (forced != Q4GSW_ROUTE_NONE) {
+        switch (route_kind(forced)) {
+            case kGeneric: return Q4GSW_ROUTE_GENERIC;
+            case kSmallM:
+                if (small_ok) return Q4GSW_ROUTE_GEMV;
+                break;
+            case kMfma:
+                if (mfma_ok) return mfma_route();
+                break;
+        }
+        *err = Q4GSW_E_ROUTE;
+        return Q4GSW_ROUTE_NONE;
+    }
+    if (small_ok) return Q4GSW_ROUTE_GEMV;
+    if (mfma_ok) return mfma_route();
+    return Q4GSW_ROUTE_GENERIC;
+}
+
+int32_t pick_bwd(const q4gsw_weight* w, int64_t M, int32_t dt, q4gsw_status* err) {
+    const WView v = view_of(w);
+    const bool small_ok = M <= 8 && w->group_size % 8 == 0;
+    const bool mfma_ok = gemm_bwd_supported(v, dt, fold_ok(w));
+    const bool fold = dt == Q4GSW_F16 && w->scale_dtype == Q4GSW_F16 && fold_ok(w);
+    const int32_t mfma_route = fold ? Q4GSW_ROUTE_BWD_FOLD : Q4GSW_ROUTE_BWD_SPLIT;
+    *err = Q4GSW_OK;
+    const int32_t forced = g_forced_route.load(std::memory_order_relaxed);
+    if (forced != Q4GSW_ROUTE_NONE) {
+        switch (route_kind(forced)) {
+            case kGeneric: return Q4GSW_ROUTE_GENERIC;
+            case kSmallM:
+                if (small_ok) return Q4GSW_ROUTE_BWD_GEMV;
+                break;
+            case kMfma:
+                if (mfma_ok) return mfma_route;
+                break;
+        }
+        *err = Q4GSW_E_ROUTE;
+        return Q4GSW_ROUTE_NONE;
+    }
+    if (small_ok) return Q4GSW_ROUTE_BWD_GEMV;
+    if (mfma_ok) return mfma_route;
+    return Q4GSW_ROUTE_GENERIC;
+}
+
+uint64_t fwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t route) {
+    const WView v = view_of(w);
+    if (route == Q4GSW_ROUTE_GEMV) {
+        const int s = gemv_fwd_splits(v, M);
+        return s > 1 ? (uint64_t)s * M * v.n_pad * 4 : 0;
+    }
+    if (route == Q4GSW_ROUTE_GEMM_FOLD || route == Q4GSW_ROUTE_GEMM_GROUP || route == Q4GSW_ROUTE_GEMM_SPLIT) {
+        FwdSeg seg{v, nullptr};
+        return (uint64_t)plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M).ws_bytes;
+    }
+    return 0;
+}
+
+uint64_t bwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t route) {
+    const WView v = view_of(w);
+    if (route == Q4GSW_ROUTE_BWD_GEMV) {
+        const int s = gemv_bwd_splits(v, M);
+        return s > 1 ? (uint64_t)s * M * v.k_pad * 4 : 0;
+    }
+    if (route == Q4GSW_ROUTE_BWD_FOLD || route == Q4GSW_ROUTE_BWD_SPLIT)
+        return (uint64_t)plan_gemm_bwd(v, dt, fold_ok(w), M).ws_bytes;
+    return 0;
+}
+
+q4gsw_status check_qkv_descs(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv) {
+    q4gsw_status st;
+    if ((st = check_desc(wq)) != Q4GSW_OK) return st;
+    if ((st = check_desc(wk)) != Q4GSW_OK) return st;
+    if ((st = check_desc(wv)) != Q4GSW_OK) return st;
+    const q4gsw_weight* ws[3] = {wq, wk, wv};
+    for (int i = 1; i < 3; ++i) {
+        if (ws[i]->K != wq->K || ws[i]->group_size != wq->group_size || ws[i]->scale_dtype != wq->scale_dtype ||
+            fold_ok(ws[i]) != fold_ok(wq))
+            return Q4GSW_E_DESC;
+    }
+    return Q4GSW_OK;
+}
+
+uint64_t qkv_ws_bytes(const q4gsw_weight* const w[3], int64_t M, int32_t dt, int32_t route) {
+    if (route == Q4GSW_ROUTE_QKV_FUSED) {
+        FwdSeg segs[3];
+        for (int i = 0; i < 3; ++i) segs[i] = FwdSeg{view_of(w[i]), nullptr};
+        return (uint64_t)plan_gemm_fwd(segs, 3, dt, fold_ok(w[0]), M).ws_bytes;
+    }
+    uint64_t b = 0;
+    for (int i = 0; i < 3; ++i) {
+        const uint64_t x = fwd_ws_bytes(w[i], M, dt, route);
+        b = x > b ? x : b;
+    }
+    return b;
+}
+
+q4gsw_status hip_status(hipError_t e) { return e == hipSuccess ? Q4GSW_OK : Q4GSW_E_HIP; }
+
+q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M, float* y, void* ws,
+                     int32_t route, hipStream_t s) {
+    const WView v = view_of(w);
+    switch (route) {
+        case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_fwd(v, x, dt, M, y, s));
+        case Q4GSW_ROUTE_GEMV: {
+            const int splits = gemv_fwd_splits(v, M);
+            if (splits == 1) return hip_status(launch_gemv_fwd(v, x, dt, M, y, 1, s));
+            float* part = static_cast<float*>(ws);
+            hipError_t e = launch_gemv_fwd(v, x, dt, M, part, splits, s);
+            if (e == hipSuccess) e = launch_reduce_splits(part, splits, M, v.N, v.n_pad, y, v.N, s);
+            return hip_status(e);
+        }
+        default: {
+            FwdSeg seg{v, y};
+            const FwdPlan plan = plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M);
+            return hip_status(launch_gemm_fwd(&seg, 1, x, dt, M, plan, static_cast<float*>(ws), s));
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+q4gsw_status q4gsw_packed_bytes(int64_t N, int64_t K, int64_t group_size, int32_t scale_dtype, uint64_t* bytes) {
+    if (!bytes) return Q4GSW_E_NULL;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return Q4GSW_E_SHAPE;
+    if (group_size < 1 || K % group_size != 0) return Q4GSW_E_GROUP;
+    if (!scale_dtype_ok(scale_dtype)) return Q4GSW_E_DTYPE;
+    *bytes = make_layout(N, K, group_size, esize(scale_dtype)).total;
+    return Q4GSW_OK;
+}
+
+q4gsw_status q4gsw_pack(const uint8_t* codes, const void* scales, int32_t scale_dtype, int64_t N, int64_t K,
+                        int64_t group_size, void* packed, uint64_t packed_bytes, void* stream, q4gsw_weight* out) {
+    if (!codes || !scales || !packed || !out) return Q4GSW_E_NULL;
+    uint64_t need = 0;
+    q4gsw_status st = q4gsw_packed_bytes(N, K, group_size, scale_dtype, &need);
+    if (st != Q4GSW_OK) return st;
+    if (packed_bytes < need) return Q4GSW_E_BUFFER;
+    const Range pr = range_of(packed, need);
+    if (overlap(pr, range_of(codes, (uint64_t)N * K)) ||
+        overlap(pr, range_of(scales, (uint64_t)(K / group_size) * N * esize(scale_dtype))))
+        return Q4GSW_E_ALIAS;
+    const Layout L = make_layout(N, K, group_size, esize(scale_dtype));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_pack(codes, scales, scale_dtype == Q4GSW_F16, N, K, group_size, L,
+                               static_cast<uint8_t*>(packed), s);
+    uint32_t hdr[2] = {0u, 0u};
+    if (e == hipSuccess) e = hipMemcpyAsync(hdr, packed, sizeof(hdr), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return Q4GSW_E_HIP;
+    if (hdr[kHdrBadCode]) return Q4GSW_E_CODE_RANGE;
+    q4gsw_weight w;
+    std::memset(&w, 0, sizeof(w));
+    w.magic = Q4GSW_MAGIC;
+    w.version = Q4GSW_LAYOUT_VERSION;
+    w.N = N;
+    w.K = K;
+    w.group_size = group_size;
+    w.n_pad = L.n_pad;
+    w.k_pad = L.k_pad;
+    w.g_pad = L.g_pad;
+    w.scale_dtype = scale_dtype;
+    w.flags = (scale_dtype == Q4GSW_F16 && !hdr[kHdrNoFold]) ? Q4GSW_FLAG_FOLD_F16 : 0u;
+    w.data = packed;
+    w.bytes = L.total;
+    w.nibble_offset = L.nibble_offset;
+    w.scale_offset = L.scale_offset;
+    *out = w;
+    return Q4GSW_OK;
+}
+
+q4gsw_status q4gsw_unpack(const q4gsw_weight* w, uint8_t* codes, void* scales, void* stream) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!codes || !scales) return Q4GSW_E_NULL;
+    const Range wr = range_of(w->data, w->bytes);
+    const Range cr = range_of(codes, (uint64_t)w->N * w->K);
+    const Range sr = range_of(scales, (uint64_t)(w->K / w->group_size) * w->N * esize(w->scale_dtype));
+    if (overlap(wr, cr) || overlap(wr, sr) || overlap(cr, sr)) return Q4GSW_E_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_unpack(view_of(w), codes, scales, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return hip_status(e);
+}
+
+q4gsw_status q4gsw_workspace_bytes(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype, uint64_t* bytes) {
+    if (!bytes) return Q4GSW_E_NULL;
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(act_dtype)) return Q4GSW_E_DTYPE;
+    if (op == Q4GSW_OP_FWD) {
+        const int32_t r = pick_fwd(w, M, act_dtype, false, &st);
+        if (st != Q4GSW_OK) return st;
+        *bytes = fwd_ws_bytes(w, M, act_dtype, r);
+        return Q4GSW_OK;
+    }
+    if (op == Q4GSW_OP_BWD_INPUT) {
+        const int32_t r = pick_bwd(w, M, act_dtype, &st);
+        if (st != Q4GSW_OK) return st;
+        *bytes = bwd_ws_bytes(w, M, act_dtype, r);
+        return Q4GSW_OK;
+    }
+    return Q4GSW_E_SHAPE;
+}
+
+q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv,
+                                       int64_t M, int32_t x_dtype, uint64_t* bytes) {
+    if (!bytes) return Q4GSW_E_NULL;
+    q4gsw_status st = check_qkv_descs(wq, wk, wv);
+    if (st != Q4GSW_OK) return st;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
+    const int32_t r = pick_fwd(wq, M, x_dtype, true, &st);
+    if (st != Q4GSW_OK) return st;
+    const q4gsw_weight* w3[3] = {wq, wk, wv};
+    *bytes = qkv_ws_bytes(w3, M, x_dtype, r);
+    return Q4GSW_OK;
+}
+
+q4gsw_status q4gsw_linear_fwd(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y, void* ws,
+                              uint64_t ws_bytes, void* stream) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!x || !y) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
+    const int32_t route = pick_fwd(w, M, x_dtype, false, &st);
+    if (st != Q4GSW_OK) return st;
+    const uint64_t need = fwd_ws_bytes(w, M, x_dtype, route);
+    if (need > 0 && (!ws || ws_bytes < need)) return Q4GSW_E_WORKSPACE;
+    const Range yr = range_of(y, (uint64_t)M * w->N * 4);
+    if (overlap(yr, range_of(x, (uint64_t)M * w->K * esize(x_dtype))) || overlap(yr, range_of(w->data, w->bytes)) ||
+        (need > 0 && (overlap(yr, range_of(ws, need)) || overlap(range_of(ws, need), range_of(w->data, w->bytes)) ||
+                      overlap(range_of(ws, need), range_of(x, (uint64_t)M * w->K * esize(x_dtype))))))
+        return Q4GSW_E_ALIAS;
+    return run_fwd(w, x, x_dtype, M, y, ws, route, static_cast<hipStream_t>(stream));
+}
+
+q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M, float* d_x,
+                                    void* ws, uint64_t ws_bytes, void* stream) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!d_out || !d_x) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(g_dtype)) return Q4GSW_E_DTYPE;
+    const int32_t route = pick_bwd(w, M, g_dtype, &st);
+    if (st != Q4GSW_OK) return st;
+    const uint64_t need = bwd_ws_bytes(w, M, g_dtype, route);
+    if (need > 0 && (!ws || ws_bytes < need)) return Q4GSW_E_WORKSPACE;
+    const Range xr = range_of(d_x, (uint64_t)M * w->K * 4);
+    const Range gr = range_of(d_out, (uint64_t)M * w->N * esize(g_dtype));
+    if (overlap(xr, gr) || overlap(xr, range_of(w->data, w->bytes)) ||
+        (need > 0 && (overlap(xr, range_of(ws, need)) || overlap(range_of(ws, need), gr) ||
+                      overlap(range_of(ws, need), range_of(w->data, w->bytes)))))
+        return Q4GSW_E_ALIAS;
+    const WView v = view_of(w);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (route) {
+        case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_bwd(v, d_out, g_dtype, M, d_x, s));
+        case Q4GSW_ROUTE_BWD_GEMV: {
+            const int splits = gemv_bwd_splits(v, M);
+            if (splits == 1) return hip_status(launch_gemv_bwd(v, d_out, g_dtype, M, d_x, 1, s));
+            float* part = static_cast<float*>(ws);
+            hipError_t e = launch_gemv_bwd(v, d_out, g_dtype, M, part, splits, s);
+            if (e == hipSuccess) e = launch_reduce_splits(part, splits, M, v.K, v.k_pad, d_x, v.K, s);
+            return hip_status(e);
+        }
+        default: {
+            const BwdPlan plan = plan_gemm_bwd(v, g_dtype, fold_ok(w), M);
+            return hip_status(launch_gemm_bwd(v, d_out, g_dtype, M, d_x, plan, static_cast<float*>(ws), s));
+        }
+    }
+}
+
+q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, const void* x,
+                             int32_t x_dtype, int64_t M, float* q, float* k, float* v, void* ws, uint64_t ws_bytes,
+                             void* stream) {
+    q4gsw_status st = check_qkv_descs(wq, wk, wv);
+    if (st != Q4GSW_OK) return st;
+    if (!x || !q || !k || !v) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
+    const int32_t route = pick_fwd(wq, M, x_dtype, true, &st);
+    if (st != Q4GSW_OK) return st;
+    const q4gsw_weight* w3[3] = {wq, wk, wv};
+    float* o3[3] = {q, k, v};
+    const uint64_t need = qkv_ws_bytes(w3, M, x_dtype, route);
+    if (need > 0 && (!ws || ws_bytes < need)) return Q4GSW_E_WORKSPACE;
+    Range outs[3];
+    for (int i = 0; i < 3; ++i) outs[i] = range_of(o3[i], (uint64_t)M * w3[i]->N * 4);
+    const Range xr = range_of(x, (uint64_t)M * wq->K * esize(x_dtype));
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], xr)) return Q4GSW_E_ALIAS;
+        for (int j = 0; j < 3; ++j) {
+            if (j > i && overlap(outs[i], outs[j])) return Q4GSW_E_ALIAS;
+            if (overlap(outs[i], range_of(w3[j]->data, w3[j]->bytes))) return Q4GSW_E_ALIAS;
+        }
+        if (need > 0 && overlap(outs[i], range_of(ws, need))) return Q4GSW_E_ALIAS;
+    }
+    if (need > 0) {
+        if (overlap(range_of(ws, need), xr)) return Q4GSW_E_ALIAS;
+        for (int j = 0; j < 3; ++j)
+            if (overlap(range_of(ws, need), range_of(w3[j]->data, w3[j]->bytes))) return Q4GSW_E_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (route == Q4GSW_ROUTE_QKV_FUSED) {
+        FwdSeg segs[3];
+        for (int i = 0; i < 3; ++i) segs[i] = FwdSeg{view_of(w3[i]), o3[i]};
+        const FwdPlan plan = plan_gemm_fwd(segs, 3, x_dtype, fold_ok(wq), M);
+        return hip_status(launch_gemm_fwd(segs, 3, x, x_dtype, M, plan, static_cast<float*>(ws), s));
+    }
+    // Fallback outside the fused predicate: three forwards on the same stream (same contract).
+    for (int i = 0; i < 3; ++i) {
+        st = run_fwd(w3[i], x, x_dtype, M, o3[i], ws, route, s);
+        if (st != Q4GSW_OK) return st;
+    }
+    return Q4GSW_OK;
+}
+
+int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype) {
+    if (check_desc(w) != Q4GSW_OK || M < 1 || M > kMaxM || !act_dtype_ok(act_dtype)) return Q4GSW_ROUTE_NONE;
+    q4gsw_status st;
+    int32_t r = Q4GSW_ROUTE_NONE;
+    if (op == Q4GSW_OP_FWD) r = pick_fwd(w, M, act_dtype, false, &st);
+    else if (op == Q4GSW_OP_BWD_INPUT) r = pick_bwd(w, M, act_dtype, &st);
+    else if (op == Q4GSW_OP_QKV) r = pick_fwd(w, M, act_dtype, true, &st);
+    else return Q4GSW_ROUTE_NONE;
+    return st == Q4GSW_OK ? r : Q4GSW_ROUTE_NONE;
+}
+
+const char* q4gsw_route_name(int32_t route) {
+    switch (route) {
+        case Q4GSW_ROUTE_NONE: return "none";
+        case Q4GSW_ROUTE_GENERIC: return "generic";
+        case Q4GSW_ROUTE_GEMV: return "gemv";
+        case Q4GSW_ROUTE_GEMM_FOLD: return "gemm_fold";
+        case Q4GSW_ROUTE_GEMM_GROUP: return "gemm_group";
+        case Q4GSW_ROUTE_GEMM_SPLIT: return "gemm_split";
+        case Q4GSW_ROUTE_BWD_GEMV: return "bwd_gemv";
+        case Q4GSW_ROUTE_BWD_FOLD: return "bwd_fold";
+        case Q4GSW_ROUTE_BWD_SPLIT: return "bwd_split";
+        case Q4GSW_ROUTE_QKV_FUSED: return "qkv_fused";
+        default: return "unknown";
+    }
+}
+
+const char* q4gsw_status_str(int32_t status) {
+    switch (status) {
+        case Q4GSW_OK: return "ok";
+        case Q4GSW_E_NULL: return "null pointer";
+        case Q4GSW_E_SHAPE: return "size out of range";
+        case Q4GSW_E_DTYPE: return "unsupported dtype";
+        case Q4GSW_E_GROUP: return "group_size must be >= 1 and divide K";
+        case Q4GSW_E_ALIAS: return "output overlaps another buffer";
+        case Q4GSW_E_CODE_RANGE: return "code above 15";
+        case Q4GSW_E_WORKSPACE: return "workspace missing or too small";
+        case Q4GSW_E_DESC: return "invalid or mismatched weight descriptor";
+        case Q4GSW_E_HIP: return "HIP runtime error";
+        case Q4GSW_E_BUFFER: return "packed buffer too small";
+        case Q4GSW_E_ROUTE: return "forced route cannot serve this call";
+        default: return "unknown status";
+    }
+}
+
+void q4gsw_force_route(int32_t route) { g_forced_route.store(route, std::memory_order_relaxed); }
+
+uint32_t q4gsw_layout_version(void) { return Q4GSW_LAYOUT_VERSION; }
+
+const char* q4gsw_build_info(void) { return "q4gsw gfx950 layout-v1 built " __DATE__ " " __TIME__; }
+
+}  // extern "C"

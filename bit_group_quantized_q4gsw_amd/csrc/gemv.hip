@@ -1,0 +1,375 @@
+// Small-M (decode, M <= 8) q4gsw kernels: bandwidth-bound streaming over the packed codes.
+//
+// Forward:   y[m, n]   = sum_k x[m, k] * (code[n, k] - 8) * scale[k / gs, n]
+// Backward:  d_x[m, k] = sum_n d_out[m, n] * (code[n, k] - 8) * scale[k / gs, n]
+// (the input gradient of the Vulkan q4gsw-backward PR body, contracting over N).
+//
+// Every lane reads whole 32-byte micro-blocks (8 rows x 8 columns of codes) with two
+// 16-byte loads; a wave's 64 lanes cover 4 row-octets x 16 k-octets, i.e. four
+// contiguous 512-byte runs.  Codes are unpacked in registers to the exact values
+// c - 8, products are fp32 (or fp16 pairs with fp32 dot2 accumulation for fp16
+// activations), and partial sums are reduced across lanes with cross-lane
+// shuffles and across waves in LDS.  A code 8 therefore contributes exactly 0.
+// Requires group_size % 8 == 0 so a k-octet lies inside one scale group.
+#include "device.h"
+#include "internal.h"
+
+namespace q4gsw {
+
+namespace {
+
+__device__ __forceinline__ void load_micro_block(const uint8_t* p, uint32_t (&wd)[8]) {
+    const u4 a = ldg16_stream(p);
+    const u4 b = ldg16_stream(p + 16);
+    wd[0] = a.x; wd[1] = a.y; wd[2] = a.z; wd[3] = a.w;
+    wd[4] = b.x; wd[5] = b.y; wd[6] = b.z; wd[7] = b.w;
+}
+
+// Eight consecutive scales scale[g, n0 .. n0+7] as fp32.
+__device__ __forceinline__ void load_scales8(const void* plane, int scale_f16, int64_t idx, float (&sc)[8]) {
+    if (scale_f16) {
+        const u4 v = ldg16(static_cast<const uint16_t*>(plane) + idx);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[2 * i] = f16_bits_to_f32((uint16_t)(u[i] & 0xFFFFu));
+            sc[2 * i + 1] = f16_bits_to_f32((uint16_t)(u[i] >> 16));
+        }
+    } else {
+        const f4 a = *reinterpret_cast<const f4*>(static_cast<const float*>(plane) + idx);
+        const f4 b = *reinterpret_cast<const f4*>(static_cast<const float*>(plane) + idx + 4);
+        sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w;
+        sc[4] = b.x; sc[5] = b.y; sc[6] = b.z; sc[7] = b.w;
+    }
+}
+
+// Eight activation values src[base + 0..7] widened to fp32; elements at or past `limit` read as 0.
+template <int DT>
+__device__ __forceinline__ void load_act8(const void* src, int64_t base, int64_t pos, int64_t limit, int vec,
+                                          float (&v)[8]) {
+    if (vec && pos + 8 <= limit) {
+        if constexpr (DT == kF32) {
+            const f4 a = *reinterpret_cast<const f4*>(static_cast<const float*>(src) + base);
+            const f4 b = *reinterpret_cast<const f4*>(static_cast<const float*>(src) + base + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            const u4 a = ldg16(static_cast<const uint16_t*>(src) + base);
+            const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (DT == kF16) {
+                    v[2 * i] = f16_bits_to_f32((uint16_t)(u[i] & 0xFFFFu));
+                    v[2 * i + 1] = f16_bits_to_f32((uint16_t)(u[i] >> 16));
+                } else {
+                    v[2 * i] = bitcast<float>(u[i] << 16);
+                    v[2 * i + 1] = bitcast<float>(u[i] & 0xFFFF0000u);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (pos + j < limit) ? load_elem<DT>(src, base + j) : 0.0f;
+    }
+}
+
+}  // namespace
+
+// Grid: (n_pad / 32, splits).  Block: 256 threads = 4 waves.  A block owns 32 rows; its
+// waves take interleaved 128-column steps of the block's K range.
+template <int MT, int XT>
+__global__ __launch_bounds__(256) void gemv_fwd_kernel(WView w, const void* __restrict__ x, int x_vec,
+                                                       float* __restrict__ out, int64_t out_ld,
+                                                       int64_t split_stride, int64_t row_limit,
+                                                       int steps_per_split) {
+    __shared__ float red[4][4][MT][8];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ro = lane >> 4;
+    const int ko = lane & 15;
+    const int64_t R = (int64_t)blockIdx.x * 4 + ro;
+    const int64_t kocts = w.k_pad >> 3;
+    const int total_steps = (int)(w.k_pad >> 7);
+    const int s0 = (int)blockIdx.y * steps_per_split;
+    const int s1 = min(s0 + steps_per_split, total_steps);
+    const uint8_t* rowbase = w.nib + 32 * (R * kocts);
+
+    float acc[MT][8];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[m][i] = 0.0f;
+
+    for (int st = s0 + wave; st < s1; st += 4) {
+        const int64_t O = (int64_t)st * 16 + ko;
+        const int64_t k0 = O * 8;
+        uint32_t wd[8];
+        load_micro_block(rowbase + 32 * O, wd);
+        float sc[8];
+        load_scales8(w.scales, w.scale_f16, (k0 / w.gs) * w.n_pad + 8 * R, sc);
+        if constexpr (XT == kF16) {
+            h2 xp[MT][4];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int64_t base = m * w.K + k0;
+                if (x_vec && k0 + 8 <= w.K) {
+                    const u4 a = ldg16(static_cast<const uint16_t*>(x) + base);
+                    xp[m][0] = bitcast<h2>(a.x); xp[m][1] = bitcast<h2>(a.y);
+                    xp[m][2] = bitcast<h2>(a.z); xp[m][3] = bitcast<h2>(a.w);
+                } else {
+                    _Float16 t[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        t[j] = (k0 + j < w.K) ? bitcast<_Float16>(static_cast<const uint16_t*>(x)[base + j])
+                                              : (_Float16)0.0f;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) xp[m][s] = h2{t[2 * s], t[2 * s + 1]};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                h2 c8[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) c8[s] = codes_minus8_f16(wd[i], s);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_fdot2(c8[s], xp[m][s], t, false);
+                    acc[m][i] = fmaf(t, sc[i], acc[m][i]);
+                }
+            }
+        } else {
+            float xf[MT][8];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) load_act8<XT>(x, m * w.K + k0, k0, w.K, x_vec, xf[m]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float c[8];
+                word_codes_minus8_f32(wd[i], c);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) t = fmaf(xf[m][j], c[j], t);
+                    acc[m][i] = fmaf(t, sc[i], acc[m][i]);
+                }
+            }
+        }
+    }
+
+    // Sum over the 16 lanes of a row-octet, then over the 4 waves.
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v = acc[m][i];
+            v = wave_xor_sum(v, 1);
+            v = wave_xor_sum(v, 2);
+            v = wave_xor_sum(v, 4);
+            v = wave_xor_sum(v, 8);
+            acc[m][i] = v;
+        }
+    if (ko == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) red[wave][ro][m][i] = acc[m][i];
+    }
+    __syncthreads();
+    if (threadIdx.x < 32 * MT) {
+        const int m = threadIdx.x >> 5;
+        const int r = threadIdx.x & 31;
+        const float v = (red[0][r >> 3][m][r & 7] + red[1][r >> 3][m][r & 7]) +
+                        (red[2][r >> 3][m][r & 7] + red[3][r >> 3][m][r & 7]);
+        const int64_t n = (int64_t)blockIdx.x * 32 + r;
+        if (n < row_limit) out[(int64_t)blockIdx.y * split_stride + m * out_ld + n] = v;
+    }
+}
+
+// Grid: (k_pad / 128, splits).  A block owns 128 columns of d_x; its waves take interleaved
+// 32-row steps of the block's N range.  Per micro-block the output gradient is pre-scaled,
+// d'[n] = d_out[m, n] * scale[g, n], and d_x[m, k] = sum_n d'[n] * (c[n, k] - 8).
+template <int MT, int GT>
+__global__ __launch_bounds__(256) void gemv_bwd_kernel(WView w, const void* __restrict__ d_out, int g_vec,
+                                                       float* __restrict__ out, int64_t out_ld,
+                                                       int64_t split_stride, int64_t col_limit,
+                                                       int rsteps_per_split) {
+    __shared__ float red[4][16][MT][8];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ro = lane >> 4;
+    const int ko = lane & 15;
+    const int64_t kocts = w.k_pad >> 3;
+    const int64_t O = (int64_t)blockIdx.x * 16 + ko;
+    const int64_t k0 = O * 8;
+    const int64_t g = k0 / w.gs;
+    const int total = (int)(w.n_pad >> 5);
+    const int r0 = (int)blockIdx.y * rsteps_per_split;
+    const int r1 = min(r0 + rsteps_per_split, total);
+
+    float acc[MT][8];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[m][j] = 0.0f;
+
+    for (int rs = r0 + wave; rs < r1; rs += 4) {
+        const int64_t R = (int64_t)rs * 4 + ro;
+        const int64_t n0 = R * 8;
+        uint32_t wd[8];
+        load_micro_block(w.nib + 32 * (R * kocts + O), wd);
+        float sc[8];
+        load_scales8(w.scales, w.scale_f16, g * w.n_pad + n0, sc);
+        float dp[MT][8];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            load_act8<GT>(d_out, m * w.N + n0, n0, w.N, g_vec, dp[m]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dp[m][i] *= sc[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float c[8];
+            word_codes_minus8_f32(wd[i], c);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[m][j] = fmaf(dp[m][i], c[j], acc[m][j]);
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = acc[m][j];
+            v = wave_xor_sum(v, 16);
+            v = wave_xor_sum(v, 32);
+            acc[m][j] = v;
+        }
+    }
+    if (ro == 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) red[wave][ko][m][j] = acc[m][j];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < 128 * MT; t += 256) {
+        const int m = t >> 7;
+        const int c = t & 127;
+        const float v = (red[0][c >> 3][m][c & 7] + red[1][c >> 3][m][c & 7]) +
+                        (red[2][c >> 3][m][c & 7] + red[3][c >> 3][m][c & 7]);
+        const int64_t k = (int64_t)blockIdx.x * 128 + c;
+        if (k < col_limit) out[(int64_t)blockIdx.y * split_stride + m * out_ld + k] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ ws, int splits, int64_t M,
+                                                            int64_t cols, int64_t ld, float* __restrict__ y,
+                                                            int64_t y_ld) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= M * cols) return;
+    const int64_t m = t / cols;
+    const int64_t c = t % cols;
+    float v = 0.0f;
+    for (int s = 0; s < splits; ++s) v += ws[((int64_t)s * M + m) * ld + c];
+    y[m * y_ld + c] = v;
+}
+
+hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t cols, int64_t ld, float* y,
+                                int64_t y_ld, hipStream_t s) {
+    const int64_t total = M * cols;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, ws, splits,
+                       M, cols, ld, y, y_ld);
+    return hipGetLastError();
+}
+
+int gemv_fwd_splits(const WView& w, int64_t M) {
+    (void)M;
+    const int64_t blocks = w.n_pad / 32;
+    const int64_t steps = w.k_pad / 128;
+    int64_t splits = 1;
+    while (blocks * splits < 512 && steps / (splits * 2) >= 4) splits *= 2;
+    return (int)splits;
+}
+
+int gemv_bwd_splits(const WView& w, int64_t M) {
+    (void)M;
+    const int64_t blocks = w.k_pad / 128;
+    const int64_t rsteps = w.n_pad / 32;
+    int64_t splits = 1;
+    while (blocks * splits < 512 && rsteps / (splits * 2) >= 4) splits *= 2;
+    return (int)splits;
+}
+
+template <int XT>
+static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, hipStream_t s, const WView& w, const void* x, int vec,
+                                    float* out, int64_t ld, int64_t stride, int64_t limit, int per) {
+    switch (M) {
+#define Q4GSW_CASE(MT)                                                                                   \
+    case MT:                                                                                             \
+        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT>), grid, dim3(256), 0, s, w, x, vec, out, ld, stride, \
+                           limit, per);                                                                  \
+        break;
+        Q4GSW_CASE(1) Q4GSW_CASE(2) Q4GSW_CASE(3) Q4GSW_CASE(4)
+        Q4GSW_CASE(5) Q4GSW_CASE(6) Q4GSW_CASE(7) Q4GSW_CASE(8)
+#undef Q4GSW_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
+                           hipStream_t s) {
+    const int64_t steps = w.k_pad / 128;
+    const int per = (int)((steps + splits - 1) / splits);
+    const dim3 grid((unsigned)(w.n_pad / 32), (unsigned)splits);
+    const int esize = x_dtype == kF32 ? 4 : 2;
+    const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) && ((w.K * esize) % 16 == 0);
+    const int64_t ld = splits == 1 ? w.N : w.n_pad;
+    const int64_t stride = splits == 1 ? 0 : M * w.n_pad;
+    const int64_t limit = splits == 1 ? w.N : w.n_pad;
+    switch (x_dtype) {
+        case kF32: return gemv_fwd_dispatch<kF32>(M, grid, s, w, x, vec, out, ld, stride, limit, per);
+        case kF16: return gemv_fwd_dispatch<kF16>(M, grid, s, w, x, vec, out, ld, stride, limit, per);
+        default: return gemv_fwd_dispatch<kBF16>(M, grid, s, w, x, vec, out, ld, stride, limit, per);
+    }
+}
+
+template <int GT>
+static hipError_t gemv_bwd_dispatch(int64_t M, dim3 grid, hipStream_t s, const WView& w, const void* g,
+                                    int vec, float* out, int64_t ld, int64_t stride, int64_t limit, int per) {
+    switch (M) {
+#define Q4GSW_CASE(MT)                                                                                   \
+    case MT:                                                                                             \
+        hipLaunchKernelGGL((gemv_bwd_kernel<MT, GT>), grid, dim3(256), 0, s, w, g, vec, out, ld, stride, \
+                           limit, per);                                                                  \
+        break;
+        Q4GSW_CASE(1) Q4GSW_CASE(2) Q4GSW_CASE(3) Q4GSW_CASE(4)
+        Q4GSW_CASE(5) Q4GSW_CASE(6) Q4GSW_CASE(7) Q4GSW_CASE(8)
+#undef Q4GSW_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* out, int splits,
+                           hipStream_t s) {
+    const int64_t rsteps = w.n_pad / 32;
+    const int per = (int)((rsteps + splits - 1) / splits);
+    const dim3 grid((unsigned)(w.k_pad / 128), (unsigned)splits);
+    const int esize = g_dtype == kF32 ? 4 : 2;
+    const int vec = ((reinterpret_cast<uintptr_t>(d_out) & 15u) == 0) && ((w.N * esize) % 16 == 0);
+    const int64_t ld = splits == 1 ? w.K : w.k_pad;
+    const int64_t stride = splits == 1 ? 0 : M * w.k_pad;
+    const int64_t limit = splits == 1 ? w.K : w.k_pad;
+    switch (g_dtype) {
+        case kF32: return gemv_bwd_dispatch<kF32>(M, grid, s, w, d_out, vec, out, ld, stride, limit, per);
+        case kF16: return gemv_bwd_dispatch<kF16>(M, grid, s, w, d_out, vec, out, ld, stride, limit, per);
+        default: return gemv_bwd_dispatch<kBF16>(M, grid, s, w, d_out, vec, out, ld, stride, limit, per);
+    }
+}
+
+}  // namespace q4gsw

@@ -1,0 +1,68 @@
+// Internal interface between the C-ABI front end (api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace q4gsw {
+
+// Device view of one packed weight.
+struct WView {
+    const uint8_t* nib;      // nibble plane
+    const void* scales;      // scale plane [g_pad][n_pad]
+    int scale_f16;           // 1: fp16 scales, 0: fp32
+    int64_t N, K, gs, n_pad, k_pad, g_pad;
+};
+
+// pack.hip
+hipError_t launch_pack(const uint8_t* codes, const void* scales, int scale_f16, int64_t N, int64_t K,
+                       int64_t gs, const Layout& L, uint8_t* packed, hipStream_t s);
+hipError_t launch_unpack(const WView& w, uint8_t* codes, void* scales, hipStream_t s);
+
+// gemv.hip: M <= 8 routes.  `out` is y [M, N] when splits == 1, else ws [splits][M][n_pad].
+hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out,
+                           int splits, hipStream_t s);
+int gemv_fwd_splits(const WView& w, int64_t M);
+// `out` is d_x [M, K] when splits == 1, else ws [splits][M][k_pad].
+hipError_t launch_gemv_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* out,
+                           int splits, hipStream_t s);
+int gemv_bwd_splits(const WView& w, int64_t M);
+// y[m][c] = sum_s ws[s][m][c] for c < cols (ws row pitch ld).
+hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t cols, int64_t ld,
+                                float* y, int64_t y_ld, hipStream_t s);
+
+// generic.hip: any shape, any group size.
+hipError_t launch_generic_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* y,
+                              hipStream_t s);
+hipError_t launch_generic_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
+                              hipStream_t s);
+
+// gemm_fwd.hip: MFMA forward over up to three weights sharing K (fused QKV uses three).
+enum GemmMode : int { kModeFold = 0, kModeGroup = 1, kModeSplit = 2 };
+struct FwdSeg {
+    WView w;
+    float* out;              // [M, N] final output of this segment
+};
+struct FwdPlan {
+    int mode;
+    int splits;              // K splits (1: write outputs directly)
+    int64_t ws_bytes;        // workspace needed
+};
+FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M);
+bool gemm_fwd_supported(const WView& w, int x_dtype, int fold_ok);
+hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
+                           const FwdPlan& plan, float* ws, hipStream_t s);
+
+// gemm_bwd.hip: MFMA input gradient.
+struct BwdPlan {
+    int mode;                // kModeFold or kModeSplit
+    int splits;              // N (contraction) splits
+    int64_t ws_bytes;
+};
+bool gemm_bwd_supported(const WView& w, int g_dtype, int fold_ok);
+BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M);
+hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
+                           const BwdPlan& plan, float* ws, hipStream_t s);
+
+}  // namespace q4gsw

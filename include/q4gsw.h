@@ -1,0 +1,198 @@
+/*
+ * q4gsw: the 4-bit group-symmetric weight-quantized linear layer on AMD MI355X (gfx950).
+ *
+ * The operation (sources are the pages this library is built from):
+ *
+ *   dequant(W[n,k]) = (code[n,k] - 8) * scale[k / group_size, n]
+ *       codes are 4-bit (0..15); scales are [num_groups, N] with
+ *       num_groups = K / group_size.  Formula: "Solution" part of the body of
+ *       "[ExecuTorch][Vulkan] Add et_vk.linear_q4gsw_backward kernel (4-bit
+ *       input-grad)"; scale shape: the "Key changes" part of that body.  The
+ *       row index k / group_size is the reading of that shape in which groups
+ *       are contiguous runs of group_size along K.
+ *
+ *   forward          y[M,N]   = x[M,K] . dequant(W)[N,K]^T
+ *   input gradient   d_x[M,K] = d_out[M,N] . dequant(W)[N,K], contracting over N
+ *       (opening summary of the same Vulkan body: the input gradient of a frozen
+ *       4-bit base, for adapter training; there is no weight gradient).
+ *   fused QKV        q, k, v = x . dequant(Wq)^T, x . dequant(Wk)^T, x . dequant(Wv)^T
+ *       (body of "[ExecuTorch][WebGPU] Replace broad QKV fusion with BK64 kernel":
+ *       one activation, three weights packed once, three distinct outputs).
+ *
+ * Conventions for every call:
+ *   - Every tensor is dense and row-major.  Every data pointer is a device
+ *     pointer owned by the caller; the library never allocates device memory.
+ *   - Arguments are validated on the host before any HIP call.  A call that
+ *     fails validation returns a status other than Q4GSW_OK, launches nothing
+ *     and leaves every output untouched.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Compute calls are
+ *     asynchronous on it; only q4gsw_pack and q4gsw_unpack synchronize it.
+ *   - Outputs are fp32.  Activations may be fp32, fp16 or bf16; scales fp16 or
+ *     fp32.  Accumulation is fp32.
+ *   - No C++ exception crosses this interface.  The library keeps no mutable
+ *     state except the optional route override (q4gsw_force_route).
+ */
+#ifndef Q4GSW_H
+#define Q4GSW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4GSW_MAGIC 0x57534734u          /* "4GSW" */
+#define Q4GSW_LAYOUT_VERSION 1u
+
+typedef enum q4gsw_status {
+    Q4GSW_OK = 0,
+    Q4GSW_E_NULL = 1,         /* a required pointer is NULL */
+    Q4GSW_E_SHAPE = 2,        /* a size is out of range (M, N or K < 1, or too large) */
+    Q4GSW_E_DTYPE = 3,        /* an unsupported dtype code */
+    Q4GSW_E_GROUP = 4,        /* group_size < 1 or K % group_size != 0 */
+    Q4GSW_E_ALIAS = 5,        /* an output overlaps another output, an input or the workspace */
+    Q4GSW_E_CODE_RANGE = 6,   /* q4gsw_pack saw a code above 15 */
+    Q4GSW_E_WORKSPACE = 7,    /* workspace missing or smaller than q4gsw_*_workspace_bytes */
+    Q4GSW_E_DESC = 8,         /* descriptor magic/version/fields invalid, or QKV weights disagree */
+    Q4GSW_E_HIP = 9,          /* a HIP runtime call or kernel launch failed */
+    Q4GSW_E_BUFFER = 10,      /* packed buffer smaller than q4gsw_packed_bytes */
+    Q4GSW_E_ROUTE = 11        /* a forced route cannot serve this call */
+} q4gsw_status;
+
+typedef enum q4gsw_dtype {
+    Q4GSW_F32 = 0,
+    Q4GSW_F16 = 1,
+    Q4GSW_BF16 = 2
+} q4gsw_dtype;
+
+typedef enum q4gsw_op {
+    Q4GSW_OP_FWD = 0,
+    Q4GSW_OP_BWD_INPUT = 1,
+    Q4GSW_OP_QKV = 2
+} q4gsw_op;
+
+/* Kernel routes, reported by q4gsw_route (route attestation). */
+typedef enum q4gsw_route_id {
+    Q4GSW_ROUTE_NONE = 0,          /* the call would fail validation */
+    Q4GSW_ROUTE_GENERIC = 1,       /* VALU, one lane per output, any shape and group size */
+    Q4GSW_ROUTE_GEMV = 2,          /* forward, M <= 8: bandwidth-bound streaming GEMV */
+    Q4GSW_ROUTE_GEMM_FOLD = 3,     /* forward, fp16 x: MFMA f16, scale folded into the fp16 weight */
+    Q4GSW_ROUTE_GEMM_GROUP = 4,    /* forward, fp16/bf16 x: MFMA on exact codes, fp32 scale per group */
+    Q4GSW_ROUTE_GEMM_SPLIT = 5,    /* forward, fp32 x: x split into bf16 hi+lo, two MFMA passes */
+    Q4GSW_ROUTE_BWD_GEMV = 6,      /* input gradient, M <= 8: streaming transposed GEMV */
+    Q4GSW_ROUTE_BWD_FOLD = 7,      /* input gradient, fp16 d_out: MFMA f16 on folded fp16 weight */
+    Q4GSW_ROUTE_BWD_SPLIT = 8,     /* input gradient: d_out*scale split into bf16 hi+lo, two MFMA passes */
+    Q4GSW_ROUTE_QKV_FUSED = 9      /* fused QKV: one launch over the three weights */
+} q4gsw_route_id;
+
+/*
+ * Packed weight descriptor, filled by q4gsw_pack.  Plain data: copy it freely.
+ * `data` points into the caller's packed buffer; the descriptor does not own it.
+ * A descriptor is immutable after packing and serves every M (one prepack,
+ * reused by forward, input gradient and QKV).
+ */
+typedef struct q4gsw_weight {
+    uint32_t magic;           /* Q4GSW_MAGIC */
+    uint32_t version;         /* Q4GSW_LAYOUT_VERSION */
+    int64_t N;                /* output features (rows of W) */
+    int64_t K;                /* input features (columns of W) */
+    int64_t group_size;       /* K-run sharing one scale */
+    int64_t n_pad;            /* N rounded up to the packing tile */
+    int64_t k_pad;            /* K rounded up to the packing tile */
+    int64_t g_pad;            /* scale rows stored: ceil(k_pad / group_size) */
+    int32_t scale_dtype;      /* Q4GSW_F16 or Q4GSW_F32 */
+    uint32_t flags;           /* Q4GSW_FLAG_* set by q4gsw_pack */
+    void *data;               /* device pointer to the packed buffer */
+    uint64_t bytes;           /* bytes of the packed buffer in use */
+    uint64_t nibble_offset;   /* byte offset of the 4-bit code plane */
+    uint64_t scale_offset;    /* byte offset of the scale plane [g_pad, n_pad] */
+} q4gsw_weight;
+
+/* Set by q4gsw_pack when every fp16 scale s is 0 or 2^-14 <= |s| <= 8188, so that
+ * (code - 8) * s is a finite normal fp16 (rounding error at most 2^-11 relative). */
+#define Q4GSW_FLAG_FOLD_F16 1u
+
+/* Bytes of the packed buffer for an [N, K] weight.  Pure host function.
+ * Returns E_SHAPE, E_GROUP or E_DTYPE on bad arguments, E_NULL if bytes is NULL. */
+q4gsw_status q4gsw_packed_bytes(int64_t N, int64_t K, int64_t group_size, int32_t scale_dtype,
+                                uint64_t *bytes);
+
+/*
+ * One-time repack of the codes and scales into the gfx950 layout (the prepack
+ * that forward, input gradient and QKV all reuse).
+ *   codes   device, uint8 [N, K], one code (0..15) per byte
+ *   scales  device, [K / group_size, N] in scale_dtype (Q4GSW_F16 or Q4GSW_F32)
+ *   packed  device, at least q4gsw_packed_bytes(...) bytes; overwritten
+ *   out     host descriptor, filled on success
+ * Synchronizes `stream` to read back the code-range check.  Returns
+ * E_CODE_RANGE if any code exceeds 15 (the packed buffer is then undefined and
+ * `out` is left untouched).
+ */
+q4gsw_status q4gsw_pack(const uint8_t *codes, const void *scales, int32_t scale_dtype,
+                        int64_t N, int64_t K, int64_t group_size,
+                        void *packed, uint64_t packed_bytes, void *stream, q4gsw_weight *out);
+
+/* The exact inverse of q4gsw_pack: writes codes [N, K] uint8 and scales
+ * [K / group_size, N] in the weight's scale dtype.  Synchronizes `stream`. */
+q4gsw_status q4gsw_unpack(const q4gsw_weight *w, uint8_t *codes, void *scales, void *stream);
+
+/* Device workspace (bytes) the call needs; 0 when its route needs none.  Pure host. */
+q4gsw_status q4gsw_workspace_bytes(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype,
+                                   uint64_t *bytes);
+q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight *wq, const q4gsw_weight *wk,
+                                       const q4gsw_weight *wv, int64_t M, int32_t x_dtype,
+                                       uint64_t *bytes);
+
+/*
+ * Forward: y[M, N] (fp32) = x[M, K] . dequant(W)^T.
+ *   x   device [M, K] in x_dtype (Q4GSW_F32, Q4GSW_F16, Q4GSW_BF16)
+ *   y   device fp32 [M, N]; must not overlap x, the packed weight or the workspace
+ *   ws  device workspace of ws_bytes >= q4gsw_workspace_bytes(Q4GSW_OP_FWD, ...)
+ *       (may be NULL when that is 0)
+ */
+q4gsw_status q4gsw_linear_fwd(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M,
+                              float *y, void *ws, uint64_t ws_bytes, void *stream);
+
+/*
+ * Input gradient: d_x[M, K] (fp32) = d_out[M, N] . dequant(W), contracting over N.
+ * Reads the same packed buffer as the forward (no re-pack).
+ *   d_out  device [M, N] in g_dtype;  d_x device fp32 [M, K]
+ */
+q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight *w, const void *d_out, int32_t g_dtype,
+                                    int64_t M, float *d_x, void *ws, uint64_t ws_bytes,
+                                    void *stream);
+
+/*
+ * Fused QKV: q = x . dequant(Wq)^T, k = x . dequant(Wk)^T, v = x . dequant(Wv)^T.
+ * The three weights must share K, group_size and scale dtype (E_DESC otherwise);
+ * their N may differ.  q [M, Nq], k [M, Nk], v [M, Nv] are fp32 and must not
+ * overlap each other, x, the packed weights or the workspace (E_ALIAS).
+ * Shapes outside the fused kernel's predicate run as three forwards with the
+ * same result contract.
+ */
+q4gsw_status q4gsw_qkv_fused(const q4gsw_weight *wq, const q4gsw_weight *wk, const q4gsw_weight *wv,
+                             const void *x, int32_t x_dtype, int64_t M,
+                             float *q, float *k, float *v, void *ws, uint64_t ws_bytes,
+                             void *stream);
+
+/* Route attestation: the q4gsw_route_id a call with these arguments takes
+ * (Q4GSW_ROUTE_NONE if it would fail validation).  For Q4GSW_OP_QKV pass Wq. */
+int32_t q4gsw_route(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype);
+const char *q4gsw_route_name(int32_t route);
+const char *q4gsw_status_str(int32_t status);
+
+/* Force every later call to take `route` (Q4GSW_ROUTE_NONE restores automatic
+ * routing).  A call the forced route cannot serve returns E_ROUTE.  Process-wide
+ * and not synchronized: for tests and benchmarks that compare routes. */
+void q4gsw_force_route(int32_t route);
+
+/* Layout version and a build identifier string. */
+uint32_t q4gsw_layout_version(void);
+const char *q4gsw_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4GSW_H */

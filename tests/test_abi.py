@@ -1,0 +1,230 @@
+"""C-ABI checks that need no GPU: exported symbols, host-side validation, route selection.
+
+Every call here fails validation (or is a pure host function) before the library
+makes any HIP call, so fabricated descriptors and fake device addresses are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "q4gsw.h")
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_group_quantized_q4gsw_amd import build as qbuild
+    if not os.path.exists(qbuild.LIB):
+        qbuild.build()
+    import bit_group_quantized_q4gsw_amd as q
+    return q
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4gsw_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("q4gsw_pack", "q4gsw_linear_fwd", "q4gsw_linear_bwd_input", "q4gsw_qkv_fused"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(q):
+    lib = q.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/q4gsw.h but not exported"
+
+
+def test_status_and_route_names(q):
+    assert q.status_str(0) == "ok"
+    assert "group_size" in q.status_str(4)
+    assert q.route_name(2) == "gemv"
+    assert q.route_name(99) == "unknown"
+    assert q.lib().q4gsw_layout_version() == 1
+
+
+S_OK, E_NULL, E_SHAPE, E_DTYPE, E_GROUP, E_ALIAS, E_CODE, E_WS, E_DESC, E_HIP, E_BUF, E_ROUTE = range(12)
+FAKE = 1 << 40            # never dereferenced: every call below fails validation first
+
+
+def packed_bytes(q, N, K, gs, sdt):
+    out = ctypes.c_uint64()
+    st = q.lib().q4gsw_packed_bytes(N, K, gs, sdt, ctypes.byref(out))
+    return st, out.value
+
+
+def test_packed_bytes(q):
+    st, b = packed_bytes(q, 8192, 2048, 32, q.F16)
+    assert st == S_OK and b == 256 + 8192 * 2048 // 2 + 64 * 8192 * 2
+    st, b = packed_bytes(q, 32, 64, 16, q.F32)         # pads to 128 x 128, 8 scale rows
+    assert st == S_OK and b == 256 + 128 * 128 // 2 + 8 * 128 * 4
+    assert packed_bytes(q, 0, 64, 16, q.F16)[0] == E_SHAPE
+    assert packed_bytes(q, 32, 64, 0, q.F16)[0] == E_GROUP
+    assert packed_bytes(q, 32, 64, 24, q.F16)[0] == E_GROUP
+    assert packed_bytes(q, 32, 64, 16, q.BF16)[0] == E_DTYPE
+    assert q.lib().q4gsw_packed_bytes(32, 64, 16, q.F16, None) == E_NULL
+
+
+def test_pack_validation(q):
+    lib = q.lib()
+    d = q.WeightDesc()
+    _, need = packed_bytes(q, 32, 64, 16, q.F16)
+    assert lib.q4gsw_pack(None, FAKE, q.F16, 32, 64, 16, FAKE * 2, need, None, ctypes.byref(d)) == E_NULL
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, q.F16, 32, 64, 16, FAKE * 2, need, None, None) == E_NULL
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, q.F16, 32, 64, 0, FAKE * 2, need, None, ctypes.byref(d)) == E_GROUP
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, q.F16, 32, 60, 16, FAKE * 2, need, None, ctypes.byref(d)) == E_GROUP
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, 9, 32, 64, 16, FAKE * 2, need, None, ctypes.byref(d)) == E_DTYPE
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, q.F16, -1, 64, 16, FAKE * 2, need, None, ctypes.byref(d)) == E_SHAPE
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, q.F16, 32, 64, 16, FAKE * 2, need - 1, None, ctypes.byref(d)) == E_BUF
+    # packed buffer overlapping the codes
+    assert lib.q4gsw_pack(FAKE, FAKE * 3, q.F16, 32, 64, 16, FAKE + 100, need, None, ctypes.byref(d)) == E_ALIAS
+
+
+def fake_desc(q, N, K, gs, sdt=1, flags=0, data=FAKE * 4):
+    """A descriptor with the layout fields the library expects (as q4gsw_pack fills them)."""
+    def rup(v, m):
+        return (v + m - 1) // m * m
+    n_pad, k_pad = rup(N, 128), rup(K, 128)
+    g_pad = (k_pad + gs - 1) // gs
+    nib_off = 256
+    scale_off = rup(nib_off + n_pad * k_pad // 2, 256)
+    total = rup(scale_off + g_pad * n_pad * (2 if sdt == 1 else 4), 256)
+    d = q.WeightDesc()
+    d.magic, d.version = 0x57534734, 1
+    d.N, d.K, d.group_size = N, K, gs
+    d.n_pad, d.k_pad, d.g_pad = n_pad, k_pad, g_pad
+    d.scale_dtype, d.flags = sdt, flags
+    d.data, d.bytes = data, total
+    d.nibble_offset, d.scale_offset = nib_off, scale_off
+    return d
+
+
+def test_fake_descriptor_matches_packed_bytes(q):
+    for (N, K, gs, sdt) in [(32, 64, 16, 0), (8192, 2048, 32, 1), (100, 200, 8, 1), (2048, 8192, 128, 1)]:
+        d = fake_desc(q, N, K, gs, sdt)
+        assert packed_bytes(q, N, K, gs, sdt) == (S_OK, d.bytes)
+
+
+def route(q, op, d, M, dt):
+    return q.route_name(q.lib().q4gsw_route(op, ctypes.byref(d), M, dt))
+
+
+def test_route_selection(q):
+    fold = 1
+    dec = fake_desc(q, 8192, 2048, 32, 1, flags=fold)
+    assert route(q, q.OP_FWD, dec, 1, q.F16) == "gemv"
+    assert route(q, q.OP_FWD, dec, 8, q.BF16) == "gemv"
+    assert route(q, q.OP_FWD, dec, 9, q.F16) == "gemm_fold"
+    assert route(q, q.OP_FWD, dec, 512, q.BF16) == "gemm_group"
+    assert route(q, q.OP_FWD, dec, 512, q.F32) == "gemm_split"
+    nofold = fake_desc(q, 8192, 2048, 32, 1, flags=0)
+    assert route(q, q.OP_FWD, nofold, 512, q.F16) == "gemm_group"
+    assert route(q, q.OP_QKV, dec, 512, q.F16) == "qkv_fused"
+    assert route(q, q.OP_QKV, dec, 4, q.F16) == "gemv"
+    pre = fake_desc(q, 2048, 8192, 128, 1, flags=fold)
+    assert route(q, q.OP_FWD, pre, 512, q.BF16) == "gemm_group"
+    bwd = fake_desc(q, 8192, 2048, 128, 1, flags=fold)
+    assert route(q, q.OP_BWD_INPUT, bwd, 512, q.F32) == "bwd_split"
+    assert route(q, q.OP_BWD_INPUT, bwd, 512, q.F16) == "bwd_fold"
+    assert route(q, q.OP_BWD_INPUT, bwd, 512, q.BF16) == "bwd_split"
+    assert route(q, q.OP_BWD_INPUT, bwd, 4, q.F32) == "bwd_gemv"
+    # group sizes the fast kernels do not take fall back to the generic route
+    odd = fake_desc(q, 64, 96, 12, 1)
+    assert route(q, q.OP_FWD, odd, 1, q.F16) == "generic"
+    assert route(q, q.OP_FWD, odd, 100, q.F16) == "generic"
+    assert route(q, q.OP_BWD_INPUT, odd, 100, q.F32) == "generic"
+    small_gs = fake_desc(q, 256, 256, 32, 1, flags=fold)
+    assert route(q, q.OP_BWD_INPUT, small_gs, 64, q.F32) == "generic"      # split route needs gs % 128 == 0
+    assert route(q, q.OP_BWD_INPUT, small_gs, 64, q.F16) == "bwd_fold"
+    assert route(q, q.OP_FWD, dec, 0, q.F16) == "none"
+    assert route(q, q.OP_FWD, dec, 1, 5) == "none"
+
+
+def test_forced_routes(q):
+    dec = fake_desc(q, 8192, 2048, 32, 1, flags=1)
+    with q.forced_route("generic"):
+        assert route(q, q.OP_FWD, dec, 1, q.F16) == "generic"
+        assert route(q, q.OP_BWD_INPUT, dec, 512, q.F32) == "generic"
+    with q.forced_route("gemv"):
+        assert route(q, q.OP_FWD, dec, 8, q.F16) == "gemv"
+        assert route(q, q.OP_FWD, dec, 9, q.F16) == "none"          # the small-M kernels stop at M = 8
+        assert route(q, q.OP_BWD_INPUT, dec, 3, q.F16) == "bwd_gemv"
+    with q.forced_route("gemm_fold"):
+        assert route(q, q.OP_FWD, dec, 1, q.F16) == "gemm_fold"
+        assert route(q, q.OP_FWD, dec, 1, q.BF16) == "gemm_group"
+    assert route(q, q.OP_FWD, dec, 1, q.F16) == "gemv"
+
+
+def test_forward_validation(q):
+    lib = q.lib()
+    d = fake_desc(q, 256, 512, 32, 1, flags=1)
+    x, y = FAKE * 8, FAKE * 16
+    f = lib.q4gsw_linear_fwd
+    bad = fake_desc(q, 256, 512, 32, 1)
+    bad.magic = 0
+    assert f(ctypes.byref(bad), x, q.F16, 4, y, None, 0, None) == E_DESC
+    bad = fake_desc(q, 256, 512, 32, 1)
+    bad.k_pad = 640
+    assert f(ctypes.byref(bad), x, q.F16, 4, y, None, 0, None) == E_DESC
+    bad = fake_desc(q, 256, 512, 32, 1)
+    bad.bytes -= 1
+    assert f(ctypes.byref(bad), x, q.F16, 4, y, None, 0, None) == E_DESC
+    assert f(None, x, q.F16, 4, y, None, 0, None) == E_NULL
+    assert f(ctypes.byref(d), None, q.F16, 4, y, None, 0, None) == E_NULL
+    assert f(ctypes.byref(d), x, q.F16, 0, y, None, 0, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, 7, 4, y, None, 0, None) == E_DTYPE
+    assert f(ctypes.byref(d), x, q.F16, 4, x + 64, None, 0, None) == E_ALIAS        # y inside x
+    assert f(ctypes.byref(d), x, q.F16, 4, FAKE * 4 + 512, None, 0, None) == E_ALIAS  # y inside the weight
+    big = fake_desc(q, 2048, 8192, 128, 1, flags=1)
+    need = ctypes.c_uint64()
+    assert lib.q4gsw_workspace_bytes(q.OP_FWD, ctypes.byref(big), 512, q.BF16, ctypes.byref(need)) == S_OK
+    assert need.value > 0                    # the prefill shape splits K across blocks
+    assert f(ctypes.byref(big), x, q.BF16, 512, y, None, 0, None) == E_WS
+    assert f(ctypes.byref(big), x, q.BF16, 512, y, FAKE * 32, need.value - 4, None) == E_WS
+    assert f(ctypes.byref(big), x, q.BF16, 512, y, y + 16, need.value, None) == E_ALIAS   # ws overlaps y
+    with q.forced_route("gemv"):
+        assert f(ctypes.byref(d), x, q.F16, 64, y, None, 0, None) == E_ROUTE
+
+
+def test_backward_and_qkv_validation(q):
+    lib = q.lib()
+    d = fake_desc(q, 256, 512, 32, 1)
+    g, dx = FAKE * 8, FAKE * 16
+    b = lib.q4gsw_linear_bwd_input
+    assert b(ctypes.byref(d), g, q.F32, 4, None, None, 0, None) == E_NULL
+    assert b(ctypes.byref(d), g, q.F32, -3, dx, None, 0, None) == E_SHAPE
+    assert b(ctypes.byref(d), g, q.F32, 4, g + 4, FAKE * 32, 1 << 30, None) == E_ALIAS
+    wq = fake_desc(q, 2048, 2048, 32, 1, flags=1, data=FAKE * 4)
+    wk = fake_desc(q, 512, 2048, 32, 1, flags=1, data=FAKE * 5)
+    wv = fake_desc(q, 512, 2048, 32, 1, flags=1, data=FAKE * 6)
+    qf = lib.q4gsw_qkv_fused
+    x, o1, o2, o3 = FAKE * 8, FAKE * 16, FAKE * 17, FAKE * 18
+    wrong_k = fake_desc(q, 512, 1024, 32, 1, flags=1, data=FAKE * 5)
+    assert qf(ctypes.byref(wq), ctypes.byref(wrong_k), ctypes.byref(wv), x, q.F16, 4, o1, o2, o3, None, 0,
+              None) == E_DESC
+    wrong_gs = fake_desc(q, 512, 2048, 64, 1, flags=1, data=FAKE * 5)
+    assert qf(ctypes.byref(wq), ctypes.byref(wrong_gs), ctypes.byref(wv), x, q.F16, 4, o1, o2, o3, None, 0,
+              None) == E_DESC
+    # outputs that overlap each other
+    assert qf(ctypes.byref(wq), ctypes.byref(wk), ctypes.byref(wv), x, q.F16, 4, o1, o1 + 8, o3, FAKE * 40,
+              1 << 30, None) == E_ALIAS
+    assert qf(ctypes.byref(wq), ctypes.byref(wk), ctypes.byref(wv), x, q.F16, 4, o1, o2, None, None, 0,
+              None) == E_NULL
+    need = ctypes.c_uint64()
+    assert lib.q4gsw_qkv_workspace_bytes(ctypes.byref(wq), ctypes.byref(wk), ctypes.byref(wv), 128, q.F16,
+                                         ctypes.byref(need)) == S_OK
+    if need.value:
+        assert qf(ctypes.byref(wq), ctypes.byref(wk), ctypes.byref(wv), x, q.F16, 128, o1, o2, o3, None, 0,
+                  None) == E_WS
+
+
+def test_python_wrappers_reject_host_tensors(q):
+    with pytest.raises(ValueError):
+        q.pack(torch.zeros(4, 8, dtype=torch.uint8), torch.ones(1, 4, dtype=torch.float16), 8)

@@ -1,0 +1,191 @@
+"""GPU parity: every entry point and route against the fp64 oracle, elementwise.
+
+Acceptance: |gpu - oracle| <= tol * R with R = sum |activation| * |dequant(W)| over the
+contraction; tol = 1e-5 for fp32 activations and 2e-3 for fp16 / bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synthetic_inputs import make_linear, make_qkv, make_workload
+from tests.gpu_helpers import (TOL, assert_within, dev, lib, oracle_bwd, oracle_fwd, pack, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+ROUTE_FAMILIES = ("auto", "generic", "gemv", "gemm_fold")
+
+
+def run_routes(q, fn, family_list=ROUTE_FAMILIES):
+    """Yield (family, result) for every route family that can serve the call."""
+    out = []
+    for fam in family_list:
+        try:
+            if fam == "auto":
+                res = fn()
+            else:
+                with q.forced_route(fam):
+                    res = fn()
+        except q.Q4gswError as e:
+            if e.status == 11:          # E_ROUTE: this family cannot serve the shape
+                continue
+            raise
+        torch.cuda.synchronize()
+        out.append((fam, res))
+    return out
+
+
+FWD_CASES = [
+    # M, N, K, gs, act, scale
+    (4, 32, 64, 16, "f32", "f32"),        # tiny workload
+    (1, 200, 256, 32, "f16", "f16"),
+    (3, 384, 200, 8, "bf16", "f16"),
+    (8, 256, 512, 64, "f32", "f32"),
+    (5, 130, 136, 8, "f16", "f32"),
+    (9, 256, 512, 32, "f16", "f16"),
+    (17, 300, 256, 32, "bf16", "f16"),
+    (130, 512, 1024, 128, "bf16", "f16"),
+    (64, 256, 384, 64, "f16", "f32"),
+    (33, 256, 256, 32, "f32", "f16"),
+    (200, 640, 512, 16, "f16", "f16"),
+    (100, 192, 96, 12, "f16", "f16"),
+    (20, 128, 104, 8, "bf16", "f16"),
+    (2, 40, 44, 4, "f32", "f16"),
+    (257, 136, 320, 64, "bf16", "f32"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,gs,act,sdt", FWD_CASES)
+def test_forward_all_routes(M, N, K, gs, act, sdt):
+    q = lib()
+    case = make_linear(M, K, N, gs, act, sdt, seed=M * 7 + N, s_lo=0.005 if sdt == "f32" else 0.002)
+    w = case.w
+    pw = pack(q, w)
+    x = dev(case.x)
+    ref, norm = oracle_fwd(case.x, w)
+    tol = TOL[case.x.dtype]
+    ran = run_routes(q, lambda: q.linear_fwd(pw, x))
+    assert ran and ran[0][0] == "auto"
+    for fam, y in ran:
+        assert_within(y, ref, norm, tol, f"fwd {fam} route={q.route(q.OP_FWD, pw, M, case.x.dtype)}")
+
+
+BWD_CASES = [
+    (4, 32, 64, 16, "f32", "f32"),        # tiny workload
+    (2, 300, 256, 32, "f16", "f16"),
+    (8, 256, 200, 8, "f32", "f16"),
+    (64, 512, 512, 128, "f32", "f16"),
+    (130, 1000, 256, 128, "bf16", "f16"),
+    (96, 512, 384, 32, "f16", "f16"),
+    (40, 384, 256, 256, "f16", "f32"),
+    (50, 100, 96, 32, "f32", "f16"),
+    (12, 64, 72, 24, "bf16", "f16"),
+    (7, 136, 512, 128, "bf16", "f32"),
+    (200, 200, 384, 128, "f16", "f16"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,gs,act,sdt", BWD_CASES)
+def test_backward_all_routes(M, N, K, gs, act, sdt):
+    q = lib()
+    case = make_linear(M, K, N, gs, act, sdt, seed=M * 11 + K, fwd=False, bwd=True,
+                       sigma=0.1 if act == "f32" else 1.0)
+    w = case.w
+    pw = pack(q, w)
+    g = dev(case.d_out)
+    ref, norm = oracle_bwd(case.d_out, w)
+    tol = TOL[case.d_out.dtype]
+    ran = run_routes(q, lambda: q.linear_bwd_input(pw, g))
+    assert ran and ran[0][0] == "auto"
+    for fam, dx in ran:
+        assert_within(dx, ref, norm, tol, f"bwd {fam} route={q.route(q.OP_BWD_INPUT, pw, M, case.d_out.dtype)}")
+
+
+QKV_CASES = [
+    (128, 2048, (2048, 512, 512), 32, "f16"),     # the Llama projection triple at M = 128
+    (20, 96, (64, 40, 24), 32, "bf16"),
+    (9, 256, (256, 128, 128), 64, "f32"),
+    (3, 128, (128, 64, 64), 16, "f16"),
+    (300, 512, (384, 128, 200), 128, "f16"),
+]
+
+
+@pytest.mark.parametrize("M,K,Ns,gs,act", QKV_CASES)
+def test_qkv_fused(M, K, Ns, gs, act):
+    q = lib()
+    case = make_qkv(M, K, Ns, gs, act, "f16", seed=M + K)
+    pws = [pack(q, w) for w in case.weights]
+    x = dev(case.x)
+    rows = sample_rows(M, 24) if M > 128 else None
+    refs = [oracle_fwd(case.x, w, rows) for w in case.weights]
+    tol = TOL[case.x.dtype]
+    for fam, outs in run_routes(q, lambda: q.qkv_fused(*pws, x)):
+        for name, o, (ref, norm) in zip("qkv", outs, refs):
+            assert_within(o, ref, norm, tol, f"qkv {fam} {name}", rows)
+    # fused against three separate forwards: both within tol of the oracle, so within 2 tol of each other
+    fused = q.qkv_fused(*pws, x)
+    for o, pw, (_, norm) in zip(fused, pws, refs):
+        sep = q.linear_fwd(pw, x)
+        diff = (o - sep).abs().cpu().numpy().astype(np.float64)
+        if rows is not None:
+            diff = diff[rows]
+        assert np.all(diff <= 2 * tol * norm + 1e-30)
+
+
+# ---- the suite's workloads at full size (sampled rows where the oracle would be slow) ----------
+
+def test_workload_tiny():
+    q = lib()
+    case = make_workload("tiny")
+    pw = pack(q, case.w)
+    y = q.linear_fwd(pw, dev(case.x))
+    ref, norm = oracle_fwd(case.x, case.w)
+    assert_within(y, ref, norm, 1e-5, "tiny fwd")
+    dx = q.linear_bwd_input(pw, dev(case.d_out))
+    ref, norm = oracle_bwd(case.d_out, case.w)
+    assert_within(dx, ref, norm, 1e-5, "tiny bwd")
+
+
+def test_workload_decode():
+    q = lib()
+    case = make_workload("decode")
+    pw = pack(q, case.w)
+    assert q.route(q.OP_FWD, pw, 1, case.x.dtype) == "gemv"
+    y = q.linear_fwd(pw, dev(case.x))
+    ref, norm = oracle_fwd(case.x, case.w)
+    assert_within(y, ref, norm, 2e-3, "decode")
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16", "f32"])
+def test_workload_prefill(act):
+    q = lib()
+    case = make_workload("prefill", act_dtype=act)
+    pw = pack(q, case.w)
+    y = q.linear_fwd(pw, dev(case.x))
+    rows = sample_rows(case.M)
+    ref, norm = oracle_fwd(case.x, case.w, rows)
+    assert_within(y, ref, norm, TOL[case.x.dtype], f"prefill {act}", rows)
+
+
+@pytest.mark.parametrize("M", [128, 508, 512])
+def test_workload_qkv(M):
+    q = lib()
+    case = make_workload("qkv", M=M)
+    pws = [pack(q, w) for w in case.weights]
+    assert q.route(q.OP_QKV, pws[0], M, case.x.dtype) == "qkv_fused"
+    outs = q.qkv_fused(*pws, dev(case.x))
+    rows = sample_rows(M)
+    for name, o, w in zip("qkv", outs, case.weights):
+        ref, norm = oracle_fwd(case.x, w, rows)
+        assert_within(o, ref, norm, 2e-3, f"qkv M={M} {name}", rows)
+
+
+@pytest.mark.parametrize("act", ["f32", "f16", "bf16"])
+def test_workload_bwd(act):
+    q = lib()
+    case = make_workload("bwd")
+    d_out = case.d_out if act == "f32" else case.d_out.to({"f16": torch.float16, "bf16": torch.bfloat16}[act])
+    pw = pack(q, case.w)
+    dx = q.linear_bwd_input(pw, dev(d_out))
+    rows = sample_rows(case.M)
+    ref, norm = oracle_bwd(d_out, case.w, rows)
+    assert_within(dx, ref, norm, TOL[d_out.dtype], f"bwd {act}", rows)
