@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--ops", default="decode,prefill,qkv,bwd", help="comma-separated subset of the step")
     p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=32, help="rows per M=512 op in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=256, help="rows per M=512 op in the oracle sample")
     return p.parse_args()
 
 

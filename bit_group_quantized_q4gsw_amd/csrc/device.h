@@ -57,7 +57,8 @@ __device__ __forceinline__ h2 codes_minus8_f16(uint32_t w, int s) {
 // Signed code value c - 8 of nibble position p, exactly, as an integer.  XOR-ing a word with
 // 0x88888888 turns every nibble into the two's-complement 4-bit form of c - 8.
 __device__ __forceinline__ int signed_code(uint32_t wx, int p) {
-    return __builtin_amdgcn_sbfe((int)wx, 4 * p, 4);
+    // the builtin's C type is unsigned; the bits are the sign-extended field
+    return (int)__builtin_amdgcn_sbfe((int)wx, 4 * p, 4);
 }
 
 // Exact (c - 8) pair s (k-offsets 2s, 2s+1) in bf16: small integers are exact in fp32 with

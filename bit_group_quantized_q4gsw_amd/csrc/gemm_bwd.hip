@@ -45,8 +45,8 @@ __device__ __forceinline__ uint32_t byte_pair(uint32_t w_lo_row, uint32_t w_hi_r
 // Exact bf16 pair (c_even_row - 8, c_odd_row - 8) of the nibbles at bit `sh` of the two
 // 16-bit halves of tx (tx = byte pair ^ 0x00880088, so nibbles are two's-complement c - 8).
 __device__ __forceinline__ uint32_t pair_minus8_bf16(uint32_t tx, int sh) {
-    const float lo = (float)__builtin_amdgcn_sbfe((int)tx, sh, 4);
-    const float hi = (float)__builtin_amdgcn_sbfe((int)tx, 16 + sh, 4);
+    const float lo = (float)signed_code(tx, sh >> 2);
+    const float hi = (float)signed_code(tx, 4 + (sh >> 2));
     return __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
 }
 
