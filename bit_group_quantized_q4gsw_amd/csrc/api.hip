@@ -460,6 +460,6 @@ void q4gsw_force_route(int32_t route) { g_forced_route.store(route, std::memory_
 
 uint32_t q4gsw_layout_version(void) { return Q4GSW_LAYOUT_VERSION; }
 
-const char* q4gsw_build_info(void) { return "q4gsw gfx950 layout-v1 built " __DATE__ " " __TIME__; }
+const char* q4gsw_build_info(void) { return "q4gsw gfx950 layout-v2 built " __DATE__ " " __TIME__; }
 
 }  // extern "C"

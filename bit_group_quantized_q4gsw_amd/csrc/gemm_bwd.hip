@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
         if constexpr (MODE == kModeFold) {
             if (!mb_in) return;
             const int64_t g = (mb_O * 8) / w.gs;
-            const u4 v = ldg16(static_cast<const uint16_t*>(w.scales) + g * w.n_pad + nc + 8 * mb_ro);
+            const u4 v = ldg16(static_cast<const uint16_t*>(w.scales) + scale_index(w.g_pad, nc + 8 * mb_ro, g));
             sreg[0] = v.x; sreg[1] = v.y; sreg[2] = v.z; sreg[3] = v.w;
         }
     };
@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
         if constexpr (MODE == kModeSplit) {
 #pragma unroll
             for (int v = 0; v < kVals; ++v)
-                ascale[v] = (n + v < w.N) ? load_scale(w.scales, w.scale_f16, group * w.n_pad + n + v) : 0.f;
+                ascale[v] = (n + v < w.N) ? load_scale(w.scales, w.scale_f16, scale_index(w.g_pad, n + v, group))
+                                          : 0.f;
         }
 #pragma unroll
         for (int c = 0; c < kUnits; ++c) {

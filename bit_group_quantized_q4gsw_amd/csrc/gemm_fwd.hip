@@ -37,6 +37,7 @@ struct FwdSegArgs {
     int64_t n_pad[3];
     int64_t out_ld[3];            // row pitch of out
     int64_t tile_start[4];        // first N tile of each segment (prefix sums), tile_start[nseg] = total
+    int64_t g_pad;                // scale groups stored (shared: the segments share K and group size)
     int nseg;
 };
 
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(256) void gemm_fwd_kernel(FwdSegArgs seg, const voi
     const uint8_t* nib = seg.nib[sg];
     const void* scales = seg.scales[sg];
     const int64_t n_pad = seg.n_pad[sg];
+    const int64_t g_pad = seg.g_pad;
     const int64_t m0 = (int64_t)blockIdx.y * kBM;
     const int64_t kocts = k_pad >> 3;
     const int64_t n_chunks = (K + CK - 1) / CK;
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(256) void gemm_fwd_kernel(FwdSegArgs seg, const voi
                 for (int t = 0; t < C::kSteps; ++t) {
                     const int64_t g = (kc + 32 * t + 8 * lq) / gs;
                     const u2 sv = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(scales) +
-                                                               g * n_pad + n0 + 4 * lrow);
+                                                               scale_index(g_pad, n0 + 4 * lrow, g));
                     const uint32_t s01 = sv.x, s23 = sv.y;
                     const uint32_t sw[4] = {s01 & 0xFFFFu, s01 >> 16, s23 & 0xFFFFu, s23 >> 16};
                     const uint32_t wd[4] = {breg[t].x, breg[t].y, breg[t].z, breg[t].w};
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256) void gemm_fwd_kernel(FwdSegArgs seg, const voi
                 const int64_t g = kc / gs;
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    gscale[u] = load_scale(scales, scale_f16, g * n_pad + n0 + 4 * lrow + u);
+                    gscale[u] = load_scale(scales, scale_f16, scale_index(g_pad, n0 + 4 * lrow + u, g));
             }
 
             // ---- MFMA over the 8 row tiles ----
@@ -353,6 +355,7 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
         col += segs[i].w.n_pad;
     }
     a.tile_start[nseg] = tiles;
+    a.g_pad = w0.g_pad;
     const int mode = plan.mode;
     const int ck = fwd_chunk(mode, w0.gs);
     const int64_t n_chunks = (w0.K + ck - 1) / ck;

@@ -75,114 +75,170 @@ __device__ __forceinline__ void load_act8(const void* src, int64_t base, int64_t
 
 }  // namespace
 
-// Grid: (n_pad / 32, splits).  Block: 256 threads = 4 waves.  A block owns 32 rows; its
-// waves take interleaved 128-column steps of the block's K range.
+// Grid: (n_pad / 8, splits).  Block: W waves (64 * W threads, W <= 16).  A block owns one
+// row-octet (8 rows).  Each load instruction of a wave reads 1 KB of contiguous codes: lane l
+// takes bytes [16 l, 16 l + 16) of a 32-micro-block run, i.e. rows 4 (l & 1) .. +3 of
+// k-octet l / 2.  A wave takes 64 k-octets per iteration (two loads per lane, both issued
+// before any unpacking) and the W waves of a block take adjacent 512-column slices, so a
+// decode launch is many small blocks that each stream one contiguous row-octet.
 template <int MT, int XT>
-__global__ __launch_bounds__(256) void gemv_fwd_kernel(WView w, const void* __restrict__ x, int x_vec,
-                                                       float* __restrict__ out, int64_t out_ld,
-                                                       int64_t split_stride, int64_t row_limit,
-                                                       int steps_per_split) {
-    __shared__ float red[4][4][MT][8];
+__global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __restrict__ x, int x_vec,
+                                                        float* __restrict__ out, int64_t out_ld,
+                                                        int64_t split_stride, int64_t row_limit,
+                                                        int octs_per_split) {
+    __shared__ float red[16][MT][8];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int ro = lane >> 4;
-    const int ko = lane & 15;
-    const int64_t R = (int64_t)blockIdx.x * 4 + ro;
+    const int nw = blockDim.x >> 6;
+    const int half = lane & 1;
+    const int64_t R = blockIdx.x;
     const int64_t kocts = w.k_pad >> 3;
-    const int total_steps = (int)(w.k_pad >> 7);
-    const int s0 = (int)blockIdx.y * steps_per_split;
-    const int s1 = min(s0 + steps_per_split, total_steps);
-    const uint8_t* rowbase = w.nib + 32 * (R * kocts);
+    const int64_t o0 = (int64_t)blockIdx.y * octs_per_split;
+    const int64_t o1 = min(o0 + (int64_t)octs_per_split, kocts);
+    const uint8_t* rowbase = w.nib + 32 * (R * kocts) + 16 * half;
+    const int64_t row0 = 8 * R + 4 * half;
 
-    float acc[MT][8];
+    float acc[MT][4];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[m][i] = 0.0f;
+        for (int r = 0; r < 4; ++r) acc[m][r] = 0.0f;
 
-    for (int st = s0 + wave; st < s1; st += 4) {
-        const int64_t O = (int64_t)st * 16 + ko;
-        const int64_t k0 = O * 8;
-        uint32_t wd[8];
-        load_micro_block(rowbase + 32 * O, wd);
-        float sc[8];
-        load_scales8(w.scales, w.scale_f16, (k0 / w.gs) * w.n_pad + 8 * R, sc);
-        if constexpr (XT == kF16) {
-            h2 xp[MT][4];
+    for (int64_t ob = o0 + (int64_t)wave * 64; ob < o1; ob += (int64_t)nw * 64) {
+        u4 q[2];
+        float sc[2][4];
+        u4 xr[2][MT];             // 8 activations (fp16/bf16), or the first 4 (fp32)
+        f4 xr2[2][MT];            // fp32: the last 4
+        bool live[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t O = ob + 32 * j + (lane >> 1);
+            live[j] = O < o1;
+            if (!live[j]) continue;
+            const int64_t k0 = O * 8;
+            q[j] = ldg16_stream(rowbase + 32 * O);
+            const int64_t si = scale_index(w.g_pad, row0, k0 / w.gs);
+            if (w.scale_f16) {
+                const u2 v = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(w.scales) + si);
+                sc[j][0] = f16_bits_to_f32((uint16_t)(v.x & 0xFFFFu));
+                sc[j][1] = f16_bits_to_f32((uint16_t)(v.x >> 16));
+                sc[j][2] = f16_bits_to_f32((uint16_t)(v.y & 0xFFFFu));
+                sc[j][3] = f16_bits_to_f32((uint16_t)(v.y >> 16));
+            } else {
+                const f4 v = *reinterpret_cast<const f4*>(static_cast<const float*>(w.scales) + si);
+                sc[j][0] = v.x; sc[j][1] = v.y; sc[j][2] = v.z; sc[j][3] = v.w;
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const int64_t base = m * w.K + k0;
+                const int64_t xb = m * w.K + k0;
                 if (x_vec && k0 + 8 <= w.K) {
-                    const u4 a = ldg16(static_cast<const uint16_t*>(x) + base);
-                    xp[m][0] = bitcast<h2>(a.x); xp[m][1] = bitcast<h2>(a.y);
-                    xp[m][2] = bitcast<h2>(a.z); xp[m][3] = bitcast<h2>(a.w);
+                    if constexpr (XT == kF32) {
+                        xr[j][m] = ldg16(static_cast<const float*>(x) + xb);
+                        xr2[j][m] = *reinterpret_cast<const f4*>(static_cast<const float*>(x) + xb + 4);
+                    } else {
+                        xr[j][m] = ldg16(static_cast<const uint16_t*>(x) + xb);
+                    }
                 } else {
-                    _Float16 t[8];
+                    if constexpr (XT == kF32) {
+                        f4 a, b;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        t[j] = (k0 + j < w.K) ? bitcast<_Float16>(static_cast<const uint16_t*>(x)[base + j])
-                                              : (_Float16)0.0f;
+                        for (int e = 0; e < 4; ++e) {
+                            a[e] = (k0 + e < w.K) ? static_cast<const float*>(x)[xb + e] : 0.0f;
+                            b[e] = (k0 + 4 + e < w.K) ? static_cast<const float*>(x)[xb + 4 + e] : 0.0f;
+                        }
+                        xr[j][m] = bitcast<u4>(a);
+                        xr2[j][m] = b;
+                    } else {
+                        uint32_t e[8];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) xp[m][s] = h2{t[2 * s], t[2 * s + 1]};
+                        for (int t = 0; t < 8; ++t)
+                            e[t] = (k0 + t < w.K) ? static_cast<const uint16_t*>(x)[xb + t] : 0u;
+                        xr[j][m] = u4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                                      e[6] | (e[7] << 16)};
+                    }
                 }
             }
+        }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                h2 c8[4];
+        for (int j = 0; j < 2; ++j) {
+            if (!live[j]) continue;
+            const uint32_t wd[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+            if constexpr (XT == kF16) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) c8[s] = codes_minus8_f16(wd[i], s);
+                for (int r = 0; r < 4; ++r) {
+                    h2 c8[4];
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    float t = 0.0f;
+                    for (int s = 0; s < 4; ++s) c8[s] = codes_minus8_f16(wd[r], s);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_fdot2(c8[s], xp[m][s], t, false);
-                    acc[m][i] = fmaf(t, sc[i], acc[m][i]);
+                    for (int m = 0; m < MT; ++m) {
+                        float t = 0.0f;
+                        t = __builtin_amdgcn_fdot2(c8[0], bitcast<h2>(xr[j][m].x), t, false);
+                        t = __builtin_amdgcn_fdot2(c8[1], bitcast<h2>(xr[j][m].y), t, false);
+                        t = __builtin_amdgcn_fdot2(c8[2], bitcast<h2>(xr[j][m].z), t, false);
+                        t = __builtin_amdgcn_fdot2(c8[3], bitcast<h2>(xr[j][m].w), t, false);
+                        acc[m][r] = fmaf(t, sc[j][r], acc[m][r]);
+                    }
                 }
-            }
-        } else {
-            float xf[MT][8];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) load_act8<XT>(x, m * w.K + k0, k0, w.K, x_vec, xf[m]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float c[8];
-                word_codes_minus8_f32(wd[i], c);
+            } else {
+                float xf[MT][8];
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    float t = 0.0f;
+                    if constexpr (XT == kF32) {
+                        const f4 a = bitcast<f4>(xr[j][m]);
+                        const f4 b = xr2[j][m];
+                        xf[m][0] = a.x; xf[m][1] = a.y; xf[m][2] = a.z; xf[m][3] = a.w;
+                        xf[m][4] = b.x; xf[m][5] = b.y; xf[m][6] = b.z; xf[m][7] = b.w;
+                    } else {
+                        const uint32_t u[4] = {xr[j][m].x, xr[j][m].y, xr[j][m].z, xr[j][m].w};
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) t = fmaf(xf[m][j], c[j], t);
-                    acc[m][i] = fmaf(t, sc[i], acc[m][i]);
+                        for (int e = 0; e < 4; ++e) {
+                            xf[m][2 * e] = bitcast<float>(u[e] << 16);
+                            xf[m][2 * e + 1] = bitcast<float>(u[e] & 0xFFFF0000u);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float c[8];
+                    word_codes_minus8_f32(wd[r], c);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        float t = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t = fmaf(xf[m][e], c[e], t);
+                        acc[m][r] = fmaf(t, sc[j][r], acc[m][r]);
+                    }
                 }
             }
         }
     }
 
-    // Sum over the 16 lanes of a row-octet, then over the 4 waves.
+    // Sum over the 32 lanes holding the same four rows, then over the waves.
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float v = acc[m][i];
-            v = wave_xor_sum(v, 1);
+        for (int r = 0; r < 4; ++r) {
+            float v = acc[m][r];
             v = wave_xor_sum(v, 2);
             v = wave_xor_sum(v, 4);
             v = wave_xor_sum(v, 8);
-            acc[m][i] = v;
+            v = wave_xor_sum(v, 16);
+            v = wave_xor_sum(v, 32);
+            acc[m][r] = v;
         }
-    if (ko == 0) {
+    if (lane < 2) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) red[wave][ro][m][i] = acc[m][i];
+            for (int r = 0; r < 4; ++r) red[wave][m][4 * lane + r] = acc[m][r];
     }
     __syncthreads();
-    if (threadIdx.x < 32 * MT) {
-        const int m = threadIdx.x >> 5;
-        const int r = threadIdx.x & 31;
-        const float v = (red[0][r >> 3][m][r & 7] + red[1][r >> 3][m][r & 7]) +
-                        (red[2][r >> 3][m][r & 7] + red[3][r >> 3][m][r & 7]);
-        const int64_t n = (int64_t)blockIdx.x * 32 + r;
+    for (int t = threadIdx.x; t < 8 * MT; t += blockDim.x) {
+        const int m = t >> 3;
+        const int r = t & 7;
+        float v = 0.0f;
+        for (int wv = 0; wv < nw; ++wv) v += red[wv][m][r];
+        const int64_t n = 8 * R + r;
         if (n < row_limit) out[(int64_t)blockIdx.y * split_stride + m * out_ld + n] = v;
     }
 }
@@ -220,7 +276,7 @@ __global__ __launch_bounds__(256) void gemv_bwd_kernel(WView w, const void* __re
         uint32_t wd[8];
         load_micro_block(w.nib + 32 * (R * kocts + O), wd);
         float sc[8];
-        load_scales8(w.scales, w.scale_f16, g * w.n_pad + n0, sc);
+        load_scales8(w.scales, w.scale_f16, scale_index(w.g_pad, n0, g), sc);
         float dp[MT][8];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -286,12 +342,21 @@ hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t 
     return hipGetLastError();
 }
 
+// Waves per block: one per 64 k-octets of the split, at most 16.
+static int gemv_fwd_waves(const WView& w, int splits) {
+    const int64_t octs = (w.k_pad / 8 + splits - 1) / splits;
+    const int64_t nw = (octs + 63) / 64;
+    return (int)(nw > 16 ? 16 : (nw < 1 ? 1 : nw));
+}
+
 int gemv_fwd_splits(const WView& w, int64_t M) {
     (void)M;
-    const int64_t blocks = w.n_pad / 32;
-    const int64_t steps = w.k_pad / 128;
+    // One block per row-octet keeps every K step of those rows in one block (no reduction
+    // launch).  Only very short N with long K splits K across blocks.
+    const int64_t blocks = w.n_pad / 8;
+    const int64_t octs = w.k_pad / 8;
     int64_t splits = 1;
-    while (blocks * splits < 512 && steps / (splits * 2) >= 4) splits *= 2;
+    while (blocks * splits < 256 && octs / (splits * 2) >= 1024) splits *= 2;
     return (int)splits;
 }
 
@@ -305,13 +370,14 @@ int gemv_bwd_splits(const WView& w, int64_t M) {
 }
 
 template <int XT>
-static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, hipStream_t s, const WView& w, const void* x, int vec,
-                                    float* out, int64_t ld, int64_t stride, int64_t limit, int per) {
+static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_t s, const WView& w,
+                                    const void* x, int vec, float* out, int64_t ld, int64_t stride,
+                                    int64_t limit, int per) {
     switch (M) {
-#define Q4GSW_CASE(MT)                                                                                   \
-    case MT:                                                                                             \
-        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT>), grid, dim3(256), 0, s, w, x, vec, out, ld, stride, \
-                           limit, per);                                                                  \
+#define Q4GSW_CASE(MT)                                                                               \
+    case MT:                                                                                         \
+        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT>), grid, block, 0, s, w, x, vec, out, ld, stride, \
+                           limit, per);                                                              \
         break;
         Q4GSW_CASE(1) Q4GSW_CASE(2) Q4GSW_CASE(3) Q4GSW_CASE(4)
         Q4GSW_CASE(5) Q4GSW_CASE(6) Q4GSW_CASE(7) Q4GSW_CASE(8)
@@ -323,18 +389,20 @@ static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, hipStream_t s, const W
 
 hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
                            hipStream_t s) {
-    const int64_t steps = w.k_pad / 128;
-    const int per = (int)((steps + splits - 1) / splits);
-    const dim3 grid((unsigned)(w.n_pad / 32), (unsigned)splits);
+    const int64_t octs = w.k_pad / 8;
+    const int per = (int)((octs + splits - 1) / splits);
+    const int waves = gemv_fwd_waves(w, splits);
+    const dim3 grid((unsigned)(w.n_pad / 8), (unsigned)splits);
+    const dim3 block((unsigned)(64 * waves));
     const int esize = x_dtype == kF32 ? 4 : 2;
     const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) && ((w.K * esize) % 16 == 0);
     const int64_t ld = splits == 1 ? w.N : w.n_pad;
     const int64_t stride = splits == 1 ? 0 : M * w.n_pad;
     const int64_t limit = splits == 1 ? w.N : w.n_pad;
     switch (x_dtype) {
-        case kF32: return gemv_fwd_dispatch<kF32>(M, grid, s, w, x, vec, out, ld, stride, limit, per);
-        case kF16: return gemv_fwd_dispatch<kF16>(M, grid, s, w, x, vec, out, ld, stride, limit, per);
-        default: return gemv_fwd_dispatch<kBF16>(M, grid, s, w, x, vec, out, ld, stride, limit, per);
+        case kF32: return gemv_fwd_dispatch<kF32>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        case kF16: return gemv_fwd_dispatch<kF16>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        default: return gemv_fwd_dispatch<kBF16>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
     }
 }
 

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(WView w, const void* _
             const float a = load_elem<XT>(x, m * w.K + k);
             part = fmaf(a, (float)(code_at(w.nib, w.k_pad, n, k) - 8), part);
         }
-        acc = fmaf(part, load_scale(w.scales, w.scale_f16, g * w.n_pad + n), acc);
+        acc = fmaf(part, load_scale(w.scales, w.scale_f16, scale_index(w.g_pad, n, g)), acc);
     }
     y[t] = acc;
 }
@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void generic_bwd_kernel(WView w, const void* _
         float part = 0.0f;
         const int64_t n1 = n0 + 64 < w.N ? n0 + 64 : w.N;
         for (int64_t n = n0; n < n1; ++n) {
-            const float d = load_elem<GT>(d_out, m * w.N + n) * load_scale(w.scales, w.scale_f16, g * w.n_pad + n);
+            const float d =
+                load_elem<GT>(d_out, m * w.N + n) * load_scale(w.scales, w.scale_f16, scale_index(w.g_pad, n, g));
             part = fmaf(d, (float)(code_at(w.nib, w.k_pad, n, k) - 8), part);
         }
         acc += part;

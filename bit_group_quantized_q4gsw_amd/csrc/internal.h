@@ -10,7 +10,7 @@ namespace q4gsw {
 // Device view of one packed weight.
 struct WView {
     const uint8_t* nib;      // nibble plane
-    const void* scales;      // scale plane [g_pad][n_pad]
+    const void* scales;      // scale plane, indexed by scale_index(g_pad, n, g)
     int scale_f16;           // 1: fp16 scales, 0: fp32
     int64_t N, K, gs, n_pad, k_pad, g_pad;
 };

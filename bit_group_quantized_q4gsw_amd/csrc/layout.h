@@ -7,7 +7,9 @@
 //
 //   [0, 256)                      header written by the pack kernel (flags)
 //   nibble plane                  n_pad * k_pad / 2 bytes
-//   scale plane                   g_pad * n_pad scales, [group][n], input dtype
+//   scale plane                   g_pad * n_pad scales in the input dtype, row-octet major:
+//                                 [n / 8][group][n % 8], so the scales of one row-octet (the
+//                                 unit a decode block streams) are contiguous
 //
 // Nibble plane: 8x8 micro-blocks.  Micro-block (row-octet R, k-octet O) sits at
 // byte 32 * (R * (k_pad / 8) + O).  Its word i (bytes 4i..4i+3) holds row 8R+i,
@@ -54,6 +56,11 @@ inline Layout make_layout(int64_t N, int64_t K, int64_t group_size, int scale_by
     L.scale_bytes = (uint64_t)L.g_pad * (uint64_t)L.n_pad * (uint64_t)scale_bytes_per;
     L.total = (uint64_t)round_up((int64_t)(L.scale_offset + L.scale_bytes), (int64_t)kAlign);
     return L;
+}
+
+// Index of scale[group g, row n] in the scale plane.
+__host__ __device__ inline int64_t scale_index(int64_t g_pad, int64_t n, int64_t g) {
+    return (n >> 3) * (g_pad * 8) + g * 8 + (n & 7);
 }
 
 // Nibble position of k-offset j (0..7) inside a word.

@@ -39,16 +39,16 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restri
     if (bad) hdr[kHdrBadCode] = 1u;          // every writer stores the same value
 }
 
-// One thread per stored scale [g_pad][n_pad]; padding gets 0.  For fp16 scales also
-// checks that (code - 8) * s stays a finite normal fp16 for every code.
+// One thread per stored scale, in plane order [n / 8][group][n % 8]; padding gets 0.  For
+// fp16 scales also checks that (code - 8) * s stays a finite normal fp16 for every code.
 __global__ __launch_bounds__(256) void pack_scales_kernel(const void* __restrict__ src, int scale_f16,
                                                           int64_t N, int64_t G, int64_t n_pad,
                                                           int64_t g_pad, void* __restrict__ dst,
                                                           uint32_t* __restrict__ hdr) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= g_pad * n_pad) return;
-    const int64_t g = t / n_pad;
-    const int64_t n = t % n_pad;
+    const int64_t g = (t >> 3) % g_pad;
+    const int64_t n = (t / (g_pad * 8)) * 8 + (t & 7);
     const bool real = (g < G) && (n < N);
     if (scale_f16) {
         uint16_t v = real ? static_cast<const uint16_t*>(src)[g * N + n] : (uint16_t)0;
@@ -88,16 +88,16 @@ __global__ __launch_bounds__(256) void unpack_codes_kernel(const uint32_t* __res
 }
 
 __global__ __launch_bounds__(256) void unpack_scales_kernel(const void* __restrict__ plane, int scale_f16,
-                                                            int64_t N, int64_t G, int64_t n_pad,
+                                                            int64_t N, int64_t G, int64_t g_pad,
                                                             void* __restrict__ dst) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= G * N) return;
     const int64_t g = t / N;
     const int64_t n = t % N;
     if (scale_f16)
-        static_cast<uint16_t*>(dst)[t] = static_cast<const uint16_t*>(plane)[g * n_pad + n];
+        static_cast<uint16_t*>(dst)[t] = static_cast<const uint16_t*>(plane)[scale_index(g_pad, n, g)];
     else
-        static_cast<float*>(dst)[t] = static_cast<const float*>(plane)[g * n_pad + n];
+        static_cast<float*>(dst)[t] = static_cast<const float*>(plane)[scale_index(g_pad, n, g)];
 }
 
 hipError_t launch_unpack(const WView& w, uint8_t* codes, void* scales, hipStream_t s) {
@@ -107,7 +107,7 @@ hipError_t launch_unpack(const WView& w, uint8_t* codes, void* scales, hipStream
     const int64_t G = w.K / w.gs;
     const int64_t ng = G * w.N;
     hipLaunchKernelGGL(unpack_scales_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, s, w.scales,
-                       w.scale_f16, w.N, G, w.n_pad, scales);
+                       w.scale_f16, w.N, G, w.g_pad, scales);
     return hipGetLastError();
 }
 

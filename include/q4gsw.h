@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define Q4GSW_MAGIC 0x57534734u          /* "4GSW" */
-#define Q4GSW_LAYOUT_VERSION 1u
+#define Q4GSW_LAYOUT_VERSION 2u
 
 typedef enum q4gsw_status {
     Q4GSW_OK = 0,
@@ -100,13 +100,13 @@ typedef struct q4gsw_weight {
     int64_t group_size;       /* K-run sharing one scale */
     int64_t n_pad;            /* N rounded up to the packing tile */
     int64_t k_pad;            /* K rounded up to the packing tile */
-    int64_t g_pad;            /* scale rows stored: ceil(k_pad / group_size) */
+    int64_t g_pad;            /* scale groups stored: ceil(k_pad / group_size) */
     int32_t scale_dtype;      /* Q4GSW_F16 or Q4GSW_F32 */
     uint32_t flags;           /* Q4GSW_FLAG_* set by q4gsw_pack */
     void *data;               /* device pointer to the packed buffer */
     uint64_t bytes;           /* bytes of the packed buffer in use */
     uint64_t nibble_offset;   /* byte offset of the 4-bit code plane */
-    uint64_t scale_offset;    /* byte offset of the scale plane [g_pad, n_pad] */
+    uint64_t scale_offset;    /* byte offset of the scale plane (g_pad * n_pad scales) */
 } q4gsw_weight;
 
 /* Set by q4gsw_pack when every fp16 scale s is 0 or 2^-14 <= |s| <= 8188, so that

@@ -6,7 +6,9 @@ Used only to check, byte for byte, what the GPU pack kernel writes.  The layout:
                     8x8 micro-blocks: block (row-octet R, k-octet O) at byte 32*(R*(k_pad/8)+O);
                     word i (4 bytes, little endian) of a block = row 8R+i, columns 8O..8O+7;
                     column 8O+j sits in nibble position p(j) = j//2 + 4*(j%2) of the word
-  scale plane       at the next 256-byte boundary: [g_pad][n_pad] scales, g_pad = ceil(k_pad/gs)
+  scale plane       at the next 256-byte boundary: g_pad * n_pad scales, g_pad = ceil(k_pad/gs),
+                    stored row-octet major: [n_pad/8][g_pad][8] (scale of row n, group g at
+                    (n//8)*g_pad*8 + g*8 + n%8)
   padding           code 8 outside [N, K]; scale 0 outside [K/gs, N]
 """
 import numpy as np
@@ -50,4 +52,5 @@ def scale_plane(scales: np.ndarray, K: int, gs: int) -> np.ndarray:
     g_pad = (k_pad + gs - 1) // gs
     plane = np.zeros((g_pad, n_pad), dtype=scales.dtype)
     plane[:G, :N] = scales
-    return plane.reshape(-1).view(np.uint8)
+    octet_major = plane.reshape(g_pad, n_pad // 8, 8).transpose(1, 0, 2)    # [n/8][g][n%8]
+    return np.ascontiguousarray(octet_major).reshape(-1).view(np.uint8)

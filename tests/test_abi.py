@@ -47,7 +47,7 @@ def test_status_and_route_names(q):
     assert "group_size" in q.status_str(4)
     assert q.route_name(2) == "gemv"
     assert q.route_name(99) == "unknown"
-    assert q.lib().q4gsw_layout_version() == 1
+    assert q.lib().q4gsw_layout_version() == 2
 
 
 S_OK, E_NULL, E_SHAPE, E_DTYPE, E_GROUP, E_ALIAS, E_CODE, E_WS, E_DESC, E_HIP, E_BUF, E_ROUTE = range(12)
@@ -97,7 +97,7 @@ def fake_desc(q, N, K, gs, sdt=1, flags=0, data=FAKE * 4):
     scale_off = rup(nib_off + n_pad * k_pad // 2, 256)
     total = rup(scale_off + g_pad * n_pad * (2 if sdt == 1 else 4), 256)
     d = q.WeightDesc()
-    d.magic, d.version = 0x57534734, 1
+    d.magic, d.version = 0x57534734, 2
     d.N, d.K, d.group_size = N, K, gs
     d.n_pad, d.k_pad, d.g_pad = n_pad, k_pad, g_pad
     d.scale_dtype, d.flags = sdt, flags
