@@ -12,6 +12,7 @@ typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
@@ -98,10 +99,23 @@ __device__ __forceinline__ f4 mfma_bf16(u4 a, u4 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<b8>(a), bitcast<b8>(b), c, 0, 0, 0);
 }
 
+// gfx950 v_mfma_f32_32x32x16 (twice the issue rate of the 16x16x32 form on this chip):
+// A fragment: lane l holds A[l%32][8*(l/32) + 0..7]; B fragment: B[8*(l/32) + 0..7][l%32];
+// D: lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32_f16(u4 a, u4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<h8>(a), bitcast<h8>(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_bf16(u4 a, u4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<b8>(a), bitcast<b8>(b), c, 0, 0, 0);
+}
+
 // ---- global loads ---------------------------------------------------------------------------
 __device__ __forceinline__ u4 ldg16(const void* p) { return *static_cast<const u4*>(p); }
 __device__ __forceinline__ u4 ldg16_stream(const void* p) {
     return __builtin_nontemporal_load(static_cast<const u4*>(p));
+}
+__device__ __forceinline__ u2 ldg8_stream(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const u2*>(p));
 }
 
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
