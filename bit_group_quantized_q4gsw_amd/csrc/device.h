@@ -118,6 +118,28 @@ __device__ __forceinline__ u2 ldg8_stream(const void* p) {
     return __builtin_nontemporal_load(static_cast<const u2*>(p));
 }
 
+// ---- LDS-DMA (global_load_lds) and explicit load/barrier ordering ----------------------------
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Each lane's bytes land at dst + size * lane; dst must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, lds_u8* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, lds_u8* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding and all of its LDS
+// operations are done, then meet the other waves.  Vector loads (LDS-DMA included) retire in
+// issue order, so this completes every load issued more than N loads ago.  The memory
+// clobber keeps the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
     return v + __shfl_xor(v, mask, 64);
 }

@@ -1,4 +1,5 @@
-// MFMA input gradient for M > 8:
+// MFMA input gradient for M > 8, 16x16x32 form with an LDS transpose of the codes; serves
+// the group sizes the 32x32x16 kernel (gemm_bwd2.hip) does not take:
 //   d_x[m, k] = sum_n d_out[m, n] * (code[n, k] - 8) * scale[k / gs, n]     (contract over N)
 // the frozen-base input gradient of the Vulkan q4gsw-backward PR body, reading the
 // forward's packed buffer as it is (no re-pack).
@@ -298,12 +299,12 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
         }
 }
 
-bool gemm_bwd_supported(const WView& w, int g_dtype, int fold_ok) {
+bool gemm_bwd_v1_supported(const WView& w, int g_dtype, int fold_ok) {
     if (g_dtype == kF16 && w.scale_f16 && fold_ok) return w.gs % 8 == 0;
     return w.gs % BwdCfg<kModeSplit>::kBK == 0;
 }
 
-BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M) {
+BwdPlan plan_gemm_bwd_v1(const WView& w, int g_dtype, int fold_ok, int64_t M) {
     BwdPlan p{};
     p.mode = (g_dtype == kF16 && w.scale_f16 && fold_ok) ? kModeFold : kModeSplit;
     const int bk = p.mode == kModeFold ? BwdCfg<kModeFold>::kBK : BwdCfg<kModeSplit>::kBK;
@@ -323,8 +324,8 @@ static void launch_bwd_t(dim3 grid, hipStream_t s, const WView& w, const void* d
                        per);
 }
 
-hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
-                           const BwdPlan& plan, float* ws, hipStream_t s) {
+hipError_t launch_gemm_bwd_v1(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
+                              const BwdPlan& plan, float* ws, hipStream_t s) {
     const int bk = plan.mode == kModeFold ? BwdCfg<kModeFold>::kBK : BwdCfg<kModeSplit>::kBK;
     const int64_t n_chunks = (w.N + kBCN - 1) / kBCN;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);

@@ -49,9 +49,6 @@ constexpr int kRowBytes = 128;      // one 16-bit activation row of a chunk in L
 constexpr int kPlaneBytes = kBM * kRowBytes;
 constexpr int kCodeBytes = 2048;    // one wave's codes for one chunk: 64 rows x 64 columns x 4 bits
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) void lds_void;
-
 struct FwdSegArgs {
     const uint8_t* nib[3];
     const void* scales[3];
@@ -63,23 +60,6 @@ struct FwdSegArgs {
     int64_t g_pad;                // scale groups stored (shared: the segments share K and group size)
     int nseg;
 };
-
-// Wait until at most N vector-memory loads of this wave are outstanding and all of its LDS
-// operations are done, then meet the other waves.  Vector loads (LDS-DMA included) retire in
-// issue order, so this completes every load issued more than N loads ago.  The memory
-// clobber keeps the compiler from moving LDS accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void wait_loads_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void dma16(const void* src, lds_u8* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, lds_u8* dst) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
-}
 
 // bf16 pair (16 (c_lo - 8), 16 (c_hi - 8)) for the four MFMA dwords of a code word.  H holds
 // 16 x the odd nibble positions and L 16 x the even ones as signed bytes; byte b of H is

@@ -54,15 +54,21 @@ bool gemm_fwd_supported(const WView& w, int x_dtype, int fold_ok);
 hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
                            const FwdPlan& plan, float* ws, hipStream_t s);
 
-// gemm_bwd.hip: MFMA input gradient.
+// MFMA input gradient: gemm_bwd2.hip (32x32x16) dispatches, gemm_bwd.hip (16x16x32) covers
+// the group sizes the former does not take.
 struct BwdPlan {
     int mode;                // kModeFold or kModeSplit
     int splits;              // N (contraction) splits
     int64_t ws_bytes;
+    int v1;                  // 1: the 16x16x32 kernel serves this call
 };
 bool gemm_bwd_supported(const WView& w, int g_dtype, int fold_ok);
 BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M);
 hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
                            const BwdPlan& plan, float* ws, hipStream_t s);
+bool gemm_bwd_v1_supported(const WView& w, int g_dtype, int fold_ok);
+BwdPlan plan_gemm_bwd_v1(const WView& w, int g_dtype, int fold_ok, int64_t M);
+hipError_t launch_gemm_bwd_v1(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
+                              const BwdPlan& plan, float* ws, hipStream_t s);
 
 }  // namespace q4gsw
