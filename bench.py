@@ -9,9 +9,10 @@ seeded synthetic inputs already resident in HBM:
 Outputs are fp32.  Several copies of every weight and activation are rotated so the
 working set exceeds the 256 MB Infinity Cache and the weight stream comes from HBM.
 
-Prints one JSON line: whole-step TFLOP/s, per-op TFLOP/s and weight GB/s with their
-roofline fractions, the roofline object of the dominant op (HIP-event timing on the
-launch stream) and the fp64 CPU oracle timed on a bounded sample of the same step.
+Prints one JSON line: whole-step TFLOP/s (the step captured as a HIP graph per rotated
+input set and replayed), per-op TFLOP/s and weight GB/s with their roofline fractions
+(eager launches between HIP events on the launch stream), the roofline object of the
+dominant op and the fp64 CPU oracle timed on a bounded sample of the same step.
 """
 import argparse
 import hashlib
@@ -40,6 +41,12 @@ def parse():
     p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per M=512 op in the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
+    p.add_argument("--ingest-counters", nargs=4, metavar=("OP_FETCH", "OP_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of a run of --ops OP and of "
+                        "--copy-calibration); writes profiles/traffic.json for the op (no GPU needed)")
+    p.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (with --ingest-counters)")
     return p.parse_args()
 
 
@@ -142,6 +149,72 @@ def traffic_for(op_name, src_hash):
     return ent.get("bytes_per_launch")
 
 
+# kernels that make up one launch of each op (a GEMM and, with K splits, its reduction)
+OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_splits"),
+              "qkv_m128": ("gemm_fwd", "reduce_splits"), "qkv_m508": ("gemm_fwd", "reduce_splits"),
+              "qkv_m512": ("gemm_fwd", "reduce_splits"), "bwd": ("gemm_bwd", "reduce_splits")}
+
+
+def _counter_means(d, counter):
+    """Mean counter value per dispatch, per kernel-name family, from a rocprofv3 --pmc CSV dir."""
+    import csv
+    import glob
+    sums = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            v = float(r["Counter_Value"])
+            s = sums.setdefault(name, [0.0, 0])
+            s[0] += v
+            s[1] += 1
+    return {k: v[0] / v[1] for k, v in sums.items()}
+
+
+def ingest_counters(op_name, op_fetch, op_write, copy_fetch, copy_write, copy_mib):
+    """HBM bytes per launch of op_name = (FETCH_SIZE + WRITE_SIZE of its kernels) scaled by what the
+    same counters read for a plain copy of copy_mib MiB (bytes moved / counter reading)."""
+    cf = _counter_means(copy_fetch, "FETCH_SIZE")
+    cw = _counter_means(copy_write, "WRITE_SIZE")
+    copy_bytes = float(int(copy_mib) << 20)
+    # the calibration run holds only the copy; take its most frequent large-count kernel
+    kf = max(cf.values())
+    kw = max(cw.values())
+    f_fetch = copy_bytes / kf
+    f_write = copy_bytes / kw
+    of = _counter_means(op_fetch, "FETCH_SIZE")
+    ow = _counter_means(op_write, "WRITE_SIZE")
+    fams = OP_KERNELS.get(op_name, ())
+    fetch = sum(v for k, v in of.items() if any(fm in k for fm in fams))
+    write = sum(v for k, v in ow.items() if any(fm in k for fm in fams))
+    ent = {"bytes_per_launch": round(fetch * f_fetch + write * f_write), "fetch_bytes": round(fetch * f_fetch),
+           "write_bytes": round(write * f_write), "fetch_counter": round(fetch, 1), "write_counter": round(write, 1),
+           "copy_mib": copy_mib, "copy_fetch_counter": round(kf, 1), "copy_write_counter": round(kw, 1),
+           "scale_fetch": f_fetch, "scale_write": f_write, "kernels": list(fams), "src_hash": source_hash()}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        data = json.load(open(path))
+    data[op_name] = ent
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({op_name: ent}))
+
+
+def copy_calibration(mib, steps):
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "steps": steps}))
+
+
 def cpu_baseline(ops, rows_per_op):
     """The fp64 oracle (as it stands) on a bounded sample of the step: the first rows of each op."""
     from oracle import oracle as O
@@ -171,11 +244,21 @@ def cpu_baseline(ops, rows_per_op):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ops = [n.strip() for n in args.ops.split(",") if n.strip()]
+        if len(ops) != 1:
+            raise SystemExit("--ingest-counters takes exactly one op name in --ops")
+        ingest_counters(ops[0], *args.ingest_counters, copy_mib=args.copy_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import bit_group_quantized_q4gsw_amd as q
     torch.cuda.set_device(0)
     names = [n.strip() for n in args.ops.split(",") if n.strip()]
@@ -187,10 +270,10 @@ def main():
             op.run(q, i)
     torch.cuda.synchronize()
 
+    # per-op timing: eager launches, each bracketed by HIP events on the launch stream
     ev = {op.name: [] for op in ops}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
         for op in ops:
@@ -200,6 +283,27 @@ def main():
             op.run(q, args.warmup + i)
             b.record()
             ev[op.name].append((a, b))
+    stop.record()
+    torch.cuda.synchronize()
+    eager_ms_step = start.elapsed_time(stop) / args.steps
+
+    # whole-step timing: each rotated input set's step captured once as a HIP graph and
+    # replayed, so host launch latency does not pace the GPU
+    graphs = []
+    for s in range(rotate):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for op in ops:
+                op.run(q, s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % rotate].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        graphs[i % rotate].replay()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -244,11 +348,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4 weights; f16/bf16 MFMA (f32 x: bf16 hi+lo); f32 accumulate",
+        "dtype": "bf16/f16",
         "data": "synthetic",
         "config": {"workload": "llama-3.2-1b q4gsw step: " + ", ".join(
             f"{o.name} M{o.M} route={o.route}" for o in ops), "ops": names, "rotated_sets": rotate,
-            "wall_s": round(wall, 3), "src_hash": src},
+            "timing": "step: HIP-graph replay of the whole step; per_op: eager launches between HIP events",
+            "eager_ms_per_step": round(eager_ms_step, 5), "wall_s": round(wall, 3), "src_hash": src},
         "per_op": per_op,
         "roofline": roof,
     }

@@ -1,0 +1,83 @@
+"""HIP-graph capture of every entry point: each replay must equal the eager result bitwise.
+
+The kernels are deterministic (no atomics, fixed reduction order) and record no memset, so a
+captured call replayed several times, with other eager work and synchronisations between the
+replays, must reproduce the eager output exactly.  The benchmark times its step this way.
+"""
+import pytest
+import torch
+
+from synthetic_inputs import make_linear, make_qkv
+from tests.gpu_helpers import dev, lib, pack
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # kind, M, N, K, gs, act dtype, scale dtype
+    ("fwd", 1, 1024, 512, 32, "f16", "f16"),        # decode GEMV route
+    ("fwd", 130, 512, 1024, 128, "bf16", "f16"),    # MFMA forward with K splits and reduction
+    ("fwd", 64, 256, 384, 32, "f16", "f16"),        # folded fp16 forward
+    ("bwd", 3, 512, 256, 32, "f16", "f16"),         # input-gradient GEMV
+    ("bwd", 130, 1024, 512, 128, "f32", "f16"),     # input-gradient split route
+    ("qkv", 128, None, 512, 32, "f16", "f16"),      # fused QKV
+]
+
+
+def _call(q, kind, pw, a, outs, ws):
+    if kind == "fwd":
+        q.linear_fwd(pw[0], a, out=outs[0], workspace=ws)
+    elif kind == "bwd":
+        q.linear_bwd_input(pw[0], a, out=outs[0], workspace=ws)
+    else:
+        q.qkv_fused(pw[0], pw[1], pw[2], a, outs=outs, workspace=ws)
+
+
+@pytest.mark.parametrize("kind,M,N,K,gs,act,sdt", CASES)
+def test_graph_replay_matches_eager(kind, M, N, K, gs, act, sdt):
+    q = lib()
+    if kind == "qkv":
+        case = make_qkv(M=M, K=K, Ns=(512, 128, 128), group_size=gs, act_dtype=act, scale_dtype=sdt, seed=5)
+        ws_list = case.weights
+        a = dev(case.x)
+    else:
+        case = make_linear(M, K, N, gs, act, sdt, seed=M + K, fwd=(kind == "fwd"), bwd=(kind == "bwd"))
+        ws_list = [case.w]
+        a = dev(case.x if kind == "fwd" else case.d_out)
+    pw = [pack(q, w) for w in ws_list]
+    if kind == "bwd":
+        shapes = [(M, K)]
+        op = q.OP_BWD_INPUT
+    else:
+        shapes = [(M, w.N) for w in ws_list]
+        op = q.OP_QKV if kind == "qkv" else q.OP_FWD
+    if kind == "qkv":
+        need = q.qkv_workspace_bytes(pw[0], pw[1], pw[2], M, a.dtype)
+    else:
+        need = q.workspace_bytes(op, pw[0], M, a.dtype)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    eager = tuple(torch.empty(s, dtype=torch.float32, device="cuda") for s in shapes)
+    _call(q, kind, pw, a, eager, ws)
+    torch.cuda.synchronize()
+
+    outs = tuple(torch.full(s, float("nan"), dtype=torch.float32, device="cuda") for s in shapes)
+    _call(q, kind, pw, a, outs, ws)                 # warm the stream before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _call(q, kind, pw, a, outs, ws)
+    torch.cuda.synchronize()
+
+    other = torch.randn(1 << 16, device="cuda")
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"{kind} replay {rep} differs from the eager result"
+        # eager work between replays that reuses the workspace and the stream
+        _call(q, kind, pw, a, eager, ws)
+        other.mul_(1.0001)
+        torch.cuda.synchronize()
