@@ -321,7 +321,7 @@ q4gsw_status q4gsw_linear_fwd(const q4gsw_weight* w, const void* x, int32_t x_dt
     const int32_t route = pick_fwd(w, M, x_dtype, false, &st);
     if (st != Q4GSW_OK) return st;
     const uint64_t need = fwd_ws_bytes(w, M, x_dtype, route);
-    if (need > 0 && (!ws || ws_bytes < need)) return Q4GSW_E_WORKSPACE;
+    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)) return Q4GSW_E_WORKSPACE;
     const Range yr = range_of(y, (uint64_t)M * w->N * 4);
     if (overlap(yr, range_of(x, (uint64_t)M * w->K * esize(x_dtype))) || overlap(yr, range_of(w->data, w->bytes)) ||
         (need > 0 && (overlap(yr, range_of(ws, need)) || overlap(range_of(ws, need), range_of(w->data, w->bytes)) ||
@@ -340,7 +340,7 @@ q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, in
     const int32_t route = pick_bwd(w, M, g_dtype, &st);
     if (st != Q4GSW_OK) return st;
     const uint64_t need = bwd_ws_bytes(w, M, g_dtype, route);
-    if (need > 0 && (!ws || ws_bytes < need)) return Q4GSW_E_WORKSPACE;
+    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)) return Q4GSW_E_WORKSPACE;
     const Range xr = range_of(d_x, (uint64_t)M * w->K * 4);
     const Range gr = range_of(d_out, (uint64_t)M * w->N * esize(g_dtype));
     if (overlap(xr, gr) || overlap(xr, range_of(w->data, w->bytes)) ||
@@ -379,7 +379,7 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, con
     const q4gsw_weight* w3[3] = {wq, wk, wv};
     float* o3[3] = {q, k, v};
     const uint64_t need = qkv_ws_bytes(w3, M, x_dtype, route);
-    if (need > 0 && (!ws || ws_bytes < need)) return Q4GSW_E_WORKSPACE;
+    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)) return Q4GSW_E_WORKSPACE;
     Range outs[3];
     for (int i = 0; i < 3; ++i) outs[i] = range_of(o3[i], (uint64_t)M * w3[i]->N * 4);
     const Range xr = range_of(x, (uint64_t)M * wq->K * esize(x_dtype));
@@ -447,7 +447,7 @@ const char* q4gsw_status_str(int32_t status) {
         case Q4GSW_E_GROUP: return "group_size must be >= 1 and divide K";
         case Q4GSW_E_ALIAS: return "output overlaps another buffer";
         case Q4GSW_E_CODE_RANGE: return "code above 15";
-        case Q4GSW_E_WORKSPACE: return "workspace missing or too small";
+        case Q4GSW_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case Q4GSW_E_DESC: return "invalid or mismatched weight descriptor";
         case Q4GSW_E_HIP: return "HIP runtime error";
         case Q4GSW_E_BUFFER: return "packed buffer too small";

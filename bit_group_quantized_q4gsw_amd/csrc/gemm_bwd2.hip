@@ -387,24 +387,6 @@ bool v2_supported(const WView& w, int g_dtype, int fold_ok) {
     return w.gs % 128 == 0;
 }
 
-// Split count: the fewest contraction splits that minimise (rounds of blocks over the CUs) x
-// (chunks per split), one block per CU.
-int pick_splits_bwd(int64_t blocks, int64_t n_chunks) {
-    const int64_t cus = 256;
-    int best = 1;
-    int64_t best_cost = INT64_MAX;
-    for (int64_t s = 1; s <= 64 && s <= n_chunks; ++s) {
-        const int64_t per = (n_chunks + s - 1) / s;
-        if ((n_chunks + per - 1) / per != s) continue;
-        const int64_t cost = ((blocks * s + cus - 1) / cus) * (per + 2);
-        if (cost < best_cost) {
-            best_cost = cost;
-            best = (int)s;
-        }
-    }
-    return best;
-}
-
 template <int GT, int MODE, int NV, int SF>
 void launch_t(dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64_t M, float* out, int64_t ld,
               int64_t stride, int64_t limit, int g_fast, int per, int splits, int mtiles) {
@@ -435,7 +417,7 @@ BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M) {
     p.mode = v2_fold(w, g_dtype, fold_ok) ? kModeFold : kModeSplit;
     const int64_t blocks = ((w.k_pad + kBK - 1) / kBK) * ((M + kBM - 1) / kBM);
     const int64_t n_chunks = (w.N + kCN - 1) / kCN;
-    p.splits = pick_splits_bwd(blocks, n_chunks);
+    p.splits = pick_gemm_splits(blocks, n_chunks, M, w.k_pad);
     p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * M * w.k_pad * 4 : 0;
     p.v1 = 0;
     return p;

@@ -499,18 +499,21 @@ static int fwd_spc(int64_t gs) {
     return 4;
 }
 
-// Split count: the fewest K splits that minimise (rounds of blocks over the CUs) x (chunks per
-// split), one block per CU.
-static int pick_splits(int64_t blocks, int64_t n_chunks) {
+// Split count minimising a time model (microseconds): rounds of blocks over the 256 CUs times
+// (chunks per split + 2 for pipeline fill and epilogue) at ~2 us per chunk, plus, with splits,
+// a reduction launch (~3 us) and the partial buffer written and read back (splits x M x width
+// x 8 bytes at ~5 TB/s).  Ties go to fewer splits.
+int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width) {
     const int64_t cus = 256;
     int best = 1;
-    int64_t best_cost = INT64_MAX;
+    double best_cost = 1e300;
     for (int64_t s = 1; s <= 64 && s <= n_chunks; ++s) {
         const int64_t per = (n_chunks + s - 1) / s;
         if ((n_chunks + per - 1) / per != s) continue;      // some split would be empty
         const int64_t rounds = (blocks * s + cus - 1) / cus;
-        const int64_t cost = rounds * (per + 2);            // + pipeline fill and epilogue
-        if (cost < best_cost) {
+        double cost = 2.0 * (double)rounds * (double)(per + 2);
+        if (s > 1) cost += 3.0 + (double)s * (double)M * (double)width * 8.0 / 5e6;
+        if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best = (int)s;
         }
@@ -531,7 +534,7 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
     }
     const int64_t blocks = tiles * ((M + kBM - 1) / kBM);
     const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
-    const int splits = pick_splits(blocks, n_chunks);
+    const int splits = pick_gemm_splits(blocks, n_chunks, M, npad_total);
     p.splits = splits;
     p.ws_bytes = splits > 1 ? (int64_t)splits * M * npad_total * 4 : 0;
     return p;
@@ -611,11 +614,17 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
+    const float* ys[3];
+    int64_t yld[3], off[3], cols[3];
+    int64_t o = 0;
     for (int i = 0; i < nseg; ++i) {
-        e = launch_reduce_splits(a.out[i], plan.splits, M, segs[i].w.N, npad_total, segs[i].out, segs[i].w.N, s);
-        if (e != hipSuccess) return e;
+        ys[i] = segs[i].out;
+        yld[i] = segs[i].w.N;
+        off[i] = o;
+        cols[i] = segs[i].w.N;
+        o += segs[i].w.n_pad;
     }
-    return hipSuccess;
+    return launch_reduce_segments(ws, plan.splits, M, npad_total, ys, yld, off, cols, nseg, s);
 }
 
 }  // namespace q4gsw

@@ -322,24 +322,68 @@ __global__ __launch_bounds__(256) void gemv_bwd_kernel(WView w, const void* __re
     }
 }
 
+// Split-partial reduction: y_seg[m][c] = sum_s ws[s][m][off_seg + c] for c < cols_seg, over up to
+// three column segments that share the workspace rows (the fused QKV's three outputs).  A block
+// covers 4 rows x 256 columns, each thread 4 consecutive columns with 16-byte loads; segment
+// starts and the row pitch are multiples of 4 columns.
+struct ReduceSegs {
+    float* y[3];
+    int64_t y_ld[3];
+    int64_t off[3];              // first workspace column of the segment
+    int64_t cols[3];             // valid columns of the segment
+    int nseg;
+};
+
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ ws, int splits, int64_t M,
-                                                            int64_t cols, int64_t ld, float* __restrict__ y,
-                                                            int64_t y_ld) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= M * cols) return;
-    const int64_t m = t / cols;
-    const int64_t c = t % cols;
-    float v = 0.0f;
-    for (int s = 0; s < splits; ++s) v += ws[((int64_t)s * M + m) * ld + c];
-    y[m * y_ld + c] = v;
+                                                            int64_t ld, ReduceSegs seg, int vec_ok) {
+    const int64_t c = ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63)) * 4;
+    if (c >= ld) return;
+    int sg = 0;
+    while (sg + 1 < seg.nseg && c >= seg.off[sg + 1]) ++sg;
+    const int64_t cs = c - seg.off[sg];
+    if (cs >= seg.cols[sg]) return;
+    const int64_t plane = M * ld;
+    for (int64_t m = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6); m < M; m += (int64_t)gridDim.y * 4) {
+        const float* src = ws + m * ld + c;
+        f4 acc = *reinterpret_cast<const f4*>(src);
+        for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f4*>(src + s * plane);
+        float* dst = seg.y[sg] + m * seg.y_ld[sg] + cs;
+        if (vec_ok && cs + 4 <= seg.cols[sg]) {
+            *reinterpret_cast<f4*>(dst) = acc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (cs + e < seg.cols[sg]) dst[e] = acc[e];
+        }
+    }
+}
+
+hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_t ld, const float* const* y,
+                                  const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg,
+                                  hipStream_t s) {
+    ReduceSegs seg{};
+    seg.nseg = nseg;
+    int vec_ok = (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(ws) & 15u) == 0);
+    for (int i = 0; i < nseg; ++i) {
+        seg.y[i] = const_cast<float*>(y[i]);
+        seg.y_ld[i] = y_ld[i];
+        seg.off[i] = off[i];
+        seg.cols[i] = cols[i];
+        if (off[i] % 4 != 0) return hipErrorInvalidValue;
+        vec_ok = vec_ok && (y_ld[i] % 4 == 0) && ((reinterpret_cast<uintptr_t>(y[i]) & 15u) == 0);
+    }
+    if (ld % 4 != 0 || (reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return hipErrorInvalidValue;
+    const int64_t row_blocks = (M + 3) / 4;
+    const dim3 grid((unsigned)((ld / 4 + 63) / 64), (unsigned)(row_blocks < 65535 ? row_blocks : 65535));
+    hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, s, ws, splits, M, ld, seg, vec_ok);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t cols, int64_t ld, float* y,
                                 int64_t y_ld, hipStream_t s) {
-    const int64_t total = M * cols;
-    hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, ws, splits,
-                       M, cols, ld, y, y_ld);
-    return hipGetLastError();
+    const float* yy[1] = {y};
+    const int64_t yl[1] = {y_ld}, of[1] = {0}, cl[1] = {cols};
+    return launch_reduce_segments(ws, splits, M, ld, yy, yl, of, cl, 1, s);
 }
 
 // Waves per block: one per 64 k-octets of the split, at most 16.

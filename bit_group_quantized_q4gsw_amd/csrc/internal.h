@@ -28,9 +28,14 @@ int gemv_fwd_splits(const WView& w, int64_t M);
 hipError_t launch_gemv_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* out,
                            int splits, hipStream_t s);
 int gemv_bwd_splits(const WView& w, int64_t M);
-// y[m][c] = sum_s ws[s][m][c] for c < cols (ws row pitch ld).
+// y[m][c] = sum_s ws[s][m][c] for c < cols (ws row pitch ld, a multiple of 4; ws 16-byte aligned).
 hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t cols, int64_t ld,
                                 float* y, int64_t y_ld, hipStream_t s);
+// The same over up to three column segments in one launch: y[i][m][c] = sum_s ws[s][m][off[i] + c]
+// for c < cols[i] (off[i] multiples of 4).
+hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_t ld, const float* const* y,
+                                  const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg,
+                                  hipStream_t s);
 
 // generic.hip: any shape, any group size.
 hipError_t launch_generic_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* y,
@@ -50,6 +55,9 @@ struct FwdPlan {
     int64_t ws_bytes;        // workspace needed
 };
 FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M);
+// Contraction splits for an MFMA GEMM of `blocks` output blocks (one per CU), n_chunks 64-wide
+// contraction chunks and an M x width fp32 output.
+int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width);
 bool gemm_fwd_supported(const WView& w, int x_dtype, int fold_ok);
 hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
                            const FwdPlan& plan, float* ws, hipStream_t s);

@@ -53,7 +53,7 @@ typedef enum q4gsw_status {
     Q4GSW_E_GROUP = 4,        /* group_size < 1 or K % group_size != 0 */
     Q4GSW_E_ALIAS = 5,        /* an output overlaps another output, an input or the workspace */
     Q4GSW_E_CODE_RANGE = 6,   /* q4gsw_pack saw a code above 15 */
-    Q4GSW_E_WORKSPACE = 7,    /* workspace missing or smaller than q4gsw_*_workspace_bytes */
+    Q4GSW_E_WORKSPACE = 7,    /* workspace missing, smaller than q4gsw_*_workspace_bytes or not 256-byte aligned */
     Q4GSW_E_DESC = 8,         /* descriptor magic/version/fields invalid, or QKV weights disagree */
     Q4GSW_E_HIP = 9,          /* a HIP runtime call or kernel launch failed */
     Q4GSW_E_BUFFER = 10,      /* packed buffer smaller than q4gsw_packed_bytes */
@@ -137,7 +137,9 @@ q4gsw_status q4gsw_pack(const uint8_t *codes, const void *scales, int32_t scale_
  * [K / group_size, N] in the weight's scale dtype.  Synchronizes `stream`. */
 q4gsw_status q4gsw_unpack(const q4gsw_weight *w, uint8_t *codes, void *scales, void *stream);
 
-/* Device workspace (bytes) the call needs; 0 when its route needs none.  Pure host. */
+/* Device workspace (bytes) the call needs; 0 when its route needs none.  Pure host.  A workspace
+ * passed to a call that needs one must start on a 256-byte boundary (E_WORKSPACE otherwise); its
+ * contents need no initialisation and are scratch after the call. */
 q4gsw_status q4gsw_workspace_bytes(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype,
                                    uint64_t *bytes);
 q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight *wq, const q4gsw_weight *wk,

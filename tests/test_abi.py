@@ -188,7 +188,8 @@ def test_forward_validation(q):
     assert need.value > 0                    # the prefill shape splits K across blocks
     assert f(ctypes.byref(big), x, q.BF16, 512, y, None, 0, None) == E_WS
     assert f(ctypes.byref(big), x, q.BF16, 512, y, FAKE * 32, need.value - 4, None) == E_WS
-    assert f(ctypes.byref(big), x, q.BF16, 512, y, y + 16, need.value, None) == E_ALIAS   # ws overlaps y
+    assert f(ctypes.byref(big), x, q.BF16, 512, y, y + 256, need.value, None) == E_ALIAS  # ws overlaps y
+    assert f(ctypes.byref(big), x, q.BF16, 512, y, FAKE * 32 + 16, need.value, None) == E_WS  # ws not 256-aligned
     with q.forced_route("gemv"):
         assert f(ctypes.byref(d), x, q.F16, 64, y, None, 0, None) == E_ROUTE
 
