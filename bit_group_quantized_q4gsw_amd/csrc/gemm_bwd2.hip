@@ -380,6 +380,256 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
     }
 }
 
+// Split route with specialised waves: 8 waves per block, two per SIMD.  Waves 0..3 are
+// consumers (each owns 64 output columns: code DMA, per-lane transpose, MFMAs); waves 4..7 are
+// producers that stage A' = d_out * scale as bf16 hi / lo for the next chunk while the
+// consumers multiply, so the staging VALU runs beside the other wave's MFMAs.  One block
+// barrier per chunk hands the A' stage over.
+template <int GT, int NV, int SF>
+__global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const void* __restrict__ d_out, int64_t M,
+                                                                float* __restrict__ out, int64_t out_ld,
+                                                                int64_t split_stride, int64_t col_limit, int g_fast,
+                                                                int chunks_per_split, int splits, int mtiles) {
+    constexpr int kAStage = NV * 2 * kPlaneBytes;
+    constexpr int kCStage = 4 * kCodeBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kAStage + 3 * kCStage];
+    uint8_t* const Aring = smem;
+    uint8_t* const Cring = smem + 2 * kAStage;
+    lds_u8* const sm_l = (lds_u8*)smem;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const bool consumer = wave < 4;
+
+    const int64_t bid = blockIdx.x;
+    const int z = (int)(bid % splits);
+    const int64_t rest = bid / splits;
+    const int64_t mb = rest % mtiles;
+    const int64_t tile = rest / mtiles;
+    const int64_t kb0 = tile * kBK;
+    const int64_t m0 = mb * kBM;
+    const int64_t N = w.N;
+    const int64_t n_chunks = (N + kCN - 1) / kCN;
+    const int64_t c_begin = (int64_t)z * chunks_per_split;
+    const int64_t c_end = min(c_begin + (int64_t)chunks_per_split, n_chunks);
+
+    if (!consumer) {
+        // ---------------- producer: thread p stages row p >> 1, n-octets 4 (p & 1) .. +3 ----------------
+        const int p = tid - 256;
+        const int arow = p >> 1;
+        const int ahalf = p & 1;
+        const int64_t am = min(m0 + arow, M - 1);              // rows past M only feed discarded outputs
+        constexpr int kXU = (GT == kF32) ? 8 : 4;
+        constexpr int kSU = SF ? 4 : 8;
+        u4 xreg[kXU];
+        u4 sreg[NV][kSU];
+        auto load_a = [&](int64_t c) {
+            const int64_t n0 = c * kCN + 32 * ahalf;
+            if (g_fast && n0 + 32 <= N) {
+#pragma unroll
+                for (int i = 0; i < kXU; ++i) {
+                    if constexpr (GT == kF32) xreg[i] = ldg16(static_cast<const float*>(d_out) + am * N + n0 + 4 * i);
+                    else xreg[i] = ldg16(static_cast<const uint16_t*>(d_out) + am * N + n0 + 8 * i);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kXU; ++i) {
+                    uint32_t e[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (GT == kF32) {
+                            const int64_t n = n0 + 4 * i + q;
+                            e[q] = (n < N) ? static_cast<const uint32_t*>(d_out)[am * N + n] : 0u;
+                        } else {
+                            const int64_t n = n0 + 8 * i + 2 * q;
+                            const uint32_t lo = (n < N) ? static_cast<const uint16_t*>(d_out)[am * N + n] : 0u;
+                            const uint32_t hi = (n + 1 < N) ? static_cast<const uint16_t*>(d_out)[am * N + n + 1] : 0u;
+                            e[q] = lo | (hi << 16);
+                        }
+                    }
+                    xreg[i] = u4{e[0], e[1], e[2], e[3]};
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                // a copy for columns past k_pad only feeds idle consumers; keep its reads in the plane
+                const int64_t g = min((kb0 + 128 * v) / w.gs, w.g_pad - 1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t idx = ((n0 >> 3) + q) * (w.g_pad * 8) + g * 8;
+                    if constexpr (SF) {
+                        sreg[v][q] = ldg16(static_cast<const uint16_t*>(w.scales) + idx);
+                    } else {
+                        sreg[v][2 * q] = ldg16(static_cast<const float*>(w.scales) + idx);
+                        sreg[v][2 * q + 1] = ldg16(static_cast<const float*>(w.scales) + idx + 4);
+                    }
+                }
+            }
+        };
+        auto x_at = [&](int i) -> float {
+            if constexpr (GT == kF32) return bitcast<float>(xreg[i >> 2][i & 3]);
+            else {
+                const uint32_t wd = xreg[i >> 3][(i >> 1) & 3];
+                const uint16_t b = (i & 1) ? (uint16_t)(wd >> 16) : (uint16_t)(wd & 0xFFFFu);
+                if constexpr (GT == kF16) return f16_bits_to_f32(b);
+                else return bf16_bits_to_f32(b);
+            }
+        };
+        auto s_at = [&](int v, int i) -> float {
+            if constexpr (SF) {
+                const uint32_t wd = sreg[v][i >> 3][(i >> 1) & 3];
+                return f16_bits_to_f32((i & 1) ? (uint16_t)(wd >> 16) : (uint16_t)(wd & 0xFFFFu));
+            } else {
+                return bitcast<float>(sreg[v][i >> 2][i & 3]);
+            }
+        };
+        auto store_a = [&](int st) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                uint8_t* hiP = Aring + st * kAStage + v * 2 * kPlaneBytes;
+                uint8_t* loP = hiP + kPlaneBytes;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 8 * q + 2 * e;
+                        split_bf16(x_at(i) * s_at(v, i), x_at(i + 1) * s_at(v, i + 1), hw[e], lw[e]);
+                    }
+                    const int off = arow * kRowBytes + 16 * ((4 * ahalf + q) ^ ((arow >> 1) & 7));
+                    *reinterpret_cast<u4*>(hiP + off) = u4{hw[0], hw[1], hw[2], hw[3]};
+                    *reinterpret_cast<u4*>(loP + off) = u4{lw[0], lw[1], lw[2], lw[3]};
+                }
+            }
+        };
+        // A' of chunk c + 1 is built during chunk c; its loads were issued one chunk earlier
+        if (c_begin < c_end) {
+            load_a(c_begin);
+            store_a(0);
+            if (c_begin + 1 < c_end) load_a(c_begin + 1);
+        }
+        int sa = 0;
+        for (int64_t c = c_begin; c < c_end; ++c) {
+            wait_loads_barrier<63>();                  // the stores of chunk c are done
+            if (c + 1 < c_end) {
+                store_a(sa ^ 1);
+                if (c + 2 < c_end) load_a(c + 2);
+            }
+            sa ^= 1;
+        }
+        return;
+    }
+
+    // ---------------- consumer ----------------
+    const int j = lane & 31;
+    const int h = lane >> 5;
+    const int64_t kw0 = kb0 + (int64_t)wave * kWK;
+    const bool wave_active = kw0 < w.k_pad;
+    const int64_t kwc = wave_active ? kw0 : 0;
+    const int64_t kocts = w.k_pad >> 3;
+    const uint8_t* csrc[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int R = 4 * r + (lane >> 4);
+        const int o = (((lane & 15) >> 1) - R) & 7;
+        csrc[r] = w.nib + 32 * ((int64_t)R * kocts + (kwc >> 3) + o) + 16 * (lane & 1);
+    }
+    const int64_t chunk_code_stride = 32 * 8 * kocts;
+    auto issue_codes = [&](int64_t c, int st) {
+        lds_u8* base = sm_l + 2 * kAStage + st * kCStage + wave * kCodeBytes;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) dma16(csrc[r] + chunk_code_stride * c, base + 1024 * r);
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][u][r] = 0.f;
+
+    const int swz = (j >> 1) & 7;
+    const int npos = 4 * nib_pos(j & 7);
+    const int aver = (NV == 2) ? (wave >> 1) : 0;
+    auto read_b = [&](const uint8_t* Cb, int t, u4 (&wd)[2][2]) {
+        const int R = 2 * t + h;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint8_t* pp = Cb + 256 * R + 32 * (((4 * u + (j >> 3)) + R) & 7);
+            wd[u][0] = *reinterpret_cast<const u4*>(pp);
+            wd[u][1] = *reinterpret_cast<const u4*>(pp + 16);
+        }
+    };
+    auto bpiece = [&](const u4 (&wd)[2][2], u4 (&b)[2], int i) {
+        const int u = i >> 2, e = i & 3;
+        const uint32_t w0 = wd[u][e >> 1][2 * (e & 1)];
+        const uint32_t w1 = wd[u][e >> 1][2 * (e & 1) + 1];
+        const float lo = (float)(int)__builtin_amdgcn_sbfe((int)(w0 ^ 0x88888888u), npos, 4);
+        const float hi = (float)(int)__builtin_amdgcn_sbfe((int)(w1 ^ 0x88888888u), npos, 4);
+        b[u][e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
+    };
+    auto compute = [&](int sa, int sc) {
+        const uint8_t* Ab = Aring + sa * kAStage + aver * 2 * kPlaneBytes;
+        const uint8_t* Cb = Cring + sc * kCStage + wave * kCodeBytes;
+        u4 wd[2][2][2], b[2];
+        read_b(Cb, 0, wd[0]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int cur = t & 1;
+            u4 a[4], alo[4];
+            const int slot = 16 * ((2 * t + h) ^ swz);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const int off = (32 * mi + j) * kRowBytes + slot;
+                a[mi] = *reinterpret_cast<const u4*>(Ab + off);
+                alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + off);
+            }
+            if (t < 3) read_b(Cb, t + 1, wd[cur ^ 1]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bpiece(wd[cur], b, i);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int mi = i >> 1, u = i & 1;
+                acc[mi][u] = mfma32_bf16(alo[mi], b[u], mfma32_bf16(a[mi], b[u], acc[mi][u]));
+            }
+        }
+    };
+    if (c_begin < c_end) {
+        issue_codes(c_begin, 0);
+        if (c_begin + 1 < c_end) issue_codes(c_begin + 1, 1);
+    }
+    int sc = 0, sa = 0;
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        const int sc_next = (sc == 2) ? 0 : sc + 1;
+        const int sc_prev = (sc == 0) ? 2 : sc - 1;
+        // chunk c's code DMAs are done once only chunk c + 1's two may be in flight
+        if (c + 1 < c_end) wait_loads_barrier<2>();
+        else wait_loads_barrier<0>();
+        if (c + 2 < c_end) issue_codes(c + 2, sc_prev);
+        compute(sa, sc);
+        sa ^= 1;
+        sc = sc_next;
+    }
+
+    if (!wave_active) return;
+    float* dst = out + (int64_t)z * split_stride;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t k = kw0 + 32 * u + j;
+            if (k >= col_limit) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = m0 + 32 * mi + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M) dst[m * out_ld + k] = acc[mi][u][r];
+            }
+        }
+    }
+}
+
 bool v2_fold(const WView& w, int g_dtype, int fold_ok) { return g_dtype == kF16 && w.scale_f16 && fold_ok; }
 
 bool v2_supported(const WView& w, int g_dtype, int fold_ok) {
@@ -397,8 +647,12 @@ void launch_t(dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64
 template <int GT, int NV>
 void launch_split(int sf, dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64_t M, float* out,
                   int64_t ld, int64_t stride, int64_t limit, int g_fast, int per, int splits, int mtiles) {
-    if (sf) launch_t<GT, kModeSplit, NV, 1>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, splits, mtiles);
-    else launch_t<GT, kModeSplit, NV, 0>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, splits, mtiles);
+    if (sf)
+        hipLaunchKernelGGL((gemm_bwd_split_kernel<GT, NV, 1>), grid, dim3(512), 0, s, w, d_out, M, out, ld, stride,
+                           limit, g_fast, per, splits, mtiles);
+    else
+        hipLaunchKernelGGL((gemm_bwd_split_kernel<GT, NV, 0>), grid, dim3(512), 0, s, w, d_out, M, out, ld, stride,
+                           limit, g_fast, per, splits, mtiles);
 }
 
 }  // namespace
