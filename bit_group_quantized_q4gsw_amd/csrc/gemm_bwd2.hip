@@ -380,6 +380,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
     }
 }
 
+// x * s for an fp16 s held in the low / high half of sw, rounded once to fp32.  Written as an FMA
+// with a zero addend so it maps to the mixed-precision FMA, which takes the fp16 operand directly.
+__device__ __forceinline__ float mul_f16_lo(float x, uint32_t sw) {
+    return __builtin_fmaf(x, f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)), 0.0f);
+}
+__device__ __forceinline__ float mul_f16_hi(float x, uint32_t sw) {
+    return __builtin_fmaf(x, f16_bits_to_f32((uint16_t)(sw >> 16)), 0.0f);
+}
+// bf16 hi / lo split of two fp32 values (both roundings to nearest even): a = hi + lo + e with
+// |e| <= 2^-18 |a|.  a - hi is exact in fp32.  Both fp32 hi values come from the packed hi word
+// (a byte permute and a mask), so the conversion is done once.
+__device__ __forceinline__ void split_bf16_pair(float a0, float a1, uint32_t& hi, uint32_t& lo) {
+    b2 h = {(__bf16)a0, (__bf16)a1};
+    const uint32_t hb = bitcast<uint32_t>(h);
+    const float r0 = a0 - bitcast<float>(__builtin_amdgcn_perm(hb, hb, 0x05040c0cu));   // hb << 16
+    const float r1 = a1 - bitcast<float>(hb & 0xFFFF0000u);
+    b2 l = {(__bf16)r0, (__bf16)r1};
+    hi = hb;
+    lo = bitcast<uint32_t>(l);
+}
+
 // Split route with specialised waves: 8 waves per block, two per SIMD.  Waves 0..3 are
 // consumers (each owns 64 output columns: code DMA, per-lane transpose, MFMAs); waves 4..7 are
 // producers that stage A' = d_out * scale as bf16 hi / lo for the next chunk while the
@@ -495,7 +516,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 8 * q + 2 * e;
-                        split_bf16(x_at(i) * s_at(v, i), x_at(i + 1) * s_at(v, i + 1), hw[e], lw[e]);
+                        float a0, a1;
+                        if constexpr (SF) {
+                            const uint32_t sw = sreg[v][i >> 3][(i >> 1) & 3];
+                            a0 = mul_f16_lo(x_at(i), sw);
+                            a1 = mul_f16_hi(x_at(i + 1), sw);
+                        } else {
+                            a0 = x_at(i) * s_at(v, i);
+                            a1 = x_at(i + 1) * s_at(v, i + 1);
+                        }
+                        split_bf16_pair(a0, a1, hw[e], lw[e]);
                     }
                     const int off = arow * kRowBytes + 16 * ((4 * ahalf + q) ^ ((arow >> 1) & 7));
                     *reinterpret_cast<u4*>(hiP + off) = u4{hw[0], hw[1], hw[2], hw[3]};
@@ -570,29 +600,39 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
         const float hi = (float)(int)__builtin_amdgcn_sbfe((int)(w1 ^ 0x88888888u), npos, 4);
         b[u][e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
     };
+    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4], u4 (&alo)[4]) {
+        const int slot = 16 * ((2 * t + h) ^ swz);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int off = (32 * mi + j) * kRowBytes + slot;
+            a[mi] = *reinterpret_cast<const u4*>(Ab + off);
+            alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + off);
+        }
+    };
+    // Operands of step t + 1 are read (codes first, so their conversion waits on them alone)
+    // and converted between the MFMAs of step t.
     auto compute = [&](int sa, int sc) {
         const uint8_t* Ab = Aring + sa * kAStage + aver * 2 * kPlaneBytes;
         const uint8_t* Cb = Cring + sc * kCStage + wave * kCodeBytes;
-        u4 wd[2][2][2], b[2];
-        read_b(Cb, 0, wd[0]);
+        u4 a[2][4], alo[2][4], wd[2][2], b[2][2];
+        read_b(Cb, 0, wd);
+        read_a(Ab, 0, a[0], alo[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bpiece(wd, b[0], i);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int cur = t & 1;
-            u4 a[4], alo[4];
-            const int slot = 16 * ((2 * t + h) ^ swz);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const int off = (32 * mi + j) * kRowBytes + slot;
-                a[mi] = *reinterpret_cast<const u4*>(Ab + off);
-                alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + off);
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t < 3) {
+                read_b(Cb, t + 1, wd);
+                read_a(Ab, t + 1, a[nxt], alo[nxt]);
             }
-            if (t < 3) read_b(Cb, t + 1, wd[cur ^ 1]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bpiece(wd[cur], b, i);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int mi = i >> 1, u = i & 1;
-                acc[mi][u] = mfma32_bf16(alo[mi], b[u], mfma32_bf16(a[mi], b[u], acc[mi][u]));
+                acc[mi][u] = mfma32_bf16(alo[cur][mi], b[cur][u], mfma32_bf16(a[cur][mi], b[cur][u], acc[mi][u]));
+                if (t < 3) bpiece(wd, b[nxt], (i & 1) * 4 + (i >> 1));
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
