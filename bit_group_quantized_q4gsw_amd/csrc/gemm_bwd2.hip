@@ -558,18 +558,25 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
     const bool wave_active = kw0 < w.k_pad;
     const int64_t kwc = wave_active ? kw0 : 0;
     const int64_t kocts = w.k_pad >> 3;
-    const uint8_t* csrc[2];
+    // Codes in LDS: the wave's 64 n x 64 k codes of a chunk as 8-byte rows (n, P) = code words
+    // (n, octet 2P), (n, octet 2P + 1) for octet pair P = 0..3, row (n, P) at byte
+    // 8 (64 P + (n ^ 8 (P & 1))).  The xor keeps the rows that one transposing read takes for
+    // two neighbouring pairs in different banks.  Word-granular DMA builds the rows: instruction i
+    // moves LDS words 64 i .. 64 i + 63, i.e. pair P = i >> 1, n = 32 (i & 1) + (lane >> 1)
+    // (xor 8 for odd P), octet 2P + (lane & 1).
+    const uint8_t* cpt[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int R = 4 * r + (lane >> 4);
-        const int o = (((lane & 15) >> 1) - R) & 7;
-        csrc[r] = w.nib + 32 * ((int64_t)R * kocts + (kwc >> 3) + o) + 16 * (lane & 1);
+    for (int par = 0; par < 2; ++par) {
+        const int n = (lane >> 1) ^ (8 * par);
+        cpt[par] = w.nib + 32 * ((int64_t)(n >> 3) * kocts + (kwc >> 3) + (lane & 1)) + 4 * (n & 7);
     }
     const int64_t chunk_code_stride = 32 * 8 * kocts;
     auto issue_codes = [&](int64_t c, int st) {
         lds_u8* base = sm_l + 2 * kAStage + st * kCStage + wave * kCodeBytes;
+        const int64_t cofs = chunk_code_stride * c;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) dma16(csrc[r] + chunk_code_stride * c, base + 1024 * r);
+        for (int i = 0; i < 8; ++i)
+            dma4(cpt[(i >> 1) & 1] + cofs + 128 * kocts * (i & 1) + 64 * (i >> 1), base + 256 * i);
     };
 
     f32x16 acc[4][2];
@@ -581,24 +588,38 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
             for (int r = 0; r < 16; ++r) acc[i][u][r] = 0.f;
 
     const int swz = (j >> 1) & 7;
-    const int npos = 4 * nib_pos(j & 7);
     const int aver = (NV == 2) ? (wave >> 1) : 0;
-    auto read_b = [&](const uint8_t* Cb, int t, u4 (&wd)[2][2]) {
-        const int R = 2 * t + h;
+    // One transposing 4-bit read gives lane (G = lane >> 4, j = lane & 15) the nibbles of row q
+    // (the row this read's lane q of group G addresses) at column j, for q = 0..15.  Lane q of
+    // group G addresses row n = 16 (q >> 3) + 8 (G >> 1) + (q & 7) of pair 2u + (G & 1) in step
+    // pair tp, so the low word holds n = 8 h + 0..7 of step 2 tp and the high word those of step
+    // 2 tp + 1 (h = lane >> 5, as the MFMA B operand wants), at k column 32 u + 8 (j' >> 3) +
+    // (k offset of nibble j' & 7) with j' = lane & 31.
+    const int trG = lane >> 4, trq = lane & 15;
+    const int trn = 16 * (trq >> 3) + 8 * (trG >> 1) + (trq & 7);
+    const int trofs = 8 * (64 * (trG & 1) + (trn ^ (8 * (trG & 1))));
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i lds_v2i;
+    auto read_bt = [&](const uint8_t* Cb, v2i (&bt)[2][2]) {
+        const lds_u8* p = (const lds_u8*)Cb + trofs;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint8_t* pp = Cb + 256 * R + 32 * (((4 * u + (j >> 3)) + R) & 7);
-            wd[u][0] = *reinterpret_cast<const u4*>(pp);
-            wd[u][1] = *reinterpret_cast<const u4*>(pp + 16);
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp)
+                bt[u][tp] = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)(p + 1024 * u + 256 * tp));
     };
-    auto bpiece = [&](const u4 (&wd)[2][2], u4 (&b)[2], int i) {
-        const int u = i >> 2, e = i & 3;
-        const uint32_t w0 = wd[u][e >> 1][2 * (e & 1)];
-        const uint32_t w1 = wd[u][e >> 1][2 * (e & 1) + 1];
-        const float lo = (float)(int)__builtin_amdgcn_sbfe((int)(w0 ^ 0x88888888u), npos, 4);
-        const float hi = (float)(int)__builtin_amdgcn_sbfe((int)(w1 ^ 0x88888888u), npos, 4);
-        b[u][e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
+    // Eight codes (n = 0..7 in nibbles 0..7) to the bf16 B operand: the 4-bit signed convert of
+    // (c ^ 8) gives (c - 8) / 16 exactly (the output is scaled by 16 at the end); byte selects
+    // pick the even nibbles from the word and the odd ones from the word rotated by 4 bits.
+    auto bconv = [&](uint32_t wd, u4& b) {
+        const uint32_t x = wd ^ 0x88888888u;
+        const uint32_t x4 = __builtin_amdgcn_alignbit(x, x, 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = __builtin_amdgcn_cvt_off_f32_i4((int)((x >> (8 * e)) & 0xFFu));
+            const float hi = __builtin_amdgcn_cvt_off_f32_i4((int)((x4 >> (8 * e)) & 0xFFu));
+            b[e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
+        }
     };
     auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4], u4 (&alo)[4]) {
         const int slot = 16 * ((2 * t + h) ^ swz);
@@ -609,29 +630,30 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
             alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + off);
         }
     };
-    // Operands of step t + 1 are read (codes first, so their conversion waits on them alone)
-    // and converted between the MFMAs of step t.
+    // A operands of step t + 1 are read, and its B operands converted, between the MFMAs of step t.
     auto compute = [&](int sa, int sc) {
         const uint8_t* Ab = Aring + sa * kAStage + aver * 2 * kPlaneBytes;
         const uint8_t* Cb = Cring + sc * kCStage + wave * kCodeBytes;
-        u4 a[2][4], alo[2][4], wd[2][2], b[2][2];
-        read_b(Cb, 0, wd);
+        u4 a[2][4], alo[2][4], b[2][2];
+        v2i bt[2][2];
+        read_bt(Cb, bt);
         read_a(Ab, 0, a[0], alo[0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bpiece(wd, b[0], i);
+        for (int u = 0; u < 2; ++u) bconv((uint32_t)bt[u][0].x, b[0][u]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
-            if (t < 3) {
-                read_b(Cb, t + 1, wd);
-                read_a(Ab, t + 1, a[nxt], alo[nxt]);
-            }
+            if (t < 3) read_a(Ab, t + 1, a[nxt], alo[nxt]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int mi = i >> 1, u = i & 1;
                 acc[mi][u] = mfma32_bf16(alo[cur][mi], b[cur][u], mfma32_bf16(a[cur][mi], b[cur][u], acc[mi][u]));
-                if (t < 3) bpiece(wd, b[nxt], (i & 1) * 4 + (i >> 1));
+                if (t < 3 && (i & 3) == 0) {
+                    const int tn = t + 1, un = i >> 2;
+                    const v2i wv = bt[un][tn >> 1];
+                    bconv((uint32_t)((tn & 1) ? wv.y : wv.x), b[nxt][un]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -644,8 +666,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int sc_next = (sc == 2) ? 0 : sc + 1;
         const int sc_prev = (sc == 0) ? 2 : sc - 1;
-        // chunk c's code DMAs are done once only chunk c + 1's two may be in flight
-        if (c + 1 < c_end) wait_loads_barrier<2>();
+        // chunk c's code DMAs are done once only chunk c + 1's eight may be in flight
+        if (c + 1 < c_end) wait_loads_barrier<8>();
         else wait_loads_barrier<0>();
         if (c + 2 < c_end) issue_codes(c + 2, sc_prev);
         compute(sa, sc);
@@ -655,16 +677,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
 
     if (!wave_active) return;
     float* dst = out + (int64_t)z * split_stride;
+    // column of this lane in each 32-wide tile: k offset of nibble (j & 7) within octet j >> 3
+    const int kcol = (j & ~7) | (((j & 3) << 1) | ((j >> 2) & 1));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int64_t k = kw0 + 32 * u + j;
+            const int64_t k = kw0 + 32 * u + kcol;
             if (k >= col_limit) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + 32 * mi + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) dst[m * out_ld + k] = acc[mi][u][r];
+                if (m < M) dst[m * out_ld + k] = 16.0f * acc[mi][u][r];
             }
         }
     }
