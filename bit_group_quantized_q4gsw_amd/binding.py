@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
             "q4gsw_linear_bwd_input": [pw, vp, i32, i64, vp, vp, u64, vp],
             "q4gsw_qkv_fused": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, vp],
             "q4gsw_route": [i32, pw, i64, i32],
+            "q4gsw_gemm_tile_rows": [i32, pw, i64, i32],
+            "q4gsw_qkv_tile_rows": [pw, pw, pw, i64, i32],
+            "q4gsw_force_tile_rows": [i32],
         }
         for name, args in sigs.items():
             fn = getattr(h, name)
@@ -252,6 +255,26 @@ def qkv_fused(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, x: torch.Ten
 
 def route(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> str:
     return route_name(lib().q4gsw_route(op, w.ref(), M, _TORCH_DTYPE[dtype]))
+
+
+def gemm_tile_rows(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> int:
+    """Rows of the MFMA block tile the call's MFMA route uses (0: no MFMA route)."""
+    return int(lib().q4gsw_gemm_tile_rows(op, w.ref(), M, _TORCH_DTYPE[dtype]))
+
+
+def qkv_tile_rows(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, M: int, dtype: torch.dtype) -> int:
+    """Rows of the MFMA block tile of the fused QKV launch (0: no fused launch)."""
+    return int(lib().q4gsw_qkv_tile_rows(wq.ref(), wk.ref(), wv.ref(), M, _TORCH_DTYPE[dtype]))
+
+
+@contextlib.contextmanager
+def forced_tile_rows(rows: int):
+    """Force the forward / QKV MFMA block rows (64 or 128) inside the block."""
+    _check(lib().q4gsw_force_tile_rows(rows), "q4gsw_force_tile_rows")
+    try:
+        yield
+    finally:
+        lib().q4gsw_force_tile_rows(0)
 
 
 @contextlib.contextmanager

@@ -422,6 +422,22 @@ int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dt
     return st == Q4GSW_OK ? r : Q4GSW_ROUTE_NONE;
 }
 
+int32_t q4gsw_gemm_tile_rows(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype) {
+    const int32_t r = q4gsw_route(op, w, M, act_dtype);
+    if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT) return 128;
+    if (r != Q4GSW_ROUTE_GEMM_FOLD && r != Q4GSW_ROUTE_GEMM_GROUP && r != Q4GSW_ROUTE_GEMM_SPLIT) return 0;
+    FwdSeg seg{view_of(w), nullptr};
+    return 32 * plan_gemm_fwd(&seg, 1, act_dtype, fold_ok(w), M).mi;
+}
+
+int32_t q4gsw_qkv_tile_rows(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, int64_t M,
+                            int32_t act_dtype) {
+    if (check_qkv_descs(wq, wk, wv) != Q4GSW_OK) return 0;
+    if (q4gsw_route(Q4GSW_OP_QKV, wq, M, act_dtype) != Q4GSW_ROUTE_QKV_FUSED) return 0;
+    FwdSeg segs[3] = {FwdSeg{view_of(wq), nullptr}, FwdSeg{view_of(wk), nullptr}, FwdSeg{view_of(wv), nullptr}};
+    return 32 * plan_gemm_fwd(segs, 3, act_dtype, fold_ok(wq), M).mi;
+}
+
 const char* q4gsw_route_name(int32_t route) {
     switch (route) {
         case Q4GSW_ROUTE_NONE: return "none";
@@ -457,6 +473,12 @@ const char* q4gsw_status_str(int32_t status) {
 }
 
 void q4gsw_force_route(int32_t route) { g_forced_route.store(route, std::memory_order_relaxed); }
+
+q4gsw_status q4gsw_force_tile_rows(int32_t rows) {
+    if (rows != 0 && rows != 64 && rows != 128) return Q4GSW_E_SHAPE;
+    set_forced_fwd_tile_rows(rows);
+    return Q4GSW_OK;
+}
 
 uint32_t q4gsw_layout_version(void) { return Q4GSW_LAYOUT_VERSION; }
 

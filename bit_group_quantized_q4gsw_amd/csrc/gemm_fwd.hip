@@ -3,19 +3,21 @@
 // The forward GEMM of the pages (the linear_q4gsw op; the WebGPU BK64 QKV PR body
 // mirrors the Vulkan q4gsw forward GEMM per projection) re-designed for gfx950:
 //
-//   * v_mfma_f32_32x32x16 with fp32 accumulators; a wave owns a 128 (M) x 64 (N) output
-//     tile = 4 x 2 MFMA tiles, so every dequantised code feeds 128 activation rows;
-//   * block = 4 waves side by side in N (block tile 128 x 256), one block per CU;
+//   * v_mfma_f32_32x32x16 with fp32 accumulators; a wave owns a 32 MI (M) x 32 (N) output
+//     tile = MI MFMA tiles (MI = 4, or 2 for short activations), so every dequantised code
+//     feeds 32 MI activation rows;
+//   * block = 8 waves side by side in N (block tile 32 MI x 256), two waves per SIMD, so the
+//     code unpacking of one wave issues while the other wave's MFMAs run;
 //   * every global read is an LDS-DMA (global_load_lds): the 64-column activation chunk
-//     (shared by the 4 waves), each wave's 2 KB of codes and its scales travel straight
-//     into a ring of kStages LDS stages, kDepth chunks ahead of the MFMAs, with no VGPR
+//     (shared by the 8 waves), each wave's 1 KB of codes and its scales travel straight
+//     into a ring of KD + 1 LDS stages, KD chunks ahead of the MFMAs, with no VGPR
 //     staging.  Explicit vmcnt waits + s_barrier order the ring; the compiler only sees
 //     LDS reads (fp32 activations are the exception: split into bf16 hi + lo planes in
 //     registers on their way into LDS);
 //   * LDS swizzles: activation k-octet slots of row r sit at slot (octet ^ ((r >> 1) & 7)),
 //     so the 16 lanes of an A-fragment read phase (16 rows of 128 bytes) cover all 64
-//     banks; the 256-byte code run of row-octet R is rotated by R 32-byte blocks, so the 32
-//     lanes reading one k-octet of 8 row-octets hit 8 distinct bank groups;
+//     banks; the 256-byte code run of row-octet R is rotated by 2R 32-byte blocks, so the 64
+//     lanes reading one k-octet pair of the wave's 4 row-octets hit 64 distinct banks;
 //   * the K range is split across blocks when the output tiles cannot fill the GPU; the
 //     split index is the fastest-varying block coordinate, so with 8 splits every XCD owns
 //     one K slice (its activation and code slices stay in that XCD's L2); a reduction
@@ -35,19 +37,21 @@
 #include "device.h"
 #include "internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace q4gsw {
 
-constexpr int kBM = 128;            // block rows (M)
-constexpr int kWN = 64;             // wave columns (N)
-constexpr int kBN = 4 * kWN;        // block columns (N)
+constexpr int kWaves = 8;           // waves per block, two per SIMD
+constexpr int kWN = 32;             // wave columns (N)
+constexpr int kBN = kWaves * kWN;   // block columns (N)
 constexpr int kCK = 64;             // K columns per chunk
-constexpr int kDepth = 2;           // chunks in flight ahead of the chunk being multiplied
-constexpr int kStages = kDepth + 1; // LDS stages in the ring
+#ifndef Q4GSW_FWD_DEPTH
+#define Q4GSW_FWD_DEPTH 2
+#endif
+constexpr int kDepth16 = Q4GSW_FWD_DEPTH;   // chunks in flight ahead of the one multiplied (16-bit x)
 constexpr int kRowBytes = 128;      // one 16-bit activation row of a chunk in LDS
-constexpr int kPlaneBytes = kBM * kRowBytes;
-constexpr int kCodeBytes = 2048;    // one wave's codes for one chunk: 64 rows x 64 columns x 4 bits
+constexpr int kCodeBytes = 1024;    // one wave's codes for one chunk: 32 rows x 64 columns x 4 bits
 
 struct FwdSegArgs {
     const uint8_t* nib[3];
@@ -89,20 +93,39 @@ __device__ __forceinline__ u4 codes_f16(uint32_t w) {
 // SPC: scale slots per chunk (1: gs % 64 == 0; 2: gs % 32 == 0, one slot per 32 columns, which
 // the group and split modes take only for gs == 32; 4: fold mode with any gs % 8 == 0, one slot
 // per k-octet of the lane).  SF: 1 = fp16 scales.
-template <int XT, int MODE, int SPC, int SF>
-__global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const void* __restrict__ x, int64_t M,
+// Wait until at most n (clamped to 0..N) chunks of PER loads each issued after the chunk about
+// to be read are outstanding, then meet the other waves.
+template <int PER, int N>
+__device__ __forceinline__ void wait_chunks_barrier(int64_t n) {
+    if constexpr (N == 0) {
+        wait_loads_barrier<0>();
+    } else {
+        if (n >= N) wait_loads_barrier<N * PER>();
+        else wait_chunks_barrier<PER, N - 1>(n);
+    }
+}
+
+template <int XT, int MODE, int SPC, int SF, int MI, int KD>
+__global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const void* __restrict__ x, int64_t M,
                                                           int64_t K, int64_t k_pad, int64_t gs, int x_fast,
                                                           int chunks_per_split, int splits, int mtiles,
                                                           int64_t split_stride) {
+    static_assert(MI == 2 || MI == 4, "32-row MFMA tiles per wave");
+    static_assert(KD >= 2 && KD <= 6 && (XT != kF32 || KD == 2), "chunks in flight");
+    constexpr int kStages = KD + 1;                       // LDS stages in the ring
+    constexpr int kBM = 32 * MI;                          // block rows (M)
+    constexpr int kRowsPerWave = kBM / kWaves;            // activation rows each wave stages
+    constexpr int kPlaneBytes = kBM * kRowBytes;
+    constexpr int kAUnits = kBM * 16 / (64 * kWaves);     // fp32 float4 units per thread per chunk
     constexpr bool kX16 = XT != kF32;
     constexpr int kPlanes = kX16 ? 1 : 2;
-    constexpr int kADma = kX16 ? 4 : 0;                   // activation DMAs per wave per chunk
-    constexpr int kSDma = SF ? SPC : 2 * SPC;             // scale DMAs per wave per chunk
-    constexpr int kDmaPerChunk = kADma + 2 + kSDma;
+    constexpr int kADma = kX16 ? kRowsPerWave / 8 : 0;    // activation DMAs per wave per chunk
+    constexpr int kSDma = SPC;                            // scale DMAs per wave per chunk
+    constexpr int kDmaPerChunk = kADma + 1 + kSDma;
     constexpr int kAOff = 0;
     constexpr int kBOff = kPlanes * kPlaneBytes;
-    constexpr int kSOff = kBOff + 4 * kCodeBytes;
-    constexpr int kStageBytes = kSOff + 4 * kSDma * 256;
+    constexpr int kSOff = kBOff + kWaves * kCodeBytes;
+    constexpr int kStageBytes = kSOff + kWaves * kSDma * 256;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
 
     const int tid = threadIdx.x;
@@ -131,30 +154,29 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     lds_u8* const sm_l = (lds_u8*)smem;
 
     // ---------------- DMA source addresses ----------------
-    // Codes: DMA r of a wave covers row-octets 4r .. 4r+3 of the wave; lane l fills LDS
-    // bytes 16 l of it = row-octet R = 4r + (l >> 4), rotated block slot p = (l & 15) >> 1,
-    // half l & 1, which holds k-octet (p - R) & 7 of the chunk.
-    const uint8_t* csrc[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int R = 4 * r + (lane >> 4);
+    // Codes: one DMA per wave and chunk covers the wave's 4 row-octets; lane l fills LDS bytes
+    // 16 l = row-octet R = l >> 4, rotated block slot p = (l & 15) >> 1, half l & 1, which
+    // holds k-octet (p - 2R) & 7 of the chunk.
+    const uint8_t* csrc;
+    {
+        const int R = lane >> 4;
         const int p = (lane & 15) >> 1;
-        const int o = (p - R) & 7;
-        csrc[r] = seg.nib[sg] + 32 * (((nw >> 3) + R) * kocts + o) + 16 * (lane & 1);
+        const int o = (p - 2 * R) & 7;
+        csrc = seg.nib[sg] + 32 * (((nw >> 3) + R) * kocts + o) + 16 * (lane & 1);
     }
-    // Scales: lane (j, h) loads the scales of W rows nw + 2j, nw + 2j + 1 (adjacent in the
-    // scale plane) for each of its slots.
-    const int64_t srow = nw + 2 * j;
+    // Scales: DMA lane (jj, hh) = (l & 31, l >> 5) loads, for k-group hh, the fp32 scale of W
+    // row nw + jj or the fp16 pair of rows nw + 2 (jj & 15), +1 (adjacent in the scale plane).
+    const int64_t srow = SF ? nw + 2 * (j & 15) : nw + j;
     const int64_t sbase = (srow >> 3) * (seg.g_pad * 8) + (srow & 7);
     const uint8_t* sptr = static_cast<const uint8_t*>(seg.scales[sg]);
-    // Activations (16-bit): DMA q of wave w covers rows 32w + 8q .. +7; lane i fills slot i & 7
-    // of row (i >> 3), which holds k-octet (i & 7) ^ ((row >> 1) & 7).
-    const uint16_t* xa[4];
-    int xoct[4];
+    // Activations (16-bit): DMA q of wave w covers rows kRowsPerWave w + 8q .. +7; lane i fills
+    // slot i & 7 of row (i >> 3), which holds k-octet (i & 7) ^ ((row >> 1) & 7).
+    const uint16_t* xa[kADma > 0 ? kADma : 1];
+    int xoct[kADma > 0 ? kADma : 1];
     if constexpr (kX16) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = 32 * wave + 8 * q + (lane >> 3);
+        for (int q = 0; q < kADma; ++q) {
+            const int row = kRowsPerWave * wave + 8 * q + (lane >> 3);
             xoct[q] = (lane & 7) ^ ((row >> 1) & 7);
             const int64_t m = min(m0 + row, M - 1);     // rows past M only feed discarded outputs
             xa[q] = static_cast<const uint16_t*>(x) + m * K + 8 * xoct[q];
@@ -163,29 +185,24 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
 
     auto issue_codes_scales = [&](int64_t c, int st) {
         lds_u8* base = sm_l + st * kStageBytes;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) dma16(csrc[r] + 256 * c, base + kBOff + wave * kCodeBytes + 1024 * r);
+        dma16(csrc + 256 * c, base + kBOff + wave * kCodeBytes);
         const uint32_t kc = (uint32_t)(c * kCK);
         const uint32_t ug = (uint32_t)gs;
 #pragma unroll
         for (int q = 0; q < SPC; ++q) {
             const uint32_t k = (SPC == 4) ? kc + 16 * q + 8 * h : kc + 32 * q;
             const int64_t idx = sbase + (int64_t)(k / ug) * 8;
-            lds_u8* sdst = base + kSOff + wave * (kSDma * 256);
-            if constexpr (SF) {
-                dma4(sptr + 2 * idx, sdst + 256 * q);
-            } else {
-                dma4(sptr + 4 * idx, sdst + 256 * (2 * q));
-                dma4(sptr + 4 * idx + 4, sdst + 256 * (2 * q + 1));
-            }
+            lds_u8* sdst = base + kSOff + wave * (kSDma * 256) + 256 * q;
+            if constexpr (SF) dma4(sptr + 2 * idx, sdst);
+            else dma4(sptr + 4 * idx, sdst);
         }
     };
     // Synchronous fallback for a ragged K tail or unaligned x: zero-filled register loads
     // into the slots the DMA would write.
     auto fill_a16_slow = [&](int64_t kc, int st) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = 32 * wave + 8 * q + (lane >> 3);
+        for (int q = 0; q < kADma; ++q) {
+            const int row = kRowsPerWave * wave + 8 * q + (lane >> 3);
             const int64_t m = m0 + row;
             const int64_t k = kc + 8 * xoct[q];
             uint32_t e[8];
@@ -200,21 +217,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         const int64_t kc = c * kCK;
         if (x_fast && kc + kCK <= K) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dma16(xa[q] + kc, sm_l + st * kStageBytes + kAOff + (32 * wave + 8 * q) * kRowBytes);
+            for (int q = 0; q < kADma; ++q)
+                dma16(xa[q] + kc, sm_l + st * kStageBytes + kAOff + (kRowsPerWave * wave + 8 * q) * kRowBytes);
         } else {
             fill_a16_slow(kc, st);
         }
     };
 
-    // fp32 activations: 8 float4 units per thread, split into bf16 hi / lo planes at store time.
-    f4 areg[8];
+    // fp32 activations: kAUnits float4 units per thread, split into bf16 hi / lo planes at store time.
+    f4 areg[kAUnits];
     auto load_a32 = [&](int64_t c) {
         const int64_t kc = c * kCK;
         const bool fast = x_fast && kc + kCK <= K;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int unit = tid + 256 * i;
+        for (int i = 0; i < kAUnits; ++i) {
+            const int unit = tid + 64 * kWaves * i;
             const int row = unit >> 4;
             const int64_t k = kc + 4 * (unit & 15);
             if (fast) {
@@ -232,8 +249,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     };
     auto store_a32 = [&](int st) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int unit = tid + 256 * i;
+        for (int i = 0; i < kAUnits; ++i) {
+            const int unit = tid + 64 * kWaves * i;
             const int row = unit >> 4;
             const int oct = (unit & 15) >> 1;
             const int off = st * kStageBytes + kAOff + row * kRowBytes + 16 * (oct ^ ((row >> 1) & 7)) + 8 * (unit & 1);
@@ -247,114 +264,98 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
 
     // ---------------- accumulators ----------------
     constexpr bool kGroup = MODE != kModeFold;
-    f32x16 acc[4][2];
-    f32x16 part[kGroup ? 4 : 1][2];          // partial sums of the open scale group
-    float gopen[2] = {0.f, 0.f};             // its scales (rows brow, brow + 1)
+    f32x16 acc[MI];
+    f32x16 part[kGroup ? MI : 1];            // partial sums of the open scale group
+    float gopen = 0.f;                       // its scale (row n0 + j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][u][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     // ---------------- one chunk of MFMAs ----------------
     const int swz = (j >> 1) & 7;     // ((row >> 1) & 7) of every A row this lane reads
-    const int Rl = j >> 2;            // this lane's row-octet inside the wave
-    // fp32 group scale of slot q for rows brow (u = 0) and brow + 1 (u = 1); bf16 codes carry
-    // a factor 16 that the scale removes exactly.
-    auto group_scale = [&](const uint8_t* S, int q, float (&g)[2]) {
+    const int Rj = j >> 3;            // this lane's row-octet inside the wave
+    // LDS byte of this lane's scale in slot q (fp16: half of a pair word; fp32: a word)
+    const int sofs = SF ? 4 * (32 * h + (j >> 1)) + 2 * (j & 1) : 4 * (32 * h + j);
+    // fp32 group scale of slot q for row n0 + j; bf16 codes carry a factor 16 that the scale
+    // removes exactly.
+    auto group_scale = [&](const uint8_t* S, int q) -> float {
         constexpr float kUnit = (XT == kF16) ? 1.0f : 0.0625f;
-        if constexpr (SF) {
-            const uint32_t sv = *reinterpret_cast<const uint32_t*>(S + 256 * q + 4 * lane);
-            g[0] = (float)bitcast<_Float16>((uint16_t)(sv & 0xFFFFu)) * kUnit;
-            g[1] = (float)bitcast<_Float16>((uint16_t)(sv >> 16)) * kUnit;
-        } else {
-            g[0] = *reinterpret_cast<const float*>(S + 256 * (2 * q) + 4 * lane) * kUnit;
-            g[1] = *reinterpret_cast<const float*>(S + 256 * (2 * q + 1) + 4 * lane) * kUnit;
-        }
+        if constexpr (SF) return (float)bitcast<_Float16>(*reinterpret_cast<const uint16_t*>(S + 256 * q + sofs)) * kUnit;
+        else return *reinterpret_cast<const float*>(S + 256 * q + sofs) * kUnit;
     };
-    // A fragments of step t for the wave's four 32-row tiles (and the lo plane for fp32 x).
-    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4], u4 (&alo)[4]) {
+    // A fragments of step t for the wave's MI 32-row tiles (and the lo plane for fp32 x).
+    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[MI], u4 (&alo)[MI]) {
         const int slot = 16 * ((2 * t + h) ^ swz);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+        for (int mi = 0; mi < MI; ++mi) {
             const int off = (32 * mi + j) * kRowBytes + slot;
             a[mi] = *reinterpret_cast<const u4*>(Ab + off);
             if constexpr (MODE == kModeSplit) alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + off);
         }
     };
-    // B fragments of step t from the lane's code words (rows brow, brow + 1).
-    auto dequant = [&](u2 bw, const uint8_t* S, int t, u4 (&b)[2]) {
+    // fp16 scale of the lane's row in slot q, duplicated into both halves
+    auto fold_scale = [&](const uint8_t* S, int q) -> uint32_t {
+        const uint32_t s16 = *reinterpret_cast<const uint16_t*>(S + 256 * q + sofs);
+        return s16 | (s16 << 16);
+    };
+    // B fragment of step t from the lane's code word (row n0 + j).
+    auto dequant = [&](uint32_t bw, const uint8_t* S, int t, u4& b) {
         if constexpr (MODE == kModeFold) {
-            const uint32_t sv = *reinterpret_cast<const uint32_t*>(S + 256 * ((t * SPC) / 4) + 4 * lane);
-            const h2 s0 = bitcast<h2>((sv & 0xFFFFu) | (sv << 16));
-            const h2 s1 = bitcast<h2>((sv >> 16) | (sv & 0xFFFF0000u));
-            uint32_t p0[4], p1[4];
+            const h2 sc = bitcast<h2>(fold_scale(S, (t * SPC) / 4));
+            uint32_t p[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                p0[s] = bitcast<uint32_t>(codes_minus8_f16(bw.x, s) * s0);
-                p1[s] = bitcast<uint32_t>(codes_minus8_f16(bw.y, s) * s1);
-            }
-            b[0] = u4{p0[0], p0[1], p0[2], p0[3]};
-            b[1] = u4{p1[0], p1[1], p1[2], p1[3]};
+            for (int s = 0; s < 4; ++s) p[s] = bitcast<uint32_t>(codes_minus8_f16(bw, s) * sc);
+            b = u4{p[0], p[1], p[2], p[3]};
         } else if constexpr (XT == kF16) {
-            b[0] = codes_f16(bw.x);
-            b[1] = codes_f16(bw.y);
+            b = codes_f16(bw);
         } else {
-            b[0] = codes16_bf16(bw.x);
-            b[1] = codes16_bf16(bw.y);
+            b = codes16_bf16(bw);
         }
     };
-    // Dword e of B fragment u of step t (piece i = 4 u + e of the step's unpacking), for
-    // interleaving one piece after each MFMA.  wpre[u] carries per-word values from piece
-    // 4 u to the later pieces of the same word.
-    auto dequant_piece = [&](u2 bw, const uint8_t* S, int t, u4 (&b)[2], int i, uint32_t (&wpre)[2][2]) {
-        const int u = i >> 2, e = i & 3;
-        const uint32_t w = u ? bw.y : bw.x;
+    // Dword e of the B fragment of step t, for interleaving pieces with the MFMAs.  wpre
+    // carries per-word values from piece 0 to the later pieces.
+    auto dequant_piece = [&](uint32_t w, const uint8_t* S, int t, u4& b, int e, uint32_t (&wpre)[2]) {
         if constexpr (MODE == kModeFold) {
-            if (e == 0) wpre[u][0] = *reinterpret_cast<const uint32_t*>(S + 256 * ((t * SPC) / 4) + 4 * lane);
-            const uint32_t sv = wpre[u][0];
-            const h2 sc = u ? bitcast<h2>((sv >> 16) | (sv & 0xFFFF0000u)) : bitcast<h2>((sv & 0xFFFFu) | (sv << 16));
-            b[u][e] = bitcast<uint32_t>(codes_minus8_f16(w, e) * sc);
+            if (e == 0) wpre[0] = fold_scale(S, (t * SPC) / 4);
+            b[e] = bitcast<uint32_t>(codes_minus8_f16(w, e) * bitcast<h2>(wpre[0]));
         } else if constexpr (XT == kF16) {
-            b[u][e] = bitcast<uint32_t>(codes_minus8_f16(w, e));
+            b[e] = bitcast<uint32_t>(codes_minus8_f16(w, e));
         } else {
             if (e == 0) {
                 const uint32_t wx = w ^ 0x88888888u;
-                wpre[u][0] = wx & 0xF0F0F0F0u;
-                wpre[u][1] = (wx << 4) & 0xF0F0F0F0u;
-                asm volatile("" : "+v"(wpre[u][0]), "+v"(wpre[u][1]));
+                wpre[0] = wx & 0xF0F0F0F0u;
+                wpre[1] = (wx << 4) & 0xF0F0F0F0u;
+                asm volatile("" : "+v"(wpre[0]), "+v"(wpre[1]));
             }
             // dword e holds nibble positions e (low half) and e + 4 (high half); even positions
             // come from L = wpre[1], odd ones from H = wpre[0], byte (position >> 1)
-            const uint32_t src = (e & 1) ? wpre[u][0] : wpre[u][1];
+            const uint32_t src = (e & 1) ? wpre[0] : wpre[1];
             const int by = e >> 1;
             const float lo = (float)(int8_t)((src >> (8 * by)) & 0xFFu);
             const float hi = (float)(int8_t)((src >> (8 * (by + 2))) & 0xFFu);
-            b[u][e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
+            b[e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
         }
     };
-    // One MFMA (two for fp32 x) on tile (mi, u); KIND as below.
-    auto mma_tile = [&](const u4& a, const u4& alo, const u4& bu, int mi, int u, auto kind) {
+    // One MFMA (two for fp32 x) on tile mi; KIND as below.
+    auto mma_tile = [&](const u4& a, const u4& alo, const u4& b, int mi, auto kind) {
         constexpr int K_ = decltype(kind)::value;
         if constexpr (MODE == kModeFold) {
-            acc[mi][u] = mfma32_f16(a, bu, acc[mi][u]);
+            acc[mi] = mfma32_f16(a, b, acc[mi]);
         } else {
-            const f32x16 c0 = (K_ == 0) ? part[mi][u] : zero16;
-            if constexpr (MODE == kModeSplit) part[mi][u] = mfma32_bf16(alo, bu, mfma32_bf16(a, bu, c0));
-            else if constexpr (XT == kF16) part[mi][u] = mfma32_f16(a, bu, c0);
-            else part[mi][u] = mfma32_bf16(a, bu, c0);
+            const f32x16 c0 = (K_ == 0) ? part[mi] : zero16;
+            if constexpr (MODE == kModeSplit) part[mi] = mfma32_bf16(alo, b, mfma32_bf16(a, b, c0));
+            else if constexpr (XT == kF16) part[mi] = mfma32_f16(a, b, c0);
+            else part[mi] = mfma32_bf16(a, b, c0);
         }
     };
     auto flush_open_group = [&]() {
         if constexpr (kGroup) {
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[mi][u][r] = fmaf(part[mi][u][r], gopen[u], acc[mi][u][r]);
+                for (int r = 0; r < 16; ++r) acc[mi][r] = fmaf(part[mi][r], gopen, acc[mi][r]);
         }
     };
     // One chunk, software-pipelined: the code words of all four steps are read first; while
@@ -368,28 +369,28 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         const uint8_t* Ab = smem + st * kStageBytes + kAOff;
         const uint8_t* Bb = smem + st * kStageBytes + kBOff + wave * kCodeBytes;
         const uint8_t* S = smem + st * kStageBytes + kSOff + wave * (kSDma * 256);
-        u2 bw[4];
+        uint32_t bw[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            bw[t] = *reinterpret_cast<const u2*>(Bb + 256 * Rl + 32 * ((2 * t + h + Rl) & 7) + 8 * (j & 3));
-        u4 a[2][4], alo[2][4], b[2][2];
+            bw[t] = *reinterpret_cast<const uint32_t*>(Bb + 256 * Rj + 32 * ((2 * t + h + 2 * Rj) & 7) + 4 * (j & 7));
+        u4 a[2][MI], alo[2][MI], b[2];
         read_a(Ab, 0, a[0], alo[0]);
         dequant(bw[0], S, 0, b[0]);
-        // Fixed issue order per step: the next step's A reads, then eight (MFMA, unpacking
-        // piece) pairs, so the single wave keeps the VALU busy while the matrix core runs and
-        // the A reads have a whole step to land.
+        // Fixed issue order per step: the next step's A reads, then the MFMAs with the next
+        // step's unpacking pieces between them (two pieces per MFMA for MI = 2).
         auto one = [&](auto tc, auto kc) {
             constexpr int t = decltype(tc)::value, KIND = decltype(kc)::value;
             if constexpr (t < 3) read_a(Ab, t + 1, a[(t + 1) & 1], alo[(t + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            uint32_t wpre[2][2] = {{0u, 0u}, {0u, 0u}};
+            uint32_t wpre[2] = {0u, 0u};
+            constexpr int kPer = 4 / MI;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                mma_tile(a[t & 1][i >> 1], alo[t & 1][i >> 1], b[t & 1][i & 1], i >> 1, i & 1, kc);
-                if constexpr (t < 3) dequant_piece(bw[t + 1], S, t + 1, b[(t + 1) & 1], (i & 1) * 4 + (i >> 1), wpre);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int e = 0; e < 4; ++e) {
+                if (e % kPer == 0) mma_tile(a[t & 1][e / kPer], alo[t & 1][e / kPer], b[t & 1], e / kPer, kc);
+                if constexpr (t < 3) dequant_piece(bw[t + 1], S, t + 1, b[(t + 1) & 1], e, wpre);
+                if (e % kPer == kPer - 1) __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (KIND != 0) group_scale(S, SPC == 2 ? (t >> 1) : 0, gopen);
+            if constexpr (KIND != 0) gopen = group_scale(S, SPC == 2 ? (t >> 1) : 0);
             if constexpr (kGroup && SPC == 2 && (t & 1)) flush_open_group();   // gs == 32
         };
         one(std::integral_constant<int, 0>{}, k0);
@@ -399,40 +400,40 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     };
 
     // ---------------- pipeline ----------------
-    // 16-bit x: chunk c's DMAs (activations, codes, scales) are issued kDepth chunks ahead;
-    // before chunk c is read only chunk c + 1's DMAs may still be in flight.  A chunk staged
-    // through the synchronous fallback drained every older load already.
-    // fp32 x: codes and scales as above; activations of chunk c + 1 are loaded into registers
-    // while chunk c is multiplied and stored after it (the register use retires every older
-    // load), so before chunk c is read only those 8 loads may be in flight.
-    static_assert(kDepth == 2, "wait counts and stage rotation assume two chunks in flight");
-    if (c_begin < c_end) {
-        if constexpr (kX16) issue_a16(c_begin, 0);
+    // 16-bit x: chunk c's DMAs (activations, codes, scales) are issued KD chunks ahead; before
+    // chunk c is read only the DMAs of the chunks after it may still be in flight.  A chunk
+    // staged through the synchronous fallback drained every older load already.
+    // fp32 x (KD = 2): codes and scales as above; activations of chunk c + 1 are loaded into
+    // registers while chunk c is multiplied and stored after it (the register use retires every
+    // older load), so before chunk c is read only those kAUnits loads may be in flight.
+    if constexpr (kX16) {
+#pragma unroll
+        for (int d = 0; d < KD; ++d) {
+            if (c_begin + d < c_end) {
+                issue_a16(c_begin + d, d);
+                issue_codes_scales(c_begin + d, d);
+            }
+        }
+    } else if (c_begin < c_end) {
         issue_codes_scales(c_begin, 0);
-        if (c_begin + 1 < c_end) {
-            if constexpr (kX16) issue_a16(c_begin + 1, 1);
-            issue_codes_scales(c_begin + 1, 1);
-        }
-        if constexpr (!kX16) {
-            load_a32(c_begin);
-            store_a32(0);
-            if (c_begin + 1 < c_end) load_a32(c_begin + 1);
-        }
+        if (c_begin + 1 < c_end) issue_codes_scales(c_begin + 1, 1);
+        load_a32(c_begin);
+        store_a32(0);
+        if (c_begin + 1 < c_end) load_a32(c_begin + 1);
     }
     int st = 0;
     auto chunk = [&](int64_t c, auto k0, auto k2) {
-        const int st_next = (st == 2) ? 0 : st + 1;
-        const int st_prev = (st == 0) ? 2 : st - 1;
+        const int st_next = (st == KD) ? 0 : st + 1;
+        const int st_prev = (st == 0) ? KD : st - 1;              // the stage chunk c - 1 used
         if constexpr (kX16) {
-            if (c + 1 < c_end) wait_loads_barrier<kDmaPerChunk>();
-            else wait_loads_barrier<0>();
-            if (c + kDepth < c_end) {
-                issue_a16(c + kDepth, st_prev);                   // the stage chunk c - 1 used
-                issue_codes_scales(c + kDepth, st_prev);
+            wait_chunks_barrier<kDmaPerChunk, KD - 1>(min((int64_t)(KD - 1), c_end - 1 - c));
+            if (c + KD < c_end) {
+                issue_a16(c + KD, st_prev);
+                issue_codes_scales(c + KD, st_prev);
             }
         } else {
-            wait_loads_barrier<8>();
-            if (c + kDepth < c_end) issue_codes_scales(c + kDepth, st_prev);
+            wait_loads_barrier<kAUnits>();
+            if (c + 2 < c_end) issue_codes_scales(c + 2, st_prev);
         }
         compute(st, k0, k2);
         if constexpr (!kX16) {
@@ -465,24 +466,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
     if (!wave_active) return;
-    const int64_t brow = n0 + 2 * j;
+    const int64_t brow = n0 + j;
     float* out = seg.out[sg] + (int64_t)z * split_stride;
     const int64_t ld = seg.out_ld[sg];
     const int64_t ncols = split_stride ? seg.n_pad[sg] : seg.N[sg];
-    const bool pair_ok = (ld % 2 == 0) && (brow + 2 <= ncols);
+    if (brow >= ncols) return;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int64_t m = m0 + 32 * mi + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (m >= M) continue;
-            float* dst = out + m * ld + brow;
-            if (pair_ok) {
-                *reinterpret_cast<float2*>(dst) = make_float2(acc[mi][0][r], acc[mi][1][r]);
-            } else {
-                if (brow < ncols) dst[0] = acc[mi][0][r];
-                if (brow + 1 < ncols) dst[1] = acc[mi][1][r];
-            }
+            if (m < M) out[m * ld + brow] = acc[mi][r];
         }
     }
 }
@@ -499,27 +493,75 @@ static int fwd_spc(int64_t gs) {
     return 4;
 }
 
-// Split count minimising a time model (microseconds): rounds of blocks over the 256 CUs times
-// (chunks per split + 2 for pipeline fill and epilogue) at ~2 us per chunk, plus, with splits,
+// Split count minimising a time model (microseconds): rounds of blocks over the CU slots times
+// (chunks per split + 2 for pipeline fill and epilogue) at chunk_us per chunk, plus, with splits,
 // a reduction launch (~3 us) and the partial buffer written and read back (splits x M x width
 // x 8 bytes at ~5 TB/s).  Ties go to fewer splits.
-int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width) {
-    const int64_t cus = 256;
+int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width, int64_t slots, double chunk_us,
+                     double* cost_out) {
     int best = 1;
     double best_cost = 1e300;
     for (int64_t s = 1; s <= 64 && s <= n_chunks; ++s) {
         const int64_t per = (n_chunks + s - 1) / s;
         if ((n_chunks + per - 1) / per != s) continue;      // some split would be empty
-        const int64_t rounds = (blocks * s + cus - 1) / cus;
-        double cost = 2.0 * (double)rounds * (double)(per + 2);
+        const int64_t rounds = (blocks * s + slots - 1) / slots;
+        double cost = chunk_us * (double)rounds * (double)(per + 2);
         if (s > 1) cost += 3.0 + (double)s * (double)M * (double)width * 8.0 / 5e6;
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best = (int)s;
         }
     }
+    if (cost_out) *cost_out = best_cost;
     return best;
 }
+
+// Kernel instance for (activation type, mode, scale slots, scale type, row tiles), handed to f.
+template <int XT, int MODE, int SF, int MI, typename F>
+static void with_spc(int spc, F&& f) {
+    constexpr int KD = XT == kF32 ? 2 : kDepth16;
+    if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD>);
+    else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD>);
+    else if constexpr (MODE == kModeFold) f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD>);
+}
+template <int XT, int MODE, int SF, typename F>
+static void with_mi(int mi, int spc, F&& f) {
+    if (mi == 4) with_spc<XT, MODE, SF, 4>(spc, f);
+    else with_spc<XT, MODE, SF, 2>(spc, f);
+}
+template <typename F>
+static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, F&& f) {
+    if (mode == kModeFold) {
+        with_mi<kF16, kModeFold, 1>(mi, spc, f);
+    } else if (mode == kModeSplit) {
+        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, f);
+        else with_mi<kF32, kModeSplit, 0>(mi, spc, f);
+    } else if (x_dtype == kF16) {
+        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, f);
+        else with_mi<kF16, kModeGroup, 0>(mi, spc, f);
+    } else {
+        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, f);
+        else with_mi<kBF16, kModeGroup, 0>(mi, spc, f);
+    }
+}
+
+// Blocks of one kernel instance resident per CU (registers and LDS decide), cached per instance.
+static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int mi) {
+    static int cache[3][3][2][5][5];
+    int& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi];
+    if (slot == 0) {
+        int n = 1;
+        dispatch_fwd(mode, x_dtype, scale_f16, spc, mi, [&](auto kern) {
+            int b = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, 64 * kWaves, 0) == hipSuccess && b > 0) n = b;
+        });
+        slot = n;
+    }
+    return slot;
+}
+
+static std::atomic<int> g_forced_tile_rows{0};
+void set_forced_fwd_tile_rows(int rows) { g_forced_tile_rows.store(rows, std::memory_order_relaxed); }
 
 FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M) {
     FwdPlan p{};
@@ -532,30 +574,31 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         tiles += (segs[i].w.n_pad + kBN - 1) / kBN;
         npad_total += segs[i].w.n_pad;
     }
-    const int64_t blocks = tiles * ((M + kBM - 1) / kBM);
     const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
-    const int splits = pick_gemm_splits(blocks, n_chunks, M, npad_total);
-    p.splits = splits;
-    p.ws_bytes = splits > 1 ? (int64_t)splits * M * npad_total * 4 : 0;
+    const int spc = fwd_spc(w0.gs);
+    double best = 1e300;
+    const int forced = g_forced_tile_rows.load(std::memory_order_relaxed);
+    for (int mi : {4, 2}) {
+        if (forced == 64 || forced == 128) {
+            if (32 * mi != forced) continue;
+        } else if (mi == 4 && p.mode == kModeSplit) {
+            continue;                                  // hi + lo planes: the 128-row tile spills
+        }
+        const int64_t bm = 32 * mi;
+        const int64_t blocks = tiles * ((M + bm - 1) / bm);
+        const int64_t slots = 256 * (int64_t)fwd_blocks_per_cu(p.mode, x_dtype, w0.scale_f16, spc, mi);
+        // a 64-row block does half the MFMA work of a 128-row one per chunk but unpacks as many codes
+        const double chunk_us = mi == 4 ? 2.0 : 1.3;
+        double cost = 0;
+        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost);
+        if (cost < best - 1e-9) {
+            best = cost;
+            p.mi = mi;
+            p.splits = s;
+        }
+    }
+    p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * M * npad_total * 4 : 0;
     return p;
-}
-
-template <int XT, int MODE, int SPC, int SF>
-static void launch_fwd_t(dim3 grid, hipStream_t s, const FwdSegArgs& a, const void* x, int64_t M, int64_t K,
-                         int64_t k_pad, int64_t gs, int x_fast, int per, int splits, int mtiles,
-                         int64_t stride) {
-    hipLaunchKernelGGL((gemm_fwd_kernel<XT, MODE, SPC, SF>), grid, dim3(256), 0, s, a, x, M, K, k_pad, gs, x_fast,
-                       per, splits, mtiles, stride);
-}
-
-template <int XT, int MODE, int SF>
-static void launch_fwd_spc(int spc, dim3 grid, hipStream_t s, const FwdSegArgs& a, const void* x, int64_t M,
-                           int64_t K, int64_t k_pad, int64_t gs, int x_fast, int per, int splits, int mtiles,
-                           int64_t stride) {
-    if (spc == 1) launch_fwd_t<XT, MODE, 1, SF>(grid, s, a, x, M, K, k_pad, gs, x_fast, per, splits, mtiles, stride);
-    else if (spc == 2) launch_fwd_t<XT, MODE, 2, SF>(grid, s, a, x, M, K, k_pad, gs, x_fast, per, splits, mtiles, stride);
-    else if constexpr (MODE == kModeFold)
-        launch_fwd_t<XT, MODE, 4, SF>(grid, s, a, x, M, K, k_pad, gs, x_fast, per, splits, mtiles, stride);
 }
 
 // One launch over every segment.  With K splits the partials go to ws laid out as
@@ -589,9 +632,11 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     const int mode = plan.mode;
     const int spc = fwd_spc(w0.gs);
     if (spc == 4 && mode != kModeFold) return hipErrorInvalidValue;
+    if (plan.mi != 4 && plan.mi != 2) return hipErrorInvalidValue;
     const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);
-    const int64_t mtiles = (M + kBM - 1) / kBM;
+    const int64_t bm = 32 * plan.mi;
+    const int64_t mtiles = (M + bm - 1) / bm;
     const int64_t blocks = tiles * mtiles * plan.splits;
     if (blocks > (int64_t(1) << 24)) return hipErrorInvalidConfiguration;
     const int esize = x_dtype == kF32 ? 4 : 2;
@@ -600,18 +645,9 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     const int64_t st = plan.splits == 1 ? 0 : M * npad_total;
     const int64_t K = w0.K, kp = w0.k_pad, gs = w0.gs;
     const int sp = plan.splits, mt = (int)mtiles;
-    if (mode == kModeFold) {
-        launch_fwd_spc<kF16, kModeFold, 1>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-    } else if (mode == kModeSplit) {
-        if (w0.scale_f16) launch_fwd_spc<kF32, kModeSplit, 1>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-        else launch_fwd_spc<kF32, kModeSplit, 0>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-    } else if (x_dtype == kF16) {
-        if (w0.scale_f16) launch_fwd_spc<kF16, kModeGroup, 1>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-        else launch_fwd_spc<kF16, kModeGroup, 0>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-    } else {
-        if (w0.scale_f16) launch_fwd_spc<kBF16, kModeGroup, 1>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-        else launch_fwd_spc<kBF16, kModeGroup, 0>(spc, g, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
-    }
+    dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, [&](auto kern) {
+        hipLaunchKernelGGL(kern, g, dim3(64 * kWaves), 0, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
+    });
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const float* ys[3];

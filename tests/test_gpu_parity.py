@@ -189,3 +189,46 @@ def test_workload_bwd(act):
     rows = sample_rows(case.M)
     ref, norm = oracle_bwd(d_out, case.w, rows)
     assert_within(dx, ref, norm, TOL[d_out.dtype], f"bwd {act}", rows)
+
+
+# ---- both forward block tiles (64 and 128 rows), forced, on every forward precision route ------
+
+TILE_CASES = [
+    # M, N, K, gs, act, scale
+    (130, 512, 1024, 128, "bf16", "f16"),     # group route, ragged M over both tile heights
+    (200, 640, 512, 32, "f16", "f16"),        # fold route, two scale slots per chunk
+    (96, 256, 320, 8, "f16", "f16"),          # fold route, a scale slot per k-octet
+    (257, 264, 256, 64, "f16", "f32"),        # group route with fp32 scales and an N tail
+    (65, 256, 384, 64, "f32", "f16"),         # split route (fp32 x)
+    (40, 512, 256, 32, "f32", "f32"),         # split route, gs = 32, fp32 scales
+]
+
+
+@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("M,N,K,gs,act,sdt", TILE_CASES)
+def test_forward_tiles(M, N, K, gs, act, sdt, rows):
+    q = lib()
+    case = make_linear(M, K, N, gs, act, sdt, seed=M * 11 + N + rows, s_lo=0.005 if sdt == "f32" else 0.002)
+    pw = pack(q, case.w)
+    x = dev(case.x)
+    ref, norm = oracle_fwd(case.x, case.w)
+    with q.forced_tile_rows(rows):
+        assert q.gemm_tile_rows(q.OP_FWD, pw, M, case.x.dtype) == rows
+        y = q.linear_fwd(pw, x)
+        torch.cuda.synchronize()
+    assert_within(y, ref, norm, TOL[case.x.dtype], f"fwd tile {rows} route={q.route(q.OP_FWD, pw, M, case.x.dtype)}")
+
+
+@pytest.mark.parametrize("rows", [64, 128])
+def test_qkv_tiles(rows):
+    q = lib()
+    case = make_qkv(M=200, K=512, Ns=(512, 256, 136), group_size=32, act_dtype="f16", scale_dtype="f16", seed=rows)
+    pws = [pack(q, w) for w in case.weights]
+    x = dev(case.x)
+    refs = [oracle_fwd(case.x, w) for w in case.weights]
+    with q.forced_tile_rows(rows):
+        assert q.qkv_tile_rows(*pws, 200, case.x.dtype) == rows
+        outs = q.qkv_fused(*pws, x)
+        torch.cuda.synchronize()
+    for name, o, (ref, norm) in zip("qkv", outs, refs):
+        assert_within(o, ref, norm, 2e-3, f"qkv tile {rows} {name}")
