@@ -120,12 +120,18 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     constexpr bool kX16 = XT != kF32;
     constexpr int kPlanes = kX16 ? 1 : 2;
     constexpr int kADma = kX16 ? kRowsPerWave / 8 : 0;    // activation DMAs per wave per chunk
-    constexpr int kSDma = SPC;                            // scale DMAs per wave per chunk
+    // Scales: with one or two groups per chunk (SPC <= 2) wave 0 fetches the block's 256 rows
+    // in kSDma0 16-byte-per-lane DMAs; with a group per k-octet pair (SPC == 4) every wave
+    // fetches its own rows, 4 bytes per lane.
+    constexpr bool kBlockScales = SPC <= 2;
+    constexpr int kSDma0 = SF ? 1 : SPC;                  // block scale DMAs of wave 0 per chunk
+    constexpr int kSDma = kBlockScales ? 0 : SPC;         // scale DMAs of every wave per chunk
     constexpr int kDmaPerChunk = kADma + 1 + kSDma;
+    constexpr int kDmaPerChunk0 = kDmaPerChunk + (kBlockScales ? kSDma0 : 0);   // wave 0
     constexpr int kAOff = 0;
     constexpr int kBOff = kPlanes * kPlaneBytes;
     constexpr int kSOff = kBOff + kWaves * kCodeBytes;
-    constexpr int kStageBytes = kSOff + kWaves * kSDma * 256;
+    constexpr int kStageBytes = kSOff + (kBlockScales ? 1024 * kSDma0 : kWaves * SPC * 256);
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
 
     const int tid = threadIdx.x;
@@ -164,11 +170,14 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         const int o = (p - 2 * R) & 7;
         csrc = seg.nib[sg] + 32 * (((nw >> 3) + R) * kocts + o) + 16 * (lane & 1);
     }
-    // Scales: DMA lane (jj, hh) = (l & 31, l >> 5) loads, for k-group hh, the fp32 scale of W
-    // row nw + jj or the fp16 pair of rows nw + 2 (jj & 15), +1 (adjacent in the scale plane).
+    // Scales, per-wave form (SPC == 4): DMA lane (jj, hh) = (l & 31, l >> 5) loads, for k-group
+    // hh, the fp32 scale of W row nw + jj or the fp16 pair of rows nw + 2 (jj & 15), +1
+    // (adjacent in the scale plane).  Block form: row-octets boct .. boct + 31 of the tile.
     const int64_t srow = SF ? nw + 2 * (j & 15) : nw + j;
     const int64_t sbase = (srow >> 3) * (seg.g_pad * 8) + (srow & 7);
     const uint8_t* sptr = static_cast<const uint8_t*>(seg.scales[sg]);
+    const int64_t boct = (tile - seg.tile_start[sg]) * (kBN / 8);
+    const int64_t n_octs = seg.n_pad[sg] / 8;
     // Activations (16-bit): DMA q of wave w covers rows kRowsPerWave w + 8q .. +7; lane i fills
     // slot i & 7 of row (i >> 3), which holds k-octet (i & 7) ^ ((row >> 1) & 7).
     const uint16_t* xa[kADma > 0 ? kADma : 1];
@@ -188,13 +197,39 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         dma16(csrc + 256 * c, base + kBOff + wave * kCodeBytes);
         const uint32_t kc = (uint32_t)(c * kCK);
         const uint32_t ug = (uint32_t)gs;
+        if constexpr (kBlockScales) {
+            if (wave == 0) {
 #pragma unroll
-        for (int q = 0; q < SPC; ++q) {
-            const uint32_t k = (SPC == 4) ? kc + 16 * q + 8 * h : kc + 32 * q;
-            const int64_t idx = sbase + (int64_t)(k / ug) * 8;
-            lds_u8* sdst = base + kSOff + wave * (kSDma * 256) + 256 * q;
-            if constexpr (SF) dma4(sptr + 2 * idx, sdst);
-            else dma4(sptr + 4 * idx, sdst);
+                for (int i = 0; i < kSDma0; ++i) {
+                    // lane -> (row-octet o of the block, slot q, 16-byte half of an fp32 run);
+                    // fp16 with SPC == 1: lanes 32..63 repeat lanes 0..31
+                    int o, q, half;
+                    if constexpr (SF) {
+                        o = (lane / SPC) & 31;
+                        q = lane % SPC;
+                        half = 0;
+                    } else {
+                        const int P = 32 * i + (lane >> 1);
+                        o = P / SPC;
+                        q = P % SPC;
+                        half = lane & 1;
+                    }
+                    const int64_t g = (int64_t)((kc + 32u * (uint32_t)q) / ug);
+                    const int64_t oct = min(boct + o, n_octs - 1);   // rows past n_pad: a valid octet
+                    const int64_t idx = (oct * seg.g_pad + g) * 8;
+                    const uint8_t* src = SF ? sptr + 2 * idx : sptr + 4 * idx + 16 * half;
+                    dma16(src, base + kSOff + 1024 * i);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SPC; ++q) {
+                const uint32_t k = kc + 16 * q + 8 * h;
+                const int64_t idx = sbase + (int64_t)(k / ug) * 8;
+                lds_u8* sdst = base + kSOff + wave * (SPC * 256) + 256 * q;
+                if constexpr (SF) dma4(sptr + 2 * idx, sdst);
+                else dma4(sptr + 4 * idx, sdst);
+            }
         }
     };
     // Synchronous fallback for a ragged K tail or unaligned x: zero-filled register loads
@@ -276,14 +311,19 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     // ---------------- one chunk of MFMAs ----------------
     const int swz = (j >> 1) & 7;     // ((row >> 1) & 7) of every A row this lane reads
     const int Rj = j >> 3;            // this lane's row-octet inside the wave
-    // LDS byte of this lane's scale in slot q (fp16: half of a pair word; fp32: a word)
-    const int sofs = SF ? 4 * (32 * h + (j >> 1)) + 2 * (j & 1) : 4 * (32 * h + j);
+    // LDS byte of this lane's scale (row r = 32 wave + j) in slot q: block form, run
+    // SPC (r >> 3) + q of 8 scales; per-wave form, half of a pair word (fp16) or a word (fp32)
+    const int srl = 32 * wave + j;
+    auto soff = [&](int q) -> int {
+        if constexpr (kBlockScales) return (SF ? 16 : 32) * (SPC * (srl >> 3) + q) + (SF ? 2 : 4) * (srl & 7);
+        else return 256 * q + (SF ? 4 * (32 * h + (j >> 1)) + 2 * (j & 1) : 4 * (32 * h + j));
+    };
     // fp32 group scale of slot q for row n0 + j; bf16 codes carry a factor 16 that the scale
     // removes exactly.
     auto group_scale = [&](const uint8_t* S, int q) -> float {
         constexpr float kUnit = (XT == kF16) ? 1.0f : 0.0625f;
-        if constexpr (SF) return (float)bitcast<_Float16>(*reinterpret_cast<const uint16_t*>(S + 256 * q + sofs)) * kUnit;
-        else return *reinterpret_cast<const float*>(S + 256 * q + sofs) * kUnit;
+        if constexpr (SF) return (float)bitcast<_Float16>(*reinterpret_cast<const uint16_t*>(S + soff(q))) * kUnit;
+        else return *reinterpret_cast<const float*>(S + soff(q)) * kUnit;
     };
     // A fragments of step t for the wave's MI 32-row tiles (and the lo plane for fp32 x).
     auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[MI], u4 (&alo)[MI]) {
@@ -297,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     };
     // fp16 scale of the lane's row in slot q, duplicated into both halves
     auto fold_scale = [&](const uint8_t* S, int q) -> uint32_t {
-        const uint32_t s16 = *reinterpret_cast<const uint16_t*>(S + 256 * q + sofs);
+        const uint32_t s16 = *reinterpret_cast<const uint16_t*>(S + soff(q));
         return s16 | (s16 << 16);
     };
     // B fragment of step t from the lane's code word (row n0 + j).
@@ -368,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         constexpr int K0 = decltype(k0)::value, K2 = decltype(k2)::value;
         const uint8_t* Ab = smem + st * kStageBytes + kAOff;
         const uint8_t* Bb = smem + st * kStageBytes + kBOff + wave * kCodeBytes;
-        const uint8_t* S = smem + st * kStageBytes + kSOff + wave * (kSDma * 256);
+        const uint8_t* S = smem + st * kStageBytes + kSOff + (kBlockScales ? 0 : wave * (SPC * 256));
         uint32_t bw[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -426,7 +466,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         const int st_next = (st == KD) ? 0 : st + 1;
         const int st_prev = (st == 0) ? KD : st - 1;              // the stage chunk c - 1 used
         if constexpr (kX16) {
-            wait_chunks_barrier<kDmaPerChunk, KD - 1>(min((int64_t)(KD - 1), c_end - 1 - c));
+            const int64_t ahead = min((int64_t)(KD - 1), c_end - 1 - c);
+            if (kBlockScales && wave == 0) wait_chunks_barrier<kDmaPerChunk0, KD - 1>(ahead);
+            else wait_chunks_barrier<kDmaPerChunk, KD - 1>(ahead);
             if (c + KD < c_end) {
                 issue_a16(c + KD, st_prev);
                 issue_codes_scales(c + KD, st_prev);
