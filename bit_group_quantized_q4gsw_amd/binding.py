@@ -45,6 +45,11 @@ class WeightDesc(ctypes.Structure):
     ]
 
 
+class PlanInfo(ctypes.Structure):
+    """q4gsw_plan_info of include/q4gsw.h."""
+    _fields_ = [("route", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -68,9 +73,8 @@ def lib() -> ctypes.CDLL:
             "q4gsw_linear_bwd_input": [pw, vp, i32, i64, vp, vp, u64, vp],
             "q4gsw_qkv_fused": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, vp],
             "q4gsw_route": [i32, pw, i64, i32],
-            "q4gsw_gemm_tile_rows": [i32, pw, i64, i32],
-            "q4gsw_qkv_tile_rows": [pw, pw, pw, i64, i32],
-            "q4gsw_force_tile_rows": [i32],
+            "q4gsw_plan": [i32, pw, pw, pw, i64, i32, ctypes.POINTER(PlanInfo)],
+            "q4gsw_force_plan": [i32, i32],
         }
         for name, args in sigs.items():
             fn = getattr(h, name)
@@ -257,24 +261,25 @@ def route(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> str:
     return route_name(lib().q4gsw_route(op, w.ref(), M, _TORCH_DTYPE[dtype]))
 
 
-def gemm_tile_rows(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> int:
-    """Rows of the MFMA block tile the call's MFMA route uses (0: no MFMA route)."""
-    return int(lib().q4gsw_gemm_tile_rows(op, w.ref(), M, _TORCH_DTYPE[dtype]))
-
-
-def qkv_tile_rows(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, M: int, dtype: torch.dtype) -> int:
-    """Rows of the MFMA block tile of the fused QKV launch (0: no fused launch)."""
-    return int(lib().q4gsw_qkv_tile_rows(wq.ref(), wk.ref(), wv.ref(), M, _TORCH_DTYPE[dtype]))
+def plan(op: int, w: PackedWeight, M: int, dtype: torch.dtype, wk: PackedWeight = None,
+         wv: PackedWeight = None) -> dict:
+    """How a call runs: route name, MFMA block rows and contraction splits.  For OP_QKV pass wk
+    and wv."""
+    info = PlanInfo()
+    refs = [x.ref() if x is not None else None for x in (wk, wv)]
+    _check(lib().q4gsw_plan(op, w.ref(), refs[0], refs[1], M, _TORCH_DTYPE[dtype], ctypes.byref(info)), "q4gsw_plan")
+    return {"route": route_name(info.route), "tile_rows": info.tile_rows, "splits": info.splits}
 
 
 @contextlib.contextmanager
-def forced_tile_rows(rows: int):
-    """Force the forward / QKV MFMA block rows (64 or 128) inside the block."""
-    _check(lib().q4gsw_force_tile_rows(rows), "q4gsw_force_tile_rows")
+def forced_plan(tile_rows: int = 0, splits: int = 0):
+    """Force the forward / QKV MFMA block rows (64 or 128) and K splits inside the block; 0
+    leaves a choice per shape."""
+    _check(lib().q4gsw_force_plan(tile_rows, splits), "q4gsw_force_plan")
     try:
         yield
     finally:
-        lib().q4gsw_force_tile_rows(0)
+        lib().q4gsw_force_plan(0, 0)
 
 
 @contextlib.contextmanager

@@ -422,20 +422,37 @@ int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dt
     return st == Q4GSW_OK ? r : Q4GSW_ROUTE_NONE;
 }
 
-int32_t q4gsw_gemm_tile_rows(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype) {
+q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* wk, const q4gsw_weight* wv,
+                        int64_t M, int32_t act_dtype, q4gsw_plan_info* info) {
+    if (!info) return Q4GSW_E_NULL;
+    *info = q4gsw_plan_info{Q4GSW_ROUTE_NONE, 0, 1};
+    q4gsw_status st = op == Q4GSW_OP_QKV ? check_qkv_descs(w, wk, wv) : check_desc(w);
+    if (st != Q4GSW_OK) return st;
     const int32_t r = q4gsw_route(op, w, M, act_dtype);
-    if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT) return 128;
-    if (r != Q4GSW_ROUTE_GEMM_FOLD && r != Q4GSW_ROUTE_GEMM_GROUP && r != Q4GSW_ROUTE_GEMM_SPLIT) return 0;
-    FwdSeg seg{view_of(w), nullptr};
-    return 32 * plan_gemm_fwd(&seg, 1, act_dtype, fold_ok(w), M).mi;
-}
-
-int32_t q4gsw_qkv_tile_rows(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, int64_t M,
-                            int32_t act_dtype) {
-    if (check_qkv_descs(wq, wk, wv) != Q4GSW_OK) return 0;
-    if (q4gsw_route(Q4GSW_OP_QKV, wq, M, act_dtype) != Q4GSW_ROUTE_QKV_FUSED) return 0;
-    FwdSeg segs[3] = {FwdSeg{view_of(wq), nullptr}, FwdSeg{view_of(wk), nullptr}, FwdSeg{view_of(wv), nullptr}};
-    return 32 * plan_gemm_fwd(segs, 3, act_dtype, fold_ok(wq), M).mi;
+    info->route = r;
+    if (r == Q4GSW_ROUTE_NONE) return Q4GSW_OK;
+    const WView v = view_of(w);
+    if (r == Q4GSW_ROUTE_GEMV) {
+        info->splits = gemv_fwd_splits(v, M);
+    } else if (r == Q4GSW_ROUTE_BWD_GEMV) {
+        info->splits = gemv_bwd_splits(v, M);
+    } else if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT) {
+        info->tile_rows = 128;
+        info->splits = plan_gemm_bwd(v, act_dtype, fold_ok(w), M).splits;
+    } else if (r == Q4GSW_ROUTE_GEMM_FOLD || r == Q4GSW_ROUTE_GEMM_GROUP || r == Q4GSW_ROUTE_GEMM_SPLIT ||
+               r == Q4GSW_ROUTE_QKV_FUSED) {
+        FwdSeg segs[3] = {FwdSeg{v, nullptr}, FwdSeg{}, FwdSeg{}};
+        int nseg = 1;
+        if (r == Q4GSW_ROUTE_QKV_FUSED) {
+            segs[1] = FwdSeg{view_of(wk), nullptr};
+            segs[2] = FwdSeg{view_of(wv), nullptr};
+            nseg = 3;
+        }
+        const FwdPlan p = plan_gemm_fwd(segs, nseg, act_dtype, fold_ok(w), M);
+        info->tile_rows = 32 * p.mi;
+        info->splits = p.splits;
+    }
+    return Q4GSW_OK;
 }
 
 const char* q4gsw_route_name(int32_t route) {
@@ -474,9 +491,10 @@ const char* q4gsw_status_str(int32_t status) {
 
 void q4gsw_force_route(int32_t route) { g_forced_route.store(route, std::memory_order_relaxed); }
 
-q4gsw_status q4gsw_force_tile_rows(int32_t rows) {
-    if (rows != 0 && rows != 64 && rows != 128) return Q4GSW_E_SHAPE;
-    set_forced_fwd_tile_rows(rows);
+q4gsw_status q4gsw_force_plan(int32_t tile_rows, int32_t splits) {
+    if (tile_rows != 0 && tile_rows != 64 && tile_rows != 128) return Q4GSW_E_SHAPE;
+    if (splits < 0 || splits > 64) return Q4GSW_E_SHAPE;
+    set_forced_fwd_plan(tile_rows, splits);
     return Q4GSW_OK;
 }
 

@@ -507,12 +507,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     }
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
-    if (!wave_active) return;
     const int64_t brow = n0 + j;
     float* out = seg.out[sg] + (int64_t)z * split_stride;
     const int64_t ld = seg.out_ld[sg];
     const int64_t ncols = split_stride ? seg.n_pad[sg] : seg.N[sg];
-    if (brow >= ncols) return;
+    if (!wave_active || brow >= ncols) return;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -538,14 +537,22 @@ static int fwd_spc(int64_t gs) {
 // Split count minimising a time model (microseconds): rounds of blocks over the CU slots times
 // (chunks per split + 2 for pipeline fill and epilogue) at chunk_us per chunk, plus, with splits,
 // a reduction launch (~3 us) and the partial buffer written and read back (splits x M x width
-// x 8 bytes at ~5 TB/s).  Ties go to fewer splits.
+// x 8 bytes at ~5 TB/s).  Ties go to fewer splits.  force_splits > 0 takes that count instead
+// (clamped to the chunks and rounded to a count without an empty split).
 int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width, int64_t slots, double chunk_us,
-                     double* cost_out) {
+                     double* cost_out, int force_splits) {
     int best = 1;
     double best_cost = 1e300;
+    int64_t want = 0;
+    if (force_splits > 0) {
+        const int64_t f = min((int64_t)force_splits, n_chunks);
+        const int64_t per = (n_chunks + f - 1) / f;
+        want = (n_chunks + per - 1) / per;
+    }
     for (int64_t s = 1; s <= 64 && s <= n_chunks; ++s) {
         const int64_t per = (n_chunks + s - 1) / s;
         if ((n_chunks + per - 1) / per != s) continue;      // some split would be empty
+        if (want > 0 && s != want) continue;
         const int64_t rounds = (blocks * s + slots - 1) / slots;
         double cost = chunk_us * (double)rounds * (double)(per + 2);
         if (s > 1) cost += 3.0 + (double)s * (double)M * (double)width * 8.0 / 5e6;
@@ -603,7 +610,11 @@ static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int 
 }
 
 static std::atomic<int> g_forced_tile_rows{0};
-void set_forced_fwd_tile_rows(int rows) { g_forced_tile_rows.store(rows, std::memory_order_relaxed); }
+static std::atomic<int> g_forced_splits{0};
+void set_forced_fwd_plan(int rows, int splits) {
+    g_forced_tile_rows.store(rows, std::memory_order_relaxed);
+    g_forced_splits.store(splits, std::memory_order_relaxed);
+}
 
 FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M) {
     FwdPlan p{};
@@ -632,7 +643,8 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         // a 64-row block does half the MFMA work of a 128-row one per chunk but unpacks as many codes
         const double chunk_us = mi == 4 ? 2.0 : 1.3;
         double cost = 0;
-        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost);
+        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost,
+                                       g_forced_splits.load(std::memory_order_relaxed));
         if (cost < best - 1e-9) {
             best = cost;
             p.mi = mi;

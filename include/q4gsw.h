@@ -183,15 +183,22 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight *wq, const q4gsw_weight *wk, con
 int32_t q4gsw_route(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype);
 const char *q4gsw_route_name(int32_t route);
 
-/* Tile attestation: rows (M) of the MFMA block tile an MFMA route of this call
- * uses (forward and QKV: 128 or 64, picked per shape; input gradient: 128), or 0
- * when the call takes no MFMA route or would fail validation.  Arguments as for
- * q4gsw_route (for Q4GSW_OP_QKV pass Wq; a call that takes the fused launch
- * reports 0 here and its tile through q4gsw_qkv_tile_rows).  Host only, no GPU
- * work; the choice weighs the resident blocks per CU of the current device. */
-int32_t q4gsw_gemm_tile_rows(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype);
-int32_t q4gsw_qkv_tile_rows(const q4gsw_weight *wq, const q4gsw_weight *wk, const q4gsw_weight *wv,
-                            int64_t M, int32_t act_dtype);
+/* Plan attestation for tests and benchmarks: how a call with these arguments runs.
+ * For Q4GSW_OP_QKV pass the three weights (wk, wv are ignored for the other ops and
+ * may be NULL).  Host only, no GPU work; the forward plan weighs the resident blocks
+ * per CU of the current device.  Returns Q4GSW_E_NULL without `info` and the
+ * validation status of the descriptors otherwise; a call that would fail validation
+ * reports route Q4GSW_ROUTE_NONE. */
+typedef struct q4gsw_plan_info {
+    int32_t route;          /* as q4gsw_route */
+    int32_t tile_rows;      /* rows (M) of the MFMA block tile (forward / QKV: 128 or 64;
+                               input gradient: 128); 0 without an MFMA GEMM */
+    int32_t splits;         /* contraction splits across blocks (1: none; more: a reduction
+                               launch sums the fp32 partials in split order) */
+} q4gsw_plan_info;
+q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight *w, const q4gsw_weight *wk, const q4gsw_weight *wv,
+                        int64_t M, int32_t act_dtype, q4gsw_plan_info *info);
+
 const char *q4gsw_status_str(int32_t status);
 
 /* Force every later call to take `route` (Q4GSW_ROUTE_NONE restores automatic
@@ -199,12 +206,13 @@ const char *q4gsw_status_str(int32_t status);
  * and not synchronized: for tests and benchmarks that compare routes. */
 void q4gsw_force_route(int32_t route);
 
-/* Force the rows (64 or 128) of the forward / QKV MFMA block tile for every later
- * call; 0 restores the per-shape choice.  Other values return Q4GSW_E_SHAPE and
- * change nothing.  Process-wide and not synchronized, like q4gsw_force_route: set
- * it before sizing the workspace of the calls it should govern (for tests and
- * benchmarks that compare tiles). */
-q4gsw_status q4gsw_force_tile_rows(int32_t rows);
+/* Force the forward / QKV MFMA plan for every later call: tile_rows 64 or 128 and
+ * splits 1..64 contraction splits (clamped to the 64-column chunks and rounded to a
+ * count with no empty split); 0 leaves each to the shape.  Other values return
+ * Q4GSW_E_SHAPE and change nothing.  Process-wide and not synchronized, like
+ * q4gsw_force_route: set it before sizing the workspace of the calls it should govern
+ * (for tests and benchmarks that compare plans). */
+q4gsw_status q4gsw_force_plan(int32_t tile_rows, int32_t splits);
 
 /* Layout version and a build identifier string. */
 uint32_t q4gsw_layout_version(void);

@@ -212,8 +212,8 @@ def test_forward_tiles(M, N, K, gs, act, sdt, rows):
     pw = pack(q, case.w)
     x = dev(case.x)
     ref, norm = oracle_fwd(case.x, case.w)
-    with q.forced_tile_rows(rows):
-        assert q.gemm_tile_rows(q.OP_FWD, pw, M, case.x.dtype) == rows
+    with q.forced_plan(tile_rows=rows):
+        assert q.plan(q.OP_FWD, pw, M, case.x.dtype)["tile_rows"] == rows
         y = q.linear_fwd(pw, x)
         torch.cuda.synchronize()
     assert_within(y, ref, norm, TOL[case.x.dtype], f"fwd tile {rows} route={q.route(q.OP_FWD, pw, M, case.x.dtype)}")
@@ -226,9 +226,47 @@ def test_qkv_tiles(rows):
     pws = [pack(q, w) for w in case.weights]
     x = dev(case.x)
     refs = [oracle_fwd(case.x, w) for w in case.weights]
-    with q.forced_tile_rows(rows):
-        assert q.qkv_tile_rows(*pws, 200, case.x.dtype) == rows
+    with q.forced_plan(tile_rows=rows):
+        assert q.plan(q.OP_QKV, pws[0], 200, case.x.dtype, pws[1], pws[2])["tile_rows"] == rows
         outs = q.qkv_fused(*pws, x)
         torch.cuda.synchronize()
     for name, o, (ref, norm) in zip("qkv", outs, refs):
         assert_within(o, ref, norm, 2e-3, f"qkv tile {rows} {name}")
+
+
+# ---- forced split counts: every split count gives the oracle's result within tol ----------------
+
+SPLIT_CASES = [
+    # kind, M, N, K, gs, act, scale, tile rows, splits
+    ("fwd", 130, 512, 1024, 128, "bf16", "f16", 128, 4),
+    ("fwd", 64, 264, 2048, 32, "f16", "f16", 64, 8),
+    ("fwd", 40, 512, 1536, 64, "f32", "f32", 64, 3),
+    ("qkv", 128, None, 2048, 32, "f16", "f16", 64, 2),
+    ("qkv", 100, None, 1280, 64, "bf16", "f16", 128, 5),
+]
+
+
+@pytest.mark.parametrize("kind,M,N,K,gs,act,sdt,rows,splits", SPLIT_CASES)
+def test_forced_splits(kind, M, N, K, gs, act, sdt, rows, splits):
+    q = lib()
+    if kind == "qkv":
+        case = make_qkv(M=M, K=K, Ns=(512, 128, 136), group_size=gs, act_dtype=act, scale_dtype=sdt, seed=M + K)
+        ws_list = case.weights
+    else:
+        case = make_linear(M, K, N, gs, act, sdt, seed=M + N + K, s_lo=0.005 if sdt == "f32" else 0.002)
+        ws_list = [case.w]
+    pws = [pack(q, w) for w in ws_list]
+    x = dev(case.x)
+    with q.forced_plan(tile_rows=rows, splits=splits):
+        if kind == "qkv":
+            info = q.plan(q.OP_QKV, pws[0], M, case.x.dtype, pws[1], pws[2])
+            outs = q.qkv_fused(*pws, x)
+        else:
+            info = q.plan(q.OP_FWD, pws[0], M, case.x.dtype)
+            outs = (q.linear_fwd(pws[0], x),)
+        torch.cuda.synchronize()
+    assert info["splits"] == splits and info["tile_rows"] == rows, f"forced plan not taken: {info}"
+    tol = TOL[case.x.dtype]
+    for o, w in zip(outs, ws_list):
+        ref, norm = oracle_fwd(case.x, w)
+        assert_within(o, ref, norm, tol, f"{kind} splits={splits} rows={rows}")
