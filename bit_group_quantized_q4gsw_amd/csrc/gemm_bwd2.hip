@@ -413,9 +413,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
                                                                 int chunks_per_split, int splits, int mtiles) {
     constexpr int kAStage = NV * 2 * kPlaneBytes;
     constexpr int kCStage = 4 * kCodeBytes;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kAStage + 3 * kCStage];
+    constexpr int kSBuf = 1024;                  // one chunk's scales (one 64-lane 16-byte DMA)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kAStage + 3 * kCStage + 2 * kSBuf];
     uint8_t* const Aring = smem;
     uint8_t* const Cring = smem + 2 * kAStage;
+    uint8_t* const Sbuf = smem + 2 * kAStage + 3 * kCStage;
     lds_u8* const sm_l = (lds_u8*)smem;
 
     const int tid = threadIdx.x;
@@ -445,6 +447,31 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
         constexpr int kSU = SF ? 4 : 8;
         u4 xreg[kXU];
         u4 sreg[NV][kSU];
+        // Scales of chunk c, NV copies x 8 n-octets x 8 rows: one DMA by the first producer wave
+        // into a 2-slot LDS buffer, lane l -> (copy v, octet o[, 16-byte half of an fp32 run]) at
+        // byte 16 l; lanes past the data repeat it.  A copy for columns past k_pad only feeds
+        // idle consumers; its group index stays in the plane.
+        const uint8_t* ssrc;
+        {
+            int v, o, half;
+            if constexpr (SF) {
+                const int l = lane & (8 * NV - 1);
+                v = l >> 3;
+                o = l & 7;
+                half = 0;
+            } else {
+                const int l = lane & (16 * NV - 1);
+                v = l >> 4;
+                o = (l >> 1) & 7;
+                half = l & 1;
+            }
+            const int64_t g = min((kb0 + 128 * v) / w.gs, w.g_pad - 1);
+            ssrc = static_cast<const uint8_t*>(w.scales) + ((int64_t)o * w.g_pad + g) * 8 * (SF ? 2 : 4) + 16 * half;
+        }
+        const int64_t s_chunk_stride = (int64_t)8 * w.g_pad * 8 * (SF ? 2 : 4);
+        auto issue_scales = [&](int64_t c) {
+            if (wave == 4) dma16(ssrc + s_chunk_stride * c, (lds_u8*)Sbuf + kSBuf * ((c - c_begin) & 1));
+        };
         auto load_a = [&](int64_t c) {
             const int64_t n0 = c * kCN + 32 * ahalf;
             if (g_fast && n0 + 32 <= N) {
@@ -472,21 +499,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
                     xreg[i] = u4{e[0], e[1], e[2], e[3]};
                 }
             }
+        };
+        // the thread's scales (octets 4 ahalf .. +3 of each copy) from the chunk's LDS slot
+        auto read_scales = [&](int64_t c) {
+            const uint8_t* Sb = Sbuf + kSBuf * ((c - c_begin) & 1);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                // a copy for columns past k_pad only feeds idle consumers; keep its reads in the plane
-                const int64_t g = min((kb0 + 128 * v) / w.gs, w.g_pad - 1);
+            for (int v = 0; v < NV; ++v)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t idx = ((n0 >> 3) + q) * (w.g_pad * 8) + g * 8;
+                    const int o = 8 * v + 4 * ahalf + q;
                     if constexpr (SF) {
-                        sreg[v][q] = ldg16(static_cast<const uint16_t*>(w.scales) + idx);
+                        sreg[v][q] = *reinterpret_cast<const u4*>(Sb + 16 * o);
                     } else {
-                        sreg[v][2 * q] = ldg16(static_cast<const float*>(w.scales) + idx);
-                        sreg[v][2 * q + 1] = ldg16(static_cast<const float*>(w.scales) + idx + 4);
+                        sreg[v][2 * q] = *reinterpret_cast<const u4*>(Sb + 32 * o);
+                        sreg[v][2 * q + 1] = *reinterpret_cast<const u4*>(Sb + 32 * o + 16);
                     }
                 }
-            }
         };
         auto x_at = [&](int i) -> float {
             if constexpr (GT == kF32) return bitcast<float>(xreg[i >> 2][i & 3]);
@@ -505,7 +533,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
                 return bitcast<float>(sreg[v][i >> 2][i & 3]);
             }
         };
-        auto store_a = [&](int st) {
+        auto store_a = [&](int st, int64_t c) {
+            read_scales(c);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 uint8_t* hiP = Aring + st * kAStage + v * 2 * kPlaneBytes;
@@ -533,18 +562,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
                 }
             }
         };
-        // A' of chunk c + 1 is built during chunk c; its loads were issued one chunk earlier
+        // A' of chunk c + 1 is built during chunk c; its loads were issued one chunk earlier, each
+        // chunk's scale DMA just before them, so allowing those kXU loads in flight completes it.
         if (c_begin < c_end) {
+            issue_scales(c_begin);
+            if (c_begin + 1 < c_end) issue_scales(c_begin + 1);
             load_a(c_begin);
-            store_a(0);
+        }
+        wait_loads_barrier<kXU>();                     // the first two scale slots are in LDS
+        if (c_begin < c_end) {
+            store_a(0, c_begin);
             if (c_begin + 1 < c_end) load_a(c_begin + 1);
         }
         int sa = 0;
         for (int64_t c = c_begin; c < c_end; ++c) {
-            wait_loads_barrier<63>();                  // the stores of chunk c are done
+            wait_loads_barrier<kXU>();                 // the stores of chunk c and scales of c + 1 are done
             if (c + 1 < c_end) {
-                store_a(sa ^ 1);
-                if (c + 2 < c_end) load_a(c + 2);
+                store_a(sa ^ 1, c + 1);
+                if (c + 2 < c_end) {
+                    issue_scales(c + 2);               // the slot chunk c's scales used
+                    load_a(c + 2);
+                }
             }
             sa ^= 1;
         }
@@ -662,6 +700,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
         issue_codes(c_begin, 0);
         if (c_begin + 1 < c_end) issue_codes(c_begin + 1, 1);
     }
+    wait_loads_barrier<63>();                          // the producers' first scale slots
     int sc = 0, sa = 0;
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int sc_next = (sc == 2) ? 0 : sc + 1;
