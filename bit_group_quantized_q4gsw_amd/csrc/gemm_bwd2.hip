@@ -3,24 +3,24 @@
 // the frozen-base input gradient of the Vulkan q4gsw-backward PR body, reading the forward's
 // packed buffer as it is (no re-pack).
 //
-// Work split: a wave owns a 128 (M) x 64 (K) output tile = 4 x 2 MFMA tiles; a block is 4 waves
-// side by side in K (block tile 128 x 256).  The contraction runs over n in 64-row chunks.
+// A wave owns a 128 (M) x 64 (K) output tile = 4 x 2 MFMA tiles; a block holds four such tiles
+// side by side in K (block tile 128 x 256).  The contraction runs over n in 64-row chunks.  Two
+// kernels:
 //
-//   * codes: each wave LDS-DMAs its 64 (n) x 64 (k) code tile per chunk (8 row-octets x 256
-//     contiguous bytes, the row-octet R run rotated by R 32-byte blocks).  The MFMA B fragment
-//     needs 8 consecutive n of one k: that is one nibble position of the 8 words of one 32-byte
-//     micro-block, so each lane reads its micro-block and extracts its nibble from every word
-//     (a register transpose, no LDS transpose);
-//   * kModeSplit (fp32 / bf16 d_out, and fp16 with scales that cannot be folded): the block's
-//     columns lie in at most two scale groups (gs % 128 == 0; a change can only fall at column
-//     128 of the block), so the scale moves to the A side: A' = d_out * scale[g, n] in fp32, split
-//     into bf16 hi + lo (|err| <= 2^-18 |A'|) while it is staged into LDS, one copy per group;
-//     B = code - 8 exactly in bf16; two MFMA passes;
-//   * kModeFold (fp16 d_out, fp16 scales checked foldable at pack time): d_out is LDS-DMA'd as
-//     it is and B = fp16((code - 8) * scale[g, n]), one rounding, |err| <= 2^-11 |w|; one pass.
-//
-// Issue order per MFMA step: the next step's LDS reads, then (MFMA, unpacking piece) pairs
-// fenced with sched_barrier, so the wave keeps unpacking while the matrix core runs.
+//   * gemm_bwd_fold_kernel (fp16 d_out, fp16 scales checked foldable at pack time), 4 waves:
+//     d_out is LDS-DMA'd as it is and B = fp16((code - 8) * scale[g, n]), one rounding,
+//     |err| <= 2^-11 |w|; one pass.  Each wave LDS-DMAs its 64 (n) x 64 (k) code tile per chunk
+//     (8 row-octets x 256 contiguous bytes, the row-octet R run rotated by R 32-byte blocks).
+//     The MFMA B fragment needs 8 consecutive n of one k: one nibble position of the 8 words of
+//     a 32-byte micro-block, so each lane reads its micro-block and extracts its nibble from
+//     every word (a register transpose).  Issue order per MFMA step: the next step's LDS reads,
+//     then (MFMA, unpacking piece) pairs fenced with sched_barrier.
+//   * gemm_bwd_split_kernel (fp32 / bf16 d_out, and fp16 with scales that cannot be folded),
+//     4 consumer + 4 producer waves: the block's columns lie in at most two scale groups
+//     (gs % 128 == 0; a change can only fall at column 128 of the block), so the scale moves to
+//     the A side: A' = d_out * scale[g, n] in fp32, split into bf16 hi + lo (|err| <= 2^-18 |A'|)
+//     by the producers while it is staged into LDS, one copy per group; B = code - 8 exactly in
+//     bf16 from the transposing 4-bit LDS read; two MFMA passes.
 #include "device.h"
 #include "internal.h"
 
@@ -37,20 +37,17 @@ constexpr int kRowBytes = 128;      // one 16-bit A row of a chunk in LDS
 constexpr int kPlaneBytes = kBM * kRowBytes;
 constexpr int kCodeBytes = 2048;    // one wave's codes per chunk: 64 n x 64 k x 4 bits
 
-// MODE kModeSplit: NV = A' copies per block (1: gs % 256 == 0, 2: gs % 128 == 0).
-// MODE kModeFold:  NV = scale groups per wave (1: gs % 64 == 0, 2: gs == 32).
-// SF: 1 = fp16 scales.
-template <int GT, int MODE, int NV, int SF>
-__global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* __restrict__ d_out, int64_t M,
-                                                           float* __restrict__ out, int64_t out_ld,
-                                                           int64_t split_stride, int64_t col_limit, int g_fast,
-                                                           int chunks_per_split, int splits, int mtiles) {
-    constexpr bool kFold = MODE == kModeFold;
-    constexpr int kARing = kFold ? 3 : 2;                       // A stages
-    constexpr int kAStage = kFold ? kPlaneBytes : NV * 2 * kPlaneBytes;
-    constexpr int kSBytes = kFold ? 256 : 0;                    // per-wave fold scales per chunk
+// NV = scale groups per wave (1: gs % 64 == 0, 2: gs == 32).
+template <int NV>
+__global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const void* __restrict__ d_out, int64_t M,
+                                                               float* __restrict__ out, int64_t out_ld,
+                                                               int64_t split_stride, int64_t col_limit, int g_fast,
+                                                               int chunks_per_split, int splits, int mtiles) {
+    constexpr int kARing = 3;                                   // A stages
+    constexpr int kAStage = kPlaneBytes;
+    constexpr int kSBytes = 256;                                // per-wave scales per chunk
     constexpr int kCStage = 4 * (kCodeBytes + kSBytes);
-    constexpr int kDmaPerChunk = kFold ? 4 + 2 + 1 : 2;
+    constexpr int kDmaPerChunk = 4 + 2 + 1;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kARing * kAStage + 3 * kCStage];
     uint8_t* const Aring = smem;
     uint8_t* const Cring = smem + kARing * kAStage;
@@ -80,7 +77,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
     const int64_t c_begin = (int64_t)z * chunks_per_split;
     const int64_t c_end = min(c_begin + (int64_t)chunks_per_split, n_chunks);
 
-    // ---------------- code (and fold-scale) DMA ----------------
+    // ---------------- code and scale DMA ----------------
     // DMA r covers row-octets 4r .. 4r+3 of the chunk; lane l fills bytes 16 l: row-octet
     // R = 4r + (l >> 4), rotated block slot p = (l & 15) >> 1, half l & 1, holding the wave's
     // k-octet (p - R) & 7.
@@ -92,7 +89,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
         csrc[r] = w.nib + 32 * ((int64_t)R * kocts + (kwc >> 3) + o) + 16 * (lane & 1);
     }
     const int64_t chunk_code_stride = 32 * 8 * kocts;         // 8 row-octets
-    // fold scales: lane l loads 4 bytes = the fp16 scales of rows 2 (l & 3), +1 of row-octet
+    // scales: lane l loads 4 bytes = the fp16 scales of rows 2 (l & 3), +1 of row-octet
     // (l & 31) >> 2 for group slot l >> 5 (two slots only when gs == 32).
     const int fgl = (NV == 2) ? (lane >> 5) : 0;
     const int64_t fgroup = (kwc + 32 * fgl) / w.gs;
@@ -101,21 +98,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
         lds_u8* base = sm_l + kCOff + st * kCStage + wave * (kCodeBytes + kSBytes);
 #pragma unroll
         for (int r = 0; r < 2; ++r) dma16(csrc[r] + chunk_code_stride * c, base + 1024 * r);
-        if constexpr (kFold)
-            dma4(static_cast<const uint16_t*>(w.scales) + fsrc + 8 * c * (w.g_pad * 8), base + kCodeBytes);
+        dma4(static_cast<const uint16_t*>(w.scales) + fsrc + 8 * c * (w.g_pad * 8), base + kCodeBytes);
     };
 
-    // ---------------- fold: d_out (fp16) DMA, as the forward's activation staging ----------------
+    // ---------------- d_out (fp16) DMA, as the forward's activation staging ----------------
     const uint16_t* xa[4];
     int xoct[4];
-    if constexpr (kFold) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = 32 * wave + 8 * q + (lane >> 3);
-            xoct[q] = (lane & 7) ^ ((row >> 1) & 7);
-            const int64_t m = min(m0 + row, M - 1);            // rows past M only feed discarded outputs
-            xa[q] = static_cast<const uint16_t*>(d_out) + m * N + 8 * xoct[q];
-        }
+    for (int q = 0; q < 4; ++q) {
+        const int row = 32 * wave + 8 * q + (lane >> 3);
+        xoct[q] = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t m = min(m0 + row, M - 1);                // rows past M only feed discarded outputs
+        xa[q] = static_cast<const uint16_t*>(d_out) + m * N + 8 * xoct[q];
     }
     auto issue_a16 = [&](int64_t c, int st) {
         const int64_t nc = c * kCN;
@@ -139,96 +133,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
         }
     };
 
-    // ---------------- split: A' = d_out * scale -> bf16 hi / lo planes ----------------
-    // thread t stages row t >> 1, n-octets 4 (t & 1) .. 4 (t & 1) + 3 of the chunk
-    const int arow = tid >> 1;
-    const int ahalf = tid & 1;
-    const int64_t am = min(m0 + arow, M - 1);                  // rows past M only feed discarded outputs
-    constexpr int kXU = (GT == kF32) ? 8 : 4;                  // 16-byte d_out loads per thread
-    constexpr int kSU = SF ? 4 : 8;                            // 16-byte scale loads per copy
-    u4 xreg[kXU];
-    u4 sreg[NV][kSU];
-    auto load_a = [&](int64_t c) {
-        const int64_t n0 = c * kCN + 32 * ahalf;
-        if (g_fast && n0 + 32 <= N) {
-#pragma unroll
-            for (int i = 0; i < kXU; ++i) {
-                if constexpr (GT == kF32) xreg[i] = ldg16(static_cast<const float*>(d_out) + am * N + n0 + 4 * i);
-                else xreg[i] = ldg16(static_cast<const uint16_t*>(d_out) + am * N + n0 + 8 * i);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kXU; ++i) {
-                uint32_t e[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if constexpr (GT == kF32) {
-                        const int64_t n = n0 + 4 * i + q;
-                        e[q] = (n < N) ? static_cast<const uint32_t*>(d_out)[am * N + n] : 0u;
-                    } else {
-                        const int64_t n = n0 + 8 * i + 2 * q;
-                        const uint32_t lo = (n < N) ? static_cast<const uint16_t*>(d_out)[am * N + n] : 0u;
-                        const uint32_t hi = (n + 1 < N) ? static_cast<const uint16_t*>(d_out)[am * N + n + 1] : 0u;
-                        e[q] = lo | (hi << 16);
-                    }
-                }
-                xreg[i] = u4{e[0], e[1], e[2], e[3]};
-            }
-        }
-        // scales of the 32 rows n0 .. n0 + 31 for each group copy (rows past N carry scale 0)
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            // (a copy for columns past k_pad only feeds idle waves; keep its reads in the plane)
-            const int64_t g = min((kb0 + 128 * v) / w.gs, w.g_pad - 1);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t idx = ((n0 >> 3) + q) * (w.g_pad * 8) + g * 8;
-                if constexpr (SF) {
-                    sreg[v][q] = ldg16(static_cast<const uint16_t*>(w.scales) + idx);
-                } else {
-                    sreg[v][2 * q] = ldg16(static_cast<const float*>(w.scales) + idx);
-                    sreg[v][2 * q + 1] = ldg16(static_cast<const float*>(w.scales) + idx + 4);
-                }
-            }
-        }
-    };
-    auto x_at = [&](int i) -> float {        // d_out value i (0..31) of the thread's row segment
-        if constexpr (GT == kF32) return bitcast<float>(xreg[i >> 2][i & 3]);
-        else {
-            const uint32_t wd = xreg[i >> 3][(i >> 1) & 3];
-            const uint16_t b = (i & 1) ? (uint16_t)(wd >> 16) : (uint16_t)(wd & 0xFFFFu);
-            if constexpr (GT == kF16) return f16_bits_to_f32(b);
-            else return bf16_bits_to_f32(b);
-        }
-    };
-    auto s_at = [&](int v, int i) -> float {  // scale of row i (0..31) for copy v
-        if constexpr (SF) {
-            const uint32_t wd = sreg[v][i >> 3][(i >> 1) & 3];
-            return f16_bits_to_f32((i & 1) ? (uint16_t)(wd >> 16) : (uint16_t)(wd & 0xFFFFu));
-        } else {
-            return bitcast<float>(sreg[v][i >> 2][i & 3]);
-        }
-    };
-    auto store_a = [&](int st) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            uint8_t* hiP = Aring + st * kAStage + v * 2 * kPlaneBytes;
-            uint8_t* loP = hiP + kPlaneBytes;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 8 * q + 2 * e;
-                    split_bf16(x_at(i) * s_at(v, i), x_at(i + 1) * s_at(v, i + 1), hw[e], lw[e]);
-                }
-                const int off = arow * kRowBytes + 16 * ((4 * ahalf + q) ^ ((arow >> 1) & 7));
-                *reinterpret_cast<u4*>(hiP + off) = u4{hw[0], hw[1], hw[2], hw[3]};
-                *reinterpret_cast<u4*>(loP + off) = u4{lw[0], lw[1], lw[2], lw[3]};
-            }
-        }
-    };
-
     // ---------------- accumulators and one chunk of MFMAs ----------------
     f32x16 acc[4][2];
 #pragma unroll
@@ -240,16 +144,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
 
     const int swz = (j >> 1) & 7;                 // ((row >> 1) & 7) of every A row this lane reads
     const int npos = 4 * nib_pos(j & 7);          // bit offset of this lane's k in each code word
-    const int aver = (!kFold && NV == 2) ? (wave >> 1) : 0;
-    // A fragments of step t (hi and, for the split mode, lo plane)
-    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4], u4 (&alo)[4]) {
+    // A fragments of step t
+    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4]) {
         const int slot = 16 * ((2 * t + h) ^ swz);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int off = (32 * mi + j) * kRowBytes + slot;
-            a[mi] = *reinterpret_cast<const u4*>(Ab + off);
-            if constexpr (!kFold) alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + off);
-        }
+        for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const u4*>(Ab + (32 * mi + j) * kRowBytes + slot);
     };
     // the 8 code words of step t for column u (micro-block row-octet 2t + h, k-octet 4u + j/8)
     auto read_b = [&](const uint8_t* Cb, int t, u4 (&wd)[2][2]) {
@@ -263,35 +162,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
         }
     };
     auto read_fs = [&](const uint8_t* Sb, int t, u4 (&fs)[2]) {
-        if constexpr (kFold) {
-            const int R = 2 * t + h;
+        const int R = 2 * t + h;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) fs[u] = *reinterpret_cast<const u4*>(Sb + 128 * (NV == 2 ? u : 0) + 16 * R);
-        }
+        for (int u = 0; u < 2; ++u) fs[u] = *reinterpret_cast<const u4*>(Sb + 128 * (NV == 2 ? u : 0) + 16 * R);
     };
     // dword e of B fragment u: rows 2e, 2e+1 of the micro-block at this lane's k
     auto bpiece = [&](const u4 (&wd)[2][2], const u4 (&fs)[2], u4 (&b)[2], int i) {
         const int u = i >> 2, e = i & 3;
         const uint32_t w0 = wd[u][e >> 1][2 * (e & 1)];
         const uint32_t w1 = wd[u][e >> 1][2 * (e & 1) + 1];
-        if constexpr (kFold) {
-            const uint32_t c0 = __builtin_amdgcn_ubfe(w0, npos, 4);
-            const uint32_t c1 = __builtin_amdgcn_ubfe(w1, npos, 4);
-            const h2 v = bitcast<h2>((c0 | (c1 << 16)) | 0x64006400u);
-            const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-            b[u][e] = bitcast<uint32_t>((v - off) * bitcast<h2>(fs[u][e]));
-        } else {
-            const float lo = (float)(int)__builtin_amdgcn_sbfe((int)(w0 ^ 0x88888888u), npos, 4);
-            const float hi = (float)(int)__builtin_amdgcn_sbfe((int)(w1 ^ 0x88888888u), npos, 4);
-            b[u][e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
-        }
+        const uint32_t c0 = __builtin_amdgcn_ubfe(w0, npos, 4);
+        const uint32_t c1 = __builtin_amdgcn_ubfe(w1, npos, 4);
+        const h2 v = bitcast<h2>((c0 | (c1 << 16)) | 0x64006400u);
+        const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        b[u][e] = bitcast<uint32_t>((v - off) * bitcast<h2>(fs[u][e]));
     };
-    auto compute = [&](int sa, int sc) {
-        const uint8_t* Ab = Aring + sa * kAStage + aver * 2 * kPlaneBytes;
-        const uint8_t* Cb = Cring + sc * kCStage + wave * (kCodeBytes + kSBytes);
+    auto compute = [&](int st) {
+        const uint8_t* Ab = Aring + st * kAStage;
+        const uint8_t* Cb = Cring + st * kCStage + wave * (kCodeBytes + kSBytes);
         const uint8_t* Sb = Cb + kCodeBytes;
-        u4 a[2][4], alo[2][4], wd[2][2][2], fs[2][2], b[2][2];
-        read_a(Ab, 0, a[0], alo[0]);
+        u4 a[2][4], wd[2][2][2], fs[2][2], b[2][2];
+        read_a(Ab, 0, a[0]);
         read_b(Cb, 0, wd[0]);
         read_fs(Sb, 0, fs[0]);
 #pragma unroll
@@ -300,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
         for (int t = 0; t < 4; ++t) {
             const int cur = t & 1, nxt = (t + 1) & 1;
             if (t < 3) {
-                read_a(Ab, t + 1, a[nxt], alo[nxt]);
+                read_a(Ab, t + 1, a[nxt]);
                 read_b(Cb, t + 1, wd[nxt]);
                 read_fs(Sb, t + 1, fs[nxt]);
             }
@@ -308,11 +199,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int mi = i >> 1, u = i & 1;
-                if constexpr (kFold) {
-                    acc[mi][u] = mfma32_f16(a[cur][mi], b[cur][u], acc[mi][u]);
-                } else {
-                    acc[mi][u] = mfma32_bf16(alo[cur][mi], b[cur][u], mfma32_bf16(a[cur][mi], b[cur][u], acc[mi][u]));
-                }
+                acc[mi][u] = mfma32_f16(a[cur][mi], b[cur][u], acc[mi][u]);
                 if (t < 3) bpiece(wd[nxt], fs[nxt], b[nxt], (i & 1) * 4 + (i >> 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -320,46 +207,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd2_kernel(WView w, const void* 
     };
 
     // ---------------- pipeline ----------------
-    // Codes (and fold scales, and fold d_out) are DMA'd kDepth = 2 chunks ahead into a 3-stage
-    // ring; before chunk c is read only chunk c + 1's DMAs may be in flight.  Split mode: A' of
-    // chunk c + 1 is loaded into registers while chunk c is multiplied and stored after it (the
-    // register use retires every older load), so only those loads may be in flight.
+    // d_out, codes and scales are DMA'd two chunks ahead into a 3-stage ring; before chunk c is
+    // read only chunk c + 1's DMAs may be in flight (a chunk staged through the synchronous
+    // fallback drained every older load already).
     if (c_begin < c_end) {
-        if constexpr (kFold) issue_a16(c_begin, 0);
+        issue_a16(c_begin, 0);
         issue_codes(c_begin, 0);
         if (c_begin + 1 < c_end) {
-            if constexpr (kFold) issue_a16(c_begin + 1, 1);
+            issue_a16(c_begin + 1, 1);
             issue_codes(c_begin + 1, 1);
         }
-        if constexpr (!kFold) {
-            load_a(c_begin);
-            store_a(0);
-            if (c_begin + 1 < c_end) load_a(c_begin + 1);
-        }
     }
-    int sc = 0, sa = 0;
+    int st = 0;
     for (int64_t c = c_begin; c < c_end; ++c) {
-        const int sc_next = (sc == 2) ? 0 : sc + 1;
-        const int sc_prev = (sc == 0) ? 2 : sc - 1;
-        if constexpr (kFold) {
-            if (c + 1 < c_end) wait_loads_barrier<kDmaPerChunk>();
-            else wait_loads_barrier<0>();
-            if (c + 2 < c_end) {
-                issue_a16(c + 2, sc_prev);
-                issue_codes(c + 2, sc_prev);
-            }
-            compute(sc, sc);
-        } else {
-            wait_loads_barrier<kXU + NV * kSU>();
-            if (c + 2 < c_end) issue_codes(c + 2, sc_prev);
-            compute(sa, sc);
-            if (c + 1 < c_end) {
-                store_a(sa ^ 1);
-                if (c + 2 < c_end) load_a(c + 2);
-            }
-            sa ^= 1;
+        const int st_next = (st == 2) ? 0 : st + 1;
+        const int st_prev = (st == 0) ? 2 : st - 1;
+        if (c + 1 < c_end) wait_loads_barrier<kDmaPerChunk>();
+        else wait_loads_barrier<0>();
+        if (c + 2 < c_end) {
+            issue_a16(c + 2, st_prev);
+            issue_codes(c + 2, st_prev);
         }
-        sc = sc_next;
+        compute(st);
+        st = st_next;
     }
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
@@ -740,11 +610,11 @@ bool v2_supported(const WView& w, int g_dtype, int fold_ok) {
     return w.gs % 128 == 0;
 }
 
-template <int GT, int MODE, int NV, int SF>
-void launch_t(dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64_t M, float* out, int64_t ld,
-              int64_t stride, int64_t limit, int g_fast, int per, int splits, int mtiles) {
-    hipLaunchKernelGGL((gemm_bwd2_kernel<GT, MODE, NV, SF>), grid, dim3(256), 0, s, w, d_out, M, out, ld, stride,
-                       limit, g_fast, per, splits, mtiles);
+template <int NV>
+void launch_fold(dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64_t M, float* out, int64_t ld,
+                 int64_t stride, int64_t limit, int g_fast, int per, int splits, int mtiles) {
+    hipLaunchKernelGGL((gemm_bwd_fold_kernel<NV>), grid, dim3(256), 0, s, w, d_out, M, out, ld, stride, limit, g_fast,
+                       per, splits, mtiles);
 }
 
 template <int GT, int NV>
@@ -797,8 +667,8 @@ hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64
     const int64_t limit = plan.splits == 1 ? w.K : w.k_pad;
     const int sp = plan.splits, mt = (int)mtiles;
     if (plan.mode == kModeFold) {
-        if (w.gs == 32) launch_t<kF16, kModeFold, 2, 1>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt);
-        else launch_t<kF16, kModeFold, 1, 1>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt);
+        if (w.gs == 32) launch_fold<2>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt);
+        else launch_fold<1>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt);
     } else {
         const bool one = w.gs % 256 == 0;
         const int sf = w.scale_f16;
