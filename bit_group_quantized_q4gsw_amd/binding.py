@@ -58,8 +58,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with bit_group_quantized_q4gsw_amd/build.py "
-                              "(or __graft_entry__.build()); there is no CPU fallback")
+            raise ImportError(f"{LIB_PATH} is missing: build it with python bit_group_quantized_q4gsw_amd/build.py; "
+                              "there is no CPU fallback")
         h = ctypes.CDLL(LIB_PATH)
         i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
         pw = ctypes.POINTER(WeightDesc)
