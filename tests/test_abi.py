@@ -229,3 +229,47 @@ def test_backward_and_qkv_validation(q):
 def test_python_wrappers_reject_host_tensors(q):
     with pytest.raises(ValueError):
         q.pack(torch.zeros(4, 8, dtype=torch.uint8), torch.ones(1, 4, dtype=torch.float16), 8)
+
+
+def plan_info(q, op, d, M, dt, dk=None, dv=None):
+    info = q.binding.PlanInfo()
+    refs = [ctypes.byref(x) if x is not None else None for x in (dk, dv)]
+    st = q.lib().q4gsw_plan(op, ctypes.byref(d), refs[0], refs[1], M, dt, ctypes.byref(info))
+    return st, info
+
+
+def test_plan_attestation_and_forcing(q):
+    """q4gsw_plan reports the route, block rows and splits; q4gsw_force_plan pins the forward
+    block rows and split count and rejects out-of-range values (host logic only)."""
+    fold = 1
+    pre = fake_desc(q, 2048, 8192, 128, 1, flags=fold)
+    st, info = plan_info(q, q.OP_FWD, pre, 512, q.BF16)
+    assert st == S_OK and q.route_name(info.route) == "gemm_group"
+    assert info.tile_rows in (64, 128) and info.splits >= 1
+    # null info, and a QKV plan without its other two weights
+    assert q.lib().q4gsw_plan(q.OP_FWD, ctypes.byref(pre), None, None, 512, q.BF16, None) == 1   # E_NULL
+    st, _ = plan_info(q, q.OP_QKV, pre, 512, q.F16)
+    assert st == 1
+    dec = fake_desc(q, 8192, 2048, 32, 1, flags=fold)
+    st, info = plan_info(q, q.OP_FWD, dec, 1, q.F16)
+    assert st == S_OK and q.route_name(info.route) == "gemv" and info.tile_rows == 0
+    bwd = fake_desc(q, 8192, 2048, 128, 1, flags=fold)
+    st, info = plan_info(q, q.OP_BWD_INPUT, bwd, 512, q.F32)
+    assert st == S_OK and q.route_name(info.route) == "bwd_split" and info.tile_rows == 128
+    try:
+        for rows, splits in [(64, 3), (128, 16)]:
+            assert q.lib().q4gsw_force_plan(rows, splits) == S_OK
+            st, info = plan_info(q, q.OP_FWD, pre, 512, q.BF16)
+            assert st == S_OK and info.tile_rows == rows and info.splits == splits
+        # a forced count is rounded to one without an empty split: 128 chunks in 5 -> 26 per split, 5
+        assert q.lib().q4gsw_force_plan(0, 5) == S_OK
+        assert plan_info(q, q.OP_FWD, pre, 512, q.BF16)[1].splits == 5
+        for rows, splits in [(96, 0), (0, -1), (0, 65)]:
+            assert q.lib().q4gsw_force_plan(rows, splits) == 2                                  # E_SHAPE
+            assert plan_info(q, q.OP_FWD, pre, 512, q.BF16)[1].splits == 5                      # unchanged
+        # the workspace size follows the forced plan: splits x M x n_pad fp32 partials
+        need = ctypes.c_uint64()
+        assert q.lib().q4gsw_workspace_bytes(q.OP_FWD, ctypes.byref(pre), 512, q.BF16, ctypes.byref(need)) == S_OK
+        assert need.value == 5 * 512 * 2048 * 4
+    finally:
+        q.lib().q4gsw_force_plan(0, 0)
