@@ -14,6 +14,8 @@
 #include "device.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace q4gsw {
 
 namespace {
@@ -81,7 +83,7 @@ __device__ __forceinline__ void load_act8(const void* src, int64_t base, int64_t
 // k-octet l / 2.  A wave takes 64 k-octets per iteration (two loads per lane, both issued
 // before any unpacking) and the W waves of a block take adjacent 512-column slices, so a
 // decode launch is many small blocks that each stream one contiguous row-octet.
-template <int MT, int XT>
+template <int MT, int XT, int SF>
 __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __restrict__ x, int x_vec,
                                                         float* __restrict__ out, int64_t out_ld,
                                                         int64_t split_stride, int64_t row_limit,
@@ -97,6 +99,10 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
     const int64_t o1 = min(o0 + (int64_t)octs_per_split, kocts);
     const uint8_t* rowbase = w.nib + 32 * (R * kocts) + 16 * half;
     const int64_t row0 = 8 * R + 4 * half;
+    // every activation octet of the range is whole and 16-byte aligned: unguarded vector loads;
+    // full: besides, every wave step covers 64 octets of the range (no dead octets to drop)
+    const bool fast = x_vec && o1 * 8 <= w.K;
+    const bool full = fast && (o1 - o0) % 64 == 0;
 
     float acc[MT][4];
 #pragma unroll
@@ -104,42 +110,43 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[m][r] = 0.0f;
 
-    for (int64_t ob = o0 + (int64_t)wave * 64; ob < o1; ob += (int64_t)nw * 64) {
-        u4 q[2];
-        float sc[2][4];
-        u4 xr[2][MT];             // 8 activations (fp16/bf16), or the first 4 (fp32)
-        f4 xr2[2][MT];            // fp32: the last 4
-        bool live[2];
+    auto body = [&](auto fast_c, auto full_c) {
+        constexpr bool kFast = decltype(fast_c)::value;
+        constexpr bool kFull = decltype(full_c)::value;
+        for (int64_t ob = o0 + (int64_t)wave * 64; ob < o1; ob += (int64_t)nw * 64) {
+            u4 q[2];
+            u4 sraw[2];               // fp16 scales: .xy; fp32 scales: all four
+            u4 xr[2][MT];             // 8 activations (fp16/bf16), or the first 4 (fp32)
+            f4 xr2[2][MT];            // fp32: the last 4
+            bool live[2];
+            // Every load of the iteration is issued before any of them is used; an octet past
+            // the range reads the last valid one and is skipped below.
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t O = ob + 32 * j + (lane >> 1);
-            live[j] = O < o1;
-            if (!live[j]) continue;
-            const int64_t k0 = O * 8;
-            q[j] = ldg16_stream(rowbase + 32 * O);
-            const int64_t si = scale_index(w.g_pad, row0, k0 / w.gs);
-            if (w.scale_f16) {
-                const u2 v = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(w.scales) + si);
-                sc[j][0] = f16_bits_to_f32((uint16_t)(v.x & 0xFFFFu));
-                sc[j][1] = f16_bits_to_f32((uint16_t)(v.x >> 16));
-                sc[j][2] = f16_bits_to_f32((uint16_t)(v.y & 0xFFFFu));
-                sc[j][3] = f16_bits_to_f32((uint16_t)(v.y >> 16));
-            } else {
-                const f4 v = *reinterpret_cast<const f4*>(static_cast<const float*>(w.scales) + si);
-                sc[j][0] = v.x; sc[j][1] = v.y; sc[j][2] = v.z; sc[j][3] = v.w;
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int64_t xb = m * w.K + k0;
-                if (x_vec && k0 + 8 <= w.K) {
-                    if constexpr (XT == kF32) {
-                        xr[j][m] = ldg16(static_cast<const float*>(x) + xb);
-                        xr2[j][m] = *reinterpret_cast<const f4*>(static_cast<const float*>(x) + xb + 4);
-                    } else {
-                        xr[j][m] = ldg16(static_cast<const uint16_t*>(x) + xb);
-                    }
+            for (int j = 0; j < 2; ++j) {
+                const int64_t O = ob + 32 * j + (lane >> 1);
+                live[j] = kFull || O < o1;
+                const int64_t Oc = live[j] ? O : o1 - 1;
+                const int64_t k0 = Oc * 8;
+                q[j] = ldg16_stream(rowbase + 32 * Oc);
+                // k0 < 2^31 (K <= 2^30): a 32-bit division, not the branchy 64-bit one
+                const int64_t si = scale_index(w.g_pad, row0, (int64_t)((uint32_t)k0 / (uint32_t)w.gs));
+                if constexpr (SF) {
+                    const u2 v = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(w.scales) + si);
+                    sraw[j] = u4{v.x, v.y, 0u, 0u};
                 } else {
-                    if constexpr (XT == kF32) {
+                    sraw[j] = *reinterpret_cast<const u4*>(static_cast<const float*>(w.scales) + si);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const int64_t xb = m * w.K + k0;
+                    if constexpr (kFast) {
+                        if constexpr (XT == kF32) {
+                            xr[j][m] = ldg16(static_cast<const float*>(x) + xb);
+                            xr2[j][m] = *reinterpret_cast<const f4*>(static_cast<const float*>(x) + xb + 4);
+                        } else {
+                            xr[j][m] = ldg16(static_cast<const uint16_t*>(x) + xb);
+                        }
+                    } else if constexpr (XT == kF32) {
                         f4 a, b;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -158,60 +165,74 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
                     }
                 }
             }
-        }
+            __builtin_amdgcn_sched_barrier(0);    // keep every load above ahead of every use below
+            // a dead octet's terms are dropped by a select
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (!live[j]) continue;
-            const uint32_t wd[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
-            if constexpr (XT == kF16) {
+            for (int j = 0; j < 2; ++j) {
+                float sc[4];
+                if constexpr (SF) {
+                    sc[0] = f16_bits_to_f32((uint16_t)(sraw[j].x & 0xFFFFu));
+                    sc[1] = f16_bits_to_f32((uint16_t)(sraw[j].x >> 16));
+                    sc[2] = f16_bits_to_f32((uint16_t)(sraw[j].y & 0xFFFFu));
+                    sc[3] = f16_bits_to_f32((uint16_t)(sraw[j].y >> 16));
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    h2 c8[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) c8[s] = codes_minus8_f16(wd[r], s);
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        float t = 0.0f;
-                        t = __builtin_amdgcn_fdot2(c8[0], bitcast<h2>(xr[j][m].x), t, false);
-                        t = __builtin_amdgcn_fdot2(c8[1], bitcast<h2>(xr[j][m].y), t, false);
-                        t = __builtin_amdgcn_fdot2(c8[2], bitcast<h2>(xr[j][m].z), t, false);
-                        t = __builtin_amdgcn_fdot2(c8[3], bitcast<h2>(xr[j][m].w), t, false);
-                        acc[m][r] = fmaf(t, sc[j][r], acc[m][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) sc[r] = bitcast<float>(sraw[j][r]);
                 }
-            } else {
-                float xf[MT][8];
+                const uint32_t wd[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+                if constexpr (XT == kF16) {
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    if constexpr (XT == kF32) {
-                        const f4 a = bitcast<f4>(xr[j][m]);
-                        const f4 b = xr2[j][m];
-                        xf[m][0] = a.x; xf[m][1] = a.y; xf[m][2] = a.z; xf[m][3] = a.w;
-                        xf[m][4] = b.x; xf[m][5] = b.y; xf[m][6] = b.z; xf[m][7] = b.w;
-                    } else {
-                        const uint32_t u[4] = {xr[j][m].x, xr[j][m].y, xr[j][m].z, xr[j][m].w};
+                    for (int r = 0; r < 4; ++r) {
+                        h2 c8[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            xf[m][2 * e] = bitcast<float>(u[e] << 16);
-                            xf[m][2 * e + 1] = bitcast<float>(u[e] & 0xFFFF0000u);
+                        for (int s = 0; s < 4; ++s) c8[s] = codes_minus8_f16(wd[r], s);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            float t = 0.0f;
+                            t = __builtin_amdgcn_fdot2(c8[0], bitcast<h2>(xr[j][m].x), t, false);
+                            t = __builtin_amdgcn_fdot2(c8[1], bitcast<h2>(xr[j][m].y), t, false);
+                            t = __builtin_amdgcn_fdot2(c8[2], bitcast<h2>(xr[j][m].z), t, false);
+                            t = __builtin_amdgcn_fdot2(c8[3], bitcast<h2>(xr[j][m].w), t, false);
+                            acc[m][r] = live[j] ? fmaf(t, sc[r], acc[m][r]) : acc[m][r];
                         }
                     }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float c[8];
-                    word_codes_minus8_f32(wd[r], c);
+                } else {
+                    float xf[MT][8];
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        float t = 0.0f;
+                        if constexpr (XT == kF32) {
+                            const f4 a = bitcast<f4>(xr[j][m]);
+                            const f4 b = xr2[j][m];
+                            xf[m][0] = a.x; xf[m][1] = a.y; xf[m][2] = a.z; xf[m][3] = a.w;
+                            xf[m][4] = b.x; xf[m][5] = b.y; xf[m][6] = b.z; xf[m][7] = b.w;
+                        } else {
+                            const uint32_t u[4] = {xr[j][m].x, xr[j][m].y, xr[j][m].z, xr[j][m].w};
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) t = fmaf(xf[m][e], c[e], t);
-                        acc[m][r] = fmaf(t, sc[j][r], acc[m][r]);
+                            for (int e = 0; e < 4; ++e) {
+                                xf[m][2 * e] = bitcast<float>(u[e] << 16);
+                                xf[m][2 * e + 1] = bitcast<float>(u[e] & 0xFFFF0000u);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float c[8];
+                        word_codes_minus8_f32(wd[r], c);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            float t = 0.0f;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) t = fmaf(xf[m][e], c[e], t);
+                            acc[m][r] = live[j] ? fmaf(t, sc[r], acc[m][r]) : acc[m][r];
+                        }
                     }
                 }
             }
         }
-    }
+    };
+    if (full) body(std::true_type{}, std::true_type{});
+    else if (fast) body(std::true_type{}, std::false_type{});
+    else body(std::false_type{}, std::false_type{});
 
     // Sum over the 32 lanes holding the same four rows, then over the waves.
 #pragma unroll
@@ -413,15 +434,15 @@ int gemv_bwd_splits(const WView& w, int64_t M) {
     return (int)splits;
 }
 
-template <int XT>
+template <int XT, int SF>
 static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_t s, const WView& w,
                                     const void* x, int vec, float* out, int64_t ld, int64_t stride,
                                     int64_t limit, int per) {
     switch (M) {
-#define Q4GSW_CASE(MT)                                                                               \
-    case MT:                                                                                         \
-        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT>), grid, block, 0, s, w, x, vec, out, ld, stride, \
-                           limit, per);                                                              \
+#define Q4GSW_CASE(MT)                                                                                   \
+    case MT:                                                                                             \
+        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT, SF>), grid, block, 0, s, w, x, vec, out, ld, stride, \
+                           limit, per);                                                                  \
         break;
         Q4GSW_CASE(1) Q4GSW_CASE(2) Q4GSW_CASE(3) Q4GSW_CASE(4)
         Q4GSW_CASE(5) Q4GSW_CASE(6) Q4GSW_CASE(7) Q4GSW_CASE(8)
@@ -443,10 +464,17 @@ hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M
     const int64_t ld = splits == 1 ? w.N : w.n_pad;
     const int64_t stride = splits == 1 ? 0 : M * w.n_pad;
     const int64_t limit = splits == 1 ? w.N : w.n_pad;
+    if (w.scale_f16) {
+        switch (x_dtype) {
+            case kF32: return gemv_fwd_dispatch<kF32, 1>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+            case kF16: return gemv_fwd_dispatch<kF16, 1>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+            default: return gemv_fwd_dispatch<kBF16, 1>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        }
+    }
     switch (x_dtype) {
-        case kF32: return gemv_fwd_dispatch<kF32>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
-        case kF16: return gemv_fwd_dispatch<kF16>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
-        default: return gemv_fwd_dispatch<kBF16>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        case kF32: return gemv_fwd_dispatch<kF32, 0>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        case kF16: return gemv_fwd_dispatch<kF16, 0>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        default: return gemv_fwd_dispatch<kBF16, 0>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
     }
 }
 
