@@ -105,7 +105,10 @@ __device__ __forceinline__ void wait_chunks_barrier(int64_t n) {
     }
 }
 
-template <int XT, int MODE, int SPC, int SF, int MI, int KD>
+// RG: the activation may be ragged (K % 64 != 0) or not 16-byte aligned, so chunks can take the
+// synchronous fallback; the aligned instance carries no fallback code (and none of its live
+// values across the chunk loop).
+template <int XT, int MODE, int SPC, int SF, int MI, int KD, bool RG>
 __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const void* __restrict__ x, int64_t M,
                                                           int64_t K, int64_t k_pad, int64_t gs, int x_fast,
                                                           int chunks_per_split, int splits, int mtiles,
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: its address math stays scalar
     const int j = lane & 31;          // MFMA row / column inside a 32x32 tile
     const int h = lane >> 5;          // MFMA k-group: k-octet 2t + h of step t
 
@@ -250,11 +253,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     };
     auto issue_a16 = [&](int64_t c, int st) {
         const int64_t kc = c * kCK;
-        if (x_fast && kc + kCK <= K) {
+        if (!RG || (x_fast && kc + kCK <= K)) {
 #pragma unroll
             for (int q = 0; q < kADma; ++q)
                 dma16(xa[q] + kc, sm_l + st * kStageBytes + kAOff + (kRowsPerWave * wave + 8 * q) * kRowBytes);
-        } else {
+        } else if constexpr (RG) {
             fill_a16_slow(kc, st);
         }
     };
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     f4 areg[kAUnits];
     auto load_a32 = [&](int64_t c) {
         const int64_t kc = c * kCK;
-        const bool fast = x_fast && kc + kCK <= K;
+        const bool fast = !RG || (x_fast && kc + kCK <= K);
 #pragma unroll
         for (int i = 0; i < kAUnits; ++i) {
             const int unit = tid + 64 * kWaves * i;
@@ -378,12 +381,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
             b[e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
         }
     };
-    // One MFMA (two for fp32 x) on tile mi; KIND as below.
+    // One MFMA (two for fp32 x) on tile mi; KIND as below.  An opening step that follows a
+    // group (KIND 2) first scales that group's partial sums of tile mi into acc: the rescale of
+    // tile mi + 1 then issues while the MFMA of tile mi runs, instead of every wave stalling on
+    // its last MFMAs and rescaling all tiles while the matrix unit idles.
     auto mma_tile = [&](const u4& a, const u4& alo, const u4& b, int mi, auto kind) {
         constexpr int K_ = decltype(kind)::value;
         if constexpr (MODE == kModeFold) {
             acc[mi] = mfma32_f16(a, b, acc[mi]);
         } else {
+            if constexpr (K_ == 2) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[mi][r] = fmaf(part[mi][r], gopen, acc[mi][r]);
+                __builtin_amdgcn_sched_barrier(0);   // old partials dead before the MFMA defines new ones
+            }
             const f32x16 c0 = (K_ == 0) ? part[mi] : zero16;
             if constexpr (MODE == kModeSplit) part[mi] = mfma32_bf16(alo, b, mfma32_bf16(a, b, c0));
             else if constexpr (XT == kF16) part[mi] = mfma32_f16(a, b, c0);
@@ -431,7 +442,6 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
                 if (e % kPer == kPer - 1) __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (KIND != 0) gopen = group_scale(S, SPC == 2 ? (t >> 1) : 0);
-            if constexpr (kGroup && SPC == 2 && (t & 1)) flush_open_group();   // gs == 32
         };
         one(std::integral_constant<int, 0>{}, k0);
         one(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
@@ -486,24 +496,34 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         }
         st = st_next;
     };
-    typedef std::integral_constant<int, 0> Acc;      // accumulate into the open group
-    typedef std::integral_constant<int, 1> Open;     // open the split's first group
+    typedef std::integral_constant<int, 0> Acc;        // accumulate into the open group
+    typedef std::integral_constant<int, 1> Open;       // open the split's first group
+    typedef std::integral_constant<int, 2> Reopen;     // scale the closed group into acc, open the next
     if constexpr (!kGroup) {
         for (int64_t c = c_begin; c < c_end; ++c) chunk(c, Acc{}, Acc{});
     } else if constexpr (SPC == 1) {
         // gs % 64 == 0: a group is cpg whole chunks (the split may start or end inside one);
-        // its partial sums are scaled into acc after its last chunk
-        const int64_t cpg = gs / kCK;
-        int64_t c = c_begin;
-        while (c < c_end) {
-            const int64_t gend = min(c_end, (c / cpg + 1) * cpg);
-            chunk(c, Open{}, Acc{});
-            for (++c; c < gend; ++c) chunk(c, Acc{}, Acc{});
+        // its partial sums are scaled into acc by the first step of the next group, the last
+        // group's after the loop
+        if (c_begin < c_end) {
+            const int64_t cpg = gs / kCK;
+            int64_t left = cpg - c_begin % cpg;       // chunks of the open group from c_begin on
+            chunk(c_begin, Open{}, Acc{});
+            for (int64_t c = c_begin + 1; c < c_end; ++c) {
+                if (--left == 0) {
+                    left = cpg;
+                    chunk(c, Reopen{}, Acc{});
+                } else {
+                    chunk(c, Acc{}, Acc{});
+                }
+            }
             flush_open_group();
         }
-    } else {
-        // gs == 32: every 32-column half of a chunk is one group, scaled in inside the chunk
-        for (int64_t c = c_begin; c < c_end; ++c) chunk(c, Open{}, Open{});
+    } else if (c_begin < c_end) {
+        // gs == 32: every 32-column half of a chunk is one group
+        chunk(c_begin, Open{}, Reopen{});
+        for (int64_t c = c_begin + 1; c < c_end; ++c) chunk(c, Reopen{}, Reopen{});
+        flush_open_group();
     }
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
@@ -565,42 +585,47 @@ int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width,
     return best;
 }
 
-// Kernel instance for (activation type, mode, scale slots, scale type, row tiles), handed to f.
-template <int XT, int MODE, int SF, int MI, typename F>
+// Kernel instance for (activation type, mode, scale slots, scale type, row tiles, fallback), handed to f.
+template <int XT, int MODE, int SF, int MI, bool RG, typename F>
 static void with_spc(int spc, F&& f) {
     constexpr int KD = XT == kF32 ? 2 : kDepth16;
-    if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD>);
-    else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD>);
-    else if constexpr (MODE == kModeFold) f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD>);
+    if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG>);
+    else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD, RG>);
+    else if constexpr (MODE == kModeFold) f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD, RG>);
 }
 template <int XT, int MODE, int SF, typename F>
-static void with_mi(int mi, int spc, F&& f) {
-    if (mi == 4) with_spc<XT, MODE, SF, 4>(spc, f);
-    else with_spc<XT, MODE, SF, 2>(spc, f);
+static void with_mi(int mi, int spc, bool rg, F&& f) {
+    if (rg) {
+        if (mi == 4) with_spc<XT, MODE, SF, 4, true>(spc, f);
+        else with_spc<XT, MODE, SF, 2, true>(spc, f);
+    } else {
+        if (mi == 4) with_spc<XT, MODE, SF, 4, false>(spc, f);
+        else with_spc<XT, MODE, SF, 2, false>(spc, f);
+    }
 }
 template <typename F>
-static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, F&& f) {
+static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, bool rg, F&& f) {
     if (mode == kModeFold) {
-        with_mi<kF16, kModeFold, 1>(mi, spc, f);
+        with_mi<kF16, kModeFold, 1>(mi, spc, rg, f);
     } else if (mode == kModeSplit) {
-        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, f);
-        else with_mi<kF32, kModeSplit, 0>(mi, spc, f);
+        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, rg, f);
+        else with_mi<kF32, kModeSplit, 0>(mi, spc, rg, f);
     } else if (x_dtype == kF16) {
-        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, f);
-        else with_mi<kF16, kModeGroup, 0>(mi, spc, f);
+        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, rg, f);
+        else with_mi<kF16, kModeGroup, 0>(mi, spc, rg, f);
     } else {
-        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, f);
-        else with_mi<kBF16, kModeGroup, 0>(mi, spc, f);
+        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, rg, f);
+        else with_mi<kBF16, kModeGroup, 0>(mi, spc, rg, f);
     }
 }
 
 // Blocks of one kernel instance resident per CU (registers and LDS decide), cached per instance.
 static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int mi) {
     static int cache[3][3][2][5][5];
-    int& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi];
+    int& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi];   // the aligned instance stands for both
     if (slot == 0) {
         int n = 1;
-        dispatch_fwd(mode, x_dtype, scale_f16, spc, mi, [&](auto kern) {
+        dispatch_fwd(mode, x_dtype, scale_f16, spc, mi, false, [&](auto kern) {
             int b = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, 64 * kWaves, 0) == hipSuccess && b > 0) n = b;
         });
@@ -699,7 +724,8 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     const int64_t st = plan.splits == 1 ? 0 : M * npad_total;
     const int64_t K = w0.K, kp = w0.k_pad, gs = w0.gs;
     const int sp = plan.splits, mt = (int)mtiles;
-    dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, [&](auto kern) {
+    const bool rg = !x_fast || (K % kCK) != 0;
+    dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, rg, [&](auto kern) {
         hipLaunchKernelGGL(kern, g, dim3(64 * kWaves), 0, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
     });
     hipError_t e = hipGetLastError();
