@@ -150,9 +150,9 @@ def traffic_for(op_name, src_hash):
 
 
 # kernels that make up one launch of each op (a GEMM and, with K splits, its reduction)
-OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_splits"),
-              "qkv_m128": ("gemm_fwd", "reduce_splits"), "qkv_m508": ("gemm_fwd", "reduce_splits"),
-              "qkv_m512": ("gemm_fwd", "reduce_splits"), "bwd": ("gemm_bwd", "reduce_splits")}
+OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_"),
+              "qkv_m128": ("gemm_fwd", "reduce_"), "qkv_m508": ("gemm_fwd", "reduce_"),
+              "qkv_m512": ("gemm_fwd", "reduce_"), "bwd": ("gemm_bwd", "reduce_")}
 
 
 def _counter_means(d, counter):

@@ -37,6 +37,26 @@ constexpr int kRowBytes = 128;      // one 16-bit A row of a chunk in LDS
 constexpr int kPlaneBytes = kBM * kRowBytes;
 constexpr int kCodeBytes = 2048;    // one wave's codes per chunk: 64 n x 64 k x 4 bits
 
+// A wave's 128 x 64 split partials (4 x 2 tiles of 32 x 32, times f) in the fragment layout of
+// a plane with ntn 32-column tiles: four 16-byte stores per lane and tile; tiles wholly past M
+// are skipped.
+__device__ __forceinline__ void store_frag_partials(float* plane, int64_t ntn, int64_t M, int64_t m0, int64_t kw0,
+                                                    int lane, const f32x16 (&acc)[4][2], float f) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int64_t tm = m0 / 32 + mi;
+        if (32 * tm >= M) break;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float* tp = plane + (tm * ntn + kw0 / 32 + u) * 1024 + 4 * lane;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<f4*>(tp + 256 * r4) = f4{f * acc[mi][u][4 * r4], f * acc[mi][u][4 * r4 + 1],
+                                                           f * acc[mi][u][4 * r4 + 2], f * acc[mi][u][4 * r4 + 3]};
+        }
+    }
+}
+
 // NV = scale groups per wave (1: gs % 64 == 0, 2: gs == 32).
 template <int NV>
 __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const void* __restrict__ d_out, int64_t M,
@@ -234,7 +254,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
     if (!wave_active) return;
-    float* dst = out + (int64_t)z * split_stride;
+    if (split_stride) {
+        store_frag_partials(out + (int64_t)z * split_stride, out_ld / 32, M, m0, kw0, lane, acc, 1.0f);
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -244,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + 32 * mi + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) dst[m * out_ld + k] = acc[mi][u][r];
+                if (m < M) out[m * out_ld + k] = acc[mi][u][r];
             }
         }
     }
@@ -585,7 +608,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
     }
 
     if (!wave_active) return;
-    float* dst = out + (int64_t)z * split_stride;
+    if (split_stride) {
+        // the fragment layout keeps the lane order; the reduction applies the column permutation
+        store_frag_partials(out + (int64_t)z * split_stride, out_ld / 32, M, m0, kw0, lane, acc, 16.0f);
+        return;
+    }
+    float* dst = out;
     // column of this lane in each 32-wide tile: k offset of nibble (j & 7) within octet j >> 3
     const int kcol = (j & ~7) | (((j & 3) << 1) | ((j >> 2) & 1));
 #pragma unroll
@@ -645,7 +673,7 @@ BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M) {
     const int64_t blocks = ((w.k_pad + kBK - 1) / kBK) * ((M + kBM - 1) / kBM);
     const int64_t n_chunks = (w.N + kCN - 1) / kCN;
     p.splits = pick_gemm_splits(blocks, n_chunks, M, w.k_pad);
-    p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * M * w.k_pad * 4 : 0;
+    p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * frag_plane_floats(M, w.k_pad) * 4 : 0;
     p.v1 = 0;
     return p;
 }
@@ -663,7 +691,7 @@ hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64
     const int g_fast = ((reinterpret_cast<uintptr_t>(d_out) & 15u) == 0) && ((w.N * esize) % 16 == 0);
     float* out = plan.splits == 1 ? d_x : ws;
     const int64_t ld = plan.splits == 1 ? w.K : w.k_pad;
-    const int64_t stride = plan.splits == 1 ? 0 : M * w.k_pad;
+    const int64_t stride = plan.splits == 1 ? 0 : frag_plane_floats(M, w.k_pad);
     const int64_t limit = plan.splits == 1 ? w.K : w.k_pad;
     const int sp = plan.splits, mt = (int)mtiles;
     if (plan.mode == kModeFold) {
@@ -689,7 +717,9 @@ hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    return launch_reduce_splits(ws, plan.splits, M, w.K, w.k_pad, d_x, w.K, s);
+    const float* ys[1] = {d_x};
+    const int64_t yld[1] = {w.K}, off[1] = {0}, cols[1] = {w.K};
+    return launch_reduce_frags(ws, plan.splits, M, w.k_pad, ys, yld, off, cols, 1, plan.mode == kModeFold ? 0 : 1, s);
 }
 
 }  // namespace q4gsw

@@ -56,10 +56,12 @@ constexpr int kCodeBytes = 1024;    // one wave's codes for one chunk: 32 rows x
 struct FwdSegArgs {
     const uint8_t* nib[3];
     const void* scales[3];
-    float* out[3];                // final output (splits == 1) or workspace base of the segment
+    float* out[3];                // final output (splits == 1) or the workspace
     int64_t N[3];
     int64_t n_pad[3];
-    int64_t out_ld[3];            // row pitch of out
+    int64_t out_ld[3];            // row pitch of out (splits == 1)
+    int64_t col0[3];              // splits > 1: first workspace column of the segment
+    int64_t ntn;                  // splits > 1: 32-column tiles across the workspace
     int64_t tile_start[4];        // first N tile of each segment (prefix sums), tile_start[nseg] = total
     int64_t g_pad;                // scale groups stored (shared: the segments share K and group size)
     int nseg;
@@ -527,11 +529,27 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     }
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
+    if (!wave_active) return;
+    if (split_stride) {
+        // split partials in the fragment layout: four 16-byte stores per lane and tile
+        float* plane = seg.out[sg] + (int64_t)z * split_stride;
+        const int64_t tn = (seg.col0[sg] + n0) / 32;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int64_t tm = m0 / 32 + mi;
+            if (32 * tm >= M) break;
+            float* tp = plane + (tm * seg.ntn + tn) * 1024 + 4 * lane;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *reinterpret_cast<f4*>(tp + 256 * r4) =
+                    f4{acc[mi][4 * r4], acc[mi][4 * r4 + 1], acc[mi][4 * r4 + 2], acc[mi][4 * r4 + 3]};
+        }
+        return;
+    }
     const int64_t brow = n0 + j;
-    float* out = seg.out[sg] + (int64_t)z * split_stride;
+    float* out = seg.out[sg];
     const int64_t ld = seg.out_ld[sg];
-    const int64_t ncols = split_stride ? seg.n_pad[sg] : seg.N[sg];
-    if (!wave_active || brow >= ncols) return;
+    if (brow >= seg.N[sg]) return;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -676,12 +694,12 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
             p.splits = s;
         }
     }
-    p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * M * npad_total * 4 : 0;
+    p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * frag_plane_floats(M, npad_total) * 4 : 0;
     return p;
 }
 
-// One launch over every segment.  With K splits the partials go to ws laid out as
-// [splits][M][sum of n_pad], segment i starting at column offset sum_{j<i} n_pad_j.
+// One launch over every segment.  With K splits the partials go to ws as splits planes in the
+// fragment layout over the columns of all segments (segment i from column sum_{j<i} n_pad_j on).
 hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
                            const FwdPlan& plan, float* ws, hipStream_t s) {
     const WView& w0 = segs[0].w;
@@ -701,13 +719,14 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
             a.out[i] = segs[i].out;
             a.out_ld[i] = segs[i].w.N;
         } else {
-            a.out[i] = ws + col;
-            a.out_ld[i] = npad_total;
+            a.out[i] = ws;
+            a.col0[i] = col;
         }
         col += segs[i].w.n_pad;
     }
     a.tile_start[nseg] = tiles;
     a.g_pad = w0.g_pad;
+    a.ntn = npad_total / 32;
     const int mode = plan.mode;
     const int spc = fwd_spc(w0.gs);
     if (spc == 4 && mode != kModeFold) return hipErrorInvalidValue;
@@ -721,7 +740,7 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     const int esize = x_dtype == kF32 ? 4 : 2;
     const int x_fast = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) && ((w0.K * esize) % 16 == 0);
     const dim3 g((unsigned)blocks);
-    const int64_t st = plan.splits == 1 ? 0 : M * npad_total;
+    const int64_t st = plan.splits == 1 ? 0 : frag_plane_floats(M, npad_total);
     const int64_t K = w0.K, kp = w0.k_pad, gs = w0.gs;
     const int sp = plan.splits, mt = (int)mtiles;
     const bool rg = !x_fast || (K % kCK) != 0;
@@ -740,7 +759,7 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
         cols[i] = segs[i].w.N;
         o += segs[i].w.n_pad;
     }
-    return launch_reduce_segments(ws, plan.splits, M, npad_total, ys, yld, off, cols, nseg, s);
+    return launch_reduce_frags(ws, plan.splits, M, npad_total, ys, yld, off, cols, nseg, 0, s);
 }
 
 }  // namespace q4gsw

@@ -400,6 +400,72 @@ hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_
     return hipGetLastError();
 }
 
+// Split-partial reduction over the 32x32 MFMA fragment layout (see internal.h): one block per
+// 32x32 tile, thread t sums the 4 rows q of fragment slot t (register group r4 = t / 64, lane
+// L = t % 64: rows 8 r4 + 4 (L / 32) + q, column j = L % 32, or its octet permutation when perm
+// is set) with one 16-byte load per split, in split order, so the result does not depend on the
+// launch.  The tile is transposed through LDS so that each thread stores 4 consecutive columns
+// of one row.
+__global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restrict__ ws, int splits, int64_t M,
+                                                           int64_t ntn, int64_t plane, ReduceSegs seg, int perm,
+                                                           int vec_ok) {
+    __shared__ float tile_s[32][33];
+    const int64_t tile = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t tm = tile / ntn, tn = tile - tm * ntn;
+    const float* src = ws + tile * 1024 + 4 * t;
+    f4 acc = *reinterpret_cast<const f4*>(src);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f4*>(src + s * plane);
+    {
+        const int L = t & 63, j = L & 31;
+        const int jc = perm ? ((j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1)) : j;
+        const int r0 = 8 * (t >> 6) + 4 * (L >> 5);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tile_s[r0 + q][jc] = acc[q];
+    }
+    __syncthreads();
+    const int row = t >> 3, c4 = 4 * (t & 7);
+    const int64_t m = 32 * tm + row;
+    if (m >= M) return;
+    const int64_t col = 32 * tn + c4;
+    int sg = 0;
+    while (sg + 1 < seg.nseg && col >= seg.off[sg + 1]) ++sg;
+    const int64_t cs = col - seg.off[sg];
+    if (cs >= seg.cols[sg]) return;
+    float* dst = seg.y[sg] + m * seg.y_ld[sg] + cs;
+    const f4 v = {tile_s[row][c4], tile_s[row][c4 + 1], tile_s[row][c4 + 2], tile_s[row][c4 + 3]};
+    if (vec_ok && cs + 4 <= seg.cols[sg]) {
+        *reinterpret_cast<f4*>(dst) = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (cs + e < seg.cols[sg]) dst[e] = v[e];
+    }
+}
+
+hipError_t launch_reduce_frags(const float* ws, int splits, int64_t M, int64_t width, const float* const* y,
+                               const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg, int perm,
+                               hipStream_t s) {
+    if (width % 32 != 0 || (reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return hipErrorInvalidValue;
+    ReduceSegs seg{};
+    seg.nseg = nseg;
+    int vec_ok = 1;
+    for (int i = 0; i < nseg; ++i) {
+        seg.y[i] = const_cast<float*>(y[i]);
+        seg.y_ld[i] = y_ld[i];
+        seg.off[i] = off[i];
+        seg.cols[i] = cols[i];
+        if (off[i] % 32 != 0) return hipErrorInvalidValue;
+        vec_ok = vec_ok && (y_ld[i] % 4 == 0) && ((reinterpret_cast<uintptr_t>(y[i]) & 15u) == 0);
+    }
+    const int64_t mt = (M + 31) / 32, ntn = width / 32;
+    const int64_t tiles = mt * ntn;
+    if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(reduce_frags_kernel, dim3((unsigned)tiles), dim3(256), 0, s, ws, splits, M, ntn, mt * 32 * width,
+                       seg, perm, vec_ok);
+    return hipGetLastError();
+}
+
 hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t cols, int64_t ld, float* y,
                                 int64_t y_ld, hipStream_t s) {
     const float* yy[1] = {y};

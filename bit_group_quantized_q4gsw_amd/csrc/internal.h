@@ -37,6 +37,17 @@ hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_
                                   const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg,
                                   hipStream_t s);
 
+// Split partials of the 32x32 MFMA GEMMs, fragment layout: plane s (of (M rounded up to 32) x
+// width floats, width a multiple of 32) holds the 32x32 output tiles (tm, tn) in order
+// tm * (width / 32) + tn, 4 KB each; inside a tile, lane L's accumulators r = 4 r4 + q (rows
+// 8 r4 + 4 (L / 32) + q, tile column L % 32, octet-permuted when perm is set) sit at float
+// 4 (64 r4 + L) + q, so a wave stores a tile with four 16-byte-per-lane writes.  The reduction
+// writes y[i][m][c] = sum_s for the tile columns of segment i (off[i] multiples of 32).
+inline int64_t frag_plane_floats(int64_t M, int64_t width) { return (M + 31) / 32 * 32 * width; }
+hipError_t launch_reduce_frags(const float* ws, int splits, int64_t M, int64_t width, const float* const* y,
+                               const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg, int perm,
+                               hipStream_t s);
+
 // generic.hip: any shape, any group size.
 hipError_t launch_generic_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* y,
                               hipStream_t s);
