@@ -273,8 +273,8 @@ def plan(op: int, w: PackedWeight, M: int, dtype: torch.dtype, wk: PackedWeight 
 
 @contextlib.contextmanager
 def forced_plan(tile_rows: int = 0, splits: int = 0):
-    """Force the forward / QKV MFMA block rows (64 or 128) and K splits inside the block; 0
-    leaves a choice per shape."""
+    """Force the forward / QKV MFMA block rows (64 or 128) and the contraction splits (the split
+    count also governs the 32x32 input-gradient routes); 0 leaves a choice per shape."""
     _check(lib().q4gsw_force_plan(tile_rows, splits), "q4gsw_force_plan")
     try:
         yield

@@ -658,6 +658,7 @@ void set_forced_fwd_plan(int rows, int splits) {
     g_forced_tile_rows.store(rows, std::memory_order_relaxed);
     g_forced_splits.store(splits, std::memory_order_relaxed);
 }
+int forced_gemm_splits() { return g_forced_splits.load(std::memory_order_relaxed); }
 
 FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M) {
     FwdPlan p{};
@@ -683,7 +684,9 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         const int64_t bm = 32 * mi;
         const int64_t blocks = tiles * ((M + bm - 1) / bm);
         const int64_t slots = 256 * (int64_t)fwd_blocks_per_cu(p.mode, x_dtype, w0.scale_f16, spc, mi);
-        // a 64-row block does half the MFMA work of a 128-row one per chunk but unpacks as many codes
+        // a 64-row block does half the MFMA work of a 128-row one per chunk but unpacks as many
+        // codes.  Tuned on input sets rotated past the 256 MB Infinity Cache (sweeps on cache-warm
+        // inputs favour other split counts).
         const double chunk_us = mi == 4 ? 2.0 : 1.3;
         double cost = 0;
         const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost,

@@ -70,6 +70,8 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
 // Forward plan choices forced for every later plan: block rows (64 or 128) and K splits (> 0);
 // 0 leaves each to the shape.
 void set_forced_fwd_plan(int rows, int splits);
+// The forced split count (0: none); the 32x32 input-gradient plan takes it too.
+int forced_gemm_splits();
 // Contraction splits for an MFMA GEMM of `blocks` output blocks, `slots` of which run at once,
 // n_chunks 64-wide contraction chunks of ~chunk_us each and an M x width fp32 output; the
 // modelled time (microseconds) goes to *cost when cost is not null; force_splits > 0 pins the

@@ -208,7 +208,8 @@ void q4gsw_force_route(int32_t route);
 
 /* Force the forward / QKV MFMA plan for every later call: tile_rows 64 or 128 and
  * splits 1..64 contraction splits (clamped to the 64-column chunks and rounded to a
- * count with no empty split); 0 leaves each to the shape.  Other values return
+ * count with no empty split; the split count also governs the 32x32 input-gradient
+ * routes bwd_fold and bwd_split); 0 leaves each to the shape.  Other values return
  * Q4GSW_E_SHAPE and change nothing.  Process-wide and not synchronized, like
  * q4gsw_force_route: set it before sizing the workspace of the calls it should govern
  * (for tests and benchmarks that compare plans). */

@@ -270,3 +270,30 @@ def test_forced_splits(kind, M, N, K, gs, act, sdt, rows, splits):
     for o, w in zip(outs, ws_list):
         ref, norm = oracle_fwd(case.x, w)
         assert_within(o, ref, norm, tol, f"{kind} splits={splits} rows={rows}")
+
+
+# ---- forced split counts of the 32x32 input-gradient routes -------------------------------------
+
+BWD_SPLIT_CASES = [
+    # M, N, K, gs, d_out dtype, scale dtype, splits; route bwd_split unless noted
+    (130, 1024, 512, 128, "f32", "f16", 3),       # ragged M, two scale groups per block
+    (64, 2048, 256, 256, "bf16", "f16", 5),       # one scale group per block
+    (200, 1536, 384, 128, "f32", "f32", 5),       # fp32 scales, K tail inside a block
+    (96, 1024, 512, 64, "f16", "f16", 4),         # bwd_fold
+]
+
+
+@pytest.mark.parametrize("M,N,K,gs,act,sdt,splits", BWD_SPLIT_CASES)
+def test_forced_bwd_splits(M, N, K, gs, act, sdt, splits):
+    q = lib()
+    case = make_linear(M, K, N, gs, act, sdt, seed=M + N + K + splits, fwd=False, bwd=True,
+                       s_lo=0.005 if sdt == "f32" else 0.002)
+    pw = pack(q, case.w)
+    g = dev(case.d_out)
+    with q.forced_plan(splits=splits):
+        info = q.plan(q.OP_BWD_INPUT, pw, M, case.d_out.dtype)
+        dx = q.linear_bwd_input(pw, g)
+        torch.cuda.synchronize()
+    assert info["splits"] == splits, f"forced split count not taken: {info}"
+    ref, norm = oracle_bwd(case.d_out, case.w)
+    assert_within(dx, ref, norm, TOL[case.d_out.dtype], f"bwd splits={splits} route={info['route']}")
