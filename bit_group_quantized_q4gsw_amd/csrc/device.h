@@ -140,8 +140,26 @@ __device__ __forceinline__ void wait_loads_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ float wave_xor_sum(float v, int mask) {
-    return v + __shfl_xor(v, mask, 64);
+// Sum of v over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one position of every 16-lane row), in
+// every lane: gfx950's row swap and half swap, register to register.  Swapping a value with
+// itself leaves row r's and row r ^ 1's copies in the two results (likewise the two halves).
+__device__ __forceinline__ float wave_sum_rows(float v) {
+    const uint32_t a = bitcast<uint32_t>(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    const float s = bitcast<float>(r[0]) + bitcast<float>(r[1]);
+    const uint32_t b = bitcast<uint32_t>(s);
+    const auto h = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return bitcast<float>(h[0]) + bitcast<float>(h[1]);
+}
+
+// Sum of v over the 32 lanes with the parity of this lane, in every lane: DPP inside each
+// 16-lane row (quad_perm [2,3,0,1] pairs lane i with i ^ 2; rotations by 4 and 8 then cover
+// the row's positions of that parity), then across the rows.
+__device__ __forceinline__ float wave_sum_same_parity(float v) {
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x4E, 0xF, 0xF, false));
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x124, 0xF, 0xF, false));
+    v += bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(v), 0x128, 0xF, 0xF, false));
+    return wave_sum_rows(v);
 }
 
 }  // namespace q4gsw

@@ -8,8 +8,9 @@
 // 16-byte loads; a wave's 64 lanes cover 4 row-octets x 16 k-octets, i.e. four
 // contiguous 512-byte runs.  Codes are unpacked in registers to the exact values
 // c - 8, products are fp32 (or fp16 pairs with fp32 dot2 accumulation for fp16
-// activations), and partial sums are reduced across lanes with cross-lane
-// shuffles and across waves in LDS.  A code 8 therefore contributes exactly 0.
+// activations), and partial sums are reduced across lanes with register-to-register
+// cross-lane operations (DPP and the gfx950 row and half swaps) and across waves in LDS.
+// A code 8 therefore contributes exactly 0.
 // Requires group_size % 8 == 0 so a k-octet lies inside one scale group.
 #include "device.h"
 #include "internal.h"
@@ -239,13 +240,7 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float v = acc[m][r];
-            v = wave_xor_sum(v, 2);
-            v = wave_xor_sum(v, 4);
-            v = wave_xor_sum(v, 8);
-            v = wave_xor_sum(v, 16);
-            v = wave_xor_sum(v, 32);
-            acc[m][r] = v;
+            acc[m][r] = wave_sum_same_parity(acc[m][r]);
         }
     if (lane < 2) {
 #pragma unroll
@@ -320,10 +315,7 @@ __global__ __launch_bounds__(256) void gemv_bwd_kernel(WView w, const void* __re
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float v = acc[m][j];
-            v = wave_xor_sum(v, 16);
-            v = wave_xor_sum(v, 32);
-            acc[m][j] = v;
+            acc[m][j] = wave_sum_rows(acc[m][j]);
         }
     }
     if (ro == 0) {
