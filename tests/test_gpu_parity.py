@@ -280,6 +280,7 @@ BWD_SPLIT_CASES = [
     (64, 2048, 256, 256, "bf16", "f16", 5),       # one scale group per block
     (200, 1536, 384, 128, "f32", "f32", 5),       # fp32 scales, K tail inside a block
     (96, 1024, 512, 64, "f16", "f16", 4),         # bwd_fold
+    (40, 1024, 96, 32, "f16", "f16", 3),          # bwd_fold, K = 96 inside one padded 128-column tile
 ]
 
 
