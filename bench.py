@@ -11,7 +11,8 @@ working set exceeds the 256 MB Infinity Cache and the weight stream comes from H
 
 Prints one JSON line: whole-step TFLOP/s (the step captured as a HIP graph per rotated
 input set and replayed), per-op TFLOP/s and weight GB/s with their roofline fractions
-(eager launches between HIP events on the launch stream), the roofline object of the
+(each op alone captured as a HIP graph of at least 32 launches over the rotated sets and
+replayed between HIP events on the launch stream; the eager per-op time is kept beside it), the roofline object of the
 dominant op and the fp64 CPU oracle timed on a bounded sample of the same step.
 """
 import argparse
@@ -114,14 +115,18 @@ def build_ops(q, names, rotate):
             specs.append(("bwd", "bwd", make_workload("bwd")))
         else:
             raise SystemExit(f"unknown op {n}")
+    def set_bytes(case):
+        act = case.x if case.x is not None else case.d_out
+        return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
+
     if rotate <= 0:
-        one = 0
-        for _, kind, case in specs:
-            act = case.x if case.x is not None else case.d_out
-            one += sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights)
-            one += act.numel() * act.element_size()
-        rotate = max(2, int(MALL_BYTES * 1.5 // one) + 1)
-    return [Op(n, k, c, q, rotate) for n, k, c in specs], rotate
+        # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
+        # copies of its own to exceed it alone, for its per-op timing
+        rotate = max(2, int(MALL_BYTES * 1.5 // sum(set_bytes(c) for _, _, c in specs)) + 1)
+        per_op = [max(rotate, int(MALL_BYTES * 1.5 // set_bytes(c)) + 1) for _, _, c in specs]
+    else:
+        per_op = [rotate] * len(specs)
+    return [Op(n, k, c, q, sets) for (n, k, c), sets in zip(specs, per_op)], rotate
 
 
 def source_hash():
@@ -309,16 +314,41 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
 
+    # per-op timing without host launch latency: each op alone, whole passes over its own rotated
+    # input sets (which alone exceed the MALL; at least 32 launches, so the graph launch itself
+    # is amortised), captured as a HIP graph and replayed between HIP events
+    graph_ms = {}
+    for op in ops:
+        nset = len(op.sets)
+        launches = nset * ((32 + nset - 1) // nset)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(launches):
+                op.run(q, s)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g.replay()
+        reps = max(3, (args.steps + launches - 1) // launches)
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        graph_ms[op.name] = start.elapsed_time(stop) / (reps * launches)
+        del g
+
     per_op = {}
     total_flops = 0.0
     for op in ops:
-        ms = sum(a.elapsed_time(b) for a, b in ev[op.name]) / args.steps
+        eager_ms = sum(a.elapsed_time(b) for a, b in ev[op.name]) / args.steps
+        ms = graph_ms[op.name]
         s = ms / 1e3
         tflops = op.flops / s / 1e12
         gbs = op.bytes / s / 1e9
         wgbs = op.weight_bytes / s / 1e9
         frac = gbs / HBM_PEAK_GBS if op.bound == "hbm" else tflops / MFMA_PEAK_TFLOPS
-        per_op[op.name] = {"ms": round(ms, 5), "tflops": round(tflops, 2), "weight_gbs": round(wgbs, 1),
+        per_op[op.name] = {"ms": round(ms, 5), "eager_ms": round(eager_ms, 5), "tflops": round(tflops, 2),
+                           "weight_gbs": round(wgbs, 1),
                            "alg_gbs": round(gbs, 1), "bound": op.bound, "roofline_frac": round(frac, 4),
                            "route": op.route, "M": op.M}
         total_flops += op.flops
@@ -352,7 +382,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama-3.2-1b q4gsw step: " + ", ".join(
             f"{o.name} M{o.M} route={o.route}" for o in ops), "ops": names, "rotated_sets": rotate,
-            "timing": "step: HIP-graph replay of the whole step; per_op: eager launches between HIP events",
+            "op_sets": {o.name: len(o.sets) for o in ops},
+            "timing": "step: HIP-graph replay of the whole step; per_op ms: HIP-graph replay of the op alone, "
+                      ">= 32 launches over the rotated sets (eager_ms: eager launches between HIP events)",
             "eager_ms_per_step": round(eager_ms_step, 5), "wall_s": round(wall, 3), "src_hash": src},
         "per_op": per_op,
         "roofline": roof,
