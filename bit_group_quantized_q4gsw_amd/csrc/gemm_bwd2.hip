@@ -38,8 +38,8 @@ constexpr int kPlaneBytes = kBM * kRowBytes;
 constexpr int kCodeBytes = 2048;    // one wave's codes per chunk: 64 n x 64 k x 4 bits
 
 // A wave's 128 x 64 split partials (4 x 2 tiles of 32 x 32, times f) in the fragment layout of
-// a plane with ntn 32-column tiles: four 16-byte stores per lane and tile; tiles wholly past M
-// are skipped.
+// a plane with ntn 32-column tiles: four 16-byte stores per lane and tile, streamed past the
+// caches (the reduction reads each byte once); tiles wholly past M are skipped.
 __device__ __forceinline__ void store_frag_partials(float* plane, int64_t ntn, int64_t M, int64_t m0, int64_t kw0,
                                                     int lane, const f32x16 (&acc)[4][2], float f) {
 #pragma unroll
@@ -51,8 +51,9 @@ __device__ __forceinline__ void store_frag_partials(float* plane, int64_t ntn, i
             float* tp = plane + (tm * ntn + kw0 / 32 + u) * 1024 + 4 * lane;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
-                *reinterpret_cast<f4*>(tp + 256 * r4) = f4{f * acc[mi][u][4 * r4], f * acc[mi][u][4 * r4 + 1],
-                                                           f * acc[mi][u][4 * r4 + 2], f * acc[mi][u][4 * r4 + 3]};
+                __builtin_nontemporal_store(f4{f * acc[mi][u][4 * r4], f * acc[mi][u][4 * r4 + 1],
+                                               f * acc[mi][u][4 * r4 + 2], f * acc[mi][u][4 * r4 + 3]},
+                                            reinterpret_cast<f4*>(tp + 256 * r4));
         }
     }
 }

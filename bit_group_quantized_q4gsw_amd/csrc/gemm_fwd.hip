@@ -531,7 +531,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
     if (!wave_active) return;
     if (split_stride) {
-        // split partials in the fragment layout: four 16-byte stores per lane and tile
+        // split partials in the fragment layout: four 16-byte stores per lane and tile, streamed
+        // past the caches (the reduction reads each byte once)
         float* plane = seg.out[sg] + (int64_t)z * split_stride;
         const int64_t tn = (seg.col0[sg] + n0) / 32;
 #pragma unroll
@@ -541,8 +542,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
             float* tp = plane + (tm * seg.ntn + tn) * 1024 + 4 * lane;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
-                *reinterpret_cast<f4*>(tp + 256 * r4) =
-                    f4{acc[mi][4 * r4], acc[mi][4 * r4 + 1], acc[mi][4 * r4 + 2], acc[mi][4 * r4 + 3]};
+                __builtin_nontemporal_store(
+                    f4{acc[mi][4 * r4], acc[mi][4 * r4 + 1], acc[mi][4 * r4 + 2], acc[mi][4 * r4 + 3]},
+                    reinterpret_cast<f4*>(tp + 256 * r4));
         }
         return;
     }

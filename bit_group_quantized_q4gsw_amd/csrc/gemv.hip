@@ -395,8 +395,8 @@ hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_
 // Split-partial reduction over the 32x32 MFMA fragment layout (see internal.h): one block per
 // 32x32 tile, thread t sums the 4 rows q of fragment slot t (register group r4 = t / 64, lane
 // L = t % 64: rows 8 r4 + 4 (L / 32) + q, column j = L % 32, or its octet permutation when perm
-// is set) with one 16-byte load per split, in split order, so the result does not depend on the
-// launch.  The tile is transposed through LDS so that each thread stores 4 consecutive columns
+// is set) with one streaming 16-byte load per split, in split order, so the result does not
+// depend on the launch.  The tile is transposed through LDS so that each thread stores 4 consecutive columns
 // of one row.
 __global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restrict__ ws, int splits, int64_t M,
                                                            int64_t ntn, int64_t plane, ReduceSegs seg, int perm,
@@ -406,8 +406,8 @@ __global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restri
     const int t = threadIdx.x;
     const int64_t tm = tile / ntn, tn = tile - tm * ntn;
     const float* src = ws + tile * 1024 + 4 * t;
-    f4 acc = *reinterpret_cast<const f4*>(src);
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f4*>(src + s * plane);
+    f4 acc = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src));
+    for (int s = 1; s < splits; ++s) acc += __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + s * plane));
     {
         const int L = t & 63, j = L & 31;
         const int jc = perm ? ((j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1)) : j;
