@@ -259,6 +259,71 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
     }
 }
 
+// Decode with one fp16 activation row (M = 1): one wave per row-octet streams the row-octet's
+// whole K, U x 64 k-octets, with every load (codes, scales, activations) issued before any use,
+// and sums its lanes with register-to-register cross-lane operations, so no cross-wave stage or
+// barrier follows.  Taken when K = 512 U with U <= 4, x is 16-byte aligned and K is not split;
+// lane l takes bytes [16 l, 16 l + 16) of each 32-micro-block run, as in gemv_fwd_kernel.
+template <int SF, int U>
+__global__ __launch_bounds__(256) void gemv_fwd_row_kernel(WView w, const void* __restrict__ x,
+                                                            float* __restrict__ out, int64_t n_octs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (R >= n_octs) return;                     // the whole wave
+    const int half = lane & 1;
+    constexpr int64_t kKocts = 64 * U;
+    const uint8_t* rowbase = w.nib + 32 * (R * kKocts) + 16 * half;
+    const int64_t row0 = 8 * R + 4 * half;
+    u4 q[2 * U], xr[2 * U], sraw[2 * U];
+#pragma unroll
+    for (int i = 0; i < 2 * U; ++i) {
+        const int O = 32 * i + (lane >> 1);
+        q[i] = ldg16_stream(rowbase + 32 * O);
+        const int64_t si = scale_index(w.g_pad, row0, (int64_t)((uint32_t)(8 * O) / (uint32_t)w.gs));
+        if constexpr (SF) {
+            const u2 v = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(w.scales) + si);
+            sraw[i] = u4{v.x, v.y, 0u, 0u};
+        } else {
+            sraw[i] = *reinterpret_cast<const u4*>(static_cast<const float*>(w.scales) + si);
+        }
+        xr[i] = ldg16(static_cast<const uint16_t*>(x) + 8 * O);
+    }
+    __builtin_amdgcn_sched_barrier(0);          // keep every load above ahead of every use below
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2 * U; ++i) {
+        float sc[4];
+        if constexpr (SF) {
+            sc[0] = f16_bits_to_f32((uint16_t)(sraw[i].x & 0xFFFFu));
+            sc[1] = f16_bits_to_f32((uint16_t)(sraw[i].x >> 16));
+            sc[2] = f16_bits_to_f32((uint16_t)(sraw[i].y & 0xFFFFu));
+            sc[3] = f16_bits_to_f32((uint16_t)(sraw[i].y >> 16));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = bitcast<float>(sraw[i][r]);
+        }
+        const uint32_t wd[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float t = 0.0f;
+            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 0), bitcast<h2>(xr[i].x), t, false);
+            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 1), bitcast<h2>(xr[i].y), t, false);
+            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 2), bitcast<h2>(xr[i].z), t, false);
+            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 3), bitcast<h2>(xr[i].w), t, false);
+            acc[r] = fmaf(t, sc[r], acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = wave_sum_same_parity(acc[r]);
+    if (lane < 2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = row0 + r;
+            if (n < w.N) out[n] = acc[r];
+        }
+    }
+}
+
 // Grid: (k_pad / 128, splits).  A block owns 128 columns of d_x; its waves take interleaved
 // 32-row steps of the block's N range.  Per micro-block the output gradient is pre-scaled,
 // d'[n] = d_out[m, n] * scale[g, n], and d_x[m, k] = sum_n d'[n] * (c[n, k] - 8).
@@ -510,9 +575,29 @@ static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_
     return hipGetLastError();
 }
 
+template <int SF>
+static void launch_gemv_row(int u, dim3 grid, hipStream_t s, const WView& w, const void* x, float* out,
+                            int64_t n_octs) {
+    switch (u) {
+        case 1: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 1>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
+        case 2: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 2>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
+        case 3: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 3>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
+        default: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 4>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
+    }
+}
+
 hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
                            hipStream_t s) {
     const int64_t octs = w.k_pad / 8;
+    const bool x_aligned = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+    if (M == 1 && splits == 1 && x_dtype == kF16 && x_aligned && w.K == w.k_pad && w.k_pad % 512 == 0 &&
+        w.k_pad / 512 <= 4) {
+        const int64_t n_octs = w.n_pad / 8;
+        const dim3 grid((unsigned)((n_octs + 3) / 4));
+        if (w.scale_f16) launch_gemv_row<1>((int)(w.k_pad / 512), grid, s, w, x, out, n_octs);
+        else launch_gemv_row<0>((int)(w.k_pad / 512), grid, s, w, x, out, n_octs);
+        return hipGetLastError();
+    }
     const int per = (int)((octs + splits - 1) / splits);
     const int waves = gemv_fwd_waves(w, splits);
     const dim3 grid((unsigned)(w.n_pad / 8), (unsigned)splits);

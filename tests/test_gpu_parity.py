@@ -298,3 +298,26 @@ def test_forced_bwd_splits(M, N, K, gs, act, sdt, splits):
     assert info["splits"] == splits, f"forced split count not taken: {info}"
     ref, norm = oracle_bwd(case.d_out, case.w)
     assert_within(dx, ref, norm, TOL[case.d_out.dtype], f"bwd splits={splits} route={info['route']}")
+
+
+# ---- one-wave-per-row-octet decode (M = 1, fp16 x, K = 512 U with U <= 4) ----------------------
+
+ROW_DECODE_CASES = [
+    # N, K, gs, scale dtype
+    (200, 512, 32, "f16"),       # U = 1, N tail inside the last row-octet block
+    (1000, 1024, 64, "f32"),     # U = 2, fp32 scales
+    (136, 1536, 8, "f16"),       # U = 3, a scale group per k-octet
+    (520, 2048, 128, "f32"),     # U = 4, fp32 scales
+]
+
+
+@pytest.mark.parametrize("N,K,gs,sdt", ROW_DECODE_CASES)
+def test_decode_row_octet_path(N, K, gs, sdt):
+    q = lib()
+    case = make_linear(1, K, N, gs, "f16", sdt, seed=N + K + gs, s_lo=0.005 if sdt == "f32" else 0.002)
+    pw = pack(q, case.w)
+    assert q.route(q.OP_FWD, pw, 1, torch.float16) == "gemv"
+    y = q.linear_fwd(pw, dev(case.x))
+    torch.cuda.synchronize()
+    ref, norm = oracle_fwd(case.x, case.w)
+    assert_within(y, ref, norm, TOL[torch.float16], f"decode row-octet N={N} K={K} gs={gs} {sdt}")
