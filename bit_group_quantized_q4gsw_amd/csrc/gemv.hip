@@ -259,25 +259,35 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
     }
 }
 
-// Decode with one fp16 activation row (M = 1): one wave per row-octet streams the row-octet's
-// whole K, U x 64 k-octets, with every load (codes, scales, activations) issued before any use,
-// and sums its lanes with register-to-register cross-lane operations, so no cross-wave stage or
-// barrier follows.  Taken when K = 512 U with U <= 4, x is 16-byte aligned and K is not split;
-// lane l takes bytes [16 l, 16 l + 16) of each 32-micro-block run, as in gemv_fwd_kernel.
-template <int SF, int U>
+// Decode with one fp16 activation row (M = 1): P waves per row-octet each stream 1/P of its K
+// (U x 64 k-octets in all), with every load (codes, scales, activations) issued before any use,
+// sum their lanes with register-to-register cross-lane operations and, for P > 1, hand their row
+// sums to the first wave through LDS (one barrier).  Taken when K = 512 U with U <= 4, x is
+// 16-byte aligned and K is not split; lane l takes bytes [16 l, 16 l + 16) of each
+// 32-micro-block run, as in gemv_fwd_kernel.
+template <int SF, int U, int P>
 __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(WView w, const void* __restrict__ x,
                                                             float* __restrict__ out, int64_t n_octs) {
+    static_assert((P == 1 || P == 2 || P == 4) && (2 * U) % P == 0, "waves per row-octet");
+    constexpr int I = 2 * U / P;                 // loads of each kind per lane
+    __shared__ float part_s[4][8];               // P > 1: the row sums of waves kp > 0
     const int lane = threadIdx.x & 63;
-    const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (R >= n_octs) return;                     // the whole wave
+    const int wave = threadIdx.x >> 6;
+    const int64_t Rw = (int64_t)blockIdx.x * (4 / P) + wave / P;
+    const int kp = wave % P;                     // which part of K the wave takes
+    const bool live = Rw < n_octs;
+    if constexpr (P == 1) {
+        if (!live) return;                       // the whole wave
+    }
+    const int64_t R = live ? Rw : 0;             // a dead wave (P > 1) reads valid bytes it never uses
     const int half = lane & 1;
     constexpr int64_t kKocts = 64 * U;
     const uint8_t* rowbase = w.nib + 32 * (R * kKocts) + 16 * half;
     const int64_t row0 = 8 * R + 4 * half;
-    u4 q[2 * U], xr[2 * U], sraw[2 * U];
+    u4 q[I], xr[I], sraw[I];
 #pragma unroll
-    for (int i = 0; i < 2 * U; ++i) {
-        const int O = 32 * i + (lane >> 1);
+    for (int i = 0; i < I; ++i) {
+        const int O = 32 * (I * kp + i) + (lane >> 1);
         q[i] = ldg16_stream(rowbase + 32 * O);
         const int64_t si = scale_index(w.g_pad, row0, (int64_t)((uint32_t)(8 * O) / (uint32_t)w.gs));
         if constexpr (SF) {
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(WView w, const void* 
     __builtin_amdgcn_sched_barrier(0);          // keep every load above ahead of every use below
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 2 * U; ++i) {
+    for (int i = 0; i < I; ++i) {
         float sc[4];
         if constexpr (SF) {
             sc[0] = f16_bits_to_f32((uint16_t)(sraw[i].x & 0xFFFFu));
@@ -315,6 +325,18 @@ __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(WView w, const void* 
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = wave_sum_same_parity(acc[r]);
+    if constexpr (P > 1) {
+        if (kp > 0 && lane < 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part_s[wave][4 * lane + r] = acc[r];
+        }
+        __syncthreads();
+        if (kp > 0 || !live) return;
+#pragma unroll
+        for (int p = 1; p < P; ++p)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += part_s[wave + p][4 * (lane & 1) + r];
+    }
     if (lane < 2) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -575,14 +597,24 @@ static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_
     return hipGetLastError();
 }
 
+// Waves per row-octet in the one-row decode: at K = 2048 two waves (half of K each) took 4.29 us
+// per launch, one wave 4.43 and four 4.41 (cache-cold graph replay).
+constexpr int kRowP = 2;
+
+template <int SF, int U>
+static void launch_gemv_row_u(hipStream_t s, const WView& w, const void* x, float* out, int64_t n_octs) {
+    constexpr int P = kRowP;
+    const dim3 grid((unsigned)((n_octs + 4 / P - 1) / (4 / P)));
+    hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, U, P>), grid, dim3(256), 0, s, w, x, out, n_octs);
+}
+
 template <int SF>
-static void launch_gemv_row(int u, dim3 grid, hipStream_t s, const WView& w, const void* x, float* out,
-                            int64_t n_octs) {
+static void launch_gemv_row(int u, hipStream_t s, const WView& w, const void* x, float* out, int64_t n_octs) {
     switch (u) {
-        case 1: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 1>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
-        case 2: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 2>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
-        case 3: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 3>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
-        default: hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, 4>), grid, dim3(256), 0, s, w, x, out, n_octs); break;
+        case 1: launch_gemv_row_u<SF, 1>(s, w, x, out, n_octs); break;
+        case 2: launch_gemv_row_u<SF, 2>(s, w, x, out, n_octs); break;
+        case 3: launch_gemv_row_u<SF, 3>(s, w, x, out, n_octs); break;
+        default: launch_gemv_row_u<SF, 4>(s, w, x, out, n_octs); break;
     }
 }
 
@@ -593,9 +625,8 @@ hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M
     if (M == 1 && splits == 1 && x_dtype == kF16 && x_aligned && w.K == w.k_pad && w.k_pad % 512 == 0 &&
         w.k_pad / 512 <= 4) {
         const int64_t n_octs = w.n_pad / 8;
-        const dim3 grid((unsigned)((n_octs + 3) / 4));
-        if (w.scale_f16) launch_gemv_row<1>((int)(w.k_pad / 512), grid, s, w, x, out, n_octs);
-        else launch_gemv_row<0>((int)(w.k_pad / 512), grid, s, w, x, out, n_octs);
+        if (w.scale_f16) launch_gemv_row<1>((int)(w.k_pad / 512), s, w, x, out, n_octs);
+        else launch_gemv_row<0>((int)(w.k_pad / 512), s, w, x, out, n_octs);
         return hipGetLastError();
     }
     const int per = (int)((octs + splits - 1) / splits);

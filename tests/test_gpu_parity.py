@@ -300,7 +300,7 @@ def test_forced_bwd_splits(M, N, K, gs, act, sdt, splits):
     assert_within(dx, ref, norm, TOL[case.d_out.dtype], f"bwd splits={splits} route={info['route']}")
 
 
-# ---- one-wave-per-row-octet decode (M = 1, fp16 x, K = 512 U with U <= 4) ----------------------
+# ---- row-octet decode (M = 1, fp16 x, K = 512 U with U <= 4) ---------------------------------
 
 ROW_DECODE_CASES = [
     # N, K, gs, scale dtype
