@@ -308,6 +308,7 @@ ROW_DECODE_CASES = [
     (1000, 1024, 64, "f32"),     # U = 2, fp32 scales
     (136, 1536, 8, "f16"),       # U = 3, a scale group per k-octet
     (520, 2048, 128, "f32"),     # U = 4, fp32 scales
+    (203, 1024, 32, "f16"),      # U = 2, N ends inside a row-octet
 ]
 
 
@@ -321,3 +322,57 @@ def test_decode_row_octet_path(N, K, gs, sdt):
     torch.cuda.synchronize()
     ref, norm = oracle_fwd(case.x, case.w)
     assert_within(y, ref, norm, TOL[torch.float16], f"decode row-octet N={N} K={K} gs={gs} {sdt}")
+
+
+# ---- activations one element off 16-byte alignment take each kernel's guarded fallback --------
+
+def _misaligned(t: torch.Tensor) -> torch.Tensor:
+    """A contiguous device copy of t whose data starts one element past an aligned allocation."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    v = buf[1:].view(t.shape)
+    v.copy_(t.cuda())
+    assert v.is_contiguous() and v.data_ptr() % 16 != 0
+    return v
+
+
+UNALIGNED_CASES = [
+    # kind, M, N, K, gs, act, scale
+    ("fwd", 1, 256, 1024, 32, "f16", "f16"),      # decode GEMV (the row-octet path needs alignment)
+    ("fwd", 3, 192, 256, 32, "bf16", "f16"),      # GEMV, M = 3
+    ("fwd", 64, 256, 512, 32, "f16", "f16"),      # MFMA fold
+    ("fwd", 70, 256, 512, 128, "bf16", "f16"),    # MFMA group
+    ("fwd", 40, 256, 384, 64, "f32", "f32"),      # MFMA split (fp32 x)
+    ("bwd", 2, 256, 512, 32, "f16", "f16"),       # GEMV input gradient
+    ("bwd", 64, 512, 256, 64, "f16", "f16"),      # bwd_fold
+    ("bwd", 50, 512, 256, 128, "f32", "f16"),     # bwd_split
+]
+
+
+@pytest.mark.parametrize("kind,M,N,K,gs,act,sdt", UNALIGNED_CASES)
+def test_unaligned_activation(kind, M, N, K, gs, act, sdt):
+    q = lib()
+    case = make_linear(M, K, N, gs, act, sdt, seed=M + N + K + gs, fwd=kind == "fwd", bwd=kind == "bwd",
+                       s_lo=0.005 if sdt == "f32" else 0.002)
+    pw = pack(q, case.w)
+    if kind == "fwd":
+        got = q.linear_fwd(pw, _misaligned(case.x))
+        ref, norm = oracle_fwd(case.x, case.w)
+        dt = case.x.dtype
+    else:
+        got = q.linear_bwd_input(pw, _misaligned(case.d_out))
+        ref, norm = oracle_bwd(case.d_out, case.w)
+        dt = case.d_out.dtype
+    torch.cuda.synchronize()
+    route = q.route(q.OP_FWD if kind == "fwd" else q.OP_BWD_INPUT, pw, M, dt)
+    assert_within(got, ref, norm, TOL[dt], f"unaligned {kind} M={M} route={route}")
+
+
+def test_unaligned_qkv():
+    q = lib()
+    case = make_qkv(M=40, K=512, Ns=(256, 128, 72), group_size=32, act_dtype="f16", scale_dtype="f16", seed=7)
+    pws = [pack(q, w) for w in case.weights]
+    outs = q.qkv_fused(*pws, _misaligned(case.x))
+    torch.cuda.synchronize()
+    for name, o, w in zip("qkv", outs, case.weights):
+        ref, norm = oracle_fwd(case.x, w)
+        assert_within(o, ref, norm, 2e-3, f"unaligned qkv {name}")
