@@ -640,18 +640,22 @@ static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, 
 }
 
 // Blocks of one kernel instance resident per CU (registers and LDS decide), cached per instance.
+// Planning may run on several host threads: the cache entries are atomics, and a race only
+// repeats the same query.
 static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int mi) {
-    static int cache[3][3][2][5][5];
-    int& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi];   // the aligned instance stands for both
-    if (slot == 0) {
-        int n = 1;
+    static std::atomic<int> cache[3][3][2][5][5];
+    // the aligned instance stands for both fallback variants
+    std::atomic<int>& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi];
+    int n = slot.load(std::memory_order_relaxed);
+    if (n == 0) {
+        n = 1;
         dispatch_fwd(mode, x_dtype, scale_f16, spc, mi, false, [&](auto kern) {
             int b = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, 64 * kWaves, 0) == hipSuccess && b > 0) n = b;
         });
-        slot = n;
+        slot.store(n, std::memory_order_relaxed);
     }
-    return slot;
+    return n;
 }
 
 static std::atomic<int> g_forced_tile_rows{0};
