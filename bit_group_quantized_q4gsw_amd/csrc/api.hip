@@ -403,6 +403,12 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, con
         const FwdPlan plan = plan_gemm_fwd(segs, 3, x_dtype, fold_ok(wq), M);
         return hip_status(launch_gemm_fwd(segs, 3, x, x_dtype, M, plan, static_cast<float*>(ws), s));
     }
+    // Decode shape (one fp16 row): the three streaming GEMVs in one launch, each weight with the
+    // per-row work of its own call, so the outputs equal three separate forwards bit for bit.
+    if (route == Q4GSW_ROUTE_GEMV && gemv_row_eligible(view_of(wq), x, x_dtype, M)) {
+        const WView v3[3] = {view_of(wq), view_of(wk), view_of(wv)};
+        return hip_status(launch_gemv_fwd_row(v3, o3, 3, x, s));
+    }
     // Fallback outside the fused predicate: three forwards on the same stream (same contract).
     for (int i = 0; i < 3; ++i) {
         st = run_fwd(w3[i], x, x_dtype, M, o3[i], ws, route, s);

@@ -259,42 +259,60 @@ __global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __r
     }
 }
 
+// Weights of one row-octet decode launch (fields of one weight at index i).
+struct RowSegs {
+    const uint8_t* nib[3];
+    const void* scales[3];
+    float* out[3];
+    int64_t N[3];
+    int64_t n_octs[3];           // row-octets of the nibble plane (n_pad / 8)
+    int64_t blk_start[4];        // first block of each weight; blk_start[nseg] = grid size
+    int64_t g_pad, gs;           // shared: the weights share K and group size
+    int nseg;
+};
+
 // Decode with one fp16 activation row (M = 1): P waves per row-octet each stream 1/P of its K
 // (U x 64 k-octets in all), with every load (codes, scales, activations) issued before any use,
 // sum their lanes with register-to-register cross-lane operations and, for P > 1, hand their row
 // sums to the first wave through LDS (one barrier).  Taken when K = 512 U with U <= 4, x is
 // 16-byte aligned and K is not split; lane l takes bytes [16 l, 16 l + 16) of each
-// 32-micro-block run, as in gemv_fwd_kernel.
+// 32-micro-block run, as in gemv_fwd_kernel.  One launch serves up to three weights that share
+// K, group size and scale dtype (the decode-shaped fused QKV): blocks [blk_start[i],
+// blk_start[i + 1]) take weight i, with exactly the per-row work of a launch for weight i alone.
 template <int SF, int U, int P>
-__global__ __launch_bounds__(256) void gemv_fwd_row_kernel(WView w, const void* __restrict__ x,
-                                                            float* __restrict__ out, int64_t n_octs) {
+__global__ __launch_bounds__(256) void gemv_fwd_row_kernel(RowSegs segs, const void* __restrict__ x) {
     static_assert((P == 1 || P == 2 || P == 4) && (2 * U) % P == 0, "waves per row-octet");
     constexpr int I = 2 * U / P;                 // loads of each kind per lane
     __shared__ float part_s[4][8];               // P > 1: the row sums of waves kp > 0
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t Rw = (int64_t)blockIdx.x * (4 / P) + wave / P;
+    int sg = 0;
+    while (sg + 1 < segs.nseg && (int64_t)blockIdx.x >= segs.blk_start[sg + 1]) ++sg;
+    const uint8_t* const nib = segs.nib[sg];
+    const void* const scales = segs.scales[sg];
+    float* const out = segs.out[sg];
+    const int64_t Rw = ((int64_t)blockIdx.x - segs.blk_start[sg]) * (4 / P) + wave / P;
     const int kp = wave % P;                     // which part of K the wave takes
-    const bool live = Rw < n_octs;
+    const bool live = Rw < segs.n_octs[sg];
     if constexpr (P == 1) {
         if (!live) return;                       // the whole wave
     }
     const int64_t R = live ? Rw : 0;             // a dead wave (P > 1) reads valid bytes it never uses
     const int half = lane & 1;
     constexpr int64_t kKocts = 64 * U;
-    const uint8_t* rowbase = w.nib + 32 * (R * kKocts) + 16 * half;
+    const uint8_t* rowbase = nib + 32 * (R * kKocts) + 16 * half;
     const int64_t row0 = 8 * R + 4 * half;
     u4 q[I], xr[I], sraw[I];
 #pragma unroll
     for (int i = 0; i < I; ++i) {
         const int O = 32 * (I * kp + i) + (lane >> 1);
         q[i] = ldg16_stream(rowbase + 32 * O);
-        const int64_t si = scale_index(w.g_pad, row0, (int64_t)((uint32_t)(8 * O) / (uint32_t)w.gs));
+        const int64_t si = scale_index(segs.g_pad, row0, (int64_t)((uint32_t)(8 * O) / (uint32_t)segs.gs));
         if constexpr (SF) {
-            const u2 v = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(w.scales) + si);
+            const u2 v = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(scales) + si);
             sraw[i] = u4{v.x, v.y, 0u, 0u};
         } else {
-            sraw[i] = *reinterpret_cast<const u4*>(static_cast<const float*>(w.scales) + si);
+            sraw[i] = *reinterpret_cast<const u4*>(static_cast<const float*>(scales) + si);
         }
         xr[i] = ldg16(static_cast<const uint16_t*>(x) + 8 * O);
     }
@@ -341,7 +359,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(WView w, const void* 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t n = row0 + r;
-            if (n < w.N) out[n] = acc[r];
+            if (n < segs.N[sg]) out[n] = acc[r];
         }
     }
 }
@@ -602,33 +620,57 @@ static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_
 constexpr int kRowP = 2;
 
 template <int SF, int U>
-static void launch_gemv_row_u(hipStream_t s, const WView& w, const void* x, float* out, int64_t n_octs) {
+static void launch_gemv_row_u(hipStream_t s, RowSegs segs, const void* x) {
     constexpr int P = kRowP;
-    const dim3 grid((unsigned)((n_octs + 4 / P - 1) / (4 / P)));
-    hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, U, P>), grid, dim3(256), 0, s, w, x, out, n_octs);
+    int64_t b = 0;
+    for (int i = 0; i < segs.nseg; ++i) {
+        segs.blk_start[i] = b;
+        b += (segs.n_octs[i] + 4 / P - 1) / (4 / P);
+    }
+    segs.blk_start[segs.nseg] = b;
+    hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, U, P>), dim3((unsigned)b), dim3(256), 0, s, segs, x);
 }
 
 template <int SF>
-static void launch_gemv_row(int u, hipStream_t s, const WView& w, const void* x, float* out, int64_t n_octs) {
+static void launch_gemv_row(int u, hipStream_t s, const RowSegs& segs, const void* x) {
     switch (u) {
-        case 1: launch_gemv_row_u<SF, 1>(s, w, x, out, n_octs); break;
-        case 2: launch_gemv_row_u<SF, 2>(s, w, x, out, n_octs); break;
-        case 3: launch_gemv_row_u<SF, 3>(s, w, x, out, n_octs); break;
-        default: launch_gemv_row_u<SF, 4>(s, w, x, out, n_octs); break;
+        case 1: launch_gemv_row_u<SF, 1>(s, segs, x); break;
+        case 2: launch_gemv_row_u<SF, 2>(s, segs, x); break;
+        case 3: launch_gemv_row_u<SF, 3>(s, segs, x); break;
+        default: launch_gemv_row_u<SF, 4>(s, segs, x); break;
     }
+}
+
+bool gemv_row_eligible(const WView& w, const void* x, int x_dtype, int64_t M) {
+    return M == 1 && x_dtype == kF16 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && w.K == w.k_pad &&
+           w.k_pad % 512 == 0 && w.k_pad / 512 <= 4 && gemv_fwd_splits(w, M) == 1;
+}
+
+hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, hipStream_t s) {
+    if (nseg < 1 || nseg > 3) return hipErrorInvalidValue;
+    RowSegs segs{};
+    segs.nseg = nseg;
+    segs.g_pad = w[0].g_pad;
+    segs.gs = w[0].gs;
+    for (int i = 0; i < nseg; ++i) {
+        if (w[i].k_pad != w[0].k_pad || w[i].gs != w[0].gs || w[i].scale_f16 != w[0].scale_f16)
+            return hipErrorInvalidValue;
+        segs.nib[i] = w[i].nib;
+        segs.scales[i] = w[i].scales;
+        segs.out[i] = out[i];
+        segs.N[i] = w[i].N;
+        segs.n_octs[i] = w[i].n_pad / 8;
+    }
+    const int u = (int)(w[0].k_pad / 512);
+    if (w[0].scale_f16) launch_gemv_row<1>(u, s, segs, x);
+    else launch_gemv_row<0>(u, s, segs, x);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
                            hipStream_t s) {
     const int64_t octs = w.k_pad / 8;
-    const bool x_aligned = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
-    if (M == 1 && splits == 1 && x_dtype == kF16 && x_aligned && w.K == w.k_pad && w.k_pad % 512 == 0 &&
-        w.k_pad / 512 <= 4) {
-        const int64_t n_octs = w.n_pad / 8;
-        if (w.scale_f16) launch_gemv_row<1>((int)(w.k_pad / 512), s, w, x, out, n_octs);
-        else launch_gemv_row<0>((int)(w.k_pad / 512), s, w, x, out, n_octs);
-        return hipGetLastError();
-    }
+    if (splits == 1 && gemv_row_eligible(w, x, x_dtype, M)) return launch_gemv_fwd_row(&w, &out, 1, x, s);
     const int per = (int)((octs + splits - 1) / splits);
     const int waves = gemv_fwd_waves(w, splits);
     const dim3 grid((unsigned)(w.n_pad / 8), (unsigned)splits);

@@ -24,6 +24,10 @@ hipError_t launch_unpack(const WView& w, uint8_t* codes, void* scales, hipStream
 hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out,
                            int splits, hipStream_t s);
 int gemv_fwd_splits(const WView& w, int64_t M);
+// The one-row fp16 decode path (M = 1, fp16 x 16-byte aligned, K = k_pad = 512 U with U <= 4, no
+// K split), and one launch of it over up to three weights sharing K, group size and scale dtype.
+bool gemv_row_eligible(const WView& w, const void* x, int x_dtype, int64_t M);
+hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, hipStream_t s);
 // `out` is d_x [M, K] when splits == 1, else ws [splits][M][k_pad].
 hipError_t launch_gemv_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* out,
                            int splits, hipStream_t s);

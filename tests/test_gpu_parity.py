@@ -376,3 +376,30 @@ def test_unaligned_qkv():
     for name, o, w in zip("qkv", outs, case.weights):
         ref, norm = oracle_fwd(case.x, w)
         assert_within(o, ref, norm, 2e-3, f"unaligned qkv {name}")
+
+
+# ---- decode-shaped fused QKV: one launch of the row-octet GEMV over the three weights ----------
+
+DECODE_QKV_CASES = [
+    # K, Ns, gs, scale dtype
+    (2048, (2048, 512, 512), 32, "f16"),     # the Llama projection triple at decode
+    (512, (200, 72, 136), 64, "f32"),        # ragged N per weight, fp32 scales
+    (1536, (256, 128, 8), 8, "f16"),         # a weight of a single row-octet
+]
+
+
+@pytest.mark.parametrize("K,Ns,gs,sdt", DECODE_QKV_CASES)
+def test_decode_qkv_one_launch(K, Ns, gs, sdt):
+    q = lib()
+    case = make_qkv(M=1, K=K, Ns=Ns, group_size=gs, act_dtype="f16", scale_dtype=sdt, seed=K + sum(Ns),
+                    s_lo=0.005 if sdt == "f32" else 0.002)
+    pws = [pack(q, w) for w in case.weights]
+    x = dev(case.x)
+    assert q.route(q.OP_QKV, pws[0], 1, torch.float16) == "gemv"
+    outs = q.qkv_fused(*pws, x)
+    separate = [q.linear_fwd(pw, x) for pw in pws]
+    torch.cuda.synchronize()
+    for name, o, sep, w in zip("qkv", outs, separate, case.weights):
+        ref, norm = oracle_fwd(case.x, w)
+        assert_within(o, ref, norm, TOL[torch.float16], f"decode qkv {name}")
+        assert torch.equal(o, sep), f"decode qkv {name}: fused and separate forwards differ"
