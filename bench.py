@@ -57,6 +57,7 @@ class Op:
     def __init__(self, name, kind, case, q, sets):
         import torch
         self.name, self.kind, self.case = name, kind, case
+        self.in_step = True              # False: timed per op only, outside the step
         ws = case.weights
         self.M = case.M
         N = sum(w.N for w in ws)
@@ -111,6 +112,8 @@ def build_ops(q, names, rotate):
         elif n == "qkv":
             for M in QKV_MS:
                 specs.append((f"qkv_m{M}", "qkv", make_workload("qkv", M=M)))
+            # the decode-shaped triple (one launch of the streaming GEMV), outside the step
+            specs.append(("qkv_m1", "qkv", make_workload("qkv", M=1)))
         elif n == "bwd":
             specs.append(("bwd", "bwd", make_workload("bwd")))
         else:
@@ -119,14 +122,19 @@ def build_ops(q, names, rotate):
         act = case.x if case.x is not None else case.d_out
         return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
 
+    extra = {"qkv_m1"}
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing
-        rotate = max(2, int(MALL_BYTES * 1.5 // sum(set_bytes(c) for _, _, c in specs)) + 1)
+        step_bytes = sum(set_bytes(c) for n, _, c in specs if n not in extra)
+        rotate = max(2, int(MALL_BYTES * 1.5 // step_bytes) + 1)
         per_op = [max(rotate, int(MALL_BYTES * 1.5 // set_bytes(c)) + 1) for _, _, c in specs]
     else:
         per_op = [rotate] * len(specs)
-    return [Op(n, k, c, q, sets) for (n, k, c), sets in zip(specs, per_op)], rotate
+    ops = [Op(n, k, c, q, sets) for (n, k, c), sets in zip(specs, per_op)]
+    for op in ops:
+        op.in_step = op.name not in extra
+    return ops, rotate
 
 
 def source_hash():
@@ -270,27 +278,35 @@ def main():
     ops, rotate = build_ops(q, names, args.rotate)
     torch.cuda.synchronize()
 
+    step_ops = [op for op in ops if op.in_step]
     for i in range(args.warmup):
         for op in ops:
             op.run(q, i)
     torch.cuda.synchronize()
 
-    # per-op timing: eager launches, each bracketed by HIP events on the launch stream
+    # per-op timing: eager launches, each bracketed by HIP events on the launch stream (the ops
+    # outside the step in a loop of their own)
     ev = {op.name: [] for op in ops}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+
+    def eager(group):
+        for i in range(args.steps):
+            for op in group:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                op.run(q, args.warmup + i)
+                b.record()
+                ev[op.name].append((a, b))
+
     start.record()
-    for i in range(args.steps):
-        for op in ops:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            op.run(q, args.warmup + i)
-            b.record()
-            ev[op.name].append((a, b))
+    eager(step_ops)
     stop.record()
     torch.cuda.synchronize()
     eager_ms_step = start.elapsed_time(stop) / args.steps
+    eager([op for op in ops if not op.in_step])
+    torch.cuda.synchronize()
 
     # whole-step timing: each rotated input set's step captured once as a HIP graph and
     # replayed, so host launch latency does not pace the GPU
@@ -298,7 +314,7 @@ def main():
     for s in range(rotate):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for op in ops:
+            for op in step_ops:
                 op.run(q, s)
         graphs.append(g)
     torch.cuda.synchronize()
@@ -347,13 +363,15 @@ def main():
         gbs = op.bytes / s / 1e9
         wgbs = op.weight_bytes / s / 1e9
         frac = gbs / HBM_PEAK_GBS if op.bound == "hbm" else tflops / MFMA_PEAK_TFLOPS
-        per_op[op.name] = {"ms": round(ms, 5), "eager_ms": round(eager_ms, 5), "tflops": round(tflops, 2),
+        per_op[op.name] = {"ms": round(ms, 5), "eager_ms": round(eager_ms, 5), "in_step": op.in_step,
+                           "tflops": round(tflops, 2),
                            "weight_gbs": round(wgbs, 1),
                            "alg_gbs": round(gbs, 1), "bound": op.bound, "roofline_frac": round(frac, 4),
                            "route": op.route, "M": op.M}
-        total_flops += op.flops
+        if op.in_step:
+            total_flops += op.flops
 
-    dom = max(ops, key=lambda o: per_op[o.name]["ms"])
+    dom = max(step_ops, key=lambda o: per_op[o.name]["ms"])
     d = per_op[dom.name]
     src = source_hash()
     if dom.bound == "hbm":
@@ -381,7 +399,8 @@ def main():
         "dtype": "bf16/f16",
         "data": "synthetic",
         "config": {"workload": "llama-3.2-1b q4gsw step: " + ", ".join(
-            f"{o.name} M{o.M} route={o.route}" for o in ops), "ops": names, "rotated_sets": rotate,
+            f"{o.name} M{o.M} route={o.route}" for o in step_ops), "ops": names, "rotated_sets": rotate,
+            "outside_step": [o.name for o in ops if not o.in_step],
             "op_sets": {o.name: len(o.sets) for o in ops},
             "timing": "step: HIP-graph replay of the whole step; per_op ms: HIP-graph replay of the op alone, "
                       ">= 32 launches over the rotated sets (eager_ms: eager launches between HIP events)",
@@ -390,7 +409,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(ops, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(step_ops, args.cpu_rows)
     print(json.dumps(line), flush=True)
 
 
