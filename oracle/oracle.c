@@ -25,6 +25,15 @@
  *       Opening summary of the same Vulkan pull request body (the input
  *       gradient of the frozen 4-bit base, contracting over N).
  *
+ *   embedding    out[t,k] = dequant(W[ids[t],k]): the embedding_q4gsw op named in a
+ *       maintainer comment on the react-native-executorch issue "Upstream the Gemma 4
+ *       Vulkan support we carry on our ExecuTorch fork" (its list of exporter changes),
+ *       whose table may share the linear weight's layout (is_linear_weight, in the
+ *       body of the WebGPU pull request that preserves the Q4 embedding's shader
+ *       controls across resize).  Read plainly: row t of the output is row ids[t] of
+ *       dequant(W).
+ *       The pages say nothing of ids outside [0, N); here they give rows of zeros.
+ *
  *   QKV          three forwards of one activation with three weights, three
  *       distinct outputs: body of "[ExecuTorch][WebGPU] Replace broad QKV
  *       fusion with BK64 kernel" (the QKV paragraph).  It is composed in the
@@ -206,6 +215,23 @@ int oracle_linear_bwd_input(const void *d_out, int act_dtype, int64_t M,
         dx[o] = sum;
         if (r)
             r[o] = norm;
+    }
+    return ORACLE_OK;
+}
+
+/* out[t,k] = dequant(W[ids[t],k]) for ids[t] in [0, N), else 0; ids has T entries, out is [T,K]. */
+int oracle_embedding(const int64_t *ids, int64_t T, const uint8_t *codes, const void *scales,
+                     int scale_dtype, int64_t N, int64_t K, int64_t group_size, double *out)
+{
+    int status = check_args(ORACLE_F32, scale_dtype, T, N, K, group_size, codes);
+    if (status != ORACLE_OK)
+        return status;
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t n = ids[t];
+        for (int64_t k = 0; k < K; ++k)
+            out[t * K + k] = (n >= 0 && n < N)
+                                 ? oracle_dequant(codes, scales, scale_dtype, N, K, group_size, n, k)
+                                 : 0.0;
     }
     return ORACLE_OK;
 }

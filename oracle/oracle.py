@@ -51,6 +51,8 @@ class Oracle:
         handle.oracle_f32_to_f64.argtypes = [ctypes.c_uint32]
         handle.oracle_threads.restype = ctypes.c_int
         handle.oracle_threads.argtypes = [ctypes.c_int]
+        handle.oracle_embedding.restype = ctypes.c_int
+        handle.oracle_embedding.argtypes = [vp, i64, vp, vp, ip, i64, i64, i64, vp]
         self.lib = handle
         self.path = path
 
@@ -101,6 +103,20 @@ class Oracle:
                 raise OracleError("q, k and v weights must share K and group_size")
         return [self.linear_fwd(x, w.codes, w.scales, w.group_size, threads) for w in weights]
 
+    def embedding(self, ids: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                  group_size: int) -> np.ndarray:
+        """Rows ids[t] of dequant(W), [T, K] float64 (rows of zeros for ids outside [0, N))."""
+        ids = ids.to(torch.int64).contiguous()
+        codes = codes.contiguous()
+        scales = scales.contiguous()
+        N, K = codes.shape
+        out = np.zeros((ids.numel(), K), dtype=np.float64)
+        status = self.lib.oracle_embedding(_ptr(ids), ids.numel(), _ptr(codes), _ptr(scales),
+                                           _DTYPE_CODE[scales.dtype], N, K, group_size, out.ctypes.data)
+        if status != 0:
+            raise OracleError(f"oracle_embedding returned {status}")
+        return out
+
     def dequant(self, codes: torch.Tensor, scales: torch.Tensor, group_size: int, n: int, k: int) -> float:
         """One element of dequant(W), as the oracle computes it."""
         codes = codes.contiguous()
@@ -147,3 +163,7 @@ def linear_bwd_input(d_out, codes, scales, group_size, threads=0):
 
 def qkv(x, weights, threads=0):
     return default().qkv(x, weights, threads)
+
+
+def embedding(ids, codes, scales, group_size):
+    return default().embedding(ids, codes, scales, group_size)

@@ -15,7 +15,9 @@ The facts:
   * the adjoint identity <d_out, fwd(x)> = <bwd(d_out), x>;
   * one-hot closed forms that read back every code and scale address;
   * QKV equals three forwards; thread-count invariance; R >= |y| with equality
-    when every term has one sign.
+    when every term has one sign;
+  * the embedding gather equals rows of the numpy-dequantised matrix and the
+    backward of a one-hot output gradient; ids outside [0, N) give zero rows.
 """
 from __future__ import annotations
 
@@ -284,6 +286,42 @@ def pin_normaliser(o):
     assert np.array_equal(dx, rdx)
 
 
+def pin_embedding(o):
+    """Row gather: rows of the numpy-dequantised matrix, the power-of-two address pin, the
+    one-hot backward, code 8 giving zero rows, and rows of zeros for ids outside [0, N)."""
+    N, K, gs = 11, 64, 16
+    g = torch.Generator().manual_seed(900)
+    codes = draw_codes(g, N, K)
+    scales = draw_scales(g, K // gs, N, "f16", 0.002, 0.02)
+    ids = torch.tensor([3, 0, 10, 3, 7, 1, 9, 2], dtype=torch.int64)
+    e = o.embedding(ids, codes, scales, gs)
+    assert e.shape == (len(ids), K)
+    assert np.array_equal(e, _dense(codes, scales, gs)[ids.numpy()])
+    # distinct power-of-two scale per (group, n) and distinct codes: pins row, group and column
+    expo = torch.tensor([[((gi * N + n) % 13) - 6 for n in range(N)] for gi in range(K // gs)],
+                        dtype=torch.float64)
+    pscales = torch.pow(2.0, expo).to(torch.float16)
+    e = o.embedding(ids, codes, pscales, gs)
+    for t, n in enumerate(ids.tolist()):
+        for k in range(K):
+            assert e[t, k] == (int(codes[n, k]) - 8) * 2.0 ** (((k // gs) * N + n) % 13 - 6), (t, k)
+    # one-hot output gradient: the backward reads back the same rows
+    onehot = torch.zeros(len(ids), N, dtype=torch.float32)
+    onehot[torch.arange(len(ids)), ids] = 1.0
+    dx, _ = o.linear_bwd_input(onehot, codes, pscales, gs)
+    assert np.array_equal(e, dx)
+    # code 8 is exactly zero
+    eight = torch.full((N, K), 8, dtype=torch.uint8)
+    assert np.array_equal(o.embedding(ids, eight, scales, gs), np.zeros((len(ids), K)))
+    # ids outside [0, N) give zero rows; valid ids beside them are unaffected
+    mixed = torch.tensor([-1, 4, N, 2**40, -2**40], dtype=torch.int64)
+    e = o.embedding(mixed, codes, scales, gs)
+    assert np.array_equal(e[[0, 2, 3, 4]], np.zeros((4, K)))
+    assert np.array_equal(e[1], _dense(codes, scales, gs)[4])
+    # no ids: an empty result
+    assert o.embedding(torch.zeros(0, dtype=torch.int64), codes, scales, gs).shape == (0, K)
+
+
 PINS = [pin_worked_example, pin_code_table, pin_decoders, pin_brute_force, pin_numpy_matmul,
         pin_code8_zero, pin_scale_linearity, pin_adjoint, pin_one_hot, pin_qkv, pin_threads,
-        pin_normaliser]
+        pin_normaliser, pin_embedding]

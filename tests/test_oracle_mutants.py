@@ -29,6 +29,9 @@ MUTANTS = {
     "bf16_hidden_bit": ("(fraction | 0x80)", "(fraction | 0x100)"),
     "f32_exponent_bias": ("exponent - 150", "exponent - 149"),
     "threads_reorder": ("int64_t m = o / N, n = o % N;", "int64_t m = o % M, n = o / M;"),
+    "embedding_ids_reversed": ("int64_t n = ids[t];", "int64_t n = ids[T - 1 - t];"),
+    "embedding_out_of_range_one": (": 0.0;", ": 1.0;"),
+    "embedding_k_reversed": ("group_size, n, k)\n", "group_size, n, K - 1 - k)\n"),
 }
 
 
