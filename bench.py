@@ -16,6 +16,7 @@ replayed between HIP events on the launch stream; the eager per-op time is kept 
 dominant op and the fp64 CPU oracle timed on a bounded sample of the same step.
 """
 import argparse
+import copy
 import hashlib
 import json
 import os
@@ -38,7 +39,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--ops", default="decode,prefill,qkv,bwd", help="comma-separated subset of the step")
+    p.add_argument("--ops", default="decode,prefill,qkv,bwd,embedding",
+                   help="comma-separated ops (embedding and the decode-shaped QKV are timed outside the step)")
     p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per M=512 op in the oracle sample")
@@ -101,6 +103,32 @@ class Op:
             q.linear_fwd(pw[0], a, out=outs[0], workspace=self.ws)
 
 
+class EmbOp:
+    """The embedding row gather (outside the step): T ids against a packed [N, K] table.
+    Algorithmic bytes per token: the row's codes (K/2) and scales, its id and its fp32 row out."""
+
+    def __init__(self, name, case, q, sets):
+        import torch
+        self.name, self.kind, self.case = name, "embedding", case
+        self.in_step = False
+        w = case.w
+        self.M = case.M
+        self.flops = 0.0
+        row = w.K / 2 + (w.K // w.group_size) * w.scales.element_size()
+        self.weight_bytes = self.M * row
+        self.bytes = self.M * (row + 8 + 4.0 * w.K)
+        self.sets = []
+        for s in range(sets):
+            pw = q.pack(w.codes.cuda(), w.scales.cuda(), w.group_size)
+            self.sets.append((pw, case.ids.cuda(), torch.empty(self.M, w.K, dtype=torch.float32, device="cuda")))
+        self.route = "embedding"
+        self.bound = "hbm"
+
+    def run(self, q, i):
+        pw, ids, out = self.sets[i % len(self.sets)]
+        q.embedding(pw, ids, out=out)
+
+
 def build_ops(q, names, rotate):
     from synthetic_inputs import make_workload
     specs = []
@@ -116,13 +144,24 @@ def build_ops(q, names, rotate):
             specs.append(("qkv_m1", "qkv", make_workload("qkv", M=1)))
         elif n == "bwd":
             specs.append(("bwd", "bwd", make_workload("bwd")))
+        elif n in ("embedding", "emb_t512", "emb_t1"):
+            # the row gather from the tied embedding table, outside the step: 512 ids and one id
+            emb = make_workload("embedding")
+            if n != "emb_t1":
+                specs.append(("emb_t512", "embedding", emb))
+            if n != "emb_t512":
+                one = copy.copy(emb)
+                one.M, one.ids = 1, emb.ids[:1].clone()
+                specs.append(("emb_t1", "embedding", one))
         else:
             raise SystemExit(f"unknown op {n}")
     def set_bytes(case):
+        if case.ids is not None:
+            return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights)
         act = case.x if case.x is not None else case.d_out
         return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
 
-    extra = {"qkv_m1"}
+    extra = {"qkv_m1", "emb_t512", "emb_t1"}
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing
@@ -131,9 +170,14 @@ def build_ops(q, names, rotate):
         per_op = [max(rotate, int(MALL_BYTES * 1.5 // set_bytes(c)) + 1) for _, _, c in specs]
     else:
         per_op = [rotate] * len(specs)
-    ops = [Op(n, k, c, q, sets) for (n, k, c), sets in zip(specs, per_op)]
+    ops = [EmbOp(n, c, q, sets) if k == "embedding" else Op(n, k, c, q, sets)
+           for (n, k, c), sets in zip(specs, per_op)]
     for op in ops:
         op.in_step = op.name not in extra
+    if not any(op.in_step for op in ops):
+        # a run of ops that are normally outside the step (counter runs): they form the step
+        for op in ops:
+            op.in_step = True
     return ops, rotate
 
 
@@ -165,7 +209,8 @@ def traffic_for(op_name, src_hash):
 # kernels that make up one launch of each op (a GEMM and, with K splits, its reduction)
 OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_"),
               "qkv_m128": ("gemm_fwd", "reduce_"), "qkv_m508": ("gemm_fwd", "reduce_"),
-              "qkv_m512": ("gemm_fwd", "reduce_"), "bwd": ("gemm_bwd", "reduce_")}
+              "qkv_m512": ("gemm_fwd", "reduce_"), "bwd": ("gemm_bwd", "reduce_"),
+              "emb_t512": ("embedding_kernel",), "emb_t1": ("embedding_kernel",)}
 
 
 def _counter_means(d, counter):

@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "q4gsw_route": [i32, pw, i64, i32],
             "q4gsw_plan": [i32, pw, pw, pw, i64, i32, ctypes.POINTER(PlanInfo)],
             "q4gsw_force_plan": [i32, i32],
+            "q4gsw_embedding": [pw, vp, i64, vp, vp],
         }
         for name, args in sigs.items():
             fn = getattr(h, name)
@@ -227,6 +228,19 @@ def linear_bwd_input(w: PackedWeight, d_out: torch.Tensor, out: Optional[torch.T
     _check(lib().q4gsw_linear_bwd_input(w.ref(), d_out.data_ptr(), _TORCH_DTYPE[d_out.dtype], M, dx.data_ptr(),
                                         wp, wb, _stream()), "q4gsw_linear_bwd_input")
     return dx
+
+
+def embedding(w: PackedWeight, ids: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out [*ids.shape, K] fp32: entry ids[i] gives row ids[i] of dequant(W) (zeros outside [0, N))."""
+    ids = _dev(ids, "ids")
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    T = ids.numel()
+    o = out if out is not None else torch.empty(*ids.shape, w.K, dtype=torch.float32, device=ids.device)
+    if o.dtype != torch.float32 or not o.is_contiguous() or o.numel() != T * w.K or o.device != ids.device:
+        raise ValueError("out must be a contiguous fp32 tensor of ids.numel() * K elements on ids' device")
+    _check(lib().q4gsw_embedding(w.ref(), ids.data_ptr(), T, o.data_ptr(), _stream()), "q4gsw_embedding")
+    return o
 
 
 def qkv_workspace_bytes(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, M: int, dtype: torch.dtype) -> int:

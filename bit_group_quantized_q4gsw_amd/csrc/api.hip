@@ -428,6 +428,17 @@ int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dt
     return st == Q4GSW_OK ? r : Q4GSW_ROUTE_NONE;
 }
 
+q4gsw_status q4gsw_embedding(const q4gsw_weight* w, const int64_t* ids, int64_t T, float* out, void* stream) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!ids || !out) return Q4GSW_E_NULL;
+    if (T < 1 || T > kMaxM || embedding_blocks(T, w->K) > 0x7FFFFFFFull) return Q4GSW_E_SHAPE;
+    const Range orng = range_of(out, (uint64_t)T * w->K * 4);
+    if (overlap(orng, range_of(ids, (uint64_t)T * 8)) || overlap(orng, range_of(w->data, w->bytes)))
+        return Q4GSW_E_ALIAS;
+    return hip_status(launch_embedding(view_of(w), ids, T, out, static_cast<hipStream_t>(stream)));
+}
+
 q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* wk, const q4gsw_weight* wv,
                         int64_t M, int32_t act_dtype, q4gsw_plan_info* info) {
     if (!info) return Q4GSW_E_NULL;

@@ -15,6 +15,11 @@ struct WView {
     int64_t N, K, gs, n_pad, k_pad, g_pad;
 };
 
+// embedding.hip: out [T, K] fp32, row t = row ids[t] of dequant(W) (zeros for ids outside [0, N)).
+// embedding_blocks is the launch's block count (it must stay below 2^31).
+uint64_t embedding_blocks(int64_t T, int64_t K);
+hipError_t launch_embedding(const WView& w, const int64_t* ids, int64_t T, float* out, hipStream_t s);
+
 // pack.hip
 hipError_t launch_pack(const uint8_t* codes, const void* scales, int scale_f16, int64_t N, int64_t K,
                        int64_t gs, const Layout& L, uint8_t* packed, hipStream_t s);

@@ -178,6 +178,24 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight *wq, const q4gsw_weight *wk, con
                              float *q, float *k, float *v, void *ws, uint64_t ws_bytes,
                              void *stream);
 
+/*
+ * Embedding row gather: out[t, k] = dequant(W)[ids[t], k], for t < T and k < K.
+ * The embedding_q4gsw op of the Gemma 4 ExecuTorch export (maintainer comment on the
+ * react-native-executorch issue "Upstream the Gemma 4 Vulkan support we carry on our
+ * ExecuTorch fork"), with the table in a linear weight's packed layout (the
+ * is_linear_weight flag of the WebGPU pull request that keeps the Q4 embedding's shader
+ * controls across resize): the weight packed once for forward, input gradient and QKV
+ * serves as the table of N rows of K columns, with no re-pack.
+ *   ids  device int64 [T]; an id outside [0, N) gives a row of zeros (the pages leave
+ *        this open; it is checked on the device, so it is not an error status)
+ *   out  device fp32 [T, K]; must not overlap ids or the packed weight (E_ALIAS)
+ * Values are exact for fp16 scales ((code - 8) * scale fits fp32) and the fp32 product,
+ * correctly rounded, for fp32 scales.  No workspace.  E_SHAPE for T < 1, T > 2^23, or
+ * T * ceil(ceil(K / 8) / 128) >= 2^31.
+ */
+q4gsw_status q4gsw_embedding(const q4gsw_weight *w, const int64_t *ids, int64_t T, float *out,
+                             void *stream);
+
 /* Route attestation: the q4gsw_route_id a call with these arguments takes
  * (Q4GSW_ROUTE_NONE if it would fail validation).  For Q4GSW_OP_QKV pass Wq. */
 int32_t q4gsw_route(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype);

@@ -13,10 +13,12 @@ Recipe (the same for every workload):
   * 4-bit codes: ``randint(0, 16)`` stored one code per byte (uint8), shape [N, K];
   * scales: ``rand * (hi - lo) + lo`` in fp32, then rounded to the scale dtype,
     shape [num_groups, N] with num_groups = K / group_size;
-  * draw order: activation(s) first, then (codes, scales) per weight.
+  * token ids (embedding gather): ``randint(0, N)`` int64, shape [M];
+  * draw order: activation(s) or ids first, then (codes, scales) per weight.
 
 Shapes are those of Llama-3.2-1B projections: MLP up/gate [8192, 2048], down
-[2048, 8192], Q [2048, 2048], K and V [512, 2048].  Random codes and scales stand
+[2048, 8192], Q [2048, 2048], K and V [512, 2048]; its tied embedding / output
+projection table is [128256, 2048].  Random codes and scales stand
 in for trained weights (no checkpoint is used).
 """
 from __future__ import annotations
@@ -40,6 +42,11 @@ def draw_activation(g: torch.Generator, rows: int, cols: int, dtype: str, sigma:
 def draw_codes(g: torch.Generator, n: int, k: int) -> torch.Tensor:
     """[n, k] uniform integer codes in 0..15, one per byte."""
     return torch.randint(0, 16, (n, k), generator=g, dtype=torch.int64).to(torch.uint8).contiguous()
+
+
+def draw_ids(g: torch.Generator, t: int, n: int) -> torch.Tensor:
+    """[t] uniform token ids in 0..n-1 (int64)."""
+    return torch.randint(0, n, (t,), generator=g, dtype=torch.int64).contiguous()
 
 
 def draw_scales(g: torch.Generator, groups: int, n: int, dtype: str, lo: float, hi: float) -> torch.Tensor:
@@ -74,6 +81,7 @@ class Case:
     x: Optional[torch.Tensor]            # [M, K] activation (forward / QKV input)
     d_out: Optional[torch.Tensor]        # [M, N] output gradient (backward input)
     weights: List[Weight] = field(default_factory=list)
+    ids: Optional[torch.Tensor] = None   # [M] token ids (embedding gather input)
 
     @property
     def w(self) -> Weight:
@@ -110,12 +118,23 @@ def make_qkv(M: int, K: int, Ns: Sequence[int], group_size: int, act_dtype: str,
     return Case(name, M, x, None, ws)
 
 
+def make_embedding(M: int, K: int, N: int, group_size: int, scale_dtype: str, seed: int = 0,
+                   s_lo: float = 0.002, s_hi: float = 0.02, name: str = "embedding") -> Case:
+    """M token ids and one [N, K] table (a packed linear weight serving as the embedding)."""
+    g = torch.Generator().manual_seed(seed)
+    ids = draw_ids(g, M, N)
+    w = make_weight(g, N, K, group_size, scale_dtype, s_lo, s_hi)
+    return Case(name, M, None, None, [w], ids=ids)
+
+
 # The five workloads of the Llama-1B-shaped suite.
 #   tiny    : fwd+bwd, M=4 K=64 N=32 gs=16, fp32 x/d_out N(0,1), fp32 scales U[0.005,0.02]
 #   decode  : fwd, M=1 K=2048 N=8192 gs=32, fp16 x, fp16 scales U[0.002,0.02]
 #   prefill : fwd, M=512 K=8192 N=2048 gs=128, bf16 x, fp16 scales
 #   qkv     : M in {128,508,512}, K=2048, N=(2048,512,512), gs=32, fp16 x and scales
 #   bwd     : d_out fp32 N(0, 0.1) [512,8192], W [8192,2048] gs=128, fp16 scales
+# and the row gather of the tied embedding / output projection table:
+#   embedding: M=512 uniform ids, table [128256, 2048] gs=32, fp16 scales
 WORKLOADS: Dict[str, dict] = {
     "tiny": dict(kind="linear", M=4, K=64, N=32, group_size=16, act_dtype="f32", scale_dtype="f32",
                  sigma=1.0, s_lo=0.005, s_hi=0.02, fwd=True, bwd=True),
@@ -127,6 +146,8 @@ WORKLOADS: Dict[str, dict] = {
                 scale_dtype="f16", sigma=1.0, s_lo=0.002, s_hi=0.02),
     "bwd": dict(kind="linear", M=512, K=2048, N=8192, group_size=128, act_dtype="f32",
                 scale_dtype="f16", sigma=0.1, s_lo=0.002, s_hi=0.02, fwd=False, bwd=True),
+    "embedding": dict(kind="embedding", M=512, K=2048, N=128256, group_size=32, scale_dtype="f16",
+                      s_lo=0.002, s_hi=0.02),
 }
 
 QKV_MS: Tuple[int, ...] = (128, 508, 512)
@@ -142,4 +163,6 @@ def make_workload(name: str, seed: int = 0, M: Optional[int] = None, act_dtype: 
         spec["act_dtype"] = act_dtype
     if kind == "qkv":
         return make_qkv(seed=seed, name=name, **spec)
+    if kind == "embedding":
+        return make_embedding(seed=seed, name=name, **spec)
     return make_linear(seed=seed, name=name, **spec)

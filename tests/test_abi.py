@@ -273,3 +273,22 @@ def test_plan_attestation_and_forcing(q):
         assert need.value == 5 * 512 * 2048 * 4
     finally:
         q.lib().q4gsw_force_plan(0, 0)
+
+
+def test_embedding_validation(q):
+    lib = q.lib()
+    d = fake_desc(q, 256, 512, 32, 1)
+    ids, out = FAKE * 8, FAKE * 16
+    e = lib.q4gsw_embedding
+    assert e(None, ids, 4, out, None) == E_NULL
+    assert e(ctypes.byref(d), None, 4, out, None) == E_NULL
+    assert e(ctypes.byref(d), ids, 4, None, None) == E_NULL
+    bad = fake_desc(q, 256, 512, 32, 1)
+    bad.magic = 0
+    assert e(ctypes.byref(bad), ids, 4, out, None) == E_DESC
+    assert e(ctypes.byref(d), ids, 0, out, None) == E_SHAPE
+    assert e(ctypes.byref(d), ids, -1, out, None) == E_SHAPE
+    assert e(ctypes.byref(d), ids, (1 << 23) + 1, out, None) == E_SHAPE
+    assert e(ctypes.byref(d), ids, 4, ids + 16, None) == E_ALIAS               # out overlaps ids
+    assert e(ctypes.byref(d), ids, 4, FAKE * 4 + 512, None) == E_ALIAS       # out inside the weight
+

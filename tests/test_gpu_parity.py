@@ -403,3 +403,82 @@ def test_decode_qkv_one_launch(K, Ns, gs, sdt):
         ref, norm = oracle_fwd(case.x, w)
         assert_within(o, ref, norm, TOL[torch.float16], f"decode qkv {name}")
         assert torch.equal(o, sep), f"decode qkv {name}: fused and separate forwards differ"
+
+
+EMB_CASES = [
+    # T, N, K, gs, scale dtype
+    (1, 200, 256, 32, "f16"),              # one id (decode)
+    (37, 130, 136, 8, "f32"),              # ragged K past the packing tile, fp32 scales
+    (300, 9, 64, 16, "f16"),               # many repeated ids over a 9-row table
+    (19, 40, 44, 4, "f16"),                # K not a multiple of 8, group smaller than an octet
+    (5, 100, 96, 12, "f16"),               # group size not a multiple of 8
+    (64, 1000, 8192, 128, "f32"),          # long rows, fp32 scales
+]
+
+
+def _emb_ref(ids, w):
+    from oracle import oracle as O
+    return O.embedding(ids, w.codes, w.scales, w.group_size)
+
+
+@pytest.mark.parametrize("T,N,K,gs,sdt", EMB_CASES)
+def test_embedding_rows(T, N, K, gs, sdt):
+    """Bit-exact: (code - 8) * scale is one fp32 product, correctly rounded on both sides."""
+    from synthetic_inputs import make_embedding
+    q = lib()
+    case = make_embedding(T, K, N, gs, sdt, seed=T * 31 + N, s_lo=0.005 if sdt == "f32" else 0.002)
+    pw = pack(q, case.w)
+    out = q.embedding(pw, dev(case.ids))
+    torch.cuda.synchronize()
+    ref = _emb_ref(case.ids, case.w).astype(np.float32)
+    assert out.shape == (T, K)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_embedding_out_of_range_and_misaligned_out():
+    """Ids outside [0, N) give zero rows; an output 4 bytes off a 16-byte boundary takes the
+    scalar-store path with the same values."""
+    q = lib()
+    from synthetic_inputs import make_embedding
+    case = make_embedding(6, 64, 40, 8, "f16", seed=5)
+    ids = torch.tensor([-1, 0, 39, 40, 2**40, -2**40, 17, 17], dtype=torch.int64)
+    pw = pack(q, case.w)
+    ref = _emb_ref(ids, case.w).astype(np.float32)
+    out = q.embedding(pw, dev(ids))
+    flat = torch.full((ids.numel() * 64 + 1,), 7.0, dtype=torch.float32, device="cuda")
+    mis = flat[1:].view(ids.numel(), 64)
+    q.embedding(pw, dev(ids), out=mis)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+    assert np.array_equal(mis.cpu().numpy(), ref)
+    assert flat[0].item() == 7.0
+    assert not out[[0, 3, 4, 5]].any()
+
+
+def test_embedding_equals_one_hot_backward():
+    """A one-hot output gradient through the input-gradient kernels reads back the same rows."""
+    q = lib()
+    from synthetic_inputs import make_embedding
+    case = make_embedding(8, 512, 256, 32, "f16", seed=11)
+    pw = pack(q, case.w)
+    emb = q.embedding(pw, dev(case.ids))
+    onehot = torch.zeros(8, 256, dtype=torch.float32)
+    onehot[torch.arange(8), case.ids] = 1.0
+    dx = q.linear_bwd_input(pw, dev(onehot))
+    torch.cuda.synchronize()
+    assert torch.equal(emb, dx)
+
+
+def test_workload_embedding():
+    """The tied-embedding table of the suite [128256, 2048], 512 ids, all rows checked."""
+    q = lib()
+    case = make_workload("embedding")
+    pw = pack(q, case.w)
+    out = q.embedding(pw, dev(case.ids))
+    torch.cuda.synchronize()
+    ref = _emb_ref(case.ids, case.w).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy(), ref)
+    # a decode-sized gather (one id) from the same packed table
+    one = q.embedding(pw, dev(case.ids[-1:]))
+    torch.cuda.synchronize()
+    assert np.array_equal(one.cpu().numpy(), ref[-1:])
