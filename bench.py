@@ -140,8 +140,9 @@ def build_ops(q, names, rotate):
         elif n == "qkv":
             for M in QKV_MS:
                 specs.append((f"qkv_m{M}", "qkv", make_workload("qkv", M=M)))
-            # the decode-shaped triple (one launch of the streaming GEMV), outside the step
+            # the decode-shaped triples (one launch of the streaming GEMV), outside the step
             specs.append(("qkv_m1", "qkv", make_workload("qkv", M=1)))
+            specs.append(("qkv_m4", "qkv", make_workload("qkv", M=4)))
         elif n == "bwd":
             specs.append(("bwd", "bwd", make_workload("bwd")))
         elif n in ("embedding", "emb_t512", "emb_t1"):
@@ -161,7 +162,7 @@ def build_ops(q, names, rotate):
         act = case.x if case.x is not None else case.d_out
         return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
 
-    extra = {"qkv_m1", "emb_t512", "emb_t1"}
+    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1"}
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing

@@ -403,11 +403,13 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, con
         const FwdPlan plan = plan_gemm_fwd(segs, 3, x_dtype, fold_ok(wq), M);
         return hip_status(launch_gemm_fwd(segs, 3, x, x_dtype, M, plan, static_cast<float*>(ws), s));
     }
-    // Decode shape (one fp16 row): the three streaming GEMVs in one launch, each weight with the
-    // per-row work of its own call, so the outputs equal three separate forwards bit for bit.
-    if (route == Q4GSW_ROUTE_GEMV && gemv_row_eligible(view_of(wq), x, x_dtype, M)) {
+    // Decode shapes (M <= 8): the three streaming GEMVs in one launch when none of them splits K,
+    // each weight with the per-row work of its own call, so the outputs equal three separate
+    // forwards bit for bit.
+    if (route == Q4GSW_ROUTE_GEMV) {
         const WView v3[3] = {view_of(wq), view_of(wk), view_of(wv)};
-        return hip_status(launch_gemv_fwd_row(v3, o3, 3, x, s));
+        if (gemv_fwd_splits(v3[0], M) == 1 && gemv_fwd_splits(v3[1], M) == 1 && gemv_fwd_splits(v3[2], M) == 1)
+            return hip_status(launch_gemv_fwd_multi(v3, o3, 3, x, x_dtype, M, s));
     }
     // Fallback outside the fused predicate: three forwards on the same stream (same contract).
     for (int i = 0; i < 3; ++i) {

@@ -78,23 +78,40 @@ __device__ __forceinline__ void load_act8(const void* src, int64_t base, int64_t
 
 }  // namespace
 
-// Grid: (n_pad / 8, splits).  Block: W waves (64 * W threads, W <= 16).  A block owns one
+// Grid: (n_pad / 8, splits).  Block: W waves (64 * W threads, W <= 8).  A block owns one
 // row-octet (8 rows).  Each load instruction of a wave reads 1 KB of contiguous codes: lane l
 // takes bytes [16 l, 16 l + 16) of a 32-micro-block run, i.e. rows 4 (l & 1) .. +3 of
 // k-octet l / 2.  A wave takes 64 k-octets per iteration (two loads per lane, both issued
 // before any unpacking) and the W waves of a block take adjacent 512-column slices, so a
 // decode launch is many small blocks that each stream one contiguous row-octet.
+//
+// One launch serves up to three weights sharing K, group size and scale dtype (the small-M fused
+// QKV): blocks [blk_start[i], blk_start[i + 1]) take the row-octets of weight i and do exactly
+// the work of a launch for that weight alone.
+struct GemvSegs {
+    WView w[3];
+    float* out[3];
+    int64_t out_ld[3];           // row pitch of each output
+    int64_t row_limit[3];        // rows stored (N unsplit, n_pad into a split workspace)
+    int64_t blk_start[4];        // first block of each weight; blk_start[nseg] = grid.x
+    int nseg;
+};
+
 template <int MT, int XT, int SF>
-__global__ __launch_bounds__(1024) void gemv_fwd_kernel(WView w, const void* __restrict__ x, int x_vec,
-                                                        float* __restrict__ out, int64_t out_ld,
-                                                        int64_t split_stride, int64_t row_limit,
-                                                        int octs_per_split) {
-    __shared__ float red[16][MT][8];
+__global__ __launch_bounds__(512) void gemv_fwd_kernel(GemvSegs segs, const void* __restrict__ x, int x_vec,
+                                                        int64_t split_stride, int octs_per_split) {
+    __shared__ float red[8][MT][8];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     const int half = lane & 1;
-    const int64_t R = blockIdx.x;
+    const int sg = (segs.nseg > 1 && (int64_t)blockIdx.x >= segs.blk_start[1]) +
+                   (segs.nseg > 2 && (int64_t)blockIdx.x >= segs.blk_start[2]);
+    const WView& w = segs.w[sg];
+    float* __restrict__ out = segs.out[sg];
+    const int64_t out_ld = segs.out_ld[sg];
+    const int64_t row_limit = segs.row_limit[sg];
+    const int64_t R = (int64_t)blockIdx.x - segs.blk_start[sg];
     const int64_t kocts = w.k_pad >> 3;
     const int64_t o0 = (int64_t)blockIdx.y * octs_per_split;
     const int64_t o1 = min(o0 + (int64_t)octs_per_split, kocts);
@@ -570,11 +587,12 @@ hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t 
     return launch_reduce_segments(ws, splits, M, ld, yy, yl, of, cl, 1, s);
 }
 
-// Waves per block: one per 64 k-octets of the split, at most 16.
+// Waves per block: one per 64 k-octets of the split, at most 8 (a 512-thread bound leaves 256
+// VGPRs per lane, so eight activation rows stay in registers; a 1024-thread bound spilled M >= 5).
 static int gemv_fwd_waves(const WView& w, int splits) {
     const int64_t octs = (w.k_pad / 8 + splits - 1) / splits;
     const int64_t nw = (octs + 63) / 64;
-    return (int)(nw > 16 ? 16 : (nw < 1 ? 1 : nw));
+    return (int)(nw > 8 ? 8 : (nw < 1 ? 1 : nw));
 }
 
 int gemv_fwd_splits(const WView& w, int64_t M) {
@@ -598,14 +616,12 @@ int gemv_bwd_splits(const WView& w, int64_t M) {
 }
 
 template <int XT, int SF>
-static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_t s, const WView& w,
-                                    const void* x, int vec, float* out, int64_t ld, int64_t stride,
-                                    int64_t limit, int per) {
+static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_t s, const GemvSegs& segs,
+                                    const void* x, int vec, int64_t stride, int per) {
     switch (M) {
-#define Q4GSW_CASE(MT)                                                                                   \
-    case MT:                                                                                             \
-        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT, SF>), grid, block, 0, s, w, x, vec, out, ld, stride, \
-                           limit, per);                                                                  \
+#define Q4GSW_CASE(MT)                                                                                     \
+    case MT:                                                                                               \
+        hipLaunchKernelGGL((gemv_fwd_kernel<MT, XT, SF>), grid, block, 0, s, segs, x, vec, stride, per); \
         break;
         Q4GSW_CASE(1) Q4GSW_CASE(2) Q4GSW_CASE(3) Q4GSW_CASE(4)
         Q4GSW_CASE(5) Q4GSW_CASE(6) Q4GSW_CASE(7) Q4GSW_CASE(8)
@@ -667,31 +683,57 @@ hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, cons
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
-                           hipStream_t s) {
-    const int64_t octs = w.k_pad / 8;
-    if (splits == 1 && gemv_row_eligible(w, x, x_dtype, M)) return launch_gemv_fwd_row(&w, &out, 1, x, s);
+// The streaming GEMV over nseg weights sharing K, group size and scale dtype; splits > 1 only with
+// one weight (out is then the workspace [splits][M][n_pad]).
+static hipError_t launch_gemv_fwd_segs(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,
+                                       int64_t M, int splits, hipStream_t s) {
+    if (nseg < 1 || nseg > 3 || (nseg > 1 && splits != 1)) return hipErrorInvalidValue;
+    GemvSegs segs{};
+    segs.nseg = nseg;
+    int64_t b = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (w[i].k_pad != w[0].k_pad || w[i].K != w[0].K || w[i].gs != w[0].gs || w[i].scale_f16 != w[0].scale_f16)
+            return hipErrorInvalidValue;
+        segs.w[i] = w[i];
+        segs.out[i] = out[i];
+        segs.out_ld[i] = splits == 1 ? w[i].N : w[i].n_pad;
+        segs.row_limit[i] = splits == 1 ? w[i].N : w[i].n_pad;
+        segs.blk_start[i] = b;
+        b += w[i].n_pad / 8;
+    }
+    segs.blk_start[nseg] = b;
+    const int64_t octs = w[0].k_pad / 8;
     const int per = (int)((octs + splits - 1) / splits);
-    const int waves = gemv_fwd_waves(w, splits);
-    const dim3 grid((unsigned)(w.n_pad / 8), (unsigned)splits);
+    const int waves = gemv_fwd_waves(w[0], splits);
+    const dim3 grid((unsigned)b, (unsigned)splits);
     const dim3 block((unsigned)(64 * waves));
     const int esize = x_dtype == kF32 ? 4 : 2;
-    const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) && ((w.K * esize) % 16 == 0);
-    const int64_t ld = splits == 1 ? w.N : w.n_pad;
-    const int64_t stride = splits == 1 ? 0 : M * w.n_pad;
-    const int64_t limit = splits == 1 ? w.N : w.n_pad;
-    if (w.scale_f16) {
+    const int vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) && ((w[0].K * esize) % 16 == 0);
+    const int64_t stride = splits == 1 ? 0 : M * w[0].n_pad;
+    if (w[0].scale_f16) {
         switch (x_dtype) {
-            case kF32: return gemv_fwd_dispatch<kF32, 1>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
-            case kF16: return gemv_fwd_dispatch<kF16, 1>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
-            default: return gemv_fwd_dispatch<kBF16, 1>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+            case kF32: return gemv_fwd_dispatch<kF32, 1>(M, grid, block, s, segs, x, vec, stride, per);
+            case kF16: return gemv_fwd_dispatch<kF16, 1>(M, grid, block, s, segs, x, vec, stride, per);
+            default: return gemv_fwd_dispatch<kBF16, 1>(M, grid, block, s, segs, x, vec, stride, per);
         }
     }
     switch (x_dtype) {
-        case kF32: return gemv_fwd_dispatch<kF32, 0>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
-        case kF16: return gemv_fwd_dispatch<kF16, 0>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
-        default: return gemv_fwd_dispatch<kBF16, 0>(M, grid, block, s, w, x, vec, out, ld, stride, limit, per);
+        case kF32: return gemv_fwd_dispatch<kF32, 0>(M, grid, block, s, segs, x, vec, stride, per);
+        case kF16: return gemv_fwd_dispatch<kF16, 0>(M, grid, block, s, segs, x, vec, stride, per);
+        default: return gemv_fwd_dispatch<kBF16, 0>(M, grid, block, s, segs, x, vec, stride, per);
     }
+}
+
+hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
+                           hipStream_t s) {
+    if (splits == 1 && gemv_row_eligible(w, x, x_dtype, M)) return launch_gemv_fwd_row(&w, &out, 1, x, s);
+    return launch_gemv_fwd_segs(&w, &out, 1, x, x_dtype, M, splits, s);
+}
+
+hipError_t launch_gemv_fwd_multi(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,
+                                 int64_t M, hipStream_t s) {
+    if (nseg >= 1 && gemv_row_eligible(w[0], x, x_dtype, M)) return launch_gemv_fwd_row(w, out, nseg, x, s);
+    return launch_gemv_fwd_segs(w, out, nseg, x, x_dtype, M, 1, s);
 }
 
 template <int GT>

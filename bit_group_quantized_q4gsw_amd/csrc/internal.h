@@ -33,6 +33,10 @@ int gemv_fwd_splits(const WView& w, int64_t M);
 // K split), and one launch of it over up to three weights sharing K, group size and scale dtype.
 bool gemv_row_eligible(const WView& w, const void* x, int x_dtype, int64_t M);
 hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, hipStream_t s);
+// One launch of the small-M GEMV over up to three weights sharing K, group size and scale dtype,
+// none of which splits K (the row-octet decode path when it is eligible): out[i] is y_i [M, N_i].
+hipError_t launch_gemv_fwd_multi(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,
+                                 int64_t M, hipStream_t s);
 // `out` is d_x [M, K] when splits == 1, else ws [splits][M][k_pad].
 hipError_t launch_gemv_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* out,
                            int splits, hipStream_t s);

@@ -482,3 +482,34 @@ def test_workload_embedding():
     one = q.embedding(pw, dev(case.ids[-1:]))
     torch.cuda.synchronize()
     assert np.array_equal(one.cpu().numpy(), ref[-1:])
+
+
+SMALL_M_QKV_CASES = [
+    # M, K, Ns, gs, activation dtype, scale dtype
+    (4, 2048, (2048, 512, 512), 32, "f16", "f16"),     # the Llama triple, small decode batch
+    (8, 2048, (2048, 512, 512), 32, "bf16", "f16"),
+    (1, 2048, (2048, 512, 512), 32, "bf16", "f16"),    # one row outside the fp16 row-octet path
+    (3, 512, (200, 72, 136), 64, "f32", "f32"),        # ragged N per weight, fp32 everywhere
+    (5, 1000, (256, 128, 8), 8, "f16", "f16"),         # K past the packing tile, a one-octet weight
+    (7, 8192, (256, 64, 64), 128, "f32", "f16"),       # long K: eight waves per row-octet
+    (2, 32768, (64, 64, 64), 128, "f16", "f16"),       # K split across blocks: three forwards
+]
+
+
+@pytest.mark.parametrize("M,K,Ns,gs,act,sdt", SMALL_M_QKV_CASES)
+def test_small_m_qkv_one_launch(M, K, Ns, gs, act, sdt):
+    """QKV at M <= 8: one GEMV launch over the three weights when none splits K, bitwise equal to
+    three separate forwards, and within tolerance of the oracle."""
+    q = lib()
+    case = make_qkv(M=M, K=K, Ns=Ns, group_size=gs, act_dtype=act, scale_dtype=sdt, seed=M * 1000 + K,
+                    s_lo=0.005 if sdt == "f32" else 0.002)
+    pws = [pack(q, w) for w in case.weights]
+    x = dev(case.x)
+    assert q.route(q.OP_QKV, pws[0], M, x.dtype) == "gemv"
+    outs = q.qkv_fused(*pws, x)
+    separate = [q.linear_fwd(pw, x) for pw in pws]
+    torch.cuda.synchronize()
+    for name, o, sep, w in zip("qkv", outs, separate, case.weights):
+        ref, norm = oracle_fwd(case.x, w)
+        assert_within(o, ref, norm, TOL[x.dtype], f"small-M qkv {name}")
+        assert torch.equal(o, sep), f"small-M qkv {name}: fused and separate forwards differ"
