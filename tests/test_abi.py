@@ -292,3 +292,13 @@ def test_embedding_validation(q):
     assert e(ctypes.byref(d), ids, 4, ids + 16, None) == E_ALIAS               # out overlaps ids
     assert e(ctypes.byref(d), ids, 4, FAKE * 4 + 512, None) == E_ALIAS       # out inside the weight
 
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says why (no GPU touched)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

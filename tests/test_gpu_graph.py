@@ -7,7 +7,7 @@ replays, must reproduce the eager output exactly.  The benchmark times its step 
 import pytest
 import torch
 
-from synthetic_inputs import make_linear, make_qkv
+from synthetic_inputs import make_embedding, make_linear, make_qkv
 from tests.gpu_helpers import dev, lib, pack
 
 pytestmark = pytest.mark.gpu
@@ -20,11 +20,16 @@ CASES = [
     ("bwd", 3, 512, 256, 32, "f16", "f16"),         # input-gradient GEMV
     ("bwd", 130, 1024, 512, 128, "f32", "f16"),     # input-gradient split route
     ("qkv", 128, None, 512, 32, "f16", "f16"),      # fused QKV
+    ("qkv", 1, None, 512, 32, "f16", "f16"),        # decode QKV: one row-octet GEMV launch
+    ("qkv", 4, None, 512, 32, "bf16", "f32"),       # small-M QKV: one segmented GEMV launch
+    ("emb", 37, 300, 256, 32, None, "f16"),         # embedding row gather
 ]
 
 
 def _call(q, kind, pw, a, outs, ws):
-    if kind == "fwd":
+    if kind == "emb":
+        q.embedding(pw[0], a, out=outs[0])
+    elif kind == "fwd":
         q.linear_fwd(pw[0], a, out=outs[0], workspace=ws)
     elif kind == "bwd":
         q.linear_bwd_input(pw[0], a, out=outs[0], workspace=ws)
@@ -39,12 +44,16 @@ def test_graph_replay_matches_eager(kind, M, N, K, gs, act, sdt):
         case = make_qkv(M=M, K=K, Ns=(512, 128, 128), group_size=gs, act_dtype=act, scale_dtype=sdt, seed=5)
         ws_list = case.weights
         a = dev(case.x)
+    elif kind == "emb":
+        case = make_embedding(M, K, N, gs, sdt, seed=9)
+        ws_list = [case.w]
+        a = dev(case.ids)
     else:
         case = make_linear(M, K, N, gs, act, sdt, seed=M + K, fwd=(kind == "fwd"), bwd=(kind == "bwd"))
         ws_list = [case.w]
         a = dev(case.x if kind == "fwd" else case.d_out)
     pw = [pack(q, w) for w in ws_list]
-    if kind == "bwd":
+    if kind in ("bwd", "emb"):
         shapes = [(M, K)]
         op = q.OP_BWD_INPUT
     else:
@@ -52,6 +61,8 @@ def test_graph_replay_matches_eager(kind, M, N, K, gs, act, sdt):
         op = q.OP_QKV if kind == "qkv" else q.OP_FWD
     if kind == "qkv":
         need = q.qkv_workspace_bytes(pw[0], pw[1], pw[2], M, a.dtype)
+    elif kind == "emb":
+        need = 0
     else:
         need = q.workspace_bytes(op, pw[0], M, a.dtype)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
