@@ -166,7 +166,8 @@ def build_ops(q, names, rotate):
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing
-        step_bytes = sum(set_bytes(c) for n, _, c in specs if n not in extra)
+        step_bytes = sum(set_bytes(c) for n, _, c in specs if n not in extra) or \
+            sum(set_bytes(c) for _, _, c in specs)
         rotate = max(2, int(MALL_BYTES * 1.5 // step_bytes) + 1)
         per_op = [max(rotate, int(MALL_BYTES * 1.5 // set_bytes(c)) + 1) for _, _, c in specs]
     else:

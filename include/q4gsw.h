@@ -191,7 +191,7 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight *wq, const q4gsw_weight *wk, con
  *   out  device fp32 [T, K]; must not overlap ids or the packed weight (E_ALIAS)
  * Values are exact for fp16 scales ((code - 8) * scale fits fp32) and the fp32 product,
  * correctly rounded, for fp32 scales.  No workspace.  E_SHAPE for T < 1, T > 2^23, or
- * T * ceil(ceil(K / 8) / 128) >= 2^31.
+ * T * ceil(ceil(K / 8) / 64) >= 2^31.
  */
 q4gsw_status q4gsw_embedding(const q4gsw_weight *w, const int64_t *ids, int64_t T, float *out,
                              void *stream);
