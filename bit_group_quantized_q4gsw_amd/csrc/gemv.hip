@@ -78,8 +78,8 @@ __device__ __forceinline__ void load_act8(const void* src, int64_t base, int64_t
 
 }  // namespace
 
-// Grid: (n_pad / 8, splits).  Block: W waves (64 * W threads, W <= 8).  A block owns one
-// row-octet (8 rows).  Each load instruction of a wave reads 1 KB of contiguous codes: lane l
+// Grid: (n_pad / 8, splits).  Block: W waves (64 * W threads; W <= 16 for M <= 4, else 8).  A
+// block owns one row-octet (8 rows).  Each load instruction of a wave reads 1 KB of contiguous codes: lane l
 // takes bytes [16 l, 16 l + 16) of a 32-micro-block run, i.e. rows 4 (l & 1) .. +3 of
 // k-octet l / 2.  A wave takes 64 k-octets per iteration (two loads per lane, both issued
 // before any unpacking) and the W waves of a block take adjacent 512-column slices, so a
@@ -97,10 +97,14 @@ struct GemvSegs {
     int nseg;
 };
 
+// Most waves per block for MT activation rows: up to four rows fit 128 VGPRs (16 waves, 1024
+// threads); more rows take a 512-thread bound (256 VGPRs), which a 1024-thread one made spill.
+constexpr int gemv_fwd_max_waves(int64_t mt) { return mt <= 4 ? 16 : 8; }
+
 template <int MT, int XT, int SF>
-__global__ __launch_bounds__(512) void gemv_fwd_kernel(GemvSegs segs, const void* __restrict__ x, int x_vec,
+__global__ __launch_bounds__(64 * gemv_fwd_max_waves(MT)) void gemv_fwd_kernel(GemvSegs segs, const void* __restrict__ x, int x_vec,
                                                         int64_t split_stride, int octs_per_split) {
-    __shared__ float red[8][MT][8];
+    __shared__ float red[gemv_fwd_max_waves(MT)][MT][8];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
@@ -587,12 +591,14 @@ hipError_t launch_reduce_splits(const float* ws, int splits, int64_t M, int64_t 
     return launch_reduce_segments(ws, splits, M, ld, yy, yl, of, cl, 1, s);
 }
 
-// Waves per block: one per 64 k-octets of the split, at most 8 (a 512-thread bound leaves 256
-// VGPRs per lane, so eight activation rows stay in registers; a 1024-thread bound spilled M >= 5).
-static int gemv_fwd_waves(const WView& w, int splits) {
+// Waves per block: one per 64 k-octets of the split, at most gemv_fwd_max_waves(M).  At K = 8192,
+// N = 2048 the cap of 8 for M > 4 took 12.1 us at M = 8 against 33.8 with 16 waves and spills;
+// M <= 4 keeps 16 (M = 1: 5.05 against 5.26 us with 8; cache-cold graph replay).
+static int gemv_fwd_waves(const WView& w, int splits, int64_t M) {
     const int64_t octs = (w.k_pad / 8 + splits - 1) / splits;
     const int64_t nw = (octs + 63) / 64;
-    return (int)(nw > 8 ? 8 : (nw < 1 ? 1 : nw));
+    const int64_t cap = gemv_fwd_max_waves(M);
+    return (int)(nw > cap ? cap : (nw < 1 ? 1 : nw));
 }
 
 int gemv_fwd_splits(const WView& w, int64_t M) {
@@ -704,7 +710,7 @@ static hipError_t launch_gemv_fwd_segs(const WView* w, float* const* out, int ns
     segs.blk_start[nseg] = b;
     const int64_t octs = w[0].k_pad / 8;
     const int per = (int)((octs + splits - 1) / splits);
-    const int waves = gemv_fwd_waves(w[0], splits);
+    const int waves = gemv_fwd_waves(w[0], splits, M);
     const dim3 grid((unsigned)b, (unsigned)splits);
     const dim3 block((unsigned)(64 * waves));
     const int esize = x_dtype == kF32 ? 4 : 2;
