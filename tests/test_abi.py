@@ -291,6 +291,10 @@ def test_embedding_validation(q):
     assert e(ctypes.byref(d), ids, (1 << 23) + 1, out, None) == E_SHAPE
     assert e(ctypes.byref(d), ids, 4, ids + 16, None) == E_ALIAS               # out overlaps ids
     assert e(ctypes.byref(d), ids, 4, FAKE * 4 + 512, None) == E_ALIAS       # out inside the weight
+    # the launch has T * ceil(ceil(K / 8) / 64) blocks, which must stay below 2^31: K = 2^30 gives
+    # 2^21 blocks per id, so 1024 ids are refused before any HIP call
+    wide = fake_desc(q, 8, 1 << 30, 1 << 30, 1, data=FAKE * 64)
+    assert e(ctypes.byref(wide), ids, 1024, FAKE * 128, None) == E_SHAPE
 
 
 
