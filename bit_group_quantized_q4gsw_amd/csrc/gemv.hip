@@ -295,8 +295,8 @@ struct RowSegs {
 // Decode with one fp16 activation row (M = 1): P waves per row-octet each stream 1/P of its K
 // (U x 64 k-octets in all), with every load (codes, scales, activations) issued before any use,
 // sum their lanes with register-to-register cross-lane operations and, for P > 1, hand their row
-// sums to the first wave through LDS (one barrier).  Taken when K = 512 U with U <= 4, x is
-// 16-byte aligned and K is not split; lane l takes bytes [16 l, 16 l + 16) of each
+// sums to the first wave through LDS (one barrier).  Taken when K = 512 U with U in 1..4, 8 or
+// 16, x is 16-byte aligned and K is not split; lane l takes bytes [16 l, 16 l + 16) of each
 // 32-micro-block run, as in gemv_fwd_kernel.  One launch serves up to three weights that share
 // K, group size and scale dtype (the decode-shaped fused QKV): blocks [blk_start[i],
 // blk_start[i + 1]) take weight i, with exactly the per-row work of a launch for weight i alone.
@@ -638,12 +638,14 @@ static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_
 }
 
 // Waves per row-octet in the one-row decode: at K = 2048 two waves (half of K each) took 4.29 us
-// per launch, one wave 4.43 and four 4.41 (cache-cold graph replay).
+// per launch, one wave 4.43 and four 4.41 (cache-cold graph replay).  K = 4096 and 8192 take four
+// waves (U / 2 loads per lane): N = 2048, K = 8192 took 4.39 us against 4.92 with
+// gemv_fwd_kernel, and N = 14336, K = 4096 9.11 against 10.85.
 constexpr int kRowP = 2;
 
 template <int SF, int U>
 static void launch_gemv_row_u(hipStream_t s, RowSegs segs, const void* x) {
-    constexpr int P = kRowP;
+    constexpr int P = U > 4 ? 4 : kRowP;
     int64_t b = 0;
     for (int i = 0; i < segs.nseg; ++i) {
         segs.blk_start[i] = b;
@@ -659,13 +661,16 @@ static void launch_gemv_row(int u, hipStream_t s, const RowSegs& segs, const voi
         case 1: launch_gemv_row_u<SF, 1>(s, segs, x); break;
         case 2: launch_gemv_row_u<SF, 2>(s, segs, x); break;
         case 3: launch_gemv_row_u<SF, 3>(s, segs, x); break;
-        default: launch_gemv_row_u<SF, 4>(s, segs, x); break;
+        case 4: launch_gemv_row_u<SF, 4>(s, segs, x); break;
+        case 8: launch_gemv_row_u<SF, 8>(s, segs, x); break;
+        default: launch_gemv_row_u<SF, 16>(s, segs, x); break;
     }
 }
 
 bool gemv_row_eligible(const WView& w, const void* x, int x_dtype, int64_t M) {
     return M == 1 && x_dtype == kF16 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && w.K == w.k_pad &&
-           w.k_pad % 512 == 0 && w.k_pad / 512 <= 4 && gemv_fwd_splits(w, M) == 1;
+           w.k_pad % 512 == 0 && (w.k_pad / 512 <= 4 || w.k_pad / 512 == 8 || w.k_pad / 512 == 16) &&
+           gemv_fwd_splits(w, M) == 1;
 }
 
 hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, hipStream_t s) {

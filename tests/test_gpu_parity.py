@@ -309,6 +309,9 @@ ROW_DECODE_CASES = [
     (136, 1536, 8, "f16"),       # U = 3, a scale group per k-octet
     (520, 2048, 128, "f32"),     # U = 4, fp32 scales
     (203, 1024, 32, "f16"),      # U = 2, N ends inside a row-octet
+    (2048, 8192, 128, "f16"),    # U = 16, four waves per row-octet
+    (300, 4096, 64, "f32"),      # U = 8, fp32 scales, N tail
+    (8, 8192, 8, "f16"),         # U = 16, a single row-octet, a scale group per k-octet
 ]
 
 
@@ -382,6 +385,7 @@ def test_unaligned_qkv():
 
 DECODE_QKV_CASES = [
     # K, Ns, gs, scale dtype
+    (4096, (4096, 1024, 1024), 64, "f16"),   # U = 8: four waves per row-octet
     (2048, (2048, 512, 512), 32, "f16"),     # the Llama projection triple at decode
     (512, (200, 72, 136), 64, "f32"),        # ragged N per weight, fp32 scales
     (1536, (256, 128, 8), 8, "f16"),         # a weight of a single row-octet
