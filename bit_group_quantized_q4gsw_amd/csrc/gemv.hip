@@ -292,7 +292,8 @@ struct RowSegs {
     int nseg;
 };
 
-// Decode with one fp16 activation row (M = 1): P waves per row-octet each stream 1/P of its K
+// Decode with one fp16 or bf16 activation row (M = 1; fp16: exact fp16 codes and dot2, bf16: x
+// widened exactly to fp32 and fp32 FMA): P waves per row-octet each stream 1/P of its K
 // (U x 64 k-octets in all), with every load (codes, scales, activations) issued before any use,
 // sum their lanes with register-to-register cross-lane operations and, for P > 1, hand their row
 // sums to the first wave through LDS (one barrier).  Taken when K = 512 U with U in 1..4, 8 or
@@ -300,8 +301,9 @@ struct RowSegs {
 // 32-micro-block run, as in gemv_fwd_kernel.  One launch serves up to three weights that share
 // K, group size and scale dtype (the decode-shaped fused QKV): blocks [blk_start[i],
 // blk_start[i + 1]) take weight i, with exactly the per-row work of a launch for weight i alone.
-template <int SF, int U, int P>
+template <int SF, int U, int P, int XT>
 __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(RowSegs segs, const void* __restrict__ x) {
+    static_assert(XT == kF16 || XT == kBF16, "16-bit activations");
     static_assert((P == 1 || P == 2 || P == 4) && (2 * U) % P == 0, "waves per row-octet");
     constexpr int I = 2 * U / P;                 // loads of each kind per lane
     __shared__ float part_s[4][8];               // P > 1: the row sums of waves kp > 0
@@ -352,14 +354,34 @@ __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(RowSegs segs, const v
             for (int r = 0; r < 4; ++r) sc[r] = bitcast<float>(sraw[i][r]);
         }
         const uint32_t wd[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+        if constexpr (XT == kF16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float t = 0.0f;
-            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 0), bitcast<h2>(xr[i].x), t, false);
-            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 1), bitcast<h2>(xr[i].y), t, false);
-            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 2), bitcast<h2>(xr[i].z), t, false);
-            t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 3), bitcast<h2>(xr[i].w), t, false);
-            acc[r] = fmaf(t, sc[r], acc[r]);
+            for (int r = 0; r < 4; ++r) {
+                float t = 0.0f;
+                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 0), bitcast<h2>(xr[i].x), t, false);
+                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 1), bitcast<h2>(xr[i].y), t, false);
+                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 2), bitcast<h2>(xr[i].z), t, false);
+                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 3), bitcast<h2>(xr[i].w), t, false);
+                acc[r] = fmaf(t, sc[r], acc[r]);
+            }
+        } else {
+            // bf16 x widened exactly to fp32 (the upper half of a word), exact fp32 codes, fp32 FMA
+            const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+            float xf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xf[2 * e] = bitcast<float>(xw[e] << 16);
+                xf[2 * e + 1] = bitcast<float>(xw[e] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float c[8];
+                word_codes_minus8_f32(wd[r], c);
+                float t = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t = fmaf(xf[e], c[e], t);
+                acc[r] = fmaf(t, sc[r], acc[r]);
+            }
         }
     }
 #pragma unroll
@@ -643,7 +665,7 @@ static hipError_t gemv_fwd_dispatch(int64_t M, dim3 grid, dim3 block, hipStream_
 // gemv_fwd_kernel, and N = 14336, K = 4096 9.11 against 10.85.
 constexpr int kRowP = 2;
 
-template <int SF, int U>
+template <int SF, int U, int XT>
 static void launch_gemv_row_u(hipStream_t s, RowSegs segs, const void* x) {
     constexpr int P = U > 4 ? 4 : kRowP;
     int64_t b = 0;
@@ -652,28 +674,32 @@ static void launch_gemv_row_u(hipStream_t s, RowSegs segs, const void* x) {
         b += (segs.n_octs[i] + 4 / P - 1) / (4 / P);
     }
     segs.blk_start[segs.nseg] = b;
-    hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, U, P>), dim3((unsigned)b), dim3(256), 0, s, segs, x);
+    hipLaunchKernelGGL((gemv_fwd_row_kernel<SF, U, P, XT>), dim3((unsigned)b), dim3(256), 0, s, segs, x);
 }
 
-template <int SF>
+template <int SF, int XT>
 static void launch_gemv_row(int u, hipStream_t s, const RowSegs& segs, const void* x) {
     switch (u) {
-        case 1: launch_gemv_row_u<SF, 1>(s, segs, x); break;
-        case 2: launch_gemv_row_u<SF, 2>(s, segs, x); break;
-        case 3: launch_gemv_row_u<SF, 3>(s, segs, x); break;
-        case 4: launch_gemv_row_u<SF, 4>(s, segs, x); break;
-        case 8: launch_gemv_row_u<SF, 8>(s, segs, x); break;
-        default: launch_gemv_row_u<SF, 16>(s, segs, x); break;
+        case 1: launch_gemv_row_u<SF, 1, XT>(s, segs, x); break;
+        case 2: launch_gemv_row_u<SF, 2, XT>(s, segs, x); break;
+        case 3: launch_gemv_row_u<SF, 3, XT>(s, segs, x); break;
+        case 4: launch_gemv_row_u<SF, 4, XT>(s, segs, x); break;
+        case 8: launch_gemv_row_u<SF, 8, XT>(s, segs, x); break;
+        default: launch_gemv_row_u<SF, 16, XT>(s, segs, x); break;
     }
 }
 
 bool gemv_row_eligible(const WView& w, const void* x, int x_dtype, int64_t M) {
-    return M == 1 && x_dtype == kF16 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && w.K == w.k_pad &&
-           w.k_pad % 512 == 0 && (w.k_pad / 512 <= 4 || w.k_pad / 512 == 8 || w.k_pad / 512 == 16) &&
-           gemv_fwd_splits(w, M) == 1;
+    // bf16 x widens to fp32 and FMAs: at U = 16 that tail made the row kernel 4-5% slower than
+    // gemv_fwd_kernel (N = 2048, K = 8192: 5.27 against 5.03 us), while U <= 8 gained 9-15%
+    const int64_t u = w.k_pad / 512;
+    return M == 1 && (x_dtype == kF16 || (x_dtype == kBF16 && u <= 8)) &&
+           (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && w.K == w.k_pad && w.k_pad % 512 == 0 &&
+           (u <= 4 || u == 8 || u == 16) && gemv_fwd_splits(w, M) == 1;
 }
 
-hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, hipStream_t s) {
+hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,
+                               hipStream_t s) {
     if (nseg < 1 || nseg > 3) return hipErrorInvalidValue;
     RowSegs segs{};
     segs.nseg = nseg;
@@ -689,8 +715,13 @@ hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, cons
         segs.n_octs[i] = w[i].n_pad / 8;
     }
     const int u = (int)(w[0].k_pad / 512);
-    if (w[0].scale_f16) launch_gemv_row<1>(u, s, segs, x);
-    else launch_gemv_row<0>(u, s, segs, x);
+    if (x_dtype == kBF16) {
+        if (w[0].scale_f16) launch_gemv_row<1, kBF16>(u, s, segs, x);
+        else launch_gemv_row<0, kBF16>(u, s, segs, x);
+    } else {
+        if (w[0].scale_f16) launch_gemv_row<1, kF16>(u, s, segs, x);
+        else launch_gemv_row<0, kF16>(u, s, segs, x);
+    }
     return hipGetLastError();
 }
 
@@ -737,13 +768,13 @@ static hipError_t launch_gemv_fwd_segs(const WView* w, float* const* out, int ns
 
 hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out, int splits,
                            hipStream_t s) {
-    if (splits == 1 && gemv_row_eligible(w, x, x_dtype, M)) return launch_gemv_fwd_row(&w, &out, 1, x, s);
+    if (splits == 1 && gemv_row_eligible(w, x, x_dtype, M)) return launch_gemv_fwd_row(&w, &out, 1, x, x_dtype, s);
     return launch_gemv_fwd_segs(&w, &out, 1, x, x_dtype, M, splits, s);
 }
 
 hipError_t launch_gemv_fwd_multi(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,
                                  int64_t M, hipStream_t s) {
-    if (nseg >= 1 && gemv_row_eligible(w[0], x, x_dtype, M)) return launch_gemv_fwd_row(w, out, nseg, x, s);
+    if (nseg >= 1 && gemv_row_eligible(w[0], x, x_dtype, M)) return launch_gemv_fwd_row(w, out, nseg, x, x_dtype, s);
     return launch_gemv_fwd_segs(w, out, nseg, x, x_dtype, M, 1, s);
 }
 

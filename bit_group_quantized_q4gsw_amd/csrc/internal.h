@@ -29,11 +29,12 @@ hipError_t launch_unpack(const WView& w, uint8_t* codes, void* scales, hipStream
 hipError_t launch_gemv_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* out,
                            int splits, hipStream_t s);
 int gemv_fwd_splits(const WView& w, int64_t M);
-// The one-row fp16 decode path (M = 1, fp16 x 16-byte aligned, K = k_pad = 512 U with U in 1..4, 8
-// or 16, no
-// K split), and one launch of it over up to three weights sharing K, group size and scale dtype.
+// The one-row decode path (M = 1, fp16 or bf16 x 16-byte aligned, K = k_pad = 512 U with U in
+// 1..4, 8 or 16, no K split), and one launch of it over up to three weights sharing K, group size
+// and scale dtype.
 bool gemv_row_eligible(const WView& w, const void* x, int x_dtype, int64_t M);
-hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, hipStream_t s);
+hipError_t launch_gemv_fwd_row(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,
+                               hipStream_t s);
 // One launch of the small-M GEMV over up to three weights sharing K, group size and scale dtype,
 // none of which splits K (the row-octet decode path when it is eligible): out[i] is y_i [M, N_i].
 hipError_t launch_gemv_fwd_multi(const WView* w, float* const* out, int nseg, const void* x, int x_dtype,

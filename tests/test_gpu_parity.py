@@ -517,3 +517,24 @@ def test_small_m_qkv_one_launch(M, K, Ns, gs, act, sdt):
         ref, norm = oracle_fwd(case.x, w)
         assert_within(o, ref, norm, TOL[x.dtype], f"small-M qkv {name}")
         assert torch.equal(o, sep), f"small-M qkv {name}: fused and separate forwards differ"
+
+
+ROW_DECODE_BF16_CASES = [
+    # N, K, gs, scale dtype: one bf16 row through the row-octet decode kernel
+    (200, 512, 32, "f16"),
+    (520, 2048, 128, "f32"),
+    (8192, 2048, 32, "f16"),      # the decode workload's weight
+    (2048, 8192, 128, "f16"),     # four waves per row-octet
+    (203, 1024, 32, "f16"),
+]
+
+
+@pytest.mark.parametrize("N,K,gs,sdt", ROW_DECODE_BF16_CASES)
+def test_decode_row_octet_bf16(N, K, gs, sdt):
+    q = lib()
+    case = make_linear(1, K, N, gs, "bf16", sdt, seed=N + K + 7, s_lo=0.005 if sdt == "f32" else 0.002)
+    pw = pack(q, case.w)
+    y = q.linear_fwd(pw, dev(case.x))
+    torch.cuda.synchronize()
+    ref, norm = oracle_fwd(case.x, case.w)
+    assert_within(y, ref, norm, TOL[torch.bfloat16], f"bf16 decode row-octet N={N} K={K} gs={gs} {sdt}")
