@@ -370,15 +370,22 @@ def test_unaligned_activation(kind, M, N, K, gs, act, sdt):
     assert_within(got, ref, norm, TOL[dt], f"unaligned {kind} M={M} route={route}")
 
 
-def test_unaligned_qkv():
+@pytest.mark.parametrize("M", [40, 1, 5])
+def test_unaligned_qkv(M):
+    """MFMA QKV (M = 40) and the one-launch small-M GEMV (M = 1 and 5; unaligned x leaves the
+    row-octet kernel for the segmented GEMV's guarded loads), each equal to separate forwards."""
     q = lib()
-    case = make_qkv(M=40, K=512, Ns=(256, 128, 72), group_size=32, act_dtype="f16", scale_dtype="f16", seed=7)
+    case = make_qkv(M=M, K=512, Ns=(256, 128, 72), group_size=32, act_dtype="f16", scale_dtype="f16", seed=7)
     pws = [pack(q, w) for w in case.weights]
-    outs = q.qkv_fused(*pws, _misaligned(case.x))
+    x = _misaligned(case.x)
+    outs = q.qkv_fused(*pws, x)
+    separate = [q.linear_fwd(pw, x) for pw in pws]
     torch.cuda.synchronize()
-    for name, o, w in zip("qkv", outs, case.weights):
+    for name, o, sep, w in zip("qkv", outs, separate, case.weights):
         ref, norm = oracle_fwd(case.x, w)
-        assert_within(o, ref, norm, 2e-3, f"unaligned qkv {name}")
+        assert_within(o, ref, norm, 2e-3, f"unaligned qkv M={M} {name}")
+        if M <= 8:
+            assert torch.equal(o, sep), f"unaligned qkv M={M} {name}: fused and separate forwards differ"
 
 
 # ---- decode-shaped fused QKV: one launch of the row-octet GEMV over the three weights ----------
@@ -417,6 +424,7 @@ EMB_CASES = [
     (19, 40, 44, 4, "f16"),                # K not a multiple of 8, group smaller than an octet
     (5, 100, 96, 12, "f16"),               # group size not a multiple of 8
     (64, 1000, 8192, 128, "f32"),          # long rows, fp32 scales
+    (7, 50, 60, 12, "f32"),                # fp32 scales, K not a multiple of 8, gs not of 8
 ]
 
 
