@@ -68,6 +68,10 @@ def pin_worked_example(o):
         dx, rdx = o.linear_bwd_input(_t(g["d_out"], act), codes, scales, gs)
         assert np.array_equal(dx, np.array(g["d_x"])), (act, sdt, dx)
         assert np.array_equal(rdx, np.array(g["d_x_norm"])), (act, sdt, rdx)
+    ids = torch.tensor([int(v) for v in g["ids"][0]], dtype=torch.int64)
+    for sdt in SCALE_DTYPES:
+        e = o.embedding(ids, codes, _t(g["scales"], sdt), gs)
+        assert np.array_equal(e, np.array(g["embedding"])), (sdt, e)
 
 
 def pin_code_table(o):
