@@ -48,6 +48,20 @@ def test_golden_worked_example(act, sdt, M):
         assert torch.equal(dx.cpu(), dx_want), (fam, dx)
 
 
+@pytest.mark.parametrize("sdt", ["f32", "f16"])
+def test_golden_embedding(sdt):
+    """The hand-worked embedding rows of the example (one id out of range), bit for bit."""
+    q = lib()
+    g = load_golden("worked_example_4x2.txt")
+    codes = torch.tensor(g["codes"], dtype=torch.uint8)
+    scales = torch.tensor(g["scales"], dtype=torch.float64).to(DTYPES[sdt])
+    pw = q.pack(codes.cuda(), scales.cuda(), int(g["group_size"]))
+    ids = torch.tensor([int(v) for v in g["ids"][0]], dtype=torch.int64)
+    e = q.embedding(pw, ids.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(e.cpu(), torch.tensor(g["embedding"], dtype=torch.float32)), e
+
+
 @pytest.mark.parametrize("M,act", [(1, "f16"), (6, "f32"), (64, "bf16"), (64, "f16"), (40, "f32")])
 def test_code8_is_zero(M, act):
     q = lib()
