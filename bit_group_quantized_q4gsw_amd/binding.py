@@ -10,6 +10,7 @@ from __future__ import annotations
 import contextlib
 import ctypes
 import os
+import threading
 from typing import Optional, Tuple
 
 import torch
@@ -50,6 +51,24 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("route", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("splits", ctypes.c_int32)]
 
 
+class Options(ctypes.Structure):
+    """q4gsw_options of include/q4gsw.h: a per-call route family, block rows and split count."""
+    _fields_ = [("route", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("splits", ctypes.c_int32)]
+
+
+# Choices made by forced_route / forced_plan, held per Python thread and handed to each call
+# (the library itself keeps no routing state).
+_local = threading.local()
+
+
+def _opts():
+    """The current thread's options, or None (library defaults)."""
+    o = getattr(_local, "opts", None)
+    if o is None or (o.route == 0 and o.tile_rows == 0 and o.splits == 0):
+        return None
+    return ctypes.byref(o)
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -63,18 +82,23 @@ def lib() -> ctypes.CDLL:
         h = ctypes.CDLL(LIB_PATH)
         i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
         pw = ctypes.POINTER(WeightDesc)
+        po = ctypes.POINTER(Options)
         sigs = {
             "q4gsw_packed_bytes": [i64, i64, i64, i32, ctypes.POINTER(u64)],
             "q4gsw_pack": [vp, vp, i32, i64, i64, i64, vp, u64, vp, pw],
             "q4gsw_unpack": [pw, vp, vp, vp],
             "q4gsw_workspace_bytes": [i32, pw, i64, i32, ctypes.POINTER(u64)],
             "q4gsw_qkv_workspace_bytes": [pw, pw, pw, i64, i32, ctypes.POINTER(u64)],
+            "q4gsw_workspace_bytes_ex": [i32, pw, i64, i32, po, ctypes.POINTER(u64)],
+            "q4gsw_qkv_workspace_bytes_ex": [pw, pw, pw, i64, i32, po, ctypes.POINTER(u64)],
             "q4gsw_linear_fwd": [pw, vp, i32, i64, vp, vp, u64, vp],
             "q4gsw_linear_bwd_input": [pw, vp, i32, i64, vp, vp, u64, vp],
             "q4gsw_qkv_fused": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, vp],
+            "q4gsw_linear_fwd_ex": [pw, vp, i32, i64, vp, vp, u64, po, vp],
+            "q4gsw_linear_bwd_input_ex": [pw, vp, i32, i64, vp, vp, u64, po, vp],
+            "q4gsw_qkv_fused_ex": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, po, vp],
             "q4gsw_route": [i32, pw, i64, i32],
-            "q4gsw_plan": [i32, pw, pw, pw, i64, i32, ctypes.POINTER(PlanInfo)],
-            "q4gsw_force_plan": [i32, i32],
+            "q4gsw_plan": [i32, pw, pw, pw, i64, i32, po, ctypes.POINTER(PlanInfo)],
             "q4gsw_embedding": [pw, vp, i64, vp, vp],
         }
         for name, args in sigs.items():
@@ -85,8 +109,6 @@ def lib() -> ctypes.CDLL:
         h.q4gsw_route_name.restype = ctypes.c_char_p
         h.q4gsw_status_str.argtypes = [i32]
         h.q4gsw_status_str.restype = ctypes.c_char_p
-        h.q4gsw_force_route.argtypes = [i32]
-        h.q4gsw_force_route.restype = None
         h.q4gsw_layout_version.argtypes = []
         h.q4gsw_layout_version.restype = ctypes.c_uint32
         h.q4gsw_build_info.argtypes = []
@@ -116,6 +138,17 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     return t.contiguous()
+
+
+def _out(out: Optional[torch.Tensor], shape: Tuple[int, ...], device, name: str) -> torch.Tensor:
+    """A caller's output tensor, checked against what the kernels write (contiguous fp32 of
+    exactly `shape` on `device`), or a new one."""
+    if out is None:
+        return torch.empty(*shape, dtype=torch.float32, device=device)
+    if (out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != tuple(shape)
+            or out.device != device):
+        raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {list(shape)} on {device}")
+    return out
 
 
 class PackedWeight:
@@ -189,9 +222,18 @@ def _workspace(nbytes: int, device) -> Tuple[Optional[torch.Tensor], int, int]:
 
 def workspace_bytes(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> int:
     out = ctypes.c_uint64()
-    _check(lib().q4gsw_workspace_bytes(op, w.ref(), M, _TORCH_DTYPE[dtype], ctypes.byref(out)),
+    _check(lib().q4gsw_workspace_bytes_ex(op, w.ref(), M, _TORCH_DTYPE[dtype], _opts(), ctypes.byref(out)),
            "q4gsw_workspace_bytes")
     return out.value
+
+
+def _ws_args(need: int, workspace: Optional[torch.Tensor], device):
+    """(tensor kept alive, pointer, bytes): the caller's workspace when it is a large enough uint8
+    tensor on `device`, else a new one."""
+    if workspace is not None and workspace.dtype == torch.uint8 and workspace.is_contiguous() \
+            and workspace.device == device and workspace.numel() >= need:
+        return workspace, workspace.data_ptr(), workspace.numel()
+    return _workspace(need, device)
 
 
 def linear_fwd(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None,
@@ -201,14 +243,11 @@ def linear_fwd(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = N
     if x.dim() != 2 or x.shape[1] != w.K:
         raise ValueError("x must be [M, K]")
     M = x.shape[0]
-    y = out if out is not None else torch.empty(M, w.N, dtype=torch.float32, device=x.device)
+    y = _out(out, (M, w.N), x.device, "out")
     need = workspace_bytes(OP_FWD, w, M, x.dtype)
-    if workspace is not None and workspace.numel() >= need:
-        ws, wp, wb = workspace, workspace.data_ptr(), workspace.numel()
-    else:
-        ws, wp, wb = _workspace(need, x.device)
-    _check(lib().q4gsw_linear_fwd(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), wp, wb,
-                                  _stream()), "q4gsw_linear_fwd")
+    ws, wp, wb = _ws_args(need, workspace, x.device)
+    _check(lib().q4gsw_linear_fwd_ex(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), wp, wb,
+                                     _opts(), _stream()), "q4gsw_linear_fwd")
     return y
 
 
@@ -219,14 +258,11 @@ def linear_bwd_input(w: PackedWeight, d_out: torch.Tensor, out: Optional[torch.T
     if d_out.dim() != 2 or d_out.shape[1] != w.N:
         raise ValueError("d_out must be [M, N]")
     M = d_out.shape[0]
-    dx = out if out is not None else torch.empty(M, w.K, dtype=torch.float32, device=d_out.device)
+    dx = _out(out, (M, w.K), d_out.device, "out")
     need = workspace_bytes(OP_BWD_INPUT, w, M, d_out.dtype)
-    if workspace is not None and workspace.numel() >= need:
-        ws, wp, wb = workspace, workspace.data_ptr(), workspace.numel()
-    else:
-        ws, wp, wb = _workspace(need, d_out.device)
-    _check(lib().q4gsw_linear_bwd_input(w.ref(), d_out.data_ptr(), _TORCH_DTYPE[d_out.dtype], M, dx.data_ptr(),
-                                        wp, wb, _stream()), "q4gsw_linear_bwd_input")
+    ws, wp, wb = _ws_args(need, workspace, d_out.device)
+    _check(lib().q4gsw_linear_bwd_input_ex(w.ref(), d_out.data_ptr(), _TORCH_DTYPE[d_out.dtype], M,
+                                           dx.data_ptr(), wp, wb, _opts(), _stream()), "q4gsw_linear_bwd_input")
     return dx
 
 
@@ -245,8 +281,8 @@ def embedding(w: PackedWeight, ids: torch.Tensor, out: Optional[torch.Tensor] = 
 
 def qkv_workspace_bytes(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, M: int, dtype: torch.dtype) -> int:
     out = ctypes.c_uint64()
-    _check(lib().q4gsw_qkv_workspace_bytes(wq.ref(), wk.ref(), wv.ref(), M, _TORCH_DTYPE[dtype],
-                                           ctypes.byref(out)), "q4gsw_qkv_workspace_bytes")
+    _check(lib().q4gsw_qkv_workspace_bytes_ex(wq.ref(), wk.ref(), wv.ref(), M, _TORCH_DTYPE[dtype], _opts(),
+                                              ctypes.byref(out)), "q4gsw_qkv_workspace_bytes")
     return out.value
 
 
@@ -259,20 +295,28 @@ def qkv_fused(wq: PackedWeight, wk: PackedWeight, wv: PackedWeight, x: torch.Ten
         raise ValueError("x must be [M, K]")
     M = x.shape[0]
     if outs is None:
-        outs = tuple(torch.empty(M, w.N, dtype=torch.float32, device=x.device) for w in (wq, wk, wv))
+        outs = (None, None, None)
+    if len(outs) != 3:
+        raise ValueError("outs must be three tensors (q, k, v)")
+    q, k, v = (_out(o, (M, w.N), x.device, name) for o, w, name in zip(outs, (wq, wk, wv), ("q", "k", "v")))
     need = qkv_workspace_bytes(wq, wk, wv, M, x.dtype)
-    if workspace is not None and workspace.numel() >= need:
-        ws, wp, wb = workspace, workspace.data_ptr(), workspace.numel()
-    else:
-        ws, wp, wb = _workspace(need, x.device)
-    q, k, v = outs
-    _check(lib().q4gsw_qkv_fused(wq.ref(), wk.ref(), wv.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M,
-                                 q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, wb, _stream()), "q4gsw_qkv_fused")
+    ws, wp, wb = _ws_args(need, workspace, x.device)
+    _check(lib().q4gsw_qkv_fused_ex(wq.ref(), wk.ref(), wv.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M,
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, wb, _opts(), _stream()),
+           "q4gsw_qkv_fused")
     return q, k, v
 
 
 def route(op: int, w: PackedWeight, M: int, dtype: torch.dtype) -> str:
-    return route_name(lib().q4gsw_route(op, w.ref(), M, _TORCH_DTYPE[dtype]))
+    """The route a call with these arguments takes (under this thread's forced route, if any).  For
+    OP_QKV the route depends on Wq only."""
+    o = _opts()
+    if o is None:
+        return route_name(lib().q4gsw_route(op, w.ref(), M, _TORCH_DTYPE[dtype]))
+    info = PlanInfo()
+    extra = w.ref() if op == OP_QKV else None
+    _check(lib().q4gsw_plan(op, w.ref(), extra, extra, M, _TORCH_DTYPE[dtype], o, ctypes.byref(info)), "q4gsw_plan")
+    return route_name(info.route)
 
 
 def plan(op: int, w: PackedWeight, M: int, dtype: torch.dtype, wk: PackedWeight = None,
@@ -281,29 +325,44 @@ def plan(op: int, w: PackedWeight, M: int, dtype: torch.dtype, wk: PackedWeight 
     and wv."""
     info = PlanInfo()
     refs = [x.ref() if x is not None else None for x in (wk, wv)]
-    _check(lib().q4gsw_plan(op, w.ref(), refs[0], refs[1], M, _TORCH_DTYPE[dtype], ctypes.byref(info)), "q4gsw_plan")
+    _check(lib().q4gsw_plan(op, w.ref(), refs[0], refs[1], M, _TORCH_DTYPE[dtype], _opts(), ctypes.byref(info)),
+           "q4gsw_plan")
     return {"route": route_name(info.route), "tile_rows": info.tile_rows, "splits": info.splits}
 
 
 @contextlib.contextmanager
-def forced_plan(tile_rows: int = 0, splits: int = 0):
-    """Force the forward / QKV MFMA block rows (64 or 128) and the contraction splits (the split
-    count also governs the 32x32 input-gradient routes); 0 leaves a choice per shape."""
-    _check(lib().q4gsw_force_plan(tile_rows, splits), "q4gsw_force_plan")
+def _with_options(**fields):
+    """Set fields of this thread's per-call options for the calls inside the block."""
+    old = getattr(_local, "opts", None)
+    new = Options()
+    if old is not None:
+        ctypes.memmove(ctypes.byref(new), ctypes.byref(old), ctypes.sizeof(Options))
+    for k, v in fields.items():
+        setattr(new, k, v)
+    _local.opts = new
     try:
         yield
     finally:
-        lib().q4gsw_force_plan(0, 0)
+        _local.opts = old
+
+
+@contextlib.contextmanager
+def forced_plan(tile_rows: int = 0, splits: int = 0):
+    """Pin the forward / QKV MFMA block rows (64 or 128) and the contraction splits (the split
+    count also governs the 32x32 input-gradient routes) of the calls made by this thread inside the
+    block; 0 leaves a choice per shape.  Out-of-range values raise ValueError."""
+    if tile_rows not in (0, 64, 128) or not 0 <= splits <= 64:
+        raise ValueError("tile_rows must be 0, 64 or 128 and splits 0..64")
+    with _with_options(tile_rows=tile_rows, splits=splits):
+        yield
 
 
 @contextlib.contextmanager
 def forced_route(name: str):
-    """Force every call inside the block onto one route family (tests and benchmarks)."""
-    lib().q4gsw_force_route(ROUTES[name])
-    try:
+    """Send the calls made by this thread inside the block onto one route family (tests and
+    benchmarks); a call the family cannot serve raises Q4gswError with E_ROUTE."""
+    with _with_options(route=ROUTES[name]):
         yield
-    finally:
-        lib().q4gsw_force_route(0)
 
 
 def build_info() -> str:

@@ -7,7 +7,6 @@
 // body in the same stack): q4gsw_route reports the route a call takes.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstring>
 
 #include "../../include/q4gsw.h"
@@ -20,7 +19,24 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxM = int64_t(1) << 23;
 
-std::atomic<int32_t> g_forced_route{Q4GSW_ROUTE_NONE};
+// Per-call choices (q4gsw_options), validated: route family, forward block rows, K splits.
+struct Opts {
+    int32_t route = Q4GSW_ROUTE_NONE;
+    int32_t rows = 0;
+    int32_t splits = 0;
+};
+
+q4gsw_status read_opts(const q4gsw_options* o, Opts* out) {
+    *out = Opts{};
+    if (!o) return Q4GSW_OK;
+    if (o->route < Q4GSW_ROUTE_NONE || o->route > Q4GSW_ROUTE_QKV_FUSED) return Q4GSW_E_ROUTE;
+    if (o->tile_rows != 0 && o->tile_rows != 64 && o->tile_rows != 128) return Q4GSW_E_SHAPE;
+    if (o->splits < 0 || o->splits > 64) return Q4GSW_E_SHAPE;
+    out->route = o->route;
+    out->rows = o->tile_rows;
+    out->splits = o->splits;
+    return Q4GSW_OK;
+}
 
 int esize(int32_t dt) { return dt == Q4GSW_F32 ? 4 : 2; }
 bool act_dtype_ok(int32_t dt) { return dt == Q4GSW_F32 || dt == Q4GSW_F16 || dt == Q4GSW_BF16; }
@@ -78,7 +94,7 @@ Kind route_kind(int32_t route) {
 }
 
 // Route of a forward (or QKV) call; Q4GSW_ROUTE_NONE with *err set when a forced route cannot serve it.
-int32_t pick_fwd(const q4gsw_weight* w, int64_t M, int32_t dt, bool qkv, q4gsw_status* err) {
+int32_t pick_fwd(const q4gsw_weight* w, int64_t M, int32_t dt, bool qkv, int32_t forced, q4gsw_status* err) {
     const WView v = view_of(w);
     const bool small_ok = M <= 8 && w->group_size % 8 == 0;
     const bool mfma_ok = gemm_fwd_supported(v, dt, fold_ok(w));
@@ -89,7 +105,6 @@ int32_t pick_fwd(const q4gsw_weight* w, int64_t M, int32_t dt, bool qkv, q4gsw_s
         return Q4GSW_ROUTE_GEMM_GROUP;
     };
     *err = Q4GSW_OK;
-    const int32_t forced = g_forced_route.load(std::memory_order_relaxed);
     if (forced != Q4GSW_ROUTE_NONE) {
         switch (route_kind(forced)) {
             case kGeneric: return Q4GSW_ROUTE_GENERIC;
@@ -108,14 +123,13 @@ int32_t pick_fwd(const q4gsw_weight* w, int64_t M, int32_t dt, bool qkv, q4gsw_s
     return Q4GSW_ROUTE_GENERIC;
 }
 
-int32_t pick_bwd(const q4gsw_weight* w, int64_t M, int32_t dt, q4gsw_status* err) {
+int32_t pick_bwd(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t forced, q4gsw_status* err) {
     const WView v = view_of(w);
     const bool small_ok = M <= 8 && w->group_size % 8 == 0;
     const bool mfma_ok = gemm_bwd_supported(v, dt, fold_ok(w));
     const bool fold = dt == Q4GSW_F16 && w->scale_dtype == Q4GSW_F16 && fold_ok(w);
     const int32_t mfma_route = fold ? Q4GSW_ROUTE_BWD_FOLD : Q4GSW_ROUTE_BWD_SPLIT;
     *err = Q4GSW_OK;
-    const int32_t forced = g_forced_route.load(std::memory_order_relaxed);
     if (forced != Q4GSW_ROUTE_NONE) {
         switch (route_kind(forced)) {
             case kGeneric: return Q4GSW_ROUTE_GENERIC;
@@ -134,7 +148,7 @@ int32_t pick_bwd(const q4gsw_weight* w, int64_t M, int32_t dt, q4gsw_status* err
     return Q4GSW_ROUTE_GENERIC;
 }
 
-uint64_t fwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t route) {
+uint64_t fwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t route, const Opts& o) {
     const WView v = view_of(w);
     if (route == Q4GSW_ROUTE_GEMV) {
         const int s = gemv_fwd_splits(v, M);
@@ -142,19 +156,19 @@ uint64_t fwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t rout
     }
     if (route == Q4GSW_ROUTE_GEMM_FOLD || route == Q4GSW_ROUTE_GEMM_GROUP || route == Q4GSW_ROUTE_GEMM_SPLIT) {
         FwdSeg seg{v, nullptr};
-        return (uint64_t)plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M).ws_bytes;
+        return (uint64_t)plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M, o.rows, o.splits).ws_bytes;
     }
     return 0;
 }
 
-uint64_t bwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t route) {
+uint64_t bwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t route, const Opts& o) {
     const WView v = view_of(w);
     if (route == Q4GSW_ROUTE_BWD_GEMV) {
         const int s = gemv_bwd_splits(v, M);
         return s > 1 ? (uint64_t)s * M * v.k_pad * 4 : 0;
     }
     if (route == Q4GSW_ROUTE_BWD_FOLD || route == Q4GSW_ROUTE_BWD_SPLIT)
-        return (uint64_t)plan_gemm_bwd(v, dt, fold_ok(w), M).ws_bytes;
+        return (uint64_t)plan_gemm_bwd(v, dt, fold_ok(w), M, o.splits).ws_bytes;
     return 0;
 }
 
@@ -172,15 +186,15 @@ q4gsw_status check_qkv_descs(const q4gsw_weight* wq, const q4gsw_weight* wk, con
     return Q4GSW_OK;
 }
 
-uint64_t qkv_ws_bytes(const q4gsw_weight* const w[3], int64_t M, int32_t dt, int32_t route) {
+uint64_t qkv_ws_bytes(const q4gsw_weight* const w[3], int64_t M, int32_t dt, int32_t route, const Opts& o) {
     if (route == Q4GSW_ROUTE_QKV_FUSED) {
         FwdSeg segs[3];
         for (int i = 0; i < 3; ++i) segs[i] = FwdSeg{view_of(w[i]), nullptr};
-        return (uint64_t)plan_gemm_fwd(segs, 3, dt, fold_ok(w[0]), M).ws_bytes;
+        return (uint64_t)plan_gemm_fwd(segs, 3, dt, fold_ok(w[0]), M, o.rows, o.splits).ws_bytes;
     }
     uint64_t b = 0;
     for (int i = 0; i < 3; ++i) {
-        const uint64_t x = fwd_ws_bytes(w[i], M, dt, route);
+        const uint64_t x = fwd_ws_bytes(w[i], M, dt, route, o);
         b = x > b ? x : b;
     }
     return b;
@@ -189,7 +203,7 @@ uint64_t qkv_ws_bytes(const q4gsw_weight* const w[3], int64_t M, int32_t dt, int
 q4gsw_status hip_status(hipError_t e) { return e == hipSuccess ? Q4GSW_OK : Q4GSW_E_HIP; }
 
 q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M, float* y, void* ws,
-                     int32_t route, hipStream_t s) {
+                     int32_t route, const Opts& o, hipStream_t s) {
     const WView v = view_of(w);
     switch (route) {
         case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_fwd(v, x, dt, M, y, s));
@@ -203,10 +217,43 @@ q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M
         }
         default: {
             FwdSeg seg{v, y};
-            const FwdPlan plan = plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M);
+            const FwdPlan plan = plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M, o.rows, o.splits);
             return hip_status(launch_gemm_fwd(&seg, 1, x, dt, M, plan, static_cast<float*>(ws), s));
         }
     }
+}
+
+bool ws_ok(const void* ws, uint64_t ws_bytes, uint64_t need) {
+    return need == 0 || (ws && ws_bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0);
+}
+
+// Forward validation shared by q4gsw_linear_fwd_ex and the allocation-free forward: descriptor,
+// pointers, sizes, dtype and route; *route and *need are set on success.
+q4gsw_status prepare_fwd(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, const float* y,
+                         const Opts& o, int32_t* route, uint64_t* need) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!x || !y) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
+    *route = pick_fwd(w, M, x_dtype, false, o.route, &st);
+    if (st != Q4GSW_OK) return st;
+    *need = fwd_ws_bytes(w, M, x_dtype, *route, o);
+    return Q4GSW_OK;
+}
+
+// Overlap checks of a forward call whose workspace is ws[0, need).
+q4gsw_status fwd_alias(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, const float* y,
+                       const void* ws, uint64_t need) {
+    const Range yr = range_of(y, (uint64_t)M * w->N * 4);
+    const Range xr = range_of(x, (uint64_t)M * w->K * esize(x_dtype));
+    const Range wr = range_of(w->data, w->bytes);
+    if (overlap(yr, xr) || overlap(yr, wr)) return Q4GSW_E_ALIAS;
+    if (need > 0) {
+        const Range sr = range_of(ws, need);
+        if (overlap(yr, sr) || overlap(sr, wr) || overlap(sr, xr)) return Q4GSW_E_ALIAS;
+    }
+    return Q4GSW_OK;
 }
 
 }  // namespace
@@ -276,71 +323,87 @@ q4gsw_status q4gsw_unpack(const q4gsw_weight* w, uint8_t* codes, void* scales, v
     return hip_status(e);
 }
 
-q4gsw_status q4gsw_workspace_bytes(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype, uint64_t* bytes) {
+q4gsw_status q4gsw_workspace_bytes_ex(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype,
+                                      const q4gsw_options* opts, uint64_t* bytes) {
     if (!bytes) return Q4GSW_E_NULL;
     q4gsw_status st = check_desc(w);
     if (st != Q4GSW_OK) return st;
     if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
     if (!act_dtype_ok(act_dtype)) return Q4GSW_E_DTYPE;
+    Opts o;
+    if ((st = read_opts(opts, &o)) != Q4GSW_OK) return st;
     if (op == Q4GSW_OP_FWD) {
-        const int32_t r = pick_fwd(w, M, act_dtype, false, &st);
+        const int32_t r = pick_fwd(w, M, act_dtype, false, o.route, &st);
         if (st != Q4GSW_OK) return st;
-        *bytes = fwd_ws_bytes(w, M, act_dtype, r);
+        *bytes = fwd_ws_bytes(w, M, act_dtype, r, o);
         return Q4GSW_OK;
     }
     if (op == Q4GSW_OP_BWD_INPUT) {
-        const int32_t r = pick_bwd(w, M, act_dtype, &st);
+        const int32_t r = pick_bwd(w, M, act_dtype, o.route, &st);
         if (st != Q4GSW_OK) return st;
-        *bytes = bwd_ws_bytes(w, M, act_dtype, r);
+        *bytes = bwd_ws_bytes(w, M, act_dtype, r, o);
         return Q4GSW_OK;
     }
     return Q4GSW_E_SHAPE;
 }
 
-q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv,
-                                       int64_t M, int32_t x_dtype, uint64_t* bytes) {
+q4gsw_status q4gsw_workspace_bytes(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype, uint64_t* bytes) {
+    return q4gsw_workspace_bytes_ex(op, w, M, act_dtype, nullptr, bytes);
+}
+
+q4gsw_status q4gsw_qkv_workspace_bytes_ex(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv,
+                                          int64_t M, int32_t x_dtype, const q4gsw_options* opts, uint64_t* bytes) {
     if (!bytes) return Q4GSW_E_NULL;
     q4gsw_status st = check_qkv_descs(wq, wk, wv);
     if (st != Q4GSW_OK) return st;
     if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
     if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
-    const int32_t r = pick_fwd(wq, M, x_dtype, true, &st);
+    Opts o;
+    if ((st = read_opts(opts, &o)) != Q4GSW_OK) return st;
+    const int32_t r = pick_fwd(wq, M, x_dtype, true, o.route, &st);
     if (st != Q4GSW_OK) return st;
     const q4gsw_weight* w3[3] = {wq, wk, wv};
-    *bytes = qkv_ws_bytes(w3, M, x_dtype, r);
+    *bytes = qkv_ws_bytes(w3, M, x_dtype, r, o);
     return Q4GSW_OK;
+}
+
+q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv,
+                                       int64_t M, int32_t x_dtype, uint64_t* bytes) {
+    return q4gsw_qkv_workspace_bytes_ex(wq, wk, wv, M, x_dtype, nullptr, bytes);
+}
+
+q4gsw_status q4gsw_linear_fwd_ex(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y,
+                                 void* ws, uint64_t ws_bytes, const q4gsw_options* opts, void* stream) {
+    Opts o;
+    q4gsw_status st = read_opts(opts, &o);
+    if (st != Q4GSW_OK) return st;
+    int32_t route = Q4GSW_ROUTE_NONE;
+    uint64_t need = 0;
+    if ((st = prepare_fwd(w, x, x_dtype, M, y, o, &route, &need)) != Q4GSW_OK) return st;
+    if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
+    if ((st = fwd_alias(w, x, x_dtype, M, y, ws, need)) != Q4GSW_OK) return st;
+    return run_fwd(w, x, x_dtype, M, y, ws, route, o, static_cast<hipStream_t>(stream));
 }
 
 q4gsw_status q4gsw_linear_fwd(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y, void* ws,
                               uint64_t ws_bytes, void* stream) {
-    q4gsw_status st = check_desc(w);
-    if (st != Q4GSW_OK) return st;
-    if (!x || !y) return Q4GSW_E_NULL;
-    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
-    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
-    const int32_t route = pick_fwd(w, M, x_dtype, false, &st);
-    if (st != Q4GSW_OK) return st;
-    const uint64_t need = fwd_ws_bytes(w, M, x_dtype, route);
-    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)) return Q4GSW_E_WORKSPACE;
-    const Range yr = range_of(y, (uint64_t)M * w->N * 4);
-    if (overlap(yr, range_of(x, (uint64_t)M * w->K * esize(x_dtype))) || overlap(yr, range_of(w->data, w->bytes)) ||
-        (need > 0 && (overlap(yr, range_of(ws, need)) || overlap(range_of(ws, need), range_of(w->data, w->bytes)) ||
-                      overlap(range_of(ws, need), range_of(x, (uint64_t)M * w->K * esize(x_dtype))))))
-        return Q4GSW_E_ALIAS;
-    return run_fwd(w, x, x_dtype, M, y, ws, route, static_cast<hipStream_t>(stream));
+    return q4gsw_linear_fwd_ex(w, x, x_dtype, M, y, ws, ws_bytes, nullptr, stream);
 }
 
-q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M, float* d_x,
-                                    void* ws, uint64_t ws_bytes, void* stream) {
+q4gsw_status q4gsw_linear_bwd_input_ex(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M,
+                                       float* d_x, void* ws, uint64_t ws_bytes, const q4gsw_options* opts,
+                                       void* stream) {
     q4gsw_status st = check_desc(w);
     if (st != Q4GSW_OK) return st;
     if (!d_out || !d_x) return Q4GSW_E_NULL;
     if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
     if (!act_dtype_ok(g_dtype)) return Q4GSW_E_DTYPE;
-    const int32_t route = pick_bwd(w, M, g_dtype, &st);
+    Opts o;
+    if ((st = read_opts(opts, &o)) != Q4GSW_OK) return st;
+    const int32_t route = pick_bwd(w, M, g_dtype, o.route, &st);
     if (st != Q4GSW_OK) return st;
-    const uint64_t need = bwd_ws_bytes(w, M, g_dtype, route);
-    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)) return Q4GSW_E_WORKSPACE;
+    const uint64_t need = bwd_ws_bytes(w, M, g_dtype, route, o);
+    if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
     const Range xr = range_of(d_x, (uint64_t)M * w->K * 4);
     const Range gr = range_of(d_out, (uint64_t)M * w->N * esize(g_dtype));
     if (overlap(xr, gr) || overlap(xr, range_of(w->data, w->bytes)) ||
@@ -360,26 +423,33 @@ q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, in
             return hip_status(e);
         }
         default: {
-            const BwdPlan plan = plan_gemm_bwd(v, g_dtype, fold_ok(w), M);
+            const BwdPlan plan = plan_gemm_bwd(v, g_dtype, fold_ok(w), M, o.splits);
             return hip_status(launch_gemm_bwd(v, d_out, g_dtype, M, d_x, plan, static_cast<float*>(ws), s));
         }
     }
 }
 
-q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, const void* x,
-                             int32_t x_dtype, int64_t M, float* q, float* k, float* v, void* ws, uint64_t ws_bytes,
-                             void* stream) {
+q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M, float* d_x,
+                                    void* ws, uint64_t ws_bytes, void* stream) {
+    return q4gsw_linear_bwd_input_ex(w, d_out, g_dtype, M, d_x, ws, ws_bytes, nullptr, stream);
+}
+
+q4gsw_status q4gsw_qkv_fused_ex(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, const void* x,
+                                int32_t x_dtype, int64_t M, float* q, float* k, float* v, void* ws, uint64_t ws_bytes,
+                                const q4gsw_options* opts, void* stream) {
     q4gsw_status st = check_qkv_descs(wq, wk, wv);
     if (st != Q4GSW_OK) return st;
     if (!x || !q || !k || !v) return Q4GSW_E_NULL;
     if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
     if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
-    const int32_t route = pick_fwd(wq, M, x_dtype, true, &st);
+    Opts o;
+    if ((st = read_opts(opts, &o)) != Q4GSW_OK) return st;
+    const int32_t route = pick_fwd(wq, M, x_dtype, true, o.route, &st);
     if (st != Q4GSW_OK) return st;
     const q4gsw_weight* w3[3] = {wq, wk, wv};
     float* o3[3] = {q, k, v};
-    const uint64_t need = qkv_ws_bytes(w3, M, x_dtype, route);
-    if (need > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)) return Q4GSW_E_WORKSPACE;
+    const uint64_t need = qkv_ws_bytes(w3, M, x_dtype, route, o);
+    if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
     Range outs[3];
     for (int i = 0; i < 3; ++i) outs[i] = range_of(o3[i], (uint64_t)M * w3[i]->N * 4);
     const Range xr = range_of(x, (uint64_t)M * wq->K * esize(x_dtype));
@@ -400,7 +470,7 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, con
     if (route == Q4GSW_ROUTE_QKV_FUSED) {
         FwdSeg segs[3];
         for (int i = 0; i < 3; ++i) segs[i] = FwdSeg{view_of(w3[i]), o3[i]};
-        const FwdPlan plan = plan_gemm_fwd(segs, 3, x_dtype, fold_ok(wq), M);
+        const FwdPlan plan = plan_gemm_fwd(segs, 3, x_dtype, fold_ok(wq), M, o.rows, o.splits);
         return hip_status(launch_gemm_fwd(segs, 3, x, x_dtype, M, plan, static_cast<float*>(ws), s));
     }
     // Decode shapes (M <= 8): the three streaming GEMVs in one launch when none of them splits K,
@@ -413,19 +483,25 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, con
     }
     // Fallback outside the fused predicate: three forwards on the same stream (same contract).
     for (int i = 0; i < 3; ++i) {
-        st = run_fwd(w3[i], x, x_dtype, M, o3[i], ws, route, s);
+        st = run_fwd(w3[i], x, x_dtype, M, o3[i], ws, route, o, s);
         if (st != Q4GSW_OK) return st;
     }
     return Q4GSW_OK;
+}
+
+q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, const void* x,
+                             int32_t x_dtype, int64_t M, float* q, float* k, float* v, void* ws, uint64_t ws_bytes,
+                             void* stream) {
+    return q4gsw_qkv_fused_ex(wq, wk, wv, x, x_dtype, M, q, k, v, ws, ws_bytes, nullptr, stream);
 }
 
 int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype) {
     if (check_desc(w) != Q4GSW_OK || M < 1 || M > kMaxM || !act_dtype_ok(act_dtype)) return Q4GSW_ROUTE_NONE;
     q4gsw_status st;
     int32_t r = Q4GSW_ROUTE_NONE;
-    if (op == Q4GSW_OP_FWD) r = pick_fwd(w, M, act_dtype, false, &st);
-    else if (op == Q4GSW_OP_BWD_INPUT) r = pick_bwd(w, M, act_dtype, &st);
-    else if (op == Q4GSW_OP_QKV) r = pick_fwd(w, M, act_dtype, true, &st);
+    if (op == Q4GSW_OP_FWD) r = pick_fwd(w, M, act_dtype, false, Q4GSW_ROUTE_NONE, &st);
+    else if (op == Q4GSW_OP_BWD_INPUT) r = pick_bwd(w, M, act_dtype, Q4GSW_ROUTE_NONE, &st);
+    else if (op == Q4GSW_OP_QKV) r = pick_fwd(w, M, act_dtype, true, Q4GSW_ROUTE_NONE, &st);
     else return Q4GSW_ROUTE_NONE;
     return st == Q4GSW_OK ? r : Q4GSW_ROUTE_NONE;
 }
@@ -442,12 +518,20 @@ q4gsw_status q4gsw_embedding(const q4gsw_weight* w, const int64_t* ids, int64_t 
 }
 
 q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* wk, const q4gsw_weight* wv,
-                        int64_t M, int32_t act_dtype, q4gsw_plan_info* info) {
+                        int64_t M, int32_t act_dtype, const q4gsw_options* opts, q4gsw_plan_info* info) {
     if (!info) return Q4GSW_E_NULL;
     *info = q4gsw_plan_info{Q4GSW_ROUTE_NONE, 0, 1};
     q4gsw_status st = op == Q4GSW_OP_QKV ? check_qkv_descs(w, wk, wv) : check_desc(w);
     if (st != Q4GSW_OK) return st;
-    const int32_t r = q4gsw_route(op, w, M, act_dtype);
+    Opts o;
+    if ((st = read_opts(opts, &o)) != Q4GSW_OK) return st;
+    if (M < 1 || M > kMaxM || !act_dtype_ok(act_dtype)) return Q4GSW_OK;
+    int32_t r = Q4GSW_ROUTE_NONE;
+    q4gsw_status rs = Q4GSW_OK;
+    if (op == Q4GSW_OP_FWD) r = pick_fwd(w, M, act_dtype, false, o.route, &rs);
+    else if (op == Q4GSW_OP_BWD_INPUT) r = pick_bwd(w, M, act_dtype, o.route, &rs);
+    else if (op == Q4GSW_OP_QKV) r = pick_fwd(w, M, act_dtype, true, o.route, &rs);
+    if (rs != Q4GSW_OK) r = Q4GSW_ROUTE_NONE;
     info->route = r;
     if (r == Q4GSW_ROUTE_NONE) return Q4GSW_OK;
     const WView v = view_of(w);
@@ -457,7 +541,7 @@ q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* w
         info->splits = gemv_bwd_splits(v, M);
     } else if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT) {
         info->tile_rows = 128;
-        info->splits = plan_gemm_bwd(v, act_dtype, fold_ok(w), M).splits;
+        info->splits = plan_gemm_bwd(v, act_dtype, fold_ok(w), M, o.splits).splits;
     } else if (r == Q4GSW_ROUTE_GEMM_FOLD || r == Q4GSW_ROUTE_GEMM_GROUP || r == Q4GSW_ROUTE_GEMM_SPLIT ||
                r == Q4GSW_ROUTE_QKV_FUSED) {
         FwdSeg segs[3] = {FwdSeg{v, nullptr}, FwdSeg{}, FwdSeg{}};
@@ -467,7 +551,7 @@ q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* w
             segs[2] = FwdSeg{view_of(wv), nullptr};
             nseg = 3;
         }
-        const FwdPlan p = plan_gemm_fwd(segs, nseg, act_dtype, fold_ok(w), M);
+        const FwdPlan p = plan_gemm_fwd(segs, nseg, act_dtype, fold_ok(w), M, o.rows, o.splits);
         info->tile_rows = 32 * p.mi;
         info->splits = p.splits;
     }
@@ -503,18 +587,9 @@ const char* q4gsw_status_str(int32_t status) {
         case Q4GSW_E_DESC: return "invalid or mismatched weight descriptor";
         case Q4GSW_E_HIP: return "HIP runtime error";
         case Q4GSW_E_BUFFER: return "packed buffer too small";
-        case Q4GSW_E_ROUTE: return "forced route cannot serve this call";
+        case Q4GSW_E_ROUTE: return "requested route cannot serve this call";
         default: return "unknown status";
     }
-}
-
-void q4gsw_force_route(int32_t route) { g_forced_route.store(route, std::memory_order_relaxed); }
-
-q4gsw_status q4gsw_force_plan(int32_t tile_rows, int32_t splits) {
-    if (tile_rows != 0 && tile_rows != 64 && tile_rows != 128) return Q4GSW_E_SHAPE;
-    if (splits < 0 || splits > 64) return Q4GSW_E_SHAPE;
-    set_forced_fwd_plan(tile_rows, splits);
-    return Q4GSW_OK;
 }
 
 uint32_t q4gsw_layout_version(void) { return Q4GSW_LAYOUT_VERSION; }

@@ -663,7 +663,7 @@ bool gemm_bwd_supported(const WView& w, int g_dtype, int fold_ok) {
     return v2_supported(w, g_dtype, fold_ok) || gemm_bwd_v1_supported(w, g_dtype, fold_ok);
 }
 
-BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M) {
+BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M, int force_splits) {
     if (!v2_supported(w, g_dtype, fold_ok)) {
         BwdPlan p = plan_gemm_bwd_v1(w, g_dtype, fold_ok, M);
         p.v1 = 1;
@@ -673,7 +673,7 @@ BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M) {
     p.mode = v2_fold(w, g_dtype, fold_ok) ? kModeFold : kModeSplit;
     const int64_t blocks = ((w.k_pad + kBK - 1) / kBK) * ((M + kBM - 1) / kBM);
     const int64_t n_chunks = (w.N + kCN - 1) / kCN;
-    p.splits = pick_gemm_splits(blocks, n_chunks, M, w.k_pad, 256, 2.0, nullptr, forced_gemm_splits());
+    p.splits = pick_gemm_splits(blocks, n_chunks, M, w.k_pad, 256, 2.0, nullptr, force_splits);
     p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * frag_plane_floats(M, w.k_pad) * 4 : 0;
     p.v1 = 0;
     return p;

@@ -658,15 +658,8 @@ static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int 
     return n;
 }
 
-static std::atomic<int> g_forced_tile_rows{0};
-static std::atomic<int> g_forced_splits{0};
-void set_forced_fwd_plan(int rows, int splits) {
-    g_forced_tile_rows.store(rows, std::memory_order_relaxed);
-    g_forced_splits.store(splits, std::memory_order_relaxed);
-}
-int forced_gemm_splits() { return g_forced_splits.load(std::memory_order_relaxed); }
-
-FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M) {
+FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M, int force_rows,
+                      int force_splits) {
     FwdPlan p{};
     const WView& w0 = segs[0].w;
     if (x_dtype == kF32) p.mode = kModeSplit;
@@ -680,7 +673,7 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
     const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
     const int spc = fwd_spc(w0.gs);
     double best = 1e300;
-    const int forced = g_forced_tile_rows.load(std::memory_order_relaxed);
+    const int forced = force_rows;
     for (int mi : {4, 2}) {
         if (forced == 64 || forced == 128) {
             if (32 * mi != forced) continue;
@@ -695,8 +688,7 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         // inputs favour other split counts).
         const double chunk_us = mi == 4 ? 2.0 : 1.3;
         double cost = 0;
-        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost,
-                                       g_forced_splits.load(std::memory_order_relaxed));
+        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost, force_splits);
         if (cost < best - 1e-9) {
             best = cost;
             p.mi = mi;

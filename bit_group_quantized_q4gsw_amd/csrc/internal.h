@@ -81,12 +81,10 @@ struct FwdPlan {
     int splits;              // K splits (1: write outputs directly)
     int64_t ws_bytes;        // workspace needed
 };
-FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M);
-// Forward plan choices forced for every later plan: block rows (64 or 128) and K splits (> 0);
+// force_rows (64 or 128) and force_splits (> 0) pin the block rows and the K splits of this plan;
 // 0 leaves each to the shape.
-void set_forced_fwd_plan(int rows, int splits);
-// The forced split count (0: none); the 32x32 input-gradient plan takes it too.
-int forced_gemm_splits();
+FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M, int force_rows = 0,
+                      int force_splits = 0);
 // Contraction splits for an MFMA GEMM of `blocks` output blocks, `slots` of which run at once,
 // n_chunks 64-wide contraction chunks of ~chunk_us each and an M x width fp32 output; the
 // modelled time (microseconds) goes to *cost when cost is not null; force_splits > 0 pins the
@@ -106,7 +104,8 @@ struct BwdPlan {
     int v1;                  // 1: the 16x16x32 kernel serves this call
 };
 bool gemm_bwd_supported(const WView& w, int g_dtype, int fold_ok);
-BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M);
+// force_splits > 0 pins the contraction splits of the 32x32 routes (0: chosen per shape).
+BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M, int force_splits = 0);
 hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
                            const BwdPlan& plan, float* ws, hipStream_t s);
 bool gemm_bwd_v1_supported(const WView& w, int g_dtype, int fold_ok);

@@ -1,4 +1,4 @@
-// Packed q4gsw weight layout for gfx950 (layout version 1).
+// Packed q4gsw weight layout for gfx950 (layout version 2, Q4GSW_LAYOUT_VERSION).
 //
 // The pages prepack the weight once and let the backward read the forward's
 // packed buffer without a re-pack (Vulkan q4gsw-backward PR body, "Solution" and

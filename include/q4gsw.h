@@ -29,8 +29,11 @@
  *     asynchronous on it; only q4gsw_pack and q4gsw_unpack synchronize it.
  *   - Outputs are fp32.  Activations may be fp32, fp16 or bf16; scales fp16 or
  *     fp32.  Accumulation is fp32.
- *   - No C++ exception crosses this interface.  The library keeps no mutable
- *     state except the optional route override (q4gsw_force_route).
+ *   - No C++ exception crosses this interface.  Calls are independent: route and
+ *     plan choices are per call (q4gsw_options), never process-wide.  The only
+ *     state the library keeps is a cache of resident blocks per CU for each kernel
+ *     instance (filled on first use from the HIP occupancy query, then read-only;
+ *     a race between threads only repeats the same query).
  */
 #ifndef Q4GSW_H
 #define Q4GSW_H
@@ -57,7 +60,7 @@ typedef enum q4gsw_status {
     Q4GSW_E_DESC = 8,         /* descriptor magic/version/fields invalid, or QKV weights disagree */
     Q4GSW_E_HIP = 9,          /* a HIP runtime call or kernel launch failed */
     Q4GSW_E_BUFFER = 10,      /* packed buffer smaller than q4gsw_packed_bytes */
-    Q4GSW_E_ROUTE = 11        /* a forced route cannot serve this call */
+    Q4GSW_E_ROUTE = 11        /* the route requested in q4gsw_options cannot serve this call */
 } q4gsw_status;
 
 typedef enum q4gsw_dtype {
@@ -85,6 +88,30 @@ typedef enum q4gsw_route_id {
     Q4GSW_ROUTE_BWD_SPLIT = 8,     /* input gradient: d_out*scale split into bf16 hi+lo, two MFMA passes */
     Q4GSW_ROUTE_QKV_FUSED = 9      /* fused QKV: one launch over the three weights */
 } q4gsw_route_id;
+
+/*
+ * Per-call route and plan choice, for tests and benchmarks that compare routes and
+ * plans (the caller picks, q4gsw_plan reports).  All zero, or a NULL pointer,
+ * leaves every choice to the library; the plain calls take none.
+ *   route      Q4GSW_ROUTE_NONE: automatic.  Otherwise the route family to take:
+ *              GENERIC; a small-M route (GEMV, BWD_GEMV); or an MFMA route (any of
+ *              GEMM_FOLD, GEMM_GROUP, GEMM_SPLIT, BWD_FOLD, BWD_SPLIT, QKV_FUSED:
+ *              the library picks the precision route inside the family).  A call
+ *              the family cannot serve returns Q4GSW_E_ROUTE; a value outside the
+ *              enum returns Q4GSW_E_ROUTE too.
+ *   tile_rows  forward / QKV MFMA block rows: 0 (per shape), 64 or 128
+ *              (Q4GSW_E_SHAPE otherwise).
+ *   splits     contraction splits of the 32x32 MFMA GEMMs (forward, QKV and the
+ *              input-gradient routes BWD_FOLD and BWD_SPLIT): 0 (per shape) or
+ *              1..64 (Q4GSW_E_SHAPE otherwise), clamped to the 64-wide chunks and
+ *              rounded to a count with no empty split.
+ * A workspace is sized for the options it is used with (q4gsw_*_workspace_bytes_ex).
+ */
+typedef struct q4gsw_options {
+    int32_t route;
+    int32_t tile_rows;
+    int32_t splits;
+} q4gsw_options;
 
 /*
  * Packed weight descriptor, filled by q4gsw_pack.  Plain data: copy it freely.
@@ -120,7 +147,11 @@ q4gsw_status q4gsw_packed_bytes(int64_t N, int64_t K, int64_t group_size, int32_
 
 /*
  * One-time repack of the codes and scales into the gfx950 layout (the prepack
- * that forward, input gradient and QKV all reuse).
+ * that forward, input gradient and QKV all reuse).  The Vulkan q4gsw-backward
+ * pull request ("Key changes") reuses the forward's prepacked weight and scales
+ * in the backward with no re-pack, and the WebGPU BK64 QKV pull request body
+ * packs the constant weights and scales once; this call is that one packing step,
+ * into a layout of this library's own.
  *   codes   device, uint8 [N, K], one code (0..15) per byte
  *   scales  device, [K / group_size, N] in scale_dtype (Q4GSW_F16 or Q4GSW_F32)
  *   packed  device, at least q4gsw_packed_bytes(...) bytes; overwritten
@@ -134,7 +165,11 @@ q4gsw_status q4gsw_pack(const uint8_t *codes, const void *scales, int32_t scale_
                         void *packed, uint64_t packed_bytes, void *stream, q4gsw_weight *out);
 
 /* The exact inverse of q4gsw_pack: writes codes [N, K] uint8 and scales
- * [K / group_size, N] in the weight's scale dtype.  Synchronizes `stream`. */
+ * [K / group_size, N] in the weight's scale dtype.  Synchronizes `stream`.
+ * It makes the packing of the passages cited at q4gsw_pack checkable: the
+ * packed buffer holds exactly the caller's codes and scales, bit for bit.
+ * E_DESC for a bad descriptor, E_NULL for a null output, E_ALIAS when the
+ * outputs overlap each other or the packed buffer. */
 q4gsw_status q4gsw_unpack(const q4gsw_weight *w, uint8_t *codes, void *scales, void *stream);
 
 /* Device workspace (bytes) the call needs; 0 when its route needs none.  Pure host.  A workspace
@@ -145,6 +180,12 @@ q4gsw_status q4gsw_workspace_bytes(int32_t op, const q4gsw_weight *w, int64_t M,
 q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight *wq, const q4gsw_weight *wk,
                                        const q4gsw_weight *wv, int64_t M, int32_t x_dtype,
                                        uint64_t *bytes);
+/* The same sizes for a call made with `opts` (NULL: as above). */
+q4gsw_status q4gsw_workspace_bytes_ex(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype,
+                                      const q4gsw_options *opts, uint64_t *bytes);
+q4gsw_status q4gsw_qkv_workspace_bytes_ex(const q4gsw_weight *wq, const q4gsw_weight *wk,
+                                          const q4gsw_weight *wv, int64_t M, int32_t x_dtype,
+                                          const q4gsw_options *opts, uint64_t *bytes);
 
 /*
  * Forward: y[M, N] (fp32) = x[M, K] . dequant(W)^T.
@@ -155,6 +196,10 @@ q4gsw_status q4gsw_qkv_workspace_bytes(const q4gsw_weight *wq, const q4gsw_weigh
  */
 q4gsw_status q4gsw_linear_fwd(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M,
                               float *y, void *ws, uint64_t ws_bytes, void *stream);
+/* q4gsw_linear_fwd with per-call options (NULL: the same call). */
+q4gsw_status q4gsw_linear_fwd_ex(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M,
+                                 float *y, void *ws, uint64_t ws_bytes, const q4gsw_options *opts,
+                                 void *stream);
 
 /*
  * Input gradient: d_x[M, K] (fp32) = d_out[M, N] . dequant(W), contracting over N.
@@ -164,6 +209,10 @@ q4gsw_status q4gsw_linear_fwd(const q4gsw_weight *w, const void *x, int32_t x_dt
 q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight *w, const void *d_out, int32_t g_dtype,
                                     int64_t M, float *d_x, void *ws, uint64_t ws_bytes,
                                     void *stream);
+/* q4gsw_linear_bwd_input with per-call options (NULL: the same call). */
+q4gsw_status q4gsw_linear_bwd_input_ex(const q4gsw_weight *w, const void *d_out, int32_t g_dtype,
+                                       int64_t M, float *d_x, void *ws, uint64_t ws_bytes,
+                                       const q4gsw_options *opts, void *stream);
 
 /*
  * Fused QKV: q = x . dequant(Wq)^T, k = x . dequant(Wk)^T, v = x . dequant(Wv)^T.
@@ -177,6 +226,11 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight *wq, const q4gsw_weight *wk, con
                              const void *x, int32_t x_dtype, int64_t M,
                              float *q, float *k, float *v, void *ws, uint64_t ws_bytes,
                              void *stream);
+/* q4gsw_qkv_fused with per-call options (NULL: the same call). */
+q4gsw_status q4gsw_qkv_fused_ex(const q4gsw_weight *wq, const q4gsw_weight *wk, const q4gsw_weight *wv,
+                                const void *x, int32_t x_dtype, int64_t M,
+                                float *q, float *k, float *v, void *ws, uint64_t ws_bytes,
+                                const q4gsw_options *opts, void *stream);
 
 /*
  * Embedding row gather: out[t, k] = dequant(W)[ids[t], k], for t < T and k < K.
@@ -196,17 +250,21 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight *wq, const q4gsw_weight *wk, con
 q4gsw_status q4gsw_embedding(const q4gsw_weight *w, const int64_t *ids, int64_t T, float *out,
                              void *stream);
 
-/* Route attestation: the q4gsw_route_id a call with these arguments takes
- * (Q4GSW_ROUTE_NONE if it would fail validation).  For Q4GSW_OP_QKV pass Wq. */
+/* Route attestation: the q4gsw_route_id a plain call (no options) with these
+ * arguments takes (Q4GSW_ROUTE_NONE if it would fail validation).  For
+ * Q4GSW_OP_QKV pass Wq.  This is the attestation of the WebGPU SDPA routing pull
+ * request in the BK64 QKV stack, which reports the route a shape takes so a test
+ * harness can tell which kernel served it.  Pure host function. */
 int32_t q4gsw_route(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype);
 const char *q4gsw_route_name(int32_t route);
 
-/* Plan attestation for tests and benchmarks: how a call with these arguments runs.
- * For Q4GSW_OP_QKV pass the three weights (wk, wv are ignored for the other ops and
- * may be NULL).  Host only, no GPU work; the forward plan weighs the resident blocks
- * per CU of the current device.  Returns Q4GSW_E_NULL without `info` and the
- * validation status of the descriptors otherwise; a call that would fail validation
- * reports route Q4GSW_ROUTE_NONE. */
+/* Plan attestation for tests and benchmarks: how a call with these arguments and
+ * `opts` (NULL: none) runs.  For Q4GSW_OP_QKV pass the three weights (wk, wv are
+ * ignored for the other ops and may be NULL).  Host only, no GPU work; the forward
+ * plan weighs the resident blocks per CU of the current device.  Returns
+ * Q4GSW_E_NULL without `info`, the validation status of the descriptors and of
+ * `opts`, else Q4GSW_OK; a call that would fail validation (or that the requested
+ * route cannot serve) reports route Q4GSW_ROUTE_NONE. */
 typedef struct q4gsw_plan_info {
     int32_t route;          /* as q4gsw_route */
     int32_t tile_rows;      /* rows (M) of the MFMA block tile (forward / QKV: 128 or 64;
@@ -215,23 +273,9 @@ typedef struct q4gsw_plan_info {
                                launch sums the fp32 partials in split order) */
 } q4gsw_plan_info;
 q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight *w, const q4gsw_weight *wk, const q4gsw_weight *wv,
-                        int64_t M, int32_t act_dtype, q4gsw_plan_info *info);
+                        int64_t M, int32_t act_dtype, const q4gsw_options *opts, q4gsw_plan_info *info);
 
 const char *q4gsw_status_str(int32_t status);
-
-/* Force every later call to take `route` (Q4GSW_ROUTE_NONE restores automatic
- * routing).  A call the forced route cannot serve returns E_ROUTE.  Process-wide
- * and not synchronized: for tests and benchmarks that compare routes. */
-void q4gsw_force_route(int32_t route);
-
-/* Force the forward / QKV MFMA plan for every later call: tile_rows 64 or 128 and
- * splits 1..64 contraction splits (clamped to the 64-column chunks and rounded to a
- * count with no empty split; the split count also governs the 32x32 input-gradient
- * routes bwd_fold and bwd_split); 0 leaves each to the shape.  Other values return
- * Q4GSW_E_SHAPE and change nothing.  Process-wide and not synchronized, like
- * q4gsw_force_route: set it before sizing the workspace of the calls it should govern
- * (for tests and benchmarks that compare plans). */
-q4gsw_status q4gsw_force_plan(int32_t tile_rows, int32_t splits);
 
 /* Layout version and a build identifier string. */
 uint32_t q4gsw_layout_version(void);

@@ -1,4 +1,4 @@
-"""A plain numpy statement of the packed-weight byte layout (layout version 1).
+"""A plain numpy statement of the packed-weight byte layout (layout version 2).
 
 Used only to check, byte for byte, what the GPU pack kernel writes.  The layout:
   header            256 bytes

@@ -112,8 +112,15 @@ def test_fake_descriptor_matches_packed_bytes(q):
         assert packed_bytes(q, N, K, gs, sdt) == (S_OK, d.bytes)
 
 
-def route(q, op, d, M, dt):
-    return q.route_name(q.lib().q4gsw_route(op, ctypes.byref(d), M, dt))
+def route(q, op, d, M, dt, forced=None):
+    """The route of a plain call, or (forced = a route name) of a call with that route option."""
+    if forced is None:
+        return q.route_name(q.lib().q4gsw_route(op, ctypes.byref(d), M, dt))
+    o = q.binding.Options(q.ROUTES[forced], 0, 0)
+    extra = ctypes.byref(d) if op == q.OP_QKV else None
+    st, info = plan_info(q, op, d, M, dt, extra, extra, opts=o)
+    assert st == S_OK
+    return q.route_name(info.route)
 
 
 def test_route_selection(q):
@@ -148,18 +155,77 @@ def test_route_selection(q):
 
 
 def test_forced_routes(q):
+    """A route option sends one call onto a route family; the next plain call is unaffected (the
+    library keeps no routing state)."""
     dec = fake_desc(q, 8192, 2048, 32, 1, flags=1)
-    with q.forced_route("generic"):
-        assert route(q, q.OP_FWD, dec, 1, q.F16) == "generic"
-        assert route(q, q.OP_BWD_INPUT, dec, 512, q.F32) == "generic"
-    with q.forced_route("gemv"):
-        assert route(q, q.OP_FWD, dec, 8, q.F16) == "gemv"
-        assert route(q, q.OP_FWD, dec, 9, q.F16) == "none"          # the small-M kernels stop at M = 8
-        assert route(q, q.OP_BWD_INPUT, dec, 3, q.F16) == "bwd_gemv"
-    with q.forced_route("gemm_fold"):
-        assert route(q, q.OP_FWD, dec, 1, q.F16) == "gemm_fold"
-        assert route(q, q.OP_FWD, dec, 1, q.BF16) == "gemm_group"
+    assert route(q, q.OP_FWD, dec, 1, q.F16, forced="generic") == "generic"
+    assert route(q, q.OP_BWD_INPUT, dec, 512, q.F32, forced="generic") == "generic"
+    assert route(q, q.OP_FWD, dec, 8, q.F16, forced="gemv") == "gemv"
+    assert route(q, q.OP_FWD, dec, 9, q.F16, forced="gemv") == "none"     # the small-M kernels stop at M = 8
+    assert route(q, q.OP_BWD_INPUT, dec, 3, q.F16, forced="gemv") == "bwd_gemv"
+    assert route(q, q.OP_FWD, dec, 1, q.F16, forced="gemm_fold") == "gemm_fold"
+    assert route(q, q.OP_FWD, dec, 1, q.BF16, forced="gemm_fold") == "gemm_group"
+    assert route(q, q.OP_QKV, dec, 1, q.F16, forced="gemm_fold") == "qkv_fused"
     assert route(q, q.OP_FWD, dec, 1, q.F16) == "gemv"
+
+
+def test_binding_options_are_per_thread(q):
+    """forced_route / forced_plan hold the choice in the calling Python thread only, and restore the
+    enclosing choice on exit."""
+    import threading
+    assert q.binding._opts() is None
+    seen = {}
+    with q.forced_route("generic"):
+        with q.forced_plan(tile_rows=64, splits=3):
+            o = q.binding._local.opts
+            assert (o.route, o.tile_rows, o.splits) == (1, 64, 3)
+            t = threading.Thread(target=lambda: seen.setdefault("other", q.binding._opts()))
+            t.start()
+            t.join()
+        o = q.binding._local.opts
+        assert (o.route, o.tile_rows, o.splits) == (1, 0, 0)
+    assert seen["other"] is None
+    assert q.binding._opts() is None
+    with pytest.raises(ValueError):
+        with q.forced_plan(tile_rows=96):
+            pass
+
+
+def test_options_validation(q):
+    """Out-of-range options are refused before any HIP call: a route outside the enum with E_ROUTE,
+    block rows other than 0 / 64 / 128 and split counts outside 0..64 with E_SHAPE."""
+    lib = q.lib()
+    d = fake_desc(q, 256, 512, 32, 1, flags=1)
+    x, y = FAKE * 8, FAKE * 16
+    for (r, rows, splits), want in [((10, 0, 0), E_ROUTE), ((-1, 0, 0), E_ROUTE), ((0, 96, 0), E_SHAPE),
+                                    ((0, 0, -1), E_SHAPE), ((0, 0, 65), E_SHAPE)]:
+        o = q.binding.Options(r, rows, splits)
+        assert lib.q4gsw_linear_fwd_ex(ctypes.byref(d), x, q.F16, 64, y, None, 0, ctypes.byref(o), None) == want
+        assert lib.q4gsw_linear_bwd_input_ex(ctypes.byref(d), x, q.F16, 64, y, None, 0, ctypes.byref(o),
+                                             None) == want
+        need = ctypes.c_uint64()
+        assert lib.q4gsw_workspace_bytes_ex(q.OP_FWD, ctypes.byref(d), 64, q.F16, ctypes.byref(o),
+                                            ctypes.byref(need)) == want
+        assert plan_info(q, q.OP_FWD, d, 64, q.F16, opts=o)[0] == want
+
+
+def test_binding_rejects_bad_outputs(q):
+    """Every output tensor a caller hands the binding must be what the kernels write: contiguous
+    fp32 of exactly the output shape on the input's device (checked before any library call)."""
+    cpu = torch.device("cpu")
+    good = torch.empty(3, 5, dtype=torch.float32)
+    assert q.binding._out(good, (3, 5), cpu, "out") is good
+    assert q.binding._out(None, (3, 5), cpu, "out").shape == (3, 5)
+    bad = [torch.empty(3, 5, dtype=torch.float16),              # dtype
+           torch.empty(5, 3, dtype=torch.float32).t(),          # strided view
+           torch.empty(3, 4, dtype=torch.float32),              # too small
+           torch.empty(15, dtype=torch.float32),                # right size, wrong shape
+           torch.empty(4, 5, dtype=torch.float32)]              # too large
+    for t in bad:
+        with pytest.raises(ValueError):
+            q.binding._out(t, (3, 5), cpu, "out")
+    with pytest.raises(ValueError):
+        q.binding._out(good, (3, 5), torch.device("cuda", 0), "out")   # another device
 
 
 def test_forward_validation(q):
@@ -190,8 +256,8 @@ def test_forward_validation(q):
     assert f(ctypes.byref(big), x, q.BF16, 512, y, FAKE * 32, need.value - 4, None) == E_WS
     assert f(ctypes.byref(big), x, q.BF16, 512, y, y + 256, need.value, None) == E_ALIAS  # ws overlaps y
     assert f(ctypes.byref(big), x, q.BF16, 512, y, FAKE * 32 + 16, need.value, None) == E_WS  # ws not 256-aligned
-    with q.forced_route("gemv"):
-        assert f(ctypes.byref(d), x, q.F16, 64, y, None, 0, None) == E_ROUTE
+    o = q.binding.Options(q.ROUTES["gemv"], 0, 0)
+    assert lib.q4gsw_linear_fwd_ex(ctypes.byref(d), x, q.F16, 64, y, None, 0, ctypes.byref(o), None) == E_ROUTE
 
 
 def test_backward_and_qkv_validation(q):
@@ -231,23 +297,25 @@ def test_python_wrappers_reject_host_tensors(q):
         q.pack(torch.zeros(4, 8, dtype=torch.uint8), torch.ones(1, 4, dtype=torch.float16), 8)
 
 
-def plan_info(q, op, d, M, dt, dk=None, dv=None):
+def plan_info(q, op, d, M, dt, dk=None, dv=None, opts=None):
     info = q.binding.PlanInfo()
-    refs = [ctypes.byref(x) if x is not None else None for x in (dk, dv)]
-    st = q.lib().q4gsw_plan(op, ctypes.byref(d), refs[0], refs[1], M, dt, ctypes.byref(info))
+    refs = [x if x is None or isinstance(x, type(ctypes.byref(d))) else ctypes.byref(x) for x in (dk, dv)]
+    st = q.lib().q4gsw_plan(op, ctypes.byref(d), refs[0], refs[1], M, dt,
+                            ctypes.byref(opts) if opts is not None else None, ctypes.byref(info))
     return st, info
 
 
 def test_plan_attestation_and_forcing(q):
-    """q4gsw_plan reports the route, block rows and splits; q4gsw_force_plan pins the forward
-    block rows and split count and rejects out-of-range values (host logic only)."""
+    """q4gsw_plan reports the route, block rows and splits; the tile_rows and splits options pin
+    the forward block rows and split count of one call (host logic only)."""
     fold = 1
     pre = fake_desc(q, 2048, 8192, 128, 1, flags=fold)
     st, info = plan_info(q, q.OP_FWD, pre, 512, q.BF16)
     assert st == S_OK and q.route_name(info.route) == "gemm_group"
     assert info.tile_rows in (64, 128) and info.splits >= 1
+    default = (info.tile_rows, info.splits)
     # null info, and a QKV plan without its other two weights
-    assert q.lib().q4gsw_plan(q.OP_FWD, ctypes.byref(pre), None, None, 512, q.BF16, None) == 1   # E_NULL
+    assert q.lib().q4gsw_plan(q.OP_FWD, ctypes.byref(pre), None, None, 512, q.BF16, None, None) == 1   # E_NULL
     st, _ = plan_info(q, q.OP_QKV, pre, 512, q.F16)
     assert st == 1
     dec = fake_desc(q, 8192, 2048, 32, 1, flags=fold)
@@ -256,23 +324,22 @@ def test_plan_attestation_and_forcing(q):
     bwd = fake_desc(q, 8192, 2048, 128, 1, flags=fold)
     st, info = plan_info(q, q.OP_BWD_INPUT, bwd, 512, q.F32)
     assert st == S_OK and q.route_name(info.route) == "bwd_split" and info.tile_rows == 128
-    try:
-        for rows, splits in [(64, 3), (128, 16)]:
-            assert q.lib().q4gsw_force_plan(rows, splits) == S_OK
-            st, info = plan_info(q, q.OP_FWD, pre, 512, q.BF16)
-            assert st == S_OK and info.tile_rows == rows and info.splits == splits
-        # a forced count is rounded to one without an empty split: 128 chunks in 5 -> 26 per split, 5
-        assert q.lib().q4gsw_force_plan(0, 5) == S_OK
-        assert plan_info(q, q.OP_FWD, pre, 512, q.BF16)[1].splits == 5
-        for rows, splits in [(96, 0), (0, -1), (0, 65)]:
-            assert q.lib().q4gsw_force_plan(rows, splits) == 2                                  # E_SHAPE
-            assert plan_info(q, q.OP_FWD, pre, 512, q.BF16)[1].splits == 5                      # unchanged
-        # the workspace size follows the forced plan: splits x M x n_pad fp32 partials
-        need = ctypes.c_uint64()
-        assert q.lib().q4gsw_workspace_bytes(q.OP_FWD, ctypes.byref(pre), 512, q.BF16, ctypes.byref(need)) == S_OK
-        assert need.value == 5 * 512 * 2048 * 4
-    finally:
-        q.lib().q4gsw_force_plan(0, 0)
+    for rows, splits in [(64, 3), (128, 16)]:
+        st, info = plan_info(q, q.OP_FWD, pre, 512, q.BF16, opts=q.binding.Options(0, rows, splits))
+        assert st == S_OK and info.tile_rows == rows and info.splits == splits
+    # a requested count is rounded to one without an empty split: 128 chunks in 5 -> 26 per split, 5
+    five = q.binding.Options(0, 0, 5)
+    assert plan_info(q, q.OP_FWD, pre, 512, q.BF16, opts=five)[1].splits == 5
+    # the same options govern the 32x32 input-gradient plan
+    assert plan_info(q, q.OP_BWD_INPUT, bwd, 512, q.F32, opts=q.binding.Options(0, 0, 4))[1].splits == 4
+    # the workspace size follows the plan of the options: splits x M x n_pad fp32 partials
+    need = ctypes.c_uint64()
+    assert q.lib().q4gsw_workspace_bytes_ex(q.OP_FWD, ctypes.byref(pre), 512, q.BF16, ctypes.byref(five),
+                                            ctypes.byref(need)) == S_OK
+    assert need.value == 5 * 512 * 2048 * 4
+    # a plain plan right after is the library's own choice again
+    info = plan_info(q, q.OP_FWD, pre, 512, q.BF16)[1]
+    assert (info.tile_rows, info.splits) == default
 
 
 def test_embedding_validation(q):
