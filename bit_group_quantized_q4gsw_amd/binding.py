@@ -95,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "q4gsw_linear_bwd_input": [pw, vp, i32, i64, vp, vp, u64, vp],
             "q4gsw_qkv_fused": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, vp],
             "q4gsw_linear_fwd_ex": [pw, vp, i32, i64, vp, vp, u64, po, vp],
+            "q4gsw_linear_fwd_noalloc": [pw, vp, i32, i64, vp, vp],
             "q4gsw_linear_bwd_input_ex": [pw, vp, i32, i64, vp, vp, u64, po, vp],
             "q4gsw_qkv_fused_ex": [pw, pw, pw, vp, i32, i64, vp, vp, vp, vp, u64, po, vp],
             "q4gsw_route": [i32, pw, i64, i32],
@@ -248,6 +249,23 @@ def linear_fwd(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = N
     ws, wp, wb = _ws_args(need, workspace, x.device)
     _check(lib().q4gsw_linear_fwd_ex(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), wp, wb,
                                      _opts(), _stream()), "q4gsw_linear_fwd")
+    return y
+
+
+def linear_fwd_noalloc(w: PackedWeight, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """y [M, N] fp32 = x [M, K] . dequant(W)^T into the caller's `out`, through the entry point that
+    allocates nothing (its split partials live in the library's per-device scratch; calls that
+    overlap on one device race on it).  Raises Q4gswError (E_SCRATCH) when the call would need more
+    scratch than the library holds."""
+    x = _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    y = _out(out, (M, w.N), x.device, "out")
+    _check(lib().q4gsw_linear_fwd_noalloc(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), _stream()),
+           "q4gsw_linear_fwd_noalloc")
     return y
 
 

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "../../include/q4gsw.h"
 #include "internal.h"
@@ -256,6 +257,28 @@ q4gsw_status fwd_alias(const q4gsw_weight* w, const void* x, int32_t x_dtype, in
     return Q4GSW_OK;
 }
 
+// ---- the allocation-free forward's scratch ----------------------------------------------------
+// One buffer per device, held from module load until the process ends.  Host code never uses the
+// symbol itself (on the host it only names the device variable): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and every launch gets it.
+static __device__ __align__(256) uint8_t scratch[Q4GSW_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (null when it cannot be had).
+void* scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
+        g_scratch_ptr[dev] = p;
+    });
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +411,23 @@ q4gsw_status q4gsw_linear_fwd_ex(const q4gsw_weight* w, const void* x, int32_t x
 q4gsw_status q4gsw_linear_fwd(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y, void* ws,
                               uint64_t ws_bytes, void* stream) {
     return q4gsw_linear_fwd_ex(w, x, x_dtype, M, y, ws, ws_bytes, nullptr, stream);
+}
+
+q4gsw_status q4gsw_linear_fwd_noalloc(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y,
+                                      void* stream) {
+    const Opts o;
+    int32_t route = Q4GSW_ROUTE_NONE;
+    uint64_t need = 0;
+    q4gsw_status st = prepare_fwd(w, x, x_dtype, M, y, o, &route, &need);
+    if (st != Q4GSW_OK) return st;
+    if (need > Q4GSW_SCRATCH_BYTES) return Q4GSW_E_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_of_current_device();
+        if (!ws) return Q4GSW_E_HIP;
+    }
+    if ((st = fwd_alias(w, x, x_dtype, M, y, ws, need)) != Q4GSW_OK) return st;
+    return run_fwd(w, x, x_dtype, M, y, ws, route, o, static_cast<hipStream_t>(stream));
 }
 
 q4gsw_status q4gsw_linear_bwd_input_ex(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M,
@@ -588,6 +628,7 @@ const char* q4gsw_status_str(int32_t status) {
         case Q4GSW_E_HIP: return "HIP runtime error";
         case Q4GSW_E_BUFFER: return "packed buffer too small";
         case Q4GSW_E_ROUTE: return "requested route cannot serve this call";
+        case Q4GSW_E_SCRATCH: return "call needs more than the allocation-free entry point's 32 MiB scratch";
         default: return "unknown status";
     }
 }

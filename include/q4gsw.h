@@ -60,7 +60,8 @@ typedef enum q4gsw_status {
     Q4GSW_E_DESC = 8,         /* descriptor magic/version/fields invalid, or QKV weights disagree */
     Q4GSW_E_HIP = 9,          /* a HIP runtime call or kernel launch failed */
     Q4GSW_E_BUFFER = 10,      /* packed buffer smaller than q4gsw_packed_bytes */
-    Q4GSW_E_ROUTE = 11        /* the route requested in q4gsw_options cannot serve this call */
+    Q4GSW_E_ROUTE = 11,       /* the route requested in q4gsw_options cannot serve this call */
+    Q4GSW_E_SCRATCH = 12      /* q4gsw_linear_fwd_noalloc: the call needs more than Q4GSW_SCRATCH_BYTES */
 } q4gsw_status;
 
 typedef enum q4gsw_dtype {
@@ -200,6 +201,22 @@ q4gsw_status q4gsw_linear_fwd(const q4gsw_weight *w, const void *x, int32_t x_dt
 q4gsw_status q4gsw_linear_fwd_ex(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M,
                                  float *y, void *ws, uint64_t ws_bytes, const q4gsw_options *opts,
                                  void *stream);
+
+/*
+ * Forward that allocates nothing and takes no workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same routes, kernels and results as q4gsw_linear_fwd with no options (bit for
+ * bit).  The split partials that q4gsw_linear_fwd keeps in the caller's workspace go to a
+ * scratch buffer of Q4GSW_SCRATCH_BYTES that the library holds on each device from module load
+ * until the process ends.  A call whose workspace (q4gsw_workspace_bytes) would exceed it
+ * returns Q4GSW_E_SCRATCH and launches nothing.  Every call on one device shares that device's
+ * buffer and nothing in it needs to start at zero: calls that overlap on one device (other
+ * streams or host threads) race on it, so the caller must order them.  Other errors as
+ * q4gsw_linear_fwd (E_HIP also if the scratch address cannot be obtained).
+ */
+#define Q4GSW_SCRATCH_BYTES (32u << 20)
+q4gsw_status q4gsw_linear_fwd_noalloc(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M,
+                                      float *y, void *stream);
 
 /*
  * Input gradient: d_x[M, K] (fp32) = d_out[M, N] . dequant(W), contracting over N.

@@ -342,6 +342,26 @@ def test_plan_attestation_and_forcing(q):
     assert (info.tile_rows, info.splits) == default
 
 
+def test_noalloc_forward_validation(q):
+    """The allocation-free forward validates like q4gsw_linear_fwd and refuses, before any HIP call,
+    a call whose split partials would not fit its 32 MiB scratch (E_SCRATCH)."""
+    lib = q.lib()
+    f = lib.q4gsw_linear_fwd_noalloc
+    d = fake_desc(q, 256, 512, 32, 1, flags=1)
+    x, y = FAKE * 8, FAKE * 16
+    assert f(None, x, q.F16, 4, y, None) == E_NULL
+    assert f(ctypes.byref(d), None, q.F16, 4, y, None) == E_NULL
+    assert f(ctypes.byref(d), x, q.F16, 0, y, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, 7, 4, y, None) == E_DTYPE
+    assert f(ctypes.byref(d), x, q.F16, 4, x + 64, None) == E_ALIAS
+    pre = fake_desc(q, 2048, 8192, 128, 1, flags=1)
+    need = ctypes.c_uint64()
+    assert lib.q4gsw_workspace_bytes(q.OP_FWD, ctypes.byref(pre), 1536, q.BF16, ctypes.byref(need)) == S_OK
+    assert need.value > 32 << 20
+    assert f(ctypes.byref(pre), x, q.BF16, 1536, y, None) == 12                       # E_SCRATCH
+    assert "32 MiB" in q.status_str(12)
+
+
 def test_embedding_validation(q):
     lib = q.lib()
     d = fake_desc(q, 256, 512, 32, 1)
