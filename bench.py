@@ -129,8 +129,13 @@ class EmbOp:
         q.embedding(pw, ids, out=out)
 
 
+def torch_dtype(name):
+    from synthetic_inputs import DTYPES
+    return DTYPES[name]
+
+
 def build_ops(q, names, rotate):
-    from synthetic_inputs import make_workload
+    from synthetic_inputs import make_linear, make_workload
     specs = []
     for n in names:
         if n == "decode":
@@ -143,8 +148,18 @@ def build_ops(q, names, rotate):
             # the decode-shaped triples (one launch of the streaming GEMV), outside the step
             specs.append(("qkv_m1", "qkv", make_workload("qkv", M=1)))
             specs.append(("qkv_m4", "qkv", make_workload("qkv", M=4)))
-        elif n == "bwd":
-            specs.append(("bwd", "bwd", make_workload("bwd")))
+        elif n in ("bwd", "bwd_h", "bwd_gs32"):
+            if n == "bwd":
+                specs.append(("bwd", "bwd", make_workload("bwd")))
+            # outside the step: the same workload with d_out rounded to fp16 (fold route), and the
+            # input gradient through the Llama Q projection (N = K = 2048, gs = 32, fp32 d_out)
+            if n in ("bwd", "bwd_h"):
+                h = copy.copy(make_workload("bwd"))
+                h.d_out = h.d_out.to(torch_dtype("f16"))
+                specs.append(("bwd_h", "bwd", h))
+            if n in ("bwd", "bwd_gs32"):
+                specs.append(("bwd_gs32", "bwd", make_linear(512, 2048, 2048, 32, "f32", "f16", seed=0, fwd=False,
+                                                             bwd=True, sigma=0.1)))
         elif n in ("embedding", "emb_t512", "emb_t1"):
             # the row gather from the tied embedding table, outside the step: 512 ids and one id
             emb = make_workload("embedding")
@@ -162,7 +177,7 @@ def build_ops(q, names, rotate):
         act = case.x if case.x is not None else case.d_out
         return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
 
-    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1"}
+    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1", "bwd_h", "bwd_gs32"}
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing
@@ -212,6 +227,7 @@ def traffic_for(op_name, src_hash):
 OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_"),
               "qkv_m128": ("gemm_fwd", "reduce_"), "qkv_m508": ("gemm_fwd", "reduce_"),
               "qkv_m512": ("gemm_fwd", "reduce_"), "bwd": ("gemm_bwd", "reduce_"),
+              "bwd_h": ("gemm_bwd", "reduce_"), "bwd_gs32": ("gemm_bwd", "reduce_", "split_planes"),
               "emb_t512": ("embedding_kernel",), "emb_t1": ("embedding_kernel",)}
 
 

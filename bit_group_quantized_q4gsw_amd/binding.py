@@ -22,7 +22,7 @@ F32, F16, BF16 = 0, 1, 2
 OP_FWD, OP_BWD_INPUT, OP_QKV = 0, 1, 2
 ROUTES = {
     "none": 0, "generic": 1, "gemv": 2, "gemm_fold": 3, "gemm_group": 4, "gemm_split": 5,
-    "bwd_gemv": 6, "bwd_fold": 7, "bwd_split": 8, "qkv_fused": 9,
+    "bwd_gemv": 6, "bwd_fold": 7, "bwd_split": 8, "qkv_fused": 9, "bwd_bsplit": 10,
 }
 FLAG_FOLD_F16 = 1
 _TORCH_DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}

@@ -30,7 +30,7 @@ struct Opts {
 q4gsw_status read_opts(const q4gsw_options* o, Opts* out) {
     *out = Opts{};
     if (!o) return Q4GSW_OK;
-    if (o->route < Q4GSW_ROUTE_NONE || o->route > Q4GSW_ROUTE_QKV_FUSED) return Q4GSW_E_ROUTE;
+    if (o->route < Q4GSW_ROUTE_NONE || o->route > Q4GSW_ROUTE_BWD_BSPLIT) return Q4GSW_E_ROUTE;
     if (o->tile_rows != 0 && o->tile_rows != 64 && o->tile_rows != 128) return Q4GSW_E_SHAPE;
     if (o->splits < 0 || o->splits > 64) return Q4GSW_E_SHAPE;
     out->route = o->route;
@@ -128,8 +128,13 @@ int32_t pick_bwd(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t forced, q
     const WView v = view_of(w);
     const bool small_ok = M <= 8 && w->group_size % 8 == 0;
     const bool mfma_ok = gemm_bwd_supported(v, dt, fold_ok(w));
-    const bool fold = dt == Q4GSW_F16 && w->scale_dtype == Q4GSW_F16 && fold_ok(w);
-    const int32_t mfma_route = fold ? Q4GSW_ROUTE_BWD_FOLD : Q4GSW_ROUTE_BWD_SPLIT;
+    int32_t mfma_route = Q4GSW_ROUTE_NONE;
+    if (mfma_ok) {
+        const BwdPlan bp = plan_gemm_bwd(v, dt, fold_ok(w), M);
+        mfma_route = (bp.v1 || bp.mode == kModeFold) ? Q4GSW_ROUTE_BWD_FOLD
+                     : bp.mode == kModeBSplit         ? Q4GSW_ROUTE_BWD_BSPLIT
+                                                      : Q4GSW_ROUTE_BWD_SPLIT;
+    }
     *err = Q4GSW_OK;
     if (forced != Q4GSW_ROUTE_NONE) {
         switch (route_kind(forced)) {
@@ -168,7 +173,7 @@ uint64_t bwd_ws_bytes(const q4gsw_weight* w, int64_t M, int32_t dt, int32_t rout
         const int s = gemv_bwd_splits(v, M);
         return s > 1 ? (uint64_t)s * M * v.k_pad * 4 : 0;
     }
-    if (route == Q4GSW_ROUTE_BWD_FOLD || route == Q4GSW_ROUTE_BWD_SPLIT)
+    if (route == Q4GSW_ROUTE_BWD_FOLD || route == Q4GSW_ROUTE_BWD_SPLIT || route == Q4GSW_ROUTE_BWD_BSPLIT)
         return (uint64_t)plan_gemm_bwd(v, dt, fold_ok(w), M, o.splits).ws_bytes;
     return 0;
 }
@@ -579,7 +584,7 @@ q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* w
         info->splits = gemv_fwd_splits(v, M);
     } else if (r == Q4GSW_ROUTE_BWD_GEMV) {
         info->splits = gemv_bwd_splits(v, M);
-    } else if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT) {
+    } else if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT || r == Q4GSW_ROUTE_BWD_BSPLIT) {
         info->tile_rows = 128;
         info->splits = plan_gemm_bwd(v, act_dtype, fold_ok(w), M, o.splits).splits;
     } else if (r == Q4GSW_ROUTE_GEMM_FOLD || r == Q4GSW_ROUTE_GEMM_GROUP || r == Q4GSW_ROUTE_GEMM_SPLIT ||
@@ -610,6 +615,7 @@ const char* q4gsw_route_name(int32_t route) {
         case Q4GSW_ROUTE_BWD_FOLD: return "bwd_fold";
         case Q4GSW_ROUTE_BWD_SPLIT: return "bwd_split";
         case Q4GSW_ROUTE_QKV_FUSED: return "qkv_fused";
+        case Q4GSW_ROUTE_BWD_BSPLIT: return "bwd_bsplit";
         default: return "unknown";
     }
 }

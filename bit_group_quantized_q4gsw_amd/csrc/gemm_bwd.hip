@@ -1,5 +1,6 @@
 // MFMA input gradient for M > 8, 16x16x32 form with an LDS transpose of the codes; serves
-// the group sizes the 32x32x16 kernel (gemm_bwd2.hip) does not take:
+// fp16 d_out with foldable fp16 scales at the group sizes the 32x32x16 kernels (gemm_bwd2.hip)
+// do not take (gs % 8 == 0 other than 32 and multiples of 64):
 //   d_x[m, k] = sum_n d_out[m, n] * (code[n, k] - 8) * scale[k / gs, n]     (contract over N)
 // the frozen-base input gradient of the Vulkan q4gsw-backward PR body, reading the
 // forward's packed buffer as it is (no re-pack).
@@ -11,13 +12,8 @@
 // 16-byte row of Bt[k][n].  The MFMA then reads B fragments (8 consecutive n of
 // one k) and A fragments (8 consecutive n of one d_out row) with 16-byte LDS loads.
 //
-// Precision routes (fp32 accumulation):
-//   kModeFold  fp16 d_out with fp16 scales checked foldable at pack time:
-//              B = fp16((code - 8) * scale), one MFMA pass, |err| <= 2^-11 |w|.
-//   kModeSplit every other dtype: the block's 128 output columns lie in one scale
-//              group g, so the scale moves to the A side, A' = d_out * scale[g, n]
-//              (fp32), split into bf16 hi + lo (|err| <= 2^-18 |A'|), two MFMA passes
-//              against B = code - 8 (exact bf16).
+// Precision (fp32 accumulation): fp16 d_out with fp16 scales checked foldable at pack time,
+// B = fp16((code - 8) * scale), one MFMA pass, |err| <= 2^-11 |w|.
 #include "device.h"
 #include "internal.h"
 
@@ -27,13 +23,11 @@ constexpr int kBBM = 128;     // block rows (M)
 constexpr int kBCN = 64;      // contraction chunk (n) per LDS stage
 constexpr int kBPitch = kBCN + 8;
 
-template <int MODE>
 struct BwdCfg {
-    static constexpr int kWK = (MODE == kModeFold) ? 128 : 64;   // wave output columns (k)
+    static constexpr int kWK = 128;                              // wave output columns (k)
     static constexpr int kBK = 2 * kWK;                          // block output columns
     static constexpr int kUI = kWK / 16;                         // 16-column MFMA tiles per wave
-    static constexpr int kAPlanes = (MODE == kModeSplit) ? 2 : 1;
-    static constexpr int kAElems = kAPlanes * kBBM * kBPitch;
+    static constexpr int kAElems = kBBM * kBPitch;
     static constexpr int kBElems = kBK * kBPitch;
 };
 
@@ -43,19 +37,10 @@ __device__ __forceinline__ uint32_t byte_pair(uint32_t w_lo_row, uint32_t w_hi_r
     return __builtin_amdgcn_perm(w_hi_row, w_lo_row, sel);
 }
 
-// Exact bf16 pair (c_even_row - 8, c_odd_row - 8) of the nibbles at bit `sh` of the two
-// 16-bit halves of tx (tx = byte pair ^ 0x00880088, so nibbles are two's-complement c - 8).
-__device__ __forceinline__ uint32_t pair_minus8_bf16(uint32_t tx, int sh) {
-    const float lo = (float)signed_code(tx, sh >> 2);
-    const float hi = (float)signed_code(tx, 4 + (sh >> 2));
-    return __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
-}
-
-template <int GT, int MODE>
 __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __restrict__ d_out, int64_t M,
                                                        float* __restrict__ out, int64_t out_ld, int64_t split_stride,
                                                        int64_t col_limit, int g_vec, int chunks_per_split) {
-    using C = BwdCfg<MODE>;
+    using C = BwdCfg;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][C::kAElems];
     __shared__ __attribute__((aligned(16))) uint16_t Bt[2][C::kBElems];
 
@@ -73,7 +58,6 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
     const int64_t n_chunks = (w.N + kBCN - 1) / kBCN;
     const int64_t c_begin = (int64_t)blockIdx.z * chunks_per_split;
     const int64_t c_end = min(c_begin + (int64_t)chunks_per_split, n_chunks);
-    const int64_t group = kb0 / w.gs;                       // kModeSplit: one group per block
 
     f4 acc[4][C::kUI];
 #pragma unroll
@@ -97,14 +81,12 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
         wreg[0] = a.x; wreg[1] = a.y; wreg[2] = a.z; wreg[3] = a.w;
         wreg[4] = b.x; wreg[5] = b.y; wreg[6] = b.z; wreg[7] = b.w;
     };
-    uint32_t sreg[4];     // kModeFold: fp16 scale pairs (n, n+1) for the micro-block's rows
+    uint32_t sreg[4];     // fp16 scale pairs (n, n+1) for the micro-block's rows
     auto load_fold_scales = [&](int64_t nc) {
-        if constexpr (MODE == kModeFold) {
-            if (!mb_in) return;
-            const int64_t g = (mb_O * 8) / w.gs;
-            const u4 v = ldg16(static_cast<const uint16_t*>(w.scales) + scale_index(w.g_pad, nc + 8 * mb_ro, g));
-            sreg[0] = v.x; sreg[1] = v.y; sreg[2] = v.z; sreg[3] = v.w;
-        }
+        if (!mb_in) return;
+        const int64_t g = (mb_O * 8) / w.gs;
+        const u4 v = ldg16(static_cast<const uint16_t*>(w.scales) + scale_index(w.g_pad, nc + 8 * mb_ro, g));
+        sreg[0] = v.x; sreg[1] = v.y; sreg[2] = v.z; sreg[3] = v.w;
     };
     auto store_codes = [&](int buf) {
         if (!mb_active) return;
@@ -125,16 +107,10 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
                     // nibble positions 0..3 hold k-offsets 0,2,4,6 and positions 4..7 hold 1,3,5,7
                     const int jlo = ((2 * b) < 4) ? 2 * (2 * b) : 2 * (2 * b - 4) + 1;
                     const int jhi = ((2 * b + 1) < 4) ? 2 * (2 * b + 1) : 2 * (2 * b + 1 - 4) + 1;
-                    if constexpr (MODE == kModeFold) {
-                        const h2 s2 = bitcast<h2>(sreg[a]);
-                        const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-                        col[jlo][a] = bitcast<uint32_t>((bitcast<h2>(plo | 0x64006400u) - off) * s2);
-                        col[jhi][a] = bitcast<uint32_t>((bitcast<h2>(phi | 0x64006400u) - off) * s2);
-                    } else {
-                        const uint32_t tx = t ^ 0x00880088u;
-                        col[jlo][a] = pair_minus8_bf16(tx, 0);
-                        col[jhi][a] = pair_minus8_bf16(tx, 4);
-                    }
+                    const h2 s2 = bitcast<h2>(sreg[a]);
+                    const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+                    col[jlo][a] = bitcast<uint32_t>((bitcast<h2>(plo | 0x64006400u) - off) * s2);
+                    col[jhi][a] = bitcast<uint32_t>((bitcast<h2>(phi | 0x64006400u) - off) * s2);
                 }
             }
         }
@@ -144,47 +120,27 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
                 u4{col[j][0], col[j][1], col[j][2], col[j][3]};
     };
 
-    // ---- d_out tile -> As (fp16 copy, or A' = d_out * scale split into bf16 hi/lo) ----
-    constexpr int kUnitsPerRow = (GT == kF32) ? kBCN / 4 : kBCN / 8;
+    // ---- d_out tile -> As (fp16 copy) ----
+    constexpr int kUnitsPerRow = kBCN / 8;
     constexpr int kUnits = kBBM * kUnitsPerRow / 256;
-    constexpr int kVals = (GT == kF32) ? 4 : 8;
     u4 areg[kUnits];
-    float ascale[kVals];
     auto load_a = [&](int64_t nc) {
         const int colu = tid % kUnitsPerRow;           // same for every unit of this thread
-        const int64_t n = nc + kVals * colu;
-        if constexpr (MODE == kModeSplit) {
-#pragma unroll
-            for (int v = 0; v < kVals; ++v)
-                ascale[v] = (n + v < w.N) ? load_scale(w.scales, w.scale_f16, scale_index(w.g_pad, n + v, group))
-                                          : 0.f;
-        }
+        const int64_t n = nc + 8 * colu;
 #pragma unroll
         for (int c = 0; c < kUnits; ++c) {
             const int unit = tid + 256 * c;
             const int64_t m = m0 + unit / kUnitsPerRow;
             u4 v = {0u, 0u, 0u, 0u};
             if (m < M) {
-                if constexpr (GT == kF32) {
-                    const float* src = static_cast<const float*>(d_out) + m * w.N + n;
-                    if (g_vec && n + 4 <= w.N) {
-                        v = ldg16(src);
-                    } else {
-                        f4 f = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) f[j] = (n + j < w.N) ? src[j] : 0.f;
-                        v = bitcast<u4>(f);
-                    }
+                const uint16_t* src = static_cast<const uint16_t*>(d_out) + m * w.N + n;
+                if (g_vec && n + 8 <= w.N) {
+                    v = ldg16(src);
                 } else {
-                    const uint16_t* src = static_cast<const uint16_t*>(d_out) + m * w.N + n;
-                    if (g_vec && n + 8 <= w.N) {
-                        v = ldg16(src);
-                    } else {
-                        uint32_t e[8];
+                    uint32_t e[8];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) e[j] = (n + j < w.N) ? src[j] : 0u;
-                        v = u4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-                    }
+                    for (int j = 0; j < 8; ++j) e[j] = (n + j < w.N) ? src[j] : 0u;
+                    v = u4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
                 }
             }
             areg[c] = v;
@@ -196,40 +152,7 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
             const int unit = tid + 256 * c;
             const int row = unit / kUnitsPerRow;
             const int colu = unit % kUnitsPerRow;
-            if constexpr (MODE == kModeFold) {
-                *reinterpret_cast<u4*>(&As[buf][row * kBPitch + 8 * colu]) = areg[c];
-            } else {
-                float a[kVals];
-                if constexpr (GT == kF32) {
-                    const f4 f = bitcast<f4>(areg[c]);
-                    a[0] = f.x; a[1] = f.y; a[2] = f.z; a[3] = f.w;
-                } else {
-                    const uint32_t u[4] = {areg[c].x, areg[c].y, areg[c].z, areg[c].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (GT == kF16) {
-                            a[2 * i] = f16_bits_to_f32((uint16_t)(u[i] & 0xFFFFu));
-                            a[2 * i + 1] = f16_bits_to_f32((uint16_t)(u[i] >> 16));
-                        } else {
-                            a[2 * i] = bitcast<float>(u[i] << 16);
-                            a[2 * i + 1] = bitcast<float>(u[i] & 0xFFFF0000u);
-                        }
-                    }
-                }
-                uint32_t hi[kVals / 2], lo[kVals / 2];
-#pragma unroll
-                for (int i = 0; i < kVals / 2; ++i)
-                    split_bf16(a[2 * i] * ascale[2 * i], a[2 * i + 1] * ascale[2 * i + 1], hi[i], lo[i]);
-                uint16_t* ph = &As[buf][row * kBPitch + kVals * colu];
-                uint16_t* pl = ph + kBBM * kBPitch;
-                if constexpr (kVals == 4) {
-                    *reinterpret_cast<u2*>(ph) = u2{hi[0], hi[1]};
-                    *reinterpret_cast<u2*>(pl) = u2{lo[0], lo[1]};
-                } else {
-                    *reinterpret_cast<u4*>(ph) = u4{hi[0], hi[1], hi[2], hi[3]};
-                    *reinterpret_cast<u4*>(pl) = u4{lo[0], lo[1], lo[2], lo[3]};
-                }
-            }
+            *reinterpret_cast<u4*>(&As[buf][row * kBPitch + 8 * colu]) = areg[c];
         }
     };
 
@@ -263,17 +186,8 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
             for (int mi = 0; mi < 4; ++mi) {
                 const uint16_t* pa = Ab + (wm * 64 + 16 * mi + lrow) * kBPitch + 32 * t + 8 * lq;
                 const u4 a = *reinterpret_cast<const u4*>(pa);
-                if constexpr (MODE == kModeFold) {
 #pragma unroll
-                    for (int u = 0; u < C::kUI; ++u) acc[mi][u] = mfma_f16(a, bfr[u], acc[mi][u]);
-                } else {
-                    const u4 alo = *reinterpret_cast<const u4*>(pa + kBBM * kBPitch);
-#pragma unroll
-                    for (int u = 0; u < C::kUI; ++u) {
-                        acc[mi][u] = mfma_bf16(a, bfr[u], acc[mi][u]);
-                        acc[mi][u] = mfma_bf16(alo, bfr[u], acc[mi][u]);
-                    }
-                }
+                for (int u = 0; u < C::kUI; ++u) acc[mi][u] = mfma_f16(a, bfr[u], acc[mi][u]);
             }
         }
         if (has_next) {
@@ -300,14 +214,15 @@ __global__ __launch_bounds__(256) void gemm_bwd_kernel(WView w, const void* __re
 }
 
 bool gemm_bwd_v1_supported(const WView& w, int g_dtype, int fold_ok) {
-    if (g_dtype == kF16 && w.scale_f16 && fold_ok) return w.gs % 8 == 0;
-    return w.gs % BwdCfg<kModeSplit>::kBK == 0;
+    return g_dtype == kF16 && w.scale_f16 && fold_ok && w.gs % 8 == 0;
 }
 
 BwdPlan plan_gemm_bwd_v1(const WView& w, int g_dtype, int fold_ok, int64_t M) {
+    (void)g_dtype;
+    (void)fold_ok;
     BwdPlan p{};
-    p.mode = (g_dtype == kF16 && w.scale_f16 && fold_ok) ? kModeFold : kModeSplit;
-    const int bk = p.mode == kModeFold ? BwdCfg<kModeFold>::kBK : BwdCfg<kModeSplit>::kBK;
+    p.mode = kModeFold;
+    const int bk = BwdCfg::kBK;
     const int64_t blocks = ((w.k_pad + bk - 1) / bk) * ((M + kBBM - 1) / kBBM);
     const int64_t n_chunks = (w.N + kBCN - 1) / kBCN;
     int64_t splits = 1;
@@ -317,34 +232,19 @@ BwdPlan plan_gemm_bwd_v1(const WView& w, int g_dtype, int fold_ok, int64_t M) {
     return p;
 }
 
-template <int GT, int MODE>
-static void launch_bwd_t(dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64_t M, float* out,
-                         int64_t ld, int64_t stride, int64_t limit, int g_vec, int per) {
-    hipLaunchKernelGGL((gemm_bwd_kernel<GT, MODE>), grid, dim3(256), 0, s, w, d_out, M, out, ld, stride, limit, g_vec,
-                       per);
-}
-
 hipError_t launch_gemm_bwd_v1(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
                               const BwdPlan& plan, float* ws, hipStream_t s) {
-    const int bk = plan.mode == kModeFold ? BwdCfg<kModeFold>::kBK : BwdCfg<kModeSplit>::kBK;
+    if (plan.mode != kModeFold || g_dtype != kF16) return hipErrorInvalidValue;
+    const int bk = BwdCfg::kBK;
     const int64_t n_chunks = (w.N + kBCN - 1) / kBCN;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);
     const dim3 grid((unsigned)((w.k_pad + bk - 1) / bk), (unsigned)((M + kBBM - 1) / kBBM), (unsigned)plan.splits);
-    const int esize = g_dtype == kF32 ? 4 : 2;
-    const int g_vec = ((reinterpret_cast<uintptr_t>(d_out) & 15u) == 0) && ((w.N * esize) % 16 == 0);
+    const int g_vec = ((reinterpret_cast<uintptr_t>(d_out) & 15u) == 0) && ((w.N * 2) % 16 == 0);
     float* out = plan.splits == 1 ? d_x : ws;
     const int64_t ld = plan.splits == 1 ? w.K : w.k_pad;
     const int64_t stride = plan.splits == 1 ? 0 : M * w.k_pad;
     const int64_t limit = plan.splits == 1 ? w.K : w.k_pad;
-    if (plan.mode == kModeFold) {
-        launch_bwd_t<kF16, kModeFold>(grid, s, w, d_out, M, out, ld, stride, limit, g_vec, per);
-    } else {
-        switch (g_dtype) {
-            case kF32: launch_bwd_t<kF32, kModeSplit>(grid, s, w, d_out, M, out, ld, stride, limit, g_vec, per); break;
-            case kF16: launch_bwd_t<kF16, kModeSplit>(grid, s, w, d_out, M, out, ld, stride, limit, g_vec, per); break;
-            default: launch_bwd_t<kBF16, kModeSplit>(grid, s, w, d_out, M, out, ld, stride, limit, g_vec, per); break;
-        }
-    }
+    hipLaunchKernelGGL(gemm_bwd_kernel, grid, dim3(256), 0, s, w, d_out, M, out, ld, stride, limit, g_vec, per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     return launch_reduce_splits(ws, plan.splits, M, w.K, w.k_pad, d_x, w.K, s);

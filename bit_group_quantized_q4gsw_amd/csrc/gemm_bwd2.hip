@@ -15,6 +15,12 @@
 //     a 32-byte micro-block, so each lane reads its micro-block and extracts its nibble from
 //     every word (a register transpose).  Issue order per MFMA step: the next step's LDS reads,
 //     then (MFMA, unpacking piece) pairs fenced with sched_barrier.
+//   * the same kernel with an exact bf16 B (XB > 0; fp32 / bf16 d_out, and fp16 with scales that
+//     cannot be folded, at the group sizes the split kernel does not take): for fp16 scales
+//     (code - 8) * scale / 16 has at most 14 significant bits, so it is exactly the sum of two
+//     bf16 values hi + lo; d_out is staged by a pre-pass as one bf16 plane (bf16 d_out as it is)
+//     or two (fp32 / fp16 d_out split into bf16 hi + lo, |err| <= 2^-18 |d_out|, exact for fp16),
+//     and two or four MFMA passes multiply them;
 //   * gemm_bwd_split_kernel (fp32 / bf16 d_out, and fp16 with scales that cannot be folded),
 //     4 consumer + 4 producer waves: the block's columns lie in at most two scale groups
 //     (gs % 128 == 0; a change can only fall at column 128 of the block), so the scale moves to
@@ -58,17 +64,44 @@ __device__ __forceinline__ void store_frag_partials(float* plane, int64_t ntn, i
     }
 }
 
+// x * s for an fp16 s held in the low / high half of sw, rounded once to fp32.  Written as an FMA
+// with a zero addend so it maps to the mixed-precision FMA, which takes the fp16 operand directly.
+__device__ __forceinline__ float mul_f16_lo(float x, uint32_t sw) {
+    return __builtin_fmaf(x, f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)), 0.0f);
+}
+__device__ __forceinline__ float mul_f16_hi(float x, uint32_t sw) {
+    return __builtin_fmaf(x, f16_bits_to_f32((uint16_t)(sw >> 16)), 0.0f);
+}
+// bf16 hi / lo split of two fp32 values (both roundings to nearest even): a = hi + lo + e with
+// |e| <= 2^-18 |a|.  a - hi is exact in fp32.  Both fp32 hi values come from the packed hi word
+// (a byte permute and a mask), so the conversion is done once.
+__device__ __forceinline__ void split_bf16_pair(float a0, float a1, uint32_t& hi, uint32_t& lo) {
+    b2 h = {(__bf16)a0, (__bf16)a1};
+    const uint32_t hb = bitcast<uint32_t>(h);
+    const float r0 = a0 - bitcast<float>(__builtin_amdgcn_perm(hb, hb, 0x05040c0cu));   // hb << 16
+    const float r1 = a1 - bitcast<float>(hb & 0xFFFF0000u);
+    b2 l = {(__bf16)r0, (__bf16)r1};
+    hi = hb;
+    lo = bitcast<uint32_t>(l);
+}
+
 // NV = scale groups per wave (1: gs % 64 == 0, 2: gs == 32).
-template <int NV>
+// XB = 0: fp16 d_out and B = fp16((code - 8) * scale), one pass.  XB = 1 or 2: exact bf16
+// B = hi + lo of (code - 8) * scale / 16 against XB bf16 planes of d_out (a_plane elements apart),
+// two or four passes; the output carries the factor 16 back exactly.
+template <int NV, int XB>
 __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const void* __restrict__ d_out, int64_t M,
                                                                float* __restrict__ out, int64_t out_ld,
                                                                int64_t split_stride, int64_t col_limit, int g_fast,
-                                                               int chunks_per_split, int splits, int mtiles) {
+                                                               int chunks_per_split, int splits, int mtiles,
+                                                               int64_t a_plane) {
+    constexpr int kAPlanes = XB == 2 ? 2 : 1;
     constexpr int kARing = 3;                                   // A stages
-    constexpr int kAStage = kPlaneBytes;
+    constexpr int kAStage = kAPlanes * kPlaneBytes;
     constexpr int kSBytes = 256;                                // per-wave scales per chunk
     constexpr int kCStage = 4 * (kCodeBytes + kSBytes);
-    constexpr int kDmaPerChunk = 4 + 2 + 1;
+    constexpr int kDmaPerChunk = 4 * kAPlanes + 2 + 1;
+    constexpr float kOutScale = XB == 0 ? 1.0f : 16.0f;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kARing * kAStage + 3 * kCStage];
     uint8_t* const Aring = smem;
     uint8_t* const Cring = smem + kARing * kAStage;
@@ -136,21 +169,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
         const int64_t nc = c * kCN;
         if (g_fast && nc + kCN <= N) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dma16(xa[q] + nc, sm_l + st * kAStage + (32 * wave + 8 * q) * kRowBytes);
+            for (int pl = 0; pl < kAPlanes; ++pl)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dma16(xa[q] + pl * a_plane + nc,
+                          sm_l + st * kAStage + pl * kPlaneBytes + (32 * wave + 8 * q) * kRowBytes);
         } else {
             // ragged n tail or unaligned d_out: zero-filled register loads into the same slots
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = 32 * wave + 8 * q + (lane >> 3);
-                const int64_t m = m0 + row;
-                const int64_t n = nc + 8 * xoct[q];
-                uint32_t e[8];
+            for (int pl = 0; pl < kAPlanes; ++pl)
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    e[i] = (m < M && n + i < N) ? static_cast<const uint16_t*>(d_out)[m * N + n + i] : 0u;
-                *reinterpret_cast<u4*>(Aring + st * kAStage + row * kRowBytes + 16 * (lane & 7)) =
-                    u4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const int row = 32 * wave + 8 * q + (lane >> 3);
+                    const int64_t m = m0 + row;
+                    const int64_t n = nc + 8 * xoct[q];
+                    const uint16_t* src = static_cast<const uint16_t*>(d_out) + pl * a_plane;
+                    uint32_t e[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) e[i] = (m < M && n + i < N) ? src[m * N + n + i] : 0u;
+                    *reinterpret_cast<u4*>(Aring + st * kAStage + pl * kPlaneBytes + row * kRowBytes + 16 * (lane & 7)) =
+                        u4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+                }
         }
     };
 
@@ -165,11 +204,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
 
     const int swz = (j >> 1) & 7;                 // ((row >> 1) & 7) of every A row this lane reads
     const int npos = 4 * nib_pos(j & 7);          // bit offset of this lane's k in each code word
-    // A fragments of step t
-    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4]) {
+    // A fragments of step t (and of the lo plane when there is one)
+    auto read_a = [&](const uint8_t* Ab, int t, u4 (&a)[4], u4 (&alo)[4]) {
         const int slot = 16 * ((2 * t + h) ^ swz);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const u4*>(Ab + (32 * mi + j) * kRowBytes + slot);
+        for (int mi = 0; mi < 4; ++mi) {
+            a[mi] = *reinterpret_cast<const u4*>(Ab + (32 * mi + j) * kRowBytes + slot);
+            if constexpr (kAPlanes == 2) alo[mi] = *reinterpret_cast<const u4*>(Ab + kPlaneBytes + (32 * mi + j) * kRowBytes + slot);
+        }
     };
     // the 8 code words of step t for column u (micro-block row-octet 2t + h, k-octet 4u + j/8)
     auto read_b = [&](const uint8_t* Cb, int t, u4 (&wd)[2][2]) {
@@ -187,32 +229,44 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
 #pragma unroll
         for (int u = 0; u < 2; ++u) fs[u] = *reinterpret_cast<const u4*>(Sb + 128 * (NV == 2 ? u : 0) + 16 * R);
     };
-    // dword e of B fragment u: rows 2e, 2e+1 of the micro-block at this lane's k
-    auto bpiece = [&](const u4 (&wd)[2][2], const u4 (&fs)[2], u4 (&b)[2], int i) {
+    // dword e of B fragment u: rows 2e, 2e+1 of the micro-block at this lane's k.  XB = 0: fp16
+    // (code - 8) * scale, one rounding.  XB > 0: the exact fp32 value (code - 8) / 16 * scale (a
+    // 4-bit signed convert of code ^ 8, times the fp16 scale in a mixed-precision FMA) split into
+    // bf16 hi (b) + lo (blo) with no error.
+    auto bpiece = [&](const u4 (&wd)[2][2], const u4 (&fs)[2], u4 (&b)[2], u4 (&blo)[2], int i) {
         const int u = i >> 2, e = i & 3;
         const uint32_t w0 = wd[u][e >> 1][2 * (e & 1)];
         const uint32_t w1 = wd[u][e >> 1][2 * (e & 1) + 1];
-        const uint32_t c0 = __builtin_amdgcn_ubfe(w0, npos, 4);
-        const uint32_t c1 = __builtin_amdgcn_ubfe(w1, npos, 4);
-        const h2 v = bitcast<h2>((c0 | (c1 << 16)) | 0x64006400u);
-        const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-        b[u][e] = bitcast<uint32_t>((v - off) * bitcast<h2>(fs[u][e]));
+        if constexpr (XB == 0) {
+            const uint32_t c0 = __builtin_amdgcn_ubfe(w0, npos, 4);
+            const uint32_t c1 = __builtin_amdgcn_ubfe(w1, npos, 4);
+            const h2 v = bitcast<h2>((c0 | (c1 << 16)) | 0x64006400u);
+            const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+            b[u][e] = bitcast<uint32_t>((v - off) * bitcast<h2>(fs[u][e]));
+        } else {
+            const float v0 = __builtin_amdgcn_cvt_off_f32_i4((int)__builtin_amdgcn_ubfe(w0 ^ 0x88888888u, npos, 4));
+            const float v1 = __builtin_amdgcn_cvt_off_f32_i4((int)__builtin_amdgcn_ubfe(w1 ^ 0x88888888u, npos, 4));
+            uint32_t hi, lo;
+            split_bf16_pair(mul_f16_lo(v0, fs[u][e]), mul_f16_hi(v1, fs[u][e]), hi, lo);
+            b[u][e] = hi;
+            blo[u][e] = lo;
+        }
     };
     auto compute = [&](int st) {
         const uint8_t* Ab = Aring + st * kAStage;
         const uint8_t* Cb = Cring + st * kCStage + wave * (kCodeBytes + kSBytes);
         const uint8_t* Sb = Cb + kCodeBytes;
-        u4 a[2][4], wd[2][2][2], fs[2][2], b[2][2];
-        read_a(Ab, 0, a[0]);
+        u4 a[2][4], alo[2][4], wd[2][2][2], fs[2][2], b[2][2], blo[2][2];
+        read_a(Ab, 0, a[0], alo[0]);
         read_b(Cb, 0, wd[0]);
         read_fs(Sb, 0, fs[0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) bpiece(wd[0], fs[0], b[0], i);
+        for (int i = 0; i < 8; ++i) bpiece(wd[0], fs[0], b[0], blo[0], i);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int cur = t & 1, nxt = (t + 1) & 1;
             if (t < 3) {
-                read_a(Ab, t + 1, a[nxt]);
+                read_a(Ab, t + 1, a[nxt], alo[nxt]);
                 read_b(Cb, t + 1, wd[nxt]);
                 read_fs(Sb, t + 1, fs[nxt]);
             }
@@ -220,8 +274,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int mi = i >> 1, u = i & 1;
-                acc[mi][u] = mfma32_f16(a[cur][mi], b[cur][u], acc[mi][u]);
-                if (t < 3) bpiece(wd[nxt], fs[nxt], b[nxt], (i & 1) * 4 + (i >> 1));
+                if constexpr (XB == 0) {
+                    acc[mi][u] = mfma32_f16(a[cur][mi], b[cur][u], acc[mi][u]);
+                } else {
+                    acc[mi][u] = mfma32_bf16(a[cur][mi], b[cur][u], acc[mi][u]);
+                    acc[mi][u] = mfma32_bf16(a[cur][mi], blo[cur][u], acc[mi][u]);
+                    if constexpr (XB == 2) {
+                        acc[mi][u] = mfma32_bf16(alo[cur][mi], b[cur][u], acc[mi][u]);
+                        acc[mi][u] = mfma32_bf16(alo[cur][mi], blo[cur][u], acc[mi][u]);
+                    }
+                }
+                if (t < 3) bpiece(wd[nxt], fs[nxt], b[nxt], blo[nxt], (i & 1) * 4 + (i >> 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -256,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
     if (!wave_active) return;
     if (split_stride) {
-        store_frag_partials(out + (int64_t)z * split_stride, out_ld / 32, M, m0, kw0, lane, acc, 1.0f);
+        store_frag_partials(out + (int64_t)z * split_stride, out_ld / 32, M, m0, kw0, lane, acc, kOutScale);
         return;
     }
 #pragma unroll
@@ -268,31 +331,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_fold_kernel(WView w, const vo
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = m0 + 32 * mi + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) out[m * out_ld + k] = acc[mi][u][r];
+                if (m < M) out[m * out_ld + k] = kOutScale * acc[mi][u][r];
             }
         }
     }
-}
-
-// x * s for an fp16 s held in the low / high half of sw, rounded once to fp32.  Written as an FMA
-// with a zero addend so it maps to the mixed-precision FMA, which takes the fp16 operand directly.
-__device__ __forceinline__ float mul_f16_lo(float x, uint32_t sw) {
-    return __builtin_fmaf(x, f16_bits_to_f32((uint16_t)(sw & 0xFFFFu)), 0.0f);
-}
-__device__ __forceinline__ float mul_f16_hi(float x, uint32_t sw) {
-    return __builtin_fmaf(x, f16_bits_to_f32((uint16_t)(sw >> 16)), 0.0f);
-}
-// bf16 hi / lo split of two fp32 values (both roundings to nearest even): a = hi + lo + e with
-// |e| <= 2^-18 |a|.  a - hi is exact in fp32.  Both fp32 hi values come from the packed hi word
-// (a byte permute and a mask), so the conversion is done once.
-__device__ __forceinline__ void split_bf16_pair(float a0, float a1, uint32_t& hi, uint32_t& lo) {
-    b2 h = {(__bf16)a0, (__bf16)a1};
-    const uint32_t hb = bitcast<uint32_t>(h);
-    const float r0 = a0 - bitcast<float>(__builtin_amdgcn_perm(hb, hb, 0x05040c0cu));   // hb << 16
-    const float r1 = a1 - bitcast<float>(hb & 0xFFFF0000u);
-    b2 l = {(__bf16)r0, (__bf16)r1};
-    hi = hb;
-    lo = bitcast<uint32_t>(l);
 }
 
 // Split route with specialised waves: 8 waves per block, two per SIMD.  Waves 0..3 are
@@ -632,18 +674,73 @@ __global__ __launch_bounds__(512, 1) void gemm_bwd_split_kernel(WView w, const v
     }
 }
 
-bool v2_fold(const WView& w, int g_dtype, int fold_ok) { return g_dtype == kF16 && w.scale_f16 && fold_ok; }
-
-bool v2_supported(const WView& w, int g_dtype, int fold_ok) {
-    if (v2_fold(w, g_dtype, fold_ok)) return w.gs % 64 == 0 || w.gs == 32;
-    return w.gs % 128 == 0;
+// d_out -> bf16 planes hi and lo ([M][N] each): 8 values per thread, each split to nearest even
+// twice (fp32: |err| <= 2^-18 |d_out|; fp16 values split exactly).  vec: 16-byte-aligned source.
+template <int GT>
+__global__ __launch_bounds__(256) void split_planes_kernel(const void* __restrict__ src, int64_t total, int vec,
+                                                           uint32_t* __restrict__ hi, uint32_t* __restrict__ lo) {
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i0 >= total) return;
+    float v[8];
+    if (vec && i0 + 8 <= total) {
+        if constexpr (GT == kF32) {
+            const f4 a = bitcast<f4>(ldg16_stream(static_cast<const float*>(src) + i0 + 0));
+            const f4 b = bitcast<f4>(ldg16_stream(static_cast<const float*>(src) + i0 + 4));
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            const u4 a = ldg16_stream(static_cast<const uint16_t*>(src) + i0);
+            const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = f16_bits_to_f32((uint16_t)(u[e] & 0xFFFFu));
+                v[2 * e + 1] = f16_bits_to_f32((uint16_t)(u[e] >> 16));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (i0 + e < total) ? load_elem<GT>(src, i0 + e) : 0.f;
+    }
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16_pair(v[2 * e], v[2 * e + 1], h[e], l[e]);
+    if (i0 + 8 <= total) {
+        *reinterpret_cast<u4*>(hi + i0 / 2) = u4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<u4*>(lo + i0 / 2) = u4{l[0], l[1], l[2], l[3]};
+    } else {
+        uint16_t* h16 = reinterpret_cast<uint16_t*>(hi);
+        uint16_t* l16 = reinterpret_cast<uint16_t*>(lo);
+        for (int e = 0; e < 8 && i0 + e < total; ++e) {
+            h16[i0 + e] = (uint16_t)(h[e >> 1] >> (16 * (e & 1)));
+            l16[i0 + e] = (uint16_t)(l[e >> 1] >> (16 * (e & 1)));
+        }
+    }
 }
 
-template <int NV>
+bool v2_fold(const WView& w, int g_dtype, int fold_ok) { return g_dtype == kF16 && w.scale_f16 && fold_ok; }
+
+// Which 32x32 route serves an input gradient: kModeFold, kModeSplit (gs % 128 == 0), kModeBSplit
+// (the exact bf16 B, fp16 scales, gs % 64 == 0 or gs == 32), or -1.
+int v2_mode(const WView& w, int g_dtype, int fold_ok) {
+    if (v2_fold(w, g_dtype, fold_ok)) return (w.gs % 64 == 0 || w.gs == 32) ? kModeFold : -1;
+    if (w.gs % 128 == 0) return kModeSplit;
+    if (w.scale_f16 && (w.gs % 64 == 0 || w.gs == 32)) return kModeBSplit;
+    return -1;
+}
+
+bool v2_supported(const WView& w, int g_dtype, int fold_ok) { return v2_mode(w, g_dtype, fold_ok) >= 0; }
+
+// Elements from the hi plane to the lo plane of the bf16 d_out planes (a 256-byte multiple), and
+// the bytes the exact-B route stages at the start of the workspace (none for bf16 d_out).
+int64_t bsplit_plane_elems(int64_t M, int64_t N) { return round_up(M * N, 128); }
+int64_t bsplit_plane_bytes(int g_dtype, int64_t M, int64_t N) {
+    return g_dtype == kBF16 ? 0 : 2 * 2 * bsplit_plane_elems(M, N);
+}
+
+template <int NV, int XB>
 void launch_fold(dim3 grid, hipStream_t s, const WView& w, const void* d_out, int64_t M, float* out, int64_t ld,
-                 int64_t stride, int64_t limit, int g_fast, int per, int splits, int mtiles) {
-    hipLaunchKernelGGL((gemm_bwd_fold_kernel<NV>), grid, dim3(256), 0, s, w, d_out, M, out, ld, stride, limit, g_fast,
-                       per, splits, mtiles);
+                 int64_t stride, int64_t limit, int g_fast, int per, int splits, int mtiles, int64_t a_plane) {
+    hipLaunchKernelGGL((gemm_bwd_fold_kernel<NV, XB>), grid, dim3(256), 0, s, w, d_out, M, out, ld, stride, limit,
+                       g_fast, per, splits, mtiles, a_plane);
 }
 
 template <int GT, int NV>
@@ -670,11 +767,12 @@ BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M, int f
         return p;
     }
     BwdPlan p{};
-    p.mode = v2_fold(w, g_dtype, fold_ok) ? kModeFold : kModeSplit;
+    p.mode = v2_mode(w, g_dtype, fold_ok);
     const int64_t blocks = ((w.k_pad + kBK - 1) / kBK) * ((M + kBM - 1) / kBM);
     const int64_t n_chunks = (w.N + kCN - 1) / kCN;
     p.splits = pick_gemm_splits(blocks, n_chunks, M, w.k_pad, 256, 2.0, nullptr, force_splits);
     p.ws_bytes = p.splits > 1 ? (int64_t)p.splits * frag_plane_floats(M, w.k_pad) * 4 : 0;
+    if (p.mode == kModeBSplit) p.ws_bytes += bsplit_plane_bytes(g_dtype, M, w.N);
     p.v1 = 0;
     return p;
 }
@@ -696,8 +794,39 @@ hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64
     const int64_t limit = plan.splits == 1 ? w.K : w.k_pad;
     const int sp = plan.splits, mt = (int)mtiles;
     if (plan.mode == kModeFold) {
-        if (w.gs == 32) launch_fold<2>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt);
-        else launch_fold<1>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt);
+        if (w.gs == 32) launch_fold<2, 0>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt, 0);
+        else launch_fold<1, 0>(grid, s, w, d_out, M, out, ld, stride, limit, g_fast, per, sp, mt, 0);
+    } else if (plan.mode == kModeBSplit) {
+        // the workspace starts with the bf16 planes of d_out (none for bf16 d_out), then the partials
+        const int64_t pb = bsplit_plane_bytes(g_dtype, M, w.N);
+        const void* A = d_out;
+        int fast = g_fast;
+        const int64_t ap = bsplit_plane_elems(M, w.N);
+        if (pb > 0) {
+            uint32_t* hi = reinterpret_cast<uint32_t*>(ws);
+            uint32_t* lo = hi + ap / 2;
+            const int64_t total = M * w.N;
+            const int64_t nb = (total + 2047) / 2048;
+            if (nb > 0x7fffffff) return hipErrorInvalidConfiguration;
+            const int vec = (reinterpret_cast<uintptr_t>(d_out) & 15u) == 0;
+            if (g_dtype == kF32)
+                hipLaunchKernelGGL((split_planes_kernel<kF32>), dim3((unsigned)nb), dim3(256), 0, s, d_out, total, vec,
+                                   hi, lo);
+            else
+                hipLaunchKernelGGL((split_planes_kernel<kF16>), dim3((unsigned)nb), dim3(256), 0, s, d_out, total, vec,
+                                   hi, lo);
+            A = hi;
+            fast = (w.N * 2) % 16 == 0;
+            if (plan.splits > 1) out = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + pb);
+        }
+        if (pb > 0) {
+            if (w.gs == 32) launch_fold<2, 2>(grid, s, w, A, M, out, ld, stride, limit, fast, per, sp, mt, ap);
+            else launch_fold<1, 2>(grid, s, w, A, M, out, ld, stride, limit, fast, per, sp, mt, ap);
+        } else {
+            if (w.gs == 32) launch_fold<2, 1>(grid, s, w, A, M, out, ld, stride, limit, fast, per, sp, mt, ap);
+            else launch_fold<1, 1>(grid, s, w, A, M, out, ld, stride, limit, fast, per, sp, mt, ap);
+        }
+        ws = (plan.splits > 1) ? out : ws;
     } else {
         const bool one = w.gs % 256 == 0;
         const int sf = w.scale_f16;
@@ -720,7 +849,7 @@ hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64
     if (e != hipSuccess || plan.splits == 1) return e;
     const float* ys[1] = {d_x};
     const int64_t yld[1] = {w.K}, off[1] = {0}, cols[1] = {w.K};
-    return launch_reduce_frags(ws, plan.splits, M, w.k_pad, ys, yld, off, cols, 1, plan.mode == kModeFold ? 0 : 1, s);
+    return launch_reduce_frags(ws, plan.splits, M, w.k_pad, ys, yld, off, cols, 1, plan.mode == kModeSplit ? 1 : 0, s);
 }
 
 }  // namespace q4gsw

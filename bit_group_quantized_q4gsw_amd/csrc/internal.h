@@ -70,7 +70,7 @@ hipError_t launch_generic_bwd(const WView& w, const void* d_out, int g_dtype, in
                               hipStream_t s);
 
 // gemm_fwd.hip: MFMA forward over up to three weights sharing K (fused QKV uses three).
-enum GemmMode : int { kModeFold = 0, kModeGroup = 1, kModeSplit = 2 };
+enum GemmMode : int { kModeFold = 0, kModeGroup = 1, kModeSplit = 2, kModeBSplit = 3 };
 struct FwdSeg {
     WView w;
     float* out;              // [M, N] final output of this segment
@@ -98,7 +98,7 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
 // MFMA input gradient: gemm_bwd2.hip (32x32x16) dispatches, gemm_bwd.hip (16x16x32) covers
 // the group sizes the former does not take.
 struct BwdPlan {
-    int mode;                // kModeFold or kModeSplit
+    int mode;                // kModeFold, kModeSplit or kModeBSplit
     int splits;              // N (contraction) splits
     int64_t ws_bytes;
     int v1;                  // 1: the 16x16x32 kernel serves this call

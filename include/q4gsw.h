@@ -87,7 +87,9 @@ typedef enum q4gsw_route_id {
     Q4GSW_ROUTE_BWD_GEMV = 6,      /* input gradient, M <= 8: streaming transposed GEMV */
     Q4GSW_ROUTE_BWD_FOLD = 7,      /* input gradient, fp16 d_out: MFMA f16 on folded fp16 weight */
     Q4GSW_ROUTE_BWD_SPLIT = 8,     /* input gradient: d_out*scale split into bf16 hi+lo, two MFMA passes */
-    Q4GSW_ROUTE_QKV_FUSED = 9      /* fused QKV: one launch over the three weights */
+    Q4GSW_ROUTE_QKV_FUSED = 9,     /* fused QKV: one launch over the three weights */
+    Q4GSW_ROUTE_BWD_BSPLIT = 10    /* input gradient, fp16 scales, gs % 64 == 0 or 32: d_out in bf16 hi+lo
+                                      planes, (code - 8) * scale split exactly into bf16 hi+lo, 2 or 4 passes */
 } q4gsw_route_id;
 
 /*
@@ -96,14 +98,14 @@ typedef enum q4gsw_route_id {
  * leaves every choice to the library; the plain calls take none.
  *   route      Q4GSW_ROUTE_NONE: automatic.  Otherwise the route family to take:
  *              GENERIC; a small-M route (GEMV, BWD_GEMV); or an MFMA route (any of
- *              GEMM_FOLD, GEMM_GROUP, GEMM_SPLIT, BWD_FOLD, BWD_SPLIT, QKV_FUSED:
+ *              GEMM_FOLD, GEMM_GROUP, GEMM_SPLIT, BWD_FOLD, BWD_SPLIT, BWD_BSPLIT, QKV_FUSED:
  *              the library picks the precision route inside the family).  A call
  *              the family cannot serve returns Q4GSW_E_ROUTE; a value outside the
  *              enum returns Q4GSW_E_ROUTE too.
  *   tile_rows  forward / QKV MFMA block rows: 0 (per shape), 64 or 128
  *              (Q4GSW_E_SHAPE otherwise).
  *   splits     contraction splits of the 32x32 MFMA GEMMs (forward, QKV and the
- *              input-gradient routes BWD_FOLD and BWD_SPLIT): 0 (per shape) or
+ *              input-gradient routes BWD_FOLD, BWD_SPLIT and BWD_BSPLIT): 0 (per shape) or
  *              1..64 (Q4GSW_E_SHAPE otherwise), clamped to the 64-wide chunks and
  *              rounded to a count with no empty split.
  * A workspace is sized for the options it is used with (q4gsw_*_workspace_bytes_ex).

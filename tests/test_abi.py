@@ -148,8 +148,17 @@ def test_route_selection(q):
     assert route(q, q.OP_FWD, odd, 100, q.F16) == "generic"
     assert route(q, q.OP_BWD_INPUT, odd, 100, q.F32) == "generic"
     small_gs = fake_desc(q, 256, 256, 32, 1, flags=fold)
-    assert route(q, q.OP_BWD_INPUT, small_gs, 64, q.F32) == "generic"      # split route needs gs % 128 == 0
+    assert route(q, q.OP_BWD_INPUT, small_gs, 64, q.F32) == "bwd_bsplit"   # exact bf16 B, gs = 32
+    assert route(q, q.OP_BWD_INPUT, small_gs, 64, q.BF16) == "bwd_bsplit"
     assert route(q, q.OP_BWD_INPUT, small_gs, 64, q.F16) == "bwd_fold"
+    gs64 = fake_desc(q, 256, 512, 64, 1, flags=0)                           # not foldable
+    assert route(q, q.OP_BWD_INPUT, gs64, 64, q.F16) == "bwd_bsplit"
+    assert route(q, q.OP_BWD_INPUT, gs64, 64, q.F32) == "bwd_bsplit"
+    f32_scales = fake_desc(q, 256, 256, 32, 0)                             # fp32 scales: no exact hi + lo
+    assert route(q, q.OP_BWD_INPUT, f32_scales, 64, q.F32) == "generic"
+    gs16 = fake_desc(q, 256, 256, 16, 1, flags=fold)
+    assert route(q, q.OP_BWD_INPUT, gs16, 64, q.F16) == "bwd_fold"          # the 16x16x32 kernel
+    assert route(q, q.OP_BWD_INPUT, gs16, 64, q.F32) == "generic"
     assert route(q, q.OP_FWD, dec, 0, q.F16) == "none"
     assert route(q, q.OP_FWD, dec, 1, 5) == "none"
 
@@ -197,7 +206,7 @@ def test_options_validation(q):
     lib = q.lib()
     d = fake_desc(q, 256, 512, 32, 1, flags=1)
     x, y = FAKE * 8, FAKE * 16
-    for (r, rows, splits), want in [((10, 0, 0), E_ROUTE), ((-1, 0, 0), E_ROUTE), ((0, 96, 0), E_SHAPE),
+    for (r, rows, splits), want in [((11, 0, 0), E_ROUTE), ((-1, 0, 0), E_ROUTE), ((0, 96, 0), E_SHAPE),
                                     ((0, 0, -1), E_SHAPE), ((0, 0, 65), E_SHAPE)]:
         o = q.binding.Options(r, rows, splits)
         assert lib.q4gsw_linear_fwd_ex(ctypes.byref(d), x, q.F16, 64, y, None, 0, ctypes.byref(o), None) == want
