@@ -39,6 +39,20 @@
  *       fusion with BK64 kernel" (the QKV paragraph).  It is composed in the
  *       Python wrapper from three calls of oracle_linear_fwd.
  *
+ *   dq8ca        the linear_dq8ca_q4gsw op named in the "Suggested split" of the
+ *       react-native-executorch issue above: a linear whose activations are
+ *       quantised to int8 on the fly.  The pages give only the op's name; the
+ *       reading here ("dq8ca": dynamic int8, per channel of the activation, i.e. per
+ *       row / token, asymmetric) is, for each row, with every step in fp32 as
+ *       written and rint rounding half to even:
+ *         lo = min(0, min_k x[k]),  hi = max(0, max_k x[k])    (zero stays exact)
+ *         scale = (hi - lo) / 255, raised to the smallest normal fp32 if below it
+ *         inv = 1 / scale
+ *         zp = clamp(-128 - rint(lo * inv), -128, 127)
+ *         q[k] = clamp(rint(x[k] * inv) + zp, -128, 127)
+ *       and the row stands for scale * (q[k] - zp).  The linear is the forward
+ *       above applied to those values, in fp64 (oracle_linear_dq8ca).
+ *
  * Every input element is widened exactly to double: fp16 and bf16 are decoded
  * from their IEEE bit fields here.  Every product is exact in fp64 (at most
  * 24 + 3 + 24 significant bits); sums run with the contraction index
@@ -49,6 +63,7 @@
  * Threads split the output elements only, so every sum keeps its order and the
  * results are bitwise identical for any thread count.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -237,6 +252,68 @@ int oracle_embedding(const int64_t *ids, int64_t T, const uint8_t *codes, const 
 }
 
 /* The number of OpenMP threads a parallel region would use after set_threads(nthreads). */
+/* Per-row int8 quantisation of the activation (the dq8ca reading in the header).  The
+ * arithmetic is fp32 on purpose: it decides integers, and the GPU takes the same decisions in
+ * the same precision.  Outputs: q [M, K] int8, scale [M] fp32, zp [M] int32. */
+int oracle_dq8ca_quantize(const void *x, int act_dtype, int64_t M, int64_t K,
+                          int8_t *q, float *scale, int32_t *zp, int nthreads)
+{
+    if (M < 1 || K < 1 || act_dtype < ORACLE_F32 || act_dtype > ORACLE_BF16) return ORACLE_E_ARG;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t i = 0; i < K; ++i) {
+            const float v = (float)element(x, act_dtype, m * K + i);    /* exact: an fp32/fp16/bf16 value */
+            if (v < lo) lo = v;
+            if (v > hi) hi = v;
+        }
+        float s = (hi - lo) / 255.0f;
+        if (s < FLT_MIN) s = FLT_MIN;
+        const float inv = 1.0f / s;
+        int z = -128 - (int)rintf(lo * inv);
+        if (z < -128) z = -128;
+        if (z > 127) z = 127;
+        for (int64_t i = 0; i < K; ++i) {
+            const float v = (float)element(x, act_dtype, m * K + i);
+            int t = (int)rintf(v * inv) + z;
+            if (t < -128) t = -128;
+            if (t > 127) t = 127;
+            q[m * K + i] = (int8_t)t;
+        }
+        scale[m] = s;
+        zp[m] = z;
+    }
+    return ORACLE_OK;
+}
+
+/* The linear on the quantised rows: y[m,n] = sum_k scale[m] * (q[m,k] - zp[m]) * dequant(W[n,k]),
+ * in fp64 with k ascending, and its normaliser R = sum |scale[m] * (q - zp)| * |dequant(W[n,k])|. */
+int oracle_linear_dq8ca(const int8_t *q, const float *scale, const int32_t *zp, int64_t M,
+                        const uint8_t *codes, const void *scales, int scale_dtype,
+                        int64_t N, int64_t K, int64_t group_size, double *y, double *norm, int nthreads)
+{
+    int st = check_args(ORACLE_F32, scale_dtype, M, N, K, group_size, codes);
+    if (st != ORACLE_OK) return st;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < M * N; ++o) {
+        const int64_t m = o / N;
+        const int64_t n = o - m * N;
+        double acc = 0.0, nrm = 0.0;
+        const double sm = (double)scale[m];
+        for (int64_t k = 0; k != K; ++k) {
+            double a = sm * (double)((int)q[m * K + k] - (int)zp[m]);
+            double w = oracle_dequant(codes, scales, scale_dtype, N, K, group_size, n, k);
+            acc += a * w;
+            nrm += fabs(a) * fabs(w);
+        }
+        y[o] = acc;
+        norm[o] = nrm;
+    }
+    return ORACLE_OK;
+}
+
 int oracle_threads(int nthreads)
 {
     set_threads(nthreads);

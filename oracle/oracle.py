@@ -53,6 +53,10 @@ class Oracle:
         handle.oracle_threads.argtypes = [ctypes.c_int]
         handle.oracle_embedding.restype = ctypes.c_int
         handle.oracle_embedding.argtypes = [vp, i64, vp, vp, ip, i64, i64, i64, vp]
+        handle.oracle_dq8ca_quantize.restype = ctypes.c_int
+        handle.oracle_dq8ca_quantize.argtypes = [vp, ip, i64, i64, vp, vp, vp, ip]
+        handle.oracle_linear_dq8ca.restype = ctypes.c_int
+        handle.oracle_linear_dq8ca.argtypes = [vp, vp, vp, i64, vp, vp, ip, i64, i64, i64, vp, vp, ip]
         self.lib = handle
         self.path = path
 
@@ -117,6 +121,41 @@ class Oracle:
             raise OracleError(f"oracle_embedding returned {status}")
         return out
 
+    def dq8ca_quantize(self, x: torch.Tensor, threads: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Per-row int8 quantisation of x [M, K]: (q int8 [M, K], scale float32 [M], zp int32 [M])."""
+        x = x.contiguous()
+        if x.dim() != 2:
+            raise OracleError("x must be [M, K]")
+        M, K = x.shape
+        q = np.zeros((M, K), dtype=np.int8)
+        scale = np.zeros(M, dtype=np.float32)
+        zp = np.zeros(M, dtype=np.int32)
+        status = self.lib.oracle_dq8ca_quantize(_ptr(x), _DTYPE_CODE[x.dtype], M, K, q.ctypes.data,
+                                                scale.ctypes.data, zp.ctypes.data, threads)
+        if status != 0:
+            raise OracleError(f"oracle_dq8ca_quantize returned {status}")
+        return q, scale, zp
+
+    def linear_dq8ca(self, x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, group_size: int,
+                     threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """y = (scale * (q - zp)) . dequant(W)^T for the per-row int8 quantisation of x, and its
+        normaliser, both [M, N] float64."""
+        codes = codes.contiguous()
+        scales = scales.contiguous()
+        N, K = codes.shape
+        if x.dim() != 2 or x.shape[1] != K:
+            raise OracleError("x must be [M, K]")
+        q, scale, zp = self.dq8ca_quantize(x, threads)
+        M = x.shape[0]
+        out = np.zeros((M, N), dtype=np.float64)
+        norm = np.zeros((M, N), dtype=np.float64)
+        status = self.lib.oracle_linear_dq8ca(q.ctypes.data, scale.ctypes.data, zp.ctypes.data, M, _ptr(codes),
+                                              _ptr(scales), _DTYPE_CODE[scales.dtype], N, K, group_size,
+                                              out.ctypes.data, norm.ctypes.data, threads)
+        if status != 0:
+            raise OracleError(f"oracle_linear_dq8ca returned {status}")
+        return out, norm
+
     def dequant(self, codes: torch.Tensor, scales: torch.Tensor, group_size: int, n: int, k: int) -> float:
         """One element of dequant(W), as the oracle computes it."""
         codes = codes.contiguous()
@@ -167,3 +206,11 @@ def qkv(x, weights, threads=0):
 
 def embedding(ids, codes, scales, group_size):
     return default().embedding(ids, codes, scales, group_size)
+
+
+def dq8ca_quantize(x, threads=0):
+    return default().dq8ca_quantize(x, threads)
+
+
+def linear_dq8ca(x, codes, scales, group_size, threads=0):
+    return default().linear_dq8ca(x, codes, scales, group_size, threads)

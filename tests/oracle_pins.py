@@ -17,7 +17,11 @@ The facts:
   * QKV equals three forwards; thread-count invariance; R >= |y| with equality
     when every term has one sign;
   * the embedding gather equals rows of the numpy-dequantised matrix and the
-    backward of a one-hot output gradient; ids outside [0, N) give zero rows.
+    backward of a one-hot output gradient; ids outside [0, N) give zero rows;
+  * dq8ca (per-row int8 activations): hand-worked rows (tests/golden); PyTorch's own
+    quantizer reproduces the codes from the oracle's scale and zero point; nearest-grid,
+    span, zero and monotonicity properties; on-grid rows give exactly the plain forward;
+    the linear against a numpy matmul of the dequantised rows.
 """
 from __future__ import annotations
 
@@ -326,6 +330,96 @@ def pin_embedding(o):
     assert o.embedding(torch.zeros(0, dtype=torch.int64), codes, scales, gs).shape == (0, K)
 
 
+def pin_dq8ca_golden(o):
+    g = load_golden("dq8ca_rows.txt")
+    for row in "abcd":
+        x = [float(v) for v in g[f"{row}_x"][0]]
+        acts = ("f32",) if row == "a" else ACT_DTYPES      # row a holds 0.3, exact in fp32 only
+        for act in acts:
+            q, scale, zp = o.dq8ca_quantize(_t([x], act))
+            assert q[0].tolist() == [int(v) for v in g[f"{row}_q"][0]], (row, act, q)
+            assert float(scale[0]) == g[f"{row}_scale"], (row, act, scale)
+            assert int(zp[0]) == int(g[f"{row}_zp"]), (row, act, zp)
+
+
+def _dq8ca_rows(seed):
+    """Rows of several magnitudes and sign mixes (some all positive, all negative, with zeros)."""
+    g = torch.Generator().manual_seed(seed)
+    rows = []
+    for i in range(24):
+        r = torch.randn(1, 96, generator=g) * (10.0 ** (i % 7 - 3))
+        if i % 4 == 1:
+            r = r.abs()
+        elif i % 4 == 2:
+            r = -r.abs()
+        if i % 6 == 3:
+            r[0, ::5] = 0.0
+        rows.append(r)
+    return torch.cat(rows)
+
+
+def pin_dq8ca_library(o):
+    """PyTorch's quantize_per_tensor (its own implementation) maps each row to the same int8
+    codes from the oracle's scale and zero point."""
+    x = _dq8ca_rows(5)
+    q, scale, zp = o.dq8ca_quantize(x)
+    for m in range(x.shape[0]):
+        ref = torch.quantize_per_tensor(x[m], float(scale[m]), int(zp[m]), torch.qint8).int_repr().numpy()
+        assert np.array_equal(ref, q[m]), (m, np.nonzero(ref != q[m]))
+
+
+def pin_dq8ca_properties(o):
+    """Facts of an 8-bit asymmetric grid that spans each row, whatever the formulas: zero is a
+    grid point, every value is within half a step of its grid value (plus the fp32 roundings of the
+    step, its reciprocal and x / step carried over at most 255 steps: 255 * 3 * 2^-24 of a step),
+    the 255 steps span [min(0, row min), max(0, row max)], the row's extreme below zero takes code
+    -128, codes are monotone."""
+    for act in ACT_DTYPES:
+        x = _dq8ca_rows(6).to(DTYPES[act])
+        q, scale, zp = o.dq8ca_quantize(x)
+        xf = x.to(torch.float64).numpy()
+        for m in range(xf.shape[0]):
+            s = float(scale[m])
+            lo, hi = min(0.0, xf[m].min()), max(0.0, xf[m].max())
+            assert abs(s * 255 - (hi - lo)) <= 2 ** -21 * (hi - lo), (act, m)
+            back = s * (q[m].astype(np.float64) - zp[m])
+            assert np.all(np.abs(back - xf[m]) <= s * (0.5 + 255 * 3 * 2 ** -24)), (act, m)
+            assert np.all(back[xf[m] == 0] == 0.0)
+            assert np.all(np.diff(q[m][np.argsort(xf[m], kind="stable")].astype(int)) >= 0)
+            if lo < 0:
+                assert q[m][np.argmin(xf[m])] == -128
+    z = torch.zeros(2, 8)
+    q, scale, zp = o.dq8ca_quantize(z)
+    assert np.all(q == -128) and np.all(zp == -128) and np.all(scale > 0)
+
+
+def pin_dq8ca_linear(o):
+    """Rows already on the grid (scale 1/64) give exactly the plain forward; random rows match
+    a numpy matmul of the dequantised rows; code 8 contributes zero."""
+    g = torch.Generator().manual_seed(8)
+    M, N, K, gs = 5, 7, 64, 16
+    j = torch.randint(-128, 128, (M, K), generator=g)
+    j[:, 0], j[:, 1] = -128, 127                       # each row spans [-2, 127/64]: scale 1/64, zp 0
+    x = (j.to(torch.float64) / 64).to(torch.float32)
+    codes = draw_codes(g, N, K)
+    for sdt in SCALE_DTYPES:
+        scales = draw_scales(g, K // gs, N, sdt, 0.005, 0.02)
+        y, r = o.linear_dq8ca(x, codes, scales, gs)
+        y0, r0 = o.linear_fwd(x, codes, scales, gs)
+        assert np.array_equal(y, y0) and np.array_equal(r, r0), sdt
+    x = _dq8ca_rows(9)[:, :64].contiguous()
+    scales = draw_scales(g, K // gs, N, "f16", 0.005, 0.02)
+    y, r = o.linear_dq8ca(x, codes, scales, gs)
+    q, scale, zp = o.dq8ca_quantize(x)
+    xt = scale.astype(np.float64)[:, None] * (q.astype(np.float64) - zp[:, None])
+    ref = xt @ _dense(codes, scales, gs).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * r + 1e-300)
+    assert np.allclose(r, np.abs(xt) @ np.abs(_dense(codes, scales, gs)).T, rtol=1e-12, atol=0)
+    eight = torch.full((N, K), 8, dtype=torch.uint8)
+    assert np.array_equal(o.linear_dq8ca(x, eight, scales, gs)[0], np.zeros((x.shape[0], N)))
+
+
 PINS = [pin_worked_example, pin_code_table, pin_decoders, pin_brute_force, pin_numpy_matmul,
         pin_code8_zero, pin_scale_linearity, pin_adjoint, pin_one_hot, pin_qkv, pin_threads,
-        pin_normaliser, pin_embedding]
+        pin_normaliser, pin_embedding, pin_dq8ca_golden, pin_dq8ca_library, pin_dq8ca_properties,
+        pin_dq8ca_linear]

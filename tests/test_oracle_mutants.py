@@ -32,6 +32,13 @@ MUTANTS = {
     "embedding_ids_reversed": ("int64_t n = ids[t];", "int64_t n = ids[T - 1 - t];"),
     "embedding_out_of_range_one": (": 0.0;", ": 1.0;"),
     "embedding_k_reversed": ("group_size, n, k)\n", "group_size, n, K - 1 - k)\n"),
+    "dq8ca_scale_256": ("(hi - lo) / 255.0f", "(hi - lo) / 256.0f"),
+    "dq8ca_zero_point_sign": ("int z = -128 - (int)rintf(lo * inv);", "int z = -128 + (int)rintf(lo * inv);"),
+    "dq8ca_truncate": ("int t = (int)rintf(v * inv) + z;", "int t = (int)(v * inv) + z;"),
+    "dq8ca_clamp_126": ("if (t > 127) t = 127;", "if (t > 126) t = 126;"),
+    "dq8ca_range_without_zero": ("float lo = 0.0f, hi = 0.0f;", "float lo = 1e30f, hi = -1e30f;"),
+    "dq8ca_linear_without_zp": ("(double)((int)q[m * K + k] - (int)zp[m])", "(double)((int)q[m * K + k])"),
+    "dq8ca_linear_first_row_scale": ("const double sm = (double)scale[m];", "const double sm = (double)scale[0];"),
 }
 
 
