@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0        # MI355X dense fp16 / bf16 MFMA
+INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "q4gsw linear TFLOP/s + weight GB/s (decode, prefill, QKV, bwd) vs roofline"
 QKV_MS = (128, 508, 512)
@@ -39,8 +40,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--ops", default="decode,prefill,qkv,bwd,embedding",
-                   help="comma-separated ops (embedding and the decode-shaped QKV are timed outside the step)")
+    p.add_argument("--ops", default="decode,prefill,qkv,bwd,embedding,dq8ca",
+                   help="comma-separated ops (embedding, dq8ca and the decode-shaped QKV are timed outside "
+                        "the step)")
     p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per M=512 op in the oracle sample")
@@ -86,12 +88,17 @@ class Op:
         elif kind == "bwd":
             need = q.workspace_bytes(q.OP_BWD_INPUT, pw0[0], self.M, act.dtype)
             self.route = q.route(q.OP_BWD_INPUT, pw0[0], self.M, act.dtype)
+        elif kind == "dq8ca":
+            need = q.workspace_bytes(q.OP_DQ8CA, pw0[0], self.M, act.dtype)
+            self.route = q.route(q.OP_DQ8CA, pw0[0], self.M, act.dtype)
         else:
             need = q.workspace_bytes(q.OP_FWD, pw0[0], self.M, act.dtype)
             self.route = q.route(q.OP_FWD, pw0[0], self.M, act.dtype)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.set_bytes = sum(p.buffer.numel() for p in pw0) + act.numel() * act.element_size()
-        self.bound = "hbm" if self.flops / self.bytes < MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+        # the int8 path runs on int8 MFMA; the others on fp16 / bf16 MFMA
+        self.peak = INT8_PEAK_TOPS if kind == "dq8ca" else MFMA_PEAK_TFLOPS
+        self.bound = "hbm" if self.flops / self.bytes < self.peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
 
     def run(self, q, i):
         pw, a, outs = self.sets[i % len(self.sets)]
@@ -99,6 +106,8 @@ class Op:
             q.qkv_fused(pw[0], pw[1], pw[2], a, outs=outs, workspace=self.ws)
         elif self.kind == "bwd":
             q.linear_bwd_input(pw[0], a, out=outs[0], workspace=self.ws)
+        elif self.kind == "dq8ca":
+            q.linear_dq8ca(pw[0], a, out=outs[0], workspace=self.ws)
         else:
             q.linear_fwd(pw[0], a, out=outs[0], workspace=self.ws)
 
@@ -123,6 +132,7 @@ class EmbOp:
             self.sets.append((pw, case.ids.cuda(), torch.empty(self.M, w.K, dtype=torch.float32, device="cuda")))
         self.route = "embedding"
         self.bound = "hbm"
+        self.peak = MFMA_PEAK_TFLOPS
 
     def run(self, q, i):
         pw, ids, out = self.sets[i % len(self.sets)]
@@ -160,6 +170,9 @@ def build_ops(q, names, rotate):
             if n in ("bwd", "bwd_gs32"):
                 specs.append(("bwd_gs32", "bwd", make_linear(512, 2048, 2048, 32, "f32", "f16", seed=0, fwd=False,
                                                              bwd=True, sigma=0.1)))
+        elif n == "dq8ca":
+            # the prefill workload with its activation rows quantised to int8 per row, outside the step
+            specs.append(("dq8ca", "dq8ca", make_workload("prefill")))
         elif n in ("embedding", "emb_t512", "emb_t1"):
             # the row gather from the tied embedding table, outside the step: 512 ids and one id
             emb = make_workload("embedding")
@@ -177,7 +190,7 @@ def build_ops(q, names, rotate):
         act = case.x if case.x is not None else case.d_out
         return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
 
-    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1", "bwd_h", "bwd_gs32"}
+    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1", "bwd_h", "bwd_gs32", "dq8ca"}
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing
@@ -228,7 +241,8 @@ OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_"),
               "qkv_m128": ("gemm_fwd", "reduce_"), "qkv_m508": ("gemm_fwd", "reduce_"),
               "qkv_m512": ("gemm_fwd", "reduce_"), "bwd": ("gemm_bwd", "reduce_"),
               "bwd_h": ("gemm_bwd", "reduce_"), "bwd_gs32": ("gemm_bwd", "reduce_", "split_planes"),
-              "emb_t512": ("embedding_kernel",), "emb_t1": ("embedding_kernel",)}
+              "emb_t512": ("embedding_kernel",), "emb_t1": ("embedding_kernel",),
+              "dq8ca": ("dq8ca_", "reduce_")}
 
 
 def _counter_means(d, counter):
@@ -425,12 +439,12 @@ def main():
         tflops = op.flops / s / 1e12
         gbs = op.bytes / s / 1e9
         wgbs = op.weight_bytes / s / 1e9
-        frac = gbs / HBM_PEAK_GBS if op.bound == "hbm" else tflops / MFMA_PEAK_TFLOPS
+        frac = gbs / HBM_PEAK_GBS if op.bound == "hbm" else tflops / op.peak
         per_op[op.name] = {"ms": round(ms, 5), "eager_ms": round(eager_ms, 5), "in_step": op.in_step,
                            "tflops": round(tflops, 2),
                            "weight_gbs": round(wgbs, 1),
                            "alg_gbs": round(gbs, 1), "bound": op.bound, "roofline_frac": round(frac, 4),
-                           "route": op.route, "M": op.M}
+                           "route": op.route, "M": op.M, "peak": op.peak if op.bound != "hbm" else HBM_PEAK_GBS}
         if op.in_step:
             total_flops += op.flops
 

@@ -19,10 +19,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4gsw.so")
 
 F32, F16, BF16 = 0, 1, 2
-OP_FWD, OP_BWD_INPUT, OP_QKV = 0, 1, 2
+OP_FWD, OP_BWD_INPUT, OP_QKV, OP_DQ8CA = 0, 1, 2, 3
 ROUTES = {
     "none": 0, "generic": 1, "gemv": 2, "gemm_fold": 3, "gemm_group": 4, "gemm_split": 5,
-    "bwd_gemv": 6, "bwd_fold": 7, "bwd_split": 8, "qkv_fused": 9, "bwd_bsplit": 10,
+    "bwd_gemv": 6, "bwd_fold": 7, "bwd_split": 8, "qkv_fused": 9, "bwd_bsplit": 10, "dq8ca": 11,
 }
 FLAG_FOLD_F16 = 1
 _TORCH_DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
             "q4gsw_route": [i32, pw, i64, i32],
             "q4gsw_plan": [i32, pw, pw, pw, i64, i32, po, ctypes.POINTER(PlanInfo)],
             "q4gsw_embedding": [pw, vp, i64, vp, vp],
+            "q4gsw_dq8ca_quantize": [vp, i32, i64, i64, vp, vp, vp, vp],
+            "q4gsw_linear_dq8ca": [pw, vp, i32, i64, vp, vp, u64, vp],
+            "q4gsw_linear_dq8ca_ex": [pw, vp, i32, i64, vp, vp, u64, po, vp],
         }
         for name, args in sigs.items():
             fn = getattr(h, name)
@@ -282,6 +285,35 @@ def linear_bwd_input(w: PackedWeight, d_out: torch.Tensor, out: Optional[torch.T
     _check(lib().q4gsw_linear_bwd_input_ex(w.ref(), d_out.data_ptr(), _TORCH_DTYPE[d_out.dtype], M,
                                            dx.data_ptr(), wp, wb, _opts(), _stream()), "q4gsw_linear_bwd_input")
     return dx
+
+
+def dq8ca_quantize(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Per-row int8 quantisation of x [M, K]: (q int8 [M, K], scale fp32 [M], zero_point int32 [M])."""
+    x = _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    q = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    zp = torch.empty(M, dtype=torch.int32, device=x.device)
+    _check(lib().q4gsw_dq8ca_quantize(x.data_ptr(), _TORCH_DTYPE[x.dtype], M, K, q.data_ptr(), scale.data_ptr(),
+                                      zp.data_ptr(), _stream()), "q4gsw_dq8ca_quantize")
+    return q, scale, zp
+
+
+def linear_dq8ca(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M, N] fp32 = the forward of x's rows quantised to int8 per row (linear_dq8ca_q4gsw)."""
+    x = _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    y = _out(out, (M, w.N), x.device, "out")
+    need = workspace_bytes(OP_DQ8CA, w, M, x.dtype)
+    ws, wp, wb = _ws_args(need, workspace, x.device)
+    _check(lib().q4gsw_linear_dq8ca_ex(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), wp, wb,
+                                       _opts(), _stream()), "q4gsw_linear_dq8ca")
+    return y
 
 
 def embedding(w: PackedWeight, ids: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -30,7 +30,7 @@ struct Opts {
 q4gsw_status read_opts(const q4gsw_options* o, Opts* out) {
     *out = Opts{};
     if (!o) return Q4GSW_OK;
-    if (o->route < Q4GSW_ROUTE_NONE || o->route > Q4GSW_ROUTE_BWD_BSPLIT) return Q4GSW_E_ROUTE;
+    if (o->route < Q4GSW_ROUTE_NONE || o->route > Q4GSW_ROUTE_DQ8CA) return Q4GSW_E_ROUTE;
     if (o->tile_rows != 0 && o->tile_rows != 64 && o->tile_rows != 128) return Q4GSW_E_SHAPE;
     if (o->splits < 0 || o->splits > 64) return Q4GSW_E_SHAPE;
     out->route = o->route;
@@ -372,6 +372,12 @@ q4gsw_status q4gsw_workspace_bytes_ex(int32_t op, const q4gsw_weight* w, int64_t
         *bytes = bwd_ws_bytes(w, M, act_dtype, r, o);
         return Q4GSW_OK;
     }
+    if (op == Q4GSW_OP_DQ8CA) {
+        const WView v = view_of(w);
+        if (!dq8ca_supported(v)) return Q4GSW_E_GROUP;
+        *bytes = (uint64_t)plan_dq8ca(v, M, o.splits).ws_bytes;
+        return Q4GSW_OK;
+    }
     return Q4GSW_E_SHAPE;
 }
 
@@ -479,6 +485,43 @@ q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, in
     return q4gsw_linear_bwd_input_ex(w, d_out, g_dtype, M, d_x, ws, ws_bytes, nullptr, stream);
 }
 
+q4gsw_status q4gsw_dq8ca_quantize(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* q, float* scale,
+                                  int32_t* zero_point, void* stream) {
+    if (!x || !q || !scale || !zero_point) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM || K < 1 || K > kMaxDim) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
+    const Range xr = range_of(x, (uint64_t)M * K * esize(x_dtype));
+    const Range qr = range_of(q, (uint64_t)M * K);
+    const Range sr = range_of(scale, (uint64_t)M * 4);
+    const Range zr = range_of(zero_point, (uint64_t)M * 4);
+    if (overlap(qr, xr) || overlap(sr, xr) || overlap(zr, xr) || overlap(qr, sr) || overlap(qr, zr) || overlap(sr, zr))
+        return Q4GSW_E_ALIAS;
+    return hip_status(launch_dq8ca_quantize(x, x_dtype, M, K, q, scale, zero_point, static_cast<hipStream_t>(stream)));
+}
+
+q4gsw_status q4gsw_linear_dq8ca_ex(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y,
+                                   void* ws, uint64_t ws_bytes, const q4gsw_options* opts, void* stream) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!x || !y) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(x_dtype)) return Q4GSW_E_DTYPE;
+    Opts o;
+    if ((st = read_opts(opts, &o)) != Q4GSW_OK) return st;
+    const WView v = view_of(w);
+    if (!dq8ca_supported(v)) return Q4GSW_E_GROUP;
+    const Dq8caPlan plan = plan_dq8ca(v, M, o.splits);
+    const uint64_t need = (uint64_t)plan.ws_bytes;
+    if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
+    if ((st = fwd_alias(w, x, x_dtype, M, y, ws, need)) != Q4GSW_OK) return st;
+    return hip_status(launch_dq8ca(v, x, x_dtype, M, y, plan, ws, static_cast<hipStream_t>(stream)));
+}
+
+q4gsw_status q4gsw_linear_dq8ca(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, float* y, void* ws,
+                                uint64_t ws_bytes, void* stream) {
+    return q4gsw_linear_dq8ca_ex(w, x, x_dtype, M, y, ws, ws_bytes, nullptr, stream);
+}
+
 q4gsw_status q4gsw_qkv_fused_ex(const q4gsw_weight* wq, const q4gsw_weight* wk, const q4gsw_weight* wv, const void* x,
                                 int32_t x_dtype, int64_t M, float* q, float* k, float* v, void* ws, uint64_t ws_bytes,
                                 const q4gsw_options* opts, void* stream) {
@@ -547,6 +590,7 @@ int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dt
     if (op == Q4GSW_OP_FWD) r = pick_fwd(w, M, act_dtype, false, Q4GSW_ROUTE_NONE, &st);
     else if (op == Q4GSW_OP_BWD_INPUT) r = pick_bwd(w, M, act_dtype, Q4GSW_ROUTE_NONE, &st);
     else if (op == Q4GSW_OP_QKV) r = pick_fwd(w, M, act_dtype, true, Q4GSW_ROUTE_NONE, &st);
+    else if (op == Q4GSW_OP_DQ8CA) return dq8ca_supported(view_of(w)) ? Q4GSW_ROUTE_DQ8CA : Q4GSW_ROUTE_NONE;
     else return Q4GSW_ROUTE_NONE;
     return st == Q4GSW_OK ? r : Q4GSW_ROUTE_NONE;
 }
@@ -576,6 +620,7 @@ q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* w
     if (op == Q4GSW_OP_FWD) r = pick_fwd(w, M, act_dtype, false, o.route, &rs);
     else if (op == Q4GSW_OP_BWD_INPUT) r = pick_bwd(w, M, act_dtype, o.route, &rs);
     else if (op == Q4GSW_OP_QKV) r = pick_fwd(w, M, act_dtype, true, o.route, &rs);
+    else if (op == Q4GSW_OP_DQ8CA) r = dq8ca_supported(view_of(w)) ? Q4GSW_ROUTE_DQ8CA : Q4GSW_ROUTE_NONE;
     if (rs != Q4GSW_OK) r = Q4GSW_ROUTE_NONE;
     info->route = r;
     if (r == Q4GSW_ROUTE_NONE) return Q4GSW_OK;
@@ -584,6 +629,9 @@ q4gsw_status q4gsw_plan(int32_t op, const q4gsw_weight* w, const q4gsw_weight* w
         info->splits = gemv_fwd_splits(v, M);
     } else if (r == Q4GSW_ROUTE_BWD_GEMV) {
         info->splits = gemv_bwd_splits(v, M);
+    } else if (r == Q4GSW_ROUTE_DQ8CA) {
+        info->tile_rows = 128;
+        info->splits = plan_dq8ca(v, M, o.splits).splits;
     } else if (r == Q4GSW_ROUTE_BWD_FOLD || r == Q4GSW_ROUTE_BWD_SPLIT || r == Q4GSW_ROUTE_BWD_BSPLIT) {
         info->tile_rows = 128;
         info->splits = plan_gemm_bwd(v, act_dtype, fold_ok(w), M, o.splits).splits;
@@ -616,6 +664,7 @@ const char* q4gsw_route_name(int32_t route) {
         case Q4GSW_ROUTE_BWD_SPLIT: return "bwd_split";
         case Q4GSW_ROUTE_QKV_FUSED: return "qkv_fused";
         case Q4GSW_ROUTE_BWD_BSPLIT: return "bwd_bsplit";
+        case Q4GSW_ROUTE_DQ8CA: return "dq8ca";
         default: return "unknown";
     }
 }

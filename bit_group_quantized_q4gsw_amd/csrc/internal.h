@@ -113,4 +113,17 @@ BwdPlan plan_gemm_bwd_v1(const WView& w, int g_dtype, int fold_ok, int64_t M);
 hipError_t launch_gemm_bwd_v1(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
                               const BwdPlan& plan, float* ws, hipStream_t s);
 
+// dq8ca.hip: the linear on per-row int8 activations (gs % 64 == 0 or gs == 32).  The workspace
+// holds the GEMM-layout codes [M][k_pad], the row scales and -zero points, then the split partials.
+struct Dq8caPlan {
+    int splits;
+    int64_t ws_bytes;
+};
+bool dq8ca_supported(const WView& w);
+Dq8caPlan plan_dq8ca(const WView& w, int64_t M, int force_splits = 0);
+hipError_t launch_dq8ca_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* scale,
+                                 int32_t* zp, hipStream_t s);
+hipError_t launch_dq8ca(const WView& w, const void* x, int x_dtype, int64_t M, float* y, const Dq8caPlan& plan,
+                        void* ws, hipStream_t s);
+
 }  // namespace q4gsw

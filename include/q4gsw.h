@@ -73,7 +73,8 @@ typedef enum q4gsw_dtype {
 typedef enum q4gsw_op {
     Q4GSW_OP_FWD = 0,
     Q4GSW_OP_BWD_INPUT = 1,
-    Q4GSW_OP_QKV = 2
+    Q4GSW_OP_QKV = 2,
+    Q4GSW_OP_DQ8CA = 3           /* q4gsw_linear_dq8ca */
 } q4gsw_op;
 
 /* Kernel routes, reported by q4gsw_route (route attestation). */
@@ -88,8 +89,9 @@ typedef enum q4gsw_route_id {
     Q4GSW_ROUTE_BWD_FOLD = 7,      /* input gradient, fp16 d_out: MFMA f16 on folded fp16 weight */
     Q4GSW_ROUTE_BWD_SPLIT = 8,     /* input gradient: d_out*scale split into bf16 hi+lo, two MFMA passes */
     Q4GSW_ROUTE_QKV_FUSED = 9,     /* fused QKV: one launch over the three weights */
-    Q4GSW_ROUTE_BWD_BSPLIT = 10    /* input gradient, fp16 scales, gs % 64 == 0 or 32: d_out in bf16 hi+lo
+    Q4GSW_ROUTE_BWD_BSPLIT = 10,   /* input gradient, fp16 scales, gs % 64 == 0 or 32: d_out in bf16 hi+lo
                                       planes, (code - 8) * scale split exactly into bf16 hi+lo, 2 or 4 passes */
+    Q4GSW_ROUTE_DQ8CA = 11         /* q4gsw_linear_dq8ca: per-row int8 activations, int8 MFMA */
 } q4gsw_route_id;
 
 /*
@@ -250,6 +252,36 @@ q4gsw_status q4gsw_qkv_fused_ex(const q4gsw_weight *wq, const q4gsw_weight *wk, 
                                 const void *x, int32_t x_dtype, int64_t M,
                                 float *q, float *k, float *v, void *ws, uint64_t ws_bytes,
                                 const q4gsw_options *opts, void *stream);
+
+/*
+ * Per-row int8 quantisation of activations, the activation side of linear_dq8ca_q4gsw (the
+ * "Suggested split" of the react-native-executorch issue "Upstream the Gemma 4 Vulkan support we
+ * carry on our ExecuTorch fork" names the op and nothing more).  Reading: per row (token),
+ * asymmetric, zero exact, every step in fp32 as written, rint rounding half to even:
+ *   lo = min(0, min x), hi = max(0, max x), scale = (hi - lo) / 255 (at least the smallest
+ *   normal fp32), inv = 1 / scale, zero_point = clamp(-128 - rint(lo * inv), -128, 127),
+ *   q = clamp(rint(x * inv) + zero_point, -128, 127); the row stands for scale * (q - zero_point).
+ *   x           device [M, K] in x_dtype (Q4GSW_F32, Q4GSW_F16, Q4GSW_BF16)
+ *   q           device int8 [M, K];  scale device fp32 [M];  zero_point device int32 [M]
+ * E_NULL, E_SHAPE (M or K < 1 or too large), E_DTYPE, E_ALIAS (outputs overlap each other or x).
+ */
+q4gsw_status q4gsw_dq8ca_quantize(const void *x, int32_t x_dtype, int64_t M, int64_t K, int8_t *q,
+                                  float *scale, int32_t *zero_point, void *stream);
+
+/*
+ * linear_dq8ca_q4gsw: y[M, N] (fp32) = (scale * (q - zero_point)) . dequant(W)^T, the forward on
+ * the rows q4gsw_dq8ca_quantize makes of x, quantised on the fly (int8 MFMA; the zero point is
+ * applied exactly in int32, the scales in fp32).  Same packed weight as the forward.
+ *   x   device [M, K] in x_dtype;  y device fp32 [M, N]
+ *   ws  device workspace of ws_bytes >= q4gsw_workspace_bytes(Q4GSW_OP_DQ8CA, ...) (never 0:
+ *       it holds the quantised rows); contents need no initialisation
+ * E_GROUP when group_size is neither 32 nor a multiple of 64; other errors as q4gsw_linear_fwd.
+ */
+q4gsw_status q4gsw_linear_dq8ca(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M, float *y,
+                                void *ws, uint64_t ws_bytes, void *stream);
+/* q4gsw_linear_dq8ca with per-call options (only `splits` applies; NULL: the same call). */
+q4gsw_status q4gsw_linear_dq8ca_ex(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M, float *y,
+                                   void *ws, uint64_t ws_bytes, const q4gsw_options *opts, void *stream);
 
 /*
  * Embedding row gather: out[t, k] = dequant(W)[ids[t], k], for t < T and k < K.

@@ -206,7 +206,7 @@ def test_options_validation(q):
     lib = q.lib()
     d = fake_desc(q, 256, 512, 32, 1, flags=1)
     x, y = FAKE * 8, FAKE * 16
-    for (r, rows, splits), want in [((11, 0, 0), E_ROUTE), ((-1, 0, 0), E_ROUTE), ((0, 96, 0), E_SHAPE),
+    for (r, rows, splits), want in [((12, 0, 0), E_ROUTE), ((-1, 0, 0), E_ROUTE), ((0, 96, 0), E_SHAPE),
                                     ((0, 0, -1), E_SHAPE), ((0, 0, 65), E_SHAPE)]:
         o = q.binding.Options(r, rows, splits)
         assert lib.q4gsw_linear_fwd_ex(ctypes.byref(d), x, q.F16, 64, y, None, 0, ctypes.byref(o), None) == want
@@ -369,6 +369,33 @@ def test_noalloc_forward_validation(q):
     assert need.value > 32 << 20
     assert f(ctypes.byref(pre), x, q.BF16, 1536, y, None) == 12                       # E_SCRATCH
     assert "32 MiB" in q.status_str(12)
+
+
+def test_dq8ca_validation(q):
+    """linear_dq8ca validates like the forward and refuses group sizes its int8 kernel does not
+    take (E_GROUP); the quantize call checks its pointers, sizes, dtype and overlaps."""
+    lib = q.lib()
+    x, y = FAKE * 8, FAKE * 16
+    ok = fake_desc(q, 256, 512, 64, 1, flags=1)
+    assert route(q, 3, ok, 100, q.BF16) == "dq8ca"
+    for gs in (16, 96):
+        d = fake_desc(q, 256, 576 if gs == 96 else 512, gs, 1, flags=1)
+        assert lib.q4gsw_linear_dq8ca(ctypes.byref(d), x, q.BF16, 100, y, FAKE * 32, 1 << 30, None) == E_GROUP
+        assert route(q, 3, d, 100, q.BF16) == "none"
+    need = ctypes.c_uint64()
+    assert lib.q4gsw_workspace_bytes(3, ctypes.byref(ok), 100, q.BF16, ctypes.byref(need)) == S_OK
+    assert need.value >= 100 * 512                        # the quantised rows live in the workspace
+    f = lib.q4gsw_linear_dq8ca
+    assert f(ctypes.byref(ok), x, q.BF16, 100, y, None, 0, None) == E_WS
+    assert f(ctypes.byref(ok), x, q.BF16, 0, y, FAKE * 32, need.value, None) == E_SHAPE
+    assert f(ctypes.byref(ok), x, 9, 100, y, FAKE * 32, need.value, None) == E_DTYPE
+    assert f(ctypes.byref(ok), x, q.BF16, 100, x + 8, FAKE * 32, need.value, None) == E_ALIAS
+    qz = lib.q4gsw_dq8ca_quantize
+    assert qz(None, q.F32, 4, 8, FAKE * 2, FAKE * 3, FAKE * 4, None) == E_NULL
+    assert qz(x, q.F32, 0, 8, FAKE * 2, FAKE * 3, FAKE * 4, None) == E_SHAPE
+    assert qz(x, 5, 4, 8, FAKE * 2, FAKE * 3, FAKE * 4, None) == E_DTYPE
+    assert qz(x, q.F32, 4, 8, x + 16, FAKE * 3, FAKE * 4, None) == E_ALIAS            # codes inside x
+    assert qz(x, q.F32, 4, 8, FAKE * 2, FAKE * 3, FAKE * 3 + 8, None) == E_ALIAS       # zero points inside scales
 
 
 def test_embedding_validation(q):
