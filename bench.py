@@ -52,6 +52,8 @@ def parse():
                    help="rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of a run of --ops OP and of "
                         "--copy-calibration); writes profiles/traffic.json for the op (no GPU needed)")
     p.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (with --ingest-counters)")
+    p.add_argument("--stream-floor", action="store_true",
+                   help="only time a plain streaming read (torch's sum) of the decode weight bytes, cache-cold")
     return p.parse_args()
 
 
@@ -152,6 +154,9 @@ def build_ops(q, names, rotate):
             specs.append(("decode", "fwd", make_workload("decode")))
         elif n == "prefill":
             specs.append(("prefill", "fwd", make_workload("prefill")))
+        elif n.startswith("qkv_m") and n[5:].isdigit():
+            # one QKV row count alone (counter runs)
+            specs.append((n, "qkv", make_workload("qkv", M=int(n[5:]))))
         elif n == "qkv":
             for M in QKV_MS:
                 specs.append((f"qkv_m{M}", "qkv", make_workload("qkv", M=M)))
@@ -211,18 +216,31 @@ def build_ops(q, names, rotate):
     return ops, rotate
 
 
-def source_hash():
+# the sources an op's kernels are built from: the shared headers and the entry points (which
+# plan the launch), plus the files holding its kernels
+_COMMON_SRC = ("api.hip", "device.h", "internal.h", "layout.h")
+_OP_SRC = {"decode": ("gemv.hip",), "qkv_m1": ("gemv.hip",), "qkv_m4": ("gemv.hip",),
+           "prefill": ("gemm_fwd.hip", "gemv.hip"), "qkv_m128": ("gemm_fwd.hip", "gemv.hip"),
+           "qkv_m508": ("gemm_fwd.hip", "gemv.hip"), "qkv_m512": ("gemm_fwd.hip", "gemv.hip"),
+           "bwd": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "bwd_h": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"),
+           "bwd_gs32": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "emb_t512": ("embedding.hip",),
+           "emb_t1": ("embedding.hip",), "dq8ca": ("dq8ca.hip", "gemv.hip")}
+
+
+def source_hash(op_name=None):
+    """Hash of the kernel sources: of every file, or of those an op's kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_group_quantized_q4gsw_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = sorted(os.listdir(csrc)) if op_name is None else sorted(_COMMON_SRC + _OP_SRC[op_name])
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(op_name, src_hash):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this source."""
+def traffic_for(op_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the op's current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -231,7 +249,7 @@ def traffic_for(op_name, src_hash):
     except (OSError, ValueError):
         return None
     ent = data.get(op_name)
-    if not ent or ent.get("src_hash") != src_hash:
+    if not ent or ent.get("src_hash") != source_hash(op_name):
         return None
     return ent.get("bytes_per_launch")
 
@@ -281,7 +299,7 @@ def ingest_counters(op_name, op_fetch, op_write, copy_fetch, copy_write, copy_mi
     ent = {"bytes_per_launch": round(fetch * f_fetch + write * f_write), "fetch_bytes": round(fetch * f_fetch),
            "write_bytes": round(write * f_write), "fetch_counter": round(fetch, 1), "write_counter": round(write, 1),
            "copy_mib": copy_mib, "copy_fetch_counter": round(kf, 1), "copy_write_counter": round(kw, 1),
-           "scale_fetch": f_fetch, "scale_write": f_write, "kernels": list(fams), "src_hash": source_hash()}
+           "scale_fetch": f_fetch, "scale_write": f_write, "kernels": list(fams), "src_hash": source_hash(op_name)}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     data = {}
     if os.path.exists(path):
@@ -303,6 +321,50 @@ def copy_calibration(mib, steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_mib": mib, "steps": steps}))
+
+
+def stream_floor(steps):
+    """Per-launch time of plain streaming reads of the decode workload's weight bytes (codes and
+    scales of the [8192, 2048] gs-32 fp16-scale weight) and of 1 GiB, with PyTorch's own kernels:
+    a row reduction (sum over rows of 1024 floats), a full sum and a device copy (which also writes
+    the bytes).  Each runs over enough rotated copies to exceed the MALL, as a HIP graph between
+    HIP events.  The fastest read is an upper bound on what a streaming read of that size costs."""
+    import torch
+    out = {}
+    for label, nbytes in (("decode_weight_bytes", 8192 * 2048 // 2 + (2048 // 32) * 8192 * 2), ("1GiB", 1 << 30)):
+        n = nbytes // 4
+        sets = max(2, int(MALL_BYTES * 1.5 // nbytes) + 1)
+        bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(sets)]
+        dst = torch.empty(n, dtype=torch.float32, device="cuda")
+        rows = torch.empty(n // 1024, dtype=torch.float32, device="cuda")
+        res = torch.empty((), dtype=torch.float32, device="cuda")
+        kinds = {"row_sum": lambda b: torch.sum(b.view(-1, 1024), dim=1, out=rows),
+                 "full_sum": lambda b: torch.sum(b, dim=0, out=res),
+                 "copy": lambda b: dst.copy_(b)}
+        launches = sets * max(1, (32 + sets - 1) // sets)
+        ent = {"bytes": n * 4, "sets": sets, "launches_per_graph": launches}
+        for kname, fn in kinds.items():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(launches):
+                    fn(bufs[i % sets])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            reps = max(3, steps)
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (reps * launches)
+            ent[kname] = {"us_per_launch": round(us, 3), "read_gbs": round(n * 4 / us / 1e3, 1)}
+            del g
+        out[label] = ent
+        del bufs
+    print(json.dumps({"stream_floor": out}), flush=True)
 
 
 def cpu_baseline(ops, rows_per_op):
@@ -348,6 +410,10 @@ def main():
     if args.copy_calibration:
         torch.cuda.set_device(0)
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.stream_floor:
+        torch.cuda.set_device(0)
+        stream_floor(args.steps)
         return
     import bit_group_quantized_q4gsw_amd as q
     torch.cuda.set_device(0)
@@ -444,7 +510,8 @@ def main():
                            "tflops": round(tflops, 2),
                            "weight_gbs": round(wgbs, 1),
                            "alg_gbs": round(gbs, 1), "bound": op.bound, "roofline_frac": round(frac, 4),
-                           "route": op.route, "M": op.M, "peak": op.peak if op.bound != "hbm" else HBM_PEAK_GBS}
+                           "route": op.route, "M": op.M, "peak": op.peak if op.bound != "hbm" else HBM_PEAK_GBS,
+                           "traffic": traffic_for(op.name)}
         if op.in_step:
             total_flops += op.flops
 
@@ -457,7 +524,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": d["tflops"], "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(d["tflops"] / MFMA_PEAK_TFLOPS, 4)}
-    roof["traffic"] = traffic_for(dom.name, src)
+    roof["traffic"] = traffic_for(dom.name)
     roof["op"] = dom.name
     roof["route"] = dom.route
     roof["per_launch_ms"] = d["ms"]

@@ -57,21 +57,18 @@ constexpr int kCodeBytes = 1024;     // one wave's codes of a chunk
 __device__ constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
 // ---------------------------------------------------------------------------------------------
-// XT: activation dtype.  GEMM: write the GEMM layout (rows of ld bytes, permuted octets, zero
-// padding) and -zp; else the natural [M, K] codes and zp.
-template <int XT, bool GEMM>
-__global__ __launch_bounds__(256) void dq8ca_quant_kernel(const void* __restrict__ x, int64_t K, int64_t ld,
-                                                          int8_t* __restrict__ q, float* __restrict__ scale,
-                                                          int32_t* __restrict__ zpo) {
-    __shared__ float red[2][4];
-    const int64_t m = blockIdx.x;
-    const int tid = threadIdx.x;
-    float lo = 0.0f, hi = 0.0f;
-    for (int64_t k = tid; k < K; k += 256) {
-        const float v = load_elem<XT>(x, m * K + k);
-        lo = v < lo ? v : lo;
-        hi = v > hi ? v : hi;
+// The row's range, scale and zero point from its min / max (every step in fp32 as defined).
+struct RowQuant {
+    float s, inv;
+    int z;
+    __device__ int operator()(float v) const {
+        const int t = (int)rintf(v * inv) + z;
+        return t < -128 ? -128 : (t > 127 ? 127 : t);
     }
+};
+
+__device__ __forceinline__ RowQuant row_quant(float lo, float hi, float (*red)[4]) {
+    const int tid = threadIdx.x;
     for (int off = 32; off >= 1; off >>= 1) {
         const float l2 = __shfl_xor(lo, off);
         const float h2 = __shfl_xor(hi, off);
@@ -90,32 +87,111 @@ __global__ __launch_bounds__(256) void dq8ca_quant_kernel(const void* __restrict
         lo = red[0][i] < lo ? red[0][i] : lo;
         hi = red[1][i] > hi ? red[1][i] : hi;
     }
-    float s = (hi - lo) / 255.0f;
-    if (s < FLT_MIN) s = FLT_MIN;
-    const float inv = 1.0f / s;
-    int z = -128 - (int)rintf(lo * inv);
-    z = z < -128 ? -128 : (z > 127 ? 127 : z);
-    auto quant = [&](float v) -> int {
-        int t = (int)rintf(v * inv) + z;
-        return t < -128 ? -128 : (t > 127 ? 127 : t);
-    };
-    if constexpr (GEMM) {
+    RowQuant r;
+    r.s = (hi - lo) / 255.0f;
+    if (r.s < FLT_MIN) r.s = FLT_MIN;
+    r.inv = 1.0f / r.s;
+    const int z = -128 - (int)rintf(lo * r.inv);
+    r.z = z < -128 ? -128 : (z > 127 ? 127 : z);
+    return r;
+}
+
+// one k-octet of a row: 8 values from one (16-bit types) or two (fp32) 16-byte loads
+template <int XT>
+__device__ __forceinline__ void load_octet(const void* x, int64_t e, float (&v)[8]) {
+    if constexpr (XT == kF32) {
+        const f4 a = bitcast<f4>(ldg16(static_cast<const float*>(x) + e));
+        const f4 b = bitcast<f4>(ldg16(static_cast<const float*>(x) + e + 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = a[i];
+            v[4 + i] = b[i];
+        }
+    } else {
+        const u4 a = ldg16(static_cast<const uint16_t*>(x) + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t l = (uint16_t)(a[i] & 0xFFFFu), h = (uint16_t)(a[i] >> 16);
+            v[2 * i] = XT == kF16 ? f16_bits_to_f32(l) : bf16_bits_to_f32(l);
+            v[2 * i + 1] = XT == kF16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+        }
+    }
+}
+
+// XT: activation dtype.  GEMM: write the GEMM layout (rows of ld bytes, permuted octets, zero
+// padding) and -zp; else the natural [M, K] codes and zp.  VEC: K % 8 == 0 and x 16-byte aligned,
+// so every octet is read with 16-byte loads; the min / max pass keeps kOcts octets per thread in
+// flight.  One block of 256 threads per row.
+constexpr int kOcts = 4;
+
+template <int XT, bool GEMM, bool VEC>
+__global__ __launch_bounds__(256) void dq8ca_quant_kernel(const void* __restrict__ x, int64_t K, int64_t ld,
+                                                          int8_t* __restrict__ q, float* __restrict__ scale,
+                                                          int32_t* __restrict__ zpo) {
+    __shared__ float red[2][4];
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    float lo = 0.0f, hi = 0.0f;
+    if constexpr (VEC) {
+        const int64_t octs = K >> 3;
+        for (int64_t o0 = 0; o0 < octs; o0 += 256 * kOcts) {
+            float v[kOcts][8];
+#pragma unroll
+            for (int i = 0; i < kOcts; ++i) {
+                const int64_t o = o0 + tid + 256 * i;
+                if (o < octs) load_octet<XT>(x, m * K + 8 * o, v[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < kOcts; ++i) {
+                if (o0 + tid + 256 * i >= octs) continue;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    lo = v[i][e] < lo ? v[i][e] : lo;
+                    hi = v[i][e] > hi ? v[i][e] : hi;
+                }
+            }
+        }
+    } else {
+        for (int64_t k = tid; k < K; k += 256) {
+            const float v = load_elem<XT>(x, m * K + k);
+            lo = v < lo ? v : lo;
+            hi = v > hi ? v : hi;
+        }
+    }
+    const RowQuant rq = row_quant(lo, hi, red);
+    if constexpr (VEC) {
+        // second pass over the row (now in L2): 8 codes per octet, one 8-byte store
+        const int64_t octs = K >> 3;
+        for (int64_t o = tid; o < octs; o += 256) {
+            float v[8];
+            load_octet<XT>(x, m * K + 8 * o, v);
+            uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int k = GEMM ? kPerm[p] : p;
+                wd[p >> 2] |= (uint32_t)(rq(v[k]) & 0xFF) << (8 * (p & 3));
+            }
+            *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{wd[0], wd[1]};
+        }
+        if constexpr (GEMM)
+            for (int64_t o = octs + tid; o < ld / 8; o += 256) *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{0u, 0u};
+    } else if constexpr (GEMM) {
         for (int64_t o = tid; o < ld / 8; o += 256) {
             uint32_t wd[2] = {0u, 0u};
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 const int64_t k = 8 * o + kPerm[p];
-                const int t = k < K ? quant(load_elem<XT>(x, m * K + k)) : 0;
+                const int t = k < K ? rq(load_elem<XT>(x, m * K + k)) : 0;
                 wd[p >> 2] |= (uint32_t)(t & 0xFF) << (8 * (p & 3));
             }
             *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{wd[0], wd[1]};
         }
     } else {
-        for (int64_t k = tid; k < K; k += 256) q[m * K + k] = (int8_t)quant(load_elem<XT>(x, m * K + k));
+        for (int64_t k = tid; k < K; k += 256) q[m * K + k] = (int8_t)rq(load_elem<XT>(x, m * K + k));
     }
     if (tid == 0) {
-        scale[m] = s;
-        zpo[m] = GEMM ? -z : z;
+        scale[m] = rq.s;
+        zpo[m] = GEMM ? -rq.z : rq.z;
     }
 }
 
@@ -133,9 +209,12 @@ __global__ __launch_bounds__(512, 1) void dq8ca_gemm_kernel(WView w, const int8_
     constexpr int kAOff = 0, kBOff = kABytes, kSOff = kBOff + kWaves * kCodeBytes;
     constexpr int kStage = kSOff + 1024 * kSDma;
     constexpr int kDma = 2;                                    // DMAs of every wave per chunk
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
-    __shared__ __attribute__((aligned(16))) int32_t s_nzp[kBM];
-    __shared__ __attribute__((aligned(16))) float s_rs[kBM];
+    // one LDS array for everything: with several, the compiler gives each its own alias scope and
+    // then waits for every LDS-DMA in flight before any read of the ring, which drains the
+    // prefetch each chunk
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage + 8 * kBM];
+    int32_t* const s_nzp = reinterpret_cast<int32_t*>(smem + kStages * kStage);
+    float* const s_rs = reinterpret_cast<float*>(smem + kStages * kStage + 4 * kBM);
     lds_u8* const sm_l = (lds_u8*)smem;
 
     const int tid = threadIdx.x;
@@ -244,15 +323,16 @@ __global__ __launch_bounds__(512, 1) void dq8ca_gemm_kernel(WView w, const int8_
                     const int r = 4 * r4 + e;
                     const int T = acc[mi][r] + __mul24(nz[e], Wg);
                     tot[mi][r] = fmaf((float)T, sg, tot[mi][r]);
-                    acc[mi][r] = 0;
                 }
             }
         }
         wpart = 0;
     };
 
-    // one 32-column MFMA step t of the chunk in stage st
-    auto step = [&](int st, int t) {
+    // one 32-column MFMA step t of the chunk in stage st; the first step of a group (fresh)
+    // starts its sums from zero through the MFMA's accumulator operand
+    const v16i zero16 = {};
+    auto step = [&](int st, int t, auto fresh) {
         const uint8_t* Ab = smem + st * kStage + kAOff;
         const uint8_t* Bb = smem + st * kStage + kBOff + wave * kCodeBytes;
         // B: the two code words of k-octets 4t + 2h and 4t + 2h + 1 of the lane's column
@@ -275,7 +355,7 @@ __global__ __launch_bounds__(512, 1) void dq8ca_gemm_kernel(WView w, const int8_
         for (int mi = 0; mi < 4; ++mi) {
             const int row = 32 * mi + j;
             const v4i a = *reinterpret_cast<const v4i*>(Ab + kRow * row + 16 * (slot ^ ((row >> 2) & 3)));
-            acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[mi], 0, 0, 0);
+            acc[mi] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, decltype(fresh)::value ? zero16 : acc[mi], 0, 0, 0);
         }
     };
 
@@ -286,6 +366,7 @@ __global__ __launch_bounds__(512, 1) void dq8ca_gemm_kernel(WView w, const int8_
     // MFMA steps (32 columns each) per scale group and, counting down, those left in the open one
     const int spg = (int)(w.gs / 32);
     int left = spg - (int)((2 * c_begin) % spg);
+    bool fresh = true;                   // the next step opens a group
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int st_next = st == 2 ? 0 : st + 1;
         const int st_prev = st == 0 ? 2 : st - 1;
@@ -299,7 +380,8 @@ __global__ __launch_bounds__(512, 1) void dq8ca_gemm_kernel(WView w, const int8_
         const uint8_t* S = smem + st * kStage + kSOff;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            step(st, t);
+            if (SPC == 2 || fresh) step(st, t, std::true_type{});
+            else step(st, t, std::false_type{});
             // a group closes at its last step, and the open group at the split's last step
             bool close = true;
             if constexpr (SPC == 1) {
@@ -307,6 +389,7 @@ __global__ __launch_bounds__(512, 1) void dq8ca_gemm_kernel(WView w, const int8_
                 if (left == 0) left = spg;
             }
             if (close) close_group(S, SPC == 2 ? t : 0);
+            fresh = close;
         }
         st = st_next;
     }
@@ -365,16 +448,28 @@ Dq8caPlan plan_dq8ca(const WView& w, int64_t M, int force_splits) {
     return p;
 }
 
-hipError_t launch_dq8ca_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* scale,
-                                 int32_t* zp, hipStream_t s) {
+template <bool GEMM>
+static hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ld, int8_t* q, float* scale,
+                               int32_t* zp, hipStream_t s) {
     if (M > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)M);
+    const bool vec = K % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
+                     (GEMM || (reinterpret_cast<uintptr_t>(q) & 7u) == 0);
+#define Q4GSW_DQ8CA_QUANT(XT)                                                                             \
+    if (vec) hipLaunchKernelGGL((dq8ca_quant_kernel<XT, GEMM, true>), grid, dim3(256), 0, s, x, K, ld, q, scale, zp); \
+    else hipLaunchKernelGGL((dq8ca_quant_kernel<XT, GEMM, false>), grid, dim3(256), 0, s, x, K, ld, q, scale, zp);
     switch (x_dtype) {
-        case kF32: hipLaunchKernelGGL((dq8ca_quant_kernel<kF32, false>), grid, dim3(256), 0, s, x, K, K, q, scale, zp); break;
-        case kF16: hipLaunchKernelGGL((dq8ca_quant_kernel<kF16, false>), grid, dim3(256), 0, s, x, K, K, q, scale, zp); break;
-        default: hipLaunchKernelGGL((dq8ca_quant_kernel<kBF16, false>), grid, dim3(256), 0, s, x, K, K, q, scale, zp); break;
+        case kF32: Q4GSW_DQ8CA_QUANT(kF32) break;
+        case kF16: Q4GSW_DQ8CA_QUANT(kF16) break;
+        default: Q4GSW_DQ8CA_QUANT(kBF16) break;
     }
+#undef Q4GSW_DQ8CA_QUANT
     return hipGetLastError();
+}
+
+hipError_t launch_dq8ca_quantize(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* q, float* scale,
+                                 int32_t* zp, hipStream_t s) {
+    return launch_quant<false>(x, x_dtype, M, K, K, q, scale, zp, s);
 }
 
 hipError_t launch_dq8ca(const WView& w, const void* x, int x_dtype, int64_t M, float* y, const Dq8caPlan& plan,
@@ -385,19 +480,7 @@ hipError_t launch_dq8ca(const WView& w, const void* x, int x_dtype, int64_t M, f
     float* rs = reinterpret_cast<float*>(base + dq8ca_codes_bytes(M, w.k_pad));
     int32_t* nzp = reinterpret_cast<int32_t*>(base + dq8ca_codes_bytes(M, w.k_pad) + dq8ca_rows_bytes(M));
     float* part = reinterpret_cast<float*>(base + dq8ca_codes_bytes(M, w.k_pad) + 2 * dq8ca_rows_bytes(M));
-    const dim3 qgrid((unsigned)M);
-    switch (x_dtype) {
-        case kF32:
-            hipLaunchKernelGGL((dq8ca_quant_kernel<kF32, true>), qgrid, dim3(256), 0, s, x, w.K, w.k_pad, aq, rs, nzp);
-            break;
-        case kF16:
-            hipLaunchKernelGGL((dq8ca_quant_kernel<kF16, true>), qgrid, dim3(256), 0, s, x, w.K, w.k_pad, aq, rs, nzp);
-            break;
-        default:
-            hipLaunchKernelGGL((dq8ca_quant_kernel<kBF16, true>), qgrid, dim3(256), 0, s, x, w.K, w.k_pad, aq, rs, nzp);
-            break;
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_quant<true>(x, x_dtype, M, w.K, w.k_pad, aq, rs, nzp, s);
     if (e != hipSuccess) return e;
     const int64_t tiles = (w.n_pad + kBN - 1) / kBN;
     const int64_t mtiles = (M + kBM - 1) / kBM;
