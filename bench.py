@@ -40,9 +40,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--ops", default="decode,prefill,qkv,bwd,embedding,dq8ca",
-                   help="comma-separated ops (embedding, dq8ca and the decode-shaped QKV are timed outside "
-                        "the step)")
+    p.add_argument("--ops", default="decode,prefill,qkv,bwd,bwd_h,bwd_gs32,embedding,dq8ca",
+                   help="comma-separated ops (embedding, dq8ca, bwd_h, bwd_gs32 and the decode-shaped QKV are "
+                        "timed outside the step)")
     p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per M=512 op in the oracle sample")
@@ -163,18 +163,18 @@ def build_ops(q, names, rotate):
             # the decode-shaped triples (one launch of the streaming GEMV), outside the step
             specs.append(("qkv_m1", "qkv", make_workload("qkv", M=1)))
             specs.append(("qkv_m4", "qkv", make_workload("qkv", M=4)))
-        elif n in ("bwd", "bwd_h", "bwd_gs32"):
-            if n == "bwd":
-                specs.append(("bwd", "bwd", make_workload("bwd")))
-            # outside the step: the same workload with d_out rounded to fp16 (fold route), and the
-            # input gradient through the Llama Q projection (N = K = 2048, gs = 32, fp32 d_out)
-            if n in ("bwd", "bwd_h"):
-                h = copy.copy(make_workload("bwd"))
-                h.d_out = h.d_out.to(torch_dtype("f16"))
-                specs.append(("bwd_h", "bwd", h))
-            if n in ("bwd", "bwd_gs32"):
-                specs.append(("bwd_gs32", "bwd", make_linear(512, 2048, 2048, 32, "f32", "f16", seed=0, fwd=False,
-                                                             bwd=True, sigma=0.1)))
+        elif n == "bwd":
+            specs.append(("bwd", "bwd", make_workload("bwd")))
+        elif n == "bwd_h":
+            # outside the step: the bwd workload with d_out rounded to fp16 (fold route)
+            h = copy.copy(make_workload("bwd"))
+            h.d_out = h.d_out.to(torch_dtype("f16"))
+            specs.append(("bwd_h", "bwd", h))
+        elif n == "bwd_gs32":
+            # outside the step: the input gradient through the Llama Q projection (N = K = 2048,
+            # gs = 32, fp32 d_out)
+            specs.append(("bwd_gs32", "bwd", make_linear(512, 2048, 2048, 32, "f32", "f16", seed=0, fwd=False,
+                                                         bwd=True, sigma=0.1)))
         elif n == "dq8ca":
             # the prefill workload with its activation rows quantised to int8 per row, outside the step
             specs.append(("dq8ca", "dq8ca", make_workload("prefill")))
@@ -367,31 +367,57 @@ def stream_floor(steps):
     print(json.dumps({"stream_floor": out}), flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(ops, rows_per_op):
-    """The fp64 oracle (as it stands) on a bounded sample of the step: the first rows of each op."""
+    """The fp64 oracle (as it stands) on a bounded sample of the step: the first rows of each op,
+    with the host's threads (up to 16); then one thread on the first sixteenth of those rows, whose
+    outputs must equal the multi-threaded ones bit for bit (the oracle splits outputs, never sums,
+    across threads)."""
+    import numpy as np
     from oracle import oracle as O
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
     used = O.default().threads_used(threads)
-    flops = 0.0
-    parts = []
-    t0 = time.perf_counter()
-    for op in ops:
-        c = op.case
-        rows = min(op.M, rows_per_op)
-        if op.kind == "bwd":
-            d = c.d_out[:rows].contiguous()
-            O.linear_bwd_input(d, c.w.codes, c.w.scales, c.w.group_size, threads=threads)
-            flops += 2.0 * rows * c.w.N * c.w.K
-        else:
-            x = c.x[:rows].contiguous()
-            for w in c.weights:
-                O.linear_fwd(x, w.codes, w.scales, w.group_size, threads=threads)
-                flops += 2.0 * rows * w.N * w.K
-        parts.append(f"{op.name}:{rows}/{op.M} rows")
-    dt = time.perf_counter() - t0
+
+    def run(nthreads, frac):
+        flops = 0.0
+        parts, outs = [], []
+        t0 = time.perf_counter()
+        for op in ops:
+            c = op.case
+            rows = max(1, min(op.M, rows_per_op) // frac)
+            if op.kind == "bwd":
+                d = c.d_out[:rows].contiguous()
+                outs.append(O.linear_bwd_input(d, c.w.codes, c.w.scales, c.w.group_size, threads=nthreads)[0])
+                flops += 2.0 * rows * c.w.N * c.w.K
+            else:
+                x = c.x[:rows].contiguous()
+                for w in c.weights:
+                    outs.append(O.linear_fwd(x, w.codes, w.scales, w.group_size, threads=nthreads)[0])
+                    flops += 2.0 * rows * w.N * w.K
+            parts.append(f"{op.name}:{rows}/{op.M} rows")
+        return flops, time.perf_counter() - t0, parts, outs
+
+    flops, dt, parts, outs = run(threads, 1)
+    flops1, dt1, parts1, outs1 = run(1, 16)
+    same = all(np.array_equal(a[: b.shape[0]], b) for a, b in zip(outs, outs1))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
             "sample": "fp64 oracle on the first rows of each op (" + ", ".join(parts) +
-                      f"); {flops / 1e9:.2f} GFLOP in {dt:.1f} s"}
+                      f"); {flops / 1e9:.2f} GFLOP in {dt:.1f} s",
+            "cpu_model": _cpu_model(),
+            "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": "the first sixteenth of those rows (" + ", ".join(parts1) +
+                                        f"); {flops1 / 1e9:.2f} GFLOP in {dt1:.1f} s",
+                              "bitwise_equal_to_threaded": bool(same)}}
 
 
 def main():
