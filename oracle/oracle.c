@@ -53,6 +53,26 @@
  *       and the row stands for scale * (q[k] - zp).  The linear is the forward
  *       above applied to those values, in fp64 (oracle_linear_dq8ca).
  *
+ *   adapter step   The input-gradient pull request above says its op serves
+ *       on-device adapter training around the frozen base; the same page lists, in
+ *       its stack, an on-GPU AdamW optimizer step ("et_vk.adamw_step").  The pages
+ *       give no adapter mathematics.  Reading: a rank-r low-rank adapter (LoRA, Hu
+ *       et al., "LoRA: Low-Rank Adaptation of Large Language Models") beside the
+ *       frozen q4gsw weight, A [r,K] and B [N,r] in fp32:
+ *         t[m,j]   = sum_k x[m,k] A[j,k]
+ *         y[m,n]   = sum_k x[m,k] dequant(W[n,k]) + alpha sum_j t[m,j] B[n,j]
+ *       and, for an output gradient d_out, the gradients of <d_out, y>:
+ *         u[m,j]   = sum_n d_out[m,n] B[n,j]
+ *         dx[m,k]  = sum_n d_out[m,n] dequant(W[n,k]) + alpha sum_j u[m,j] A[j,k]
+ *         dA[j,k]  = alpha sum_m u[m,j] x[m,k]
+ *         dB[n,j]  = alpha sum_m d_out[m,n] t[m,j]
+ *       The optimizer is AdamW as published (Loshchilov and Hutter, "Decoupled
+ *       Weight Decay Regularization"), with bias-corrected moments and the weight
+ *       decay applied to the parameter directly, for step s >= 1:
+ *         p  <- p - lr wd p
+ *         m  <- b1 m + (1 - b1) g,      v <- b2 v + (1 - b2) g^2
+ *         p  <- p - lr (m / (1 - b1^s)) / (sqrt(v / (1 - b2^s)) + eps)
+ *
  * Every input element is widened exactly to double: fp16 and bf16 are decoded
  * from their IEEE bit fields here.  Every product is exact in fp64 (at most
  * 24 + 3 + 24 significant bits); sums run with the contraction index
@@ -310,6 +330,117 @@ int oracle_linear_dq8ca(const int8_t *q, const float *scale, const int32_t *zp, 
         }
         y[o] = acc;
         norm[o] = nrm;
+    }
+    return ORACLE_OK;
+}
+
+/* The adapter forward (see the header): y and its normaliser r are [M,N], t = x A^T is [M,r].
+ * r[m,n] = sum_k |x||dequant(W)| + |alpha| sum_j (sum_k |x[m,k]| |A[j,k]|) |B[n,j]|. */
+int oracle_lora_fwd(const void *x, int act_dtype, int64_t M,
+                    const uint8_t *codes, const void *scales, int scale_dtype,
+                    int64_t N, int64_t K, int64_t group_size,
+                    const float *A, const float *B, int64_t rank, double alpha,
+                    double *y, double *t, double *r, int nthreads)
+{
+    int status = oracle_linear_fwd(x, act_dtype, M, codes, scales, scale_dtype, N, K, group_size, y, r, nthreads);
+    if (status != ORACLE_OK)
+        return status;
+    if (rank < 0)
+        return ORACLE_E_ARG;
+    /* t = x A^T and its absolute counterpart, row by row */
+    for (int64_t row = 0; row < M; ++row) {
+        for (int64_t j = 0; j < rank; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t c = 0; c < K; ++c) {
+                double a = element(x, act_dtype, row * K + c);
+                acc += a * (double)A[j * K + c];
+                mag += fabs(a) * fabs((double)A[j * K + c]);
+            }
+            t[row * rank + j] = acc;
+            for (int64_t col = 0; col < N; ++col) {
+                y[row * N + col] += alpha * acc * (double)B[col * rank + j];
+                if (r)
+                    r[row * N + col] += fabs(alpha) * mag * fabs((double)B[col * rank + j]);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The adapter backward (see the header).  d_out is [M,N] in act_dtype, x [M,K] in act_dtype.
+ * dx and rdx are [M,K]; dA and rdA [rank,K]; dB and rdB [N,rank].  Each r* is the sum of the
+ * absolute values of the products its output sums (the base part of rdx as for the input
+ * gradient). */
+int oracle_lora_bwd(const void *x, const void *d_out, int act_dtype, int64_t M,
+                    const uint8_t *codes, const void *scales, int scale_dtype,
+                    int64_t N, int64_t K, int64_t group_size,
+                    const float *A, const float *B, int64_t rank, double alpha,
+                    double *dx, double *dA, double *dB, double *rdx, double *rdA, double *rdB, int nthreads)
+{
+    int status = oracle_linear_bwd_input(d_out, act_dtype, M, codes, scales, scale_dtype, N, K, group_size,
+                                         dx, rdx, nthreads);
+    if (status != ORACLE_OK)
+        return status;
+    if (rank < 0)
+        return ORACLE_E_ARG;
+    for (int64_t i = 0; i < rank * K; ++i) {
+        dA[i] = 0.0;
+        rdA[i] = 0.0;
+    }
+    for (int64_t i = 0; i < N * rank; ++i) {
+        dB[i] = 0.0;
+        rdB[i] = 0.0;
+    }
+    for (int64_t row = 0; row < M; ++row) {
+        for (int64_t j = 0; j < rank; ++j) {
+            /* u[row,j] = sum_n d_out[row,n] B[n,j]; tx[row,j] = sum_k x[row,k] A[j,k] */
+            double u = 0.0, umag = 0.0, tx = 0.0, tmag = 0.0;
+            for (int64_t col = 0; col < N; ++col) {
+                double g = element(d_out, act_dtype, row * N + col);
+                u += g * (double)B[col * rank + j];
+                umag += fabs(g) * fabs((double)B[col * rank + j]);
+            }
+            for (int64_t c = 0; c < K; ++c) {
+                double a = element(x, act_dtype, row * K + c);
+                tx += a * (double)A[j * K + c];
+                tmag += fabs(a) * fabs((double)A[j * K + c]);
+            }
+            for (int64_t c = 0; c < K; ++c) {
+                double a = element(x, act_dtype, row * K + c);
+                dx[row * K + c] += alpha * u * (double)A[j * K + c];
+                rdx[row * K + c] += fabs(alpha) * umag * fabs((double)A[j * K + c]);
+                dA[j * K + c] += alpha * u * a;
+                rdA[j * K + c] += fabs(alpha) * umag * fabs(a);
+            }
+            for (int64_t col = 0; col < N; ++col) {
+                double g = element(d_out, act_dtype, row * N + col);
+                dB[col * rank + j] += alpha * g * tx;
+                rdB[col * rank + j] += fabs(alpha) * fabs(g) * tmag;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* One AdamW step (see the header) on n fp32 parameters, in fp64: p_out, m_out, v_out. */
+int oracle_adamw(const float *p, const float *g, const float *m, const float *v, int64_t n,
+                 double lr, double beta1, double beta2, double eps, double weight_decay, int64_t step,
+                 double *p_out, double *m_out, double *v_out)
+{
+    if (n < 0 || step < 1)
+        return ORACLE_E_ARG;
+    const double bias1 = 1.0 - pow(beta1, (double)step);
+    const double bias2 = 1.0 - pow(beta2, (double)step);
+    for (int64_t i = 0; i < n; ++i) {
+        double param = (double)p[i];
+        const double grad = (double)g[i];
+        param -= lr * weight_decay * param;
+        const double m1 = beta1 * (double)m[i] + (1.0 - beta1) * grad;
+        const double v1 = beta2 * (double)v[i] + (1.0 - beta2) * grad * grad;
+        param -= lr * (m1 / bias1) / (sqrt(v1 / bias2) + eps);
+        p_out[i] = param;
+        m_out[i] = m1;
+        v_out[i] = v1;
     }
     return ORACLE_OK;
 }

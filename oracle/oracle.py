@@ -57,6 +57,14 @@ class Oracle:
         handle.oracle_dq8ca_quantize.argtypes = [vp, ip, i64, i64, vp, vp, vp, ip]
         handle.oracle_linear_dq8ca.restype = ctypes.c_int
         handle.oracle_linear_dq8ca.argtypes = [vp, vp, vp, i64, vp, vp, ip, i64, i64, i64, vp, vp, ip]
+        dbl = ctypes.c_double
+        handle.oracle_lora_fwd.restype = ctypes.c_int
+        handle.oracle_lora_fwd.argtypes = [vp, ip, i64, vp, vp, ip, i64, i64, i64, vp, vp, i64, dbl, vp, vp, vp, ip]
+        handle.oracle_lora_bwd.restype = ctypes.c_int
+        handle.oracle_lora_bwd.argtypes = [vp, vp, ip, i64, vp, vp, ip, i64, i64, i64, vp, vp, i64, dbl,
+                                           vp, vp, vp, vp, vp, vp, ip]
+        handle.oracle_adamw.restype = ctypes.c_int
+        handle.oracle_adamw.argtypes = [vp, vp, vp, vp, i64, dbl, dbl, dbl, dbl, dbl, i64, vp, vp, vp]
         self.lib = handle
         self.path = path
 
@@ -156,6 +164,65 @@ class Oracle:
             raise OracleError(f"oracle_linear_dq8ca returned {status}")
         return out, norm
 
+    def lora_fwd(self, x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, group_size: int,
+                 A: torch.Tensor, B: torch.Tensor, alpha: float, threads: int = 0):
+        """The adapter forward: (y [M,N], t = x A^T [M,r], R_y [M,N]) as float64 arrays.
+        A is fp32 [r,K], B fp32 [N,r]."""
+        x, codes, scales = x.contiguous(), codes.contiguous(), scales.contiguous()
+        A = A.to(torch.float32).contiguous()
+        B = B.to(torch.float32).contiguous()
+        N, K = codes.shape
+        r = A.shape[0]
+        if x.dim() != 2 or x.shape[1] != K or A.shape != (r, K) or B.shape != (N, r):
+            raise OracleError("x [M,K], A [r,K], B [N,r]")
+        M = x.shape[0]
+        y = np.zeros((M, N)); t = np.zeros((M, r)); norm = np.zeros((M, N))
+        st = self.lib.oracle_lora_fwd(_ptr(x), _DTYPE_CODE[x.dtype], M, _ptr(codes), _ptr(scales),
+                                      _DTYPE_CODE[scales.dtype], N, K, group_size, _ptr(A), _ptr(B), r,
+                                      float(alpha), y.ctypes.data, t.ctypes.data, norm.ctypes.data, threads)
+        if st != 0:
+            raise OracleError(f"oracle_lora_fwd returned {st}")
+        return y, t, norm
+
+    def lora_bwd(self, x: torch.Tensor, d_out: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                 group_size: int, A: torch.Tensor, B: torch.Tensor, alpha: float, threads: int = 0):
+        """The adapter backward: dict of float64 arrays dx [M,K], dA [r,K], dB [N,r] and their
+        normalisers r_dx, r_dA, r_dB.  x and d_out share one dtype."""
+        x, d_out = x.contiguous(), d_out.contiguous()
+        codes, scales = codes.contiguous(), scales.contiguous()
+        A = A.to(torch.float32).contiguous()
+        B = B.to(torch.float32).contiguous()
+        N, K = codes.shape
+        r = A.shape[0]
+        M = x.shape[0]
+        if x.dtype != d_out.dtype or x.shape != (M, K) or d_out.shape != (M, N) or A.shape != (r, K) \
+                or B.shape != (N, r):
+            raise OracleError("x [M,K] and d_out [M,N] of one dtype, A [r,K], B [N,r]")
+        out = {k: np.zeros(sh) for k, sh in (("dx", (M, K)), ("dA", (r, K)), ("dB", (N, r)),
+                                             ("r_dx", (M, K)), ("r_dA", (r, K)), ("r_dB", (N, r)))}
+        st = self.lib.oracle_lora_bwd(_ptr(x), _ptr(d_out), _DTYPE_CODE[x.dtype], M, _ptr(codes), _ptr(scales),
+                                      _DTYPE_CODE[scales.dtype], N, K, group_size, _ptr(A), _ptr(B), r,
+                                      float(alpha), out["dx"].ctypes.data, out["dA"].ctypes.data,
+                                      out["dB"].ctypes.data, out["r_dx"].ctypes.data, out["r_dA"].ctypes.data,
+                                      out["r_dB"].ctypes.data, threads)
+        if st != 0:
+            raise OracleError(f"oracle_lora_bwd returned {st}")
+        return out
+
+    def adamw(self, p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tensor, lr: float,
+              beta1: float, beta2: float, eps: float, weight_decay: float, step: int):
+        """One AdamW step on fp32 tensors of one size: (p, m, v) after it, float64 arrays."""
+        ts = [t.to(torch.float32).contiguous().reshape(-1) for t in (p, g, m, v)]
+        n = ts[0].numel()
+        if any(t.numel() != n for t in ts):
+            raise OracleError("p, g, m and v must have one size")
+        po, mo, vo = np.zeros(n), np.zeros(n), np.zeros(n)
+        st = self.lib.oracle_adamw(*[_ptr(t) for t in ts], n, float(lr), float(beta1), float(beta2), float(eps),
+                                   float(weight_decay), int(step), po.ctypes.data, mo.ctypes.data, vo.ctypes.data)
+        if st != 0:
+            raise OracleError(f"oracle_adamw returned {st}")
+        return po, mo, vo
+
     def dequant(self, codes: torch.Tensor, scales: torch.Tensor, group_size: int, n: int, k: int) -> float:
         """One element of dequant(W), as the oracle computes it."""
         codes = codes.contiguous()
@@ -214,3 +281,15 @@ def dq8ca_quantize(x, threads=0):
 
 def linear_dq8ca(x, codes, scales, group_size, threads=0):
     return default().linear_dq8ca(x, codes, scales, group_size, threads)
+
+
+def lora_fwd(x, codes, scales, group_size, A, B, alpha, threads=0):
+    return default().lora_fwd(x, codes, scales, group_size, A, B, alpha, threads)
+
+
+def lora_bwd(x, d_out, codes, scales, group_size, A, B, alpha, threads=0):
+    return default().lora_bwd(x, d_out, codes, scales, group_size, A, B, alpha, threads)
+
+
+def adamw(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step):
+    return default().adamw(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step)

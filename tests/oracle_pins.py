@@ -22,6 +22,11 @@ The facts:
     quantizer reproduces the codes from the oracle's scale and zero point; nearest-grid,
     span, zero and monotonicity properties; on-grid rows give exactly the plain forward;
     the linear against a numpy matmul of the dequantised rows.
+  * the adapter step (a low-rank adapter beside the frozen weight, and AdamW): zero
+    adapters reduce to the plain forward and input gradient bit for bit; a numpy matmul of
+    the dense matrices; the adjoint identities that define the three gradients (the output
+    is linear in x, in A and in B separately); PyTorch's own torch.optim.AdamW on the same
+    state; closed forms of a first step and of a decay-only step.
 """
 from __future__ import annotations
 
@@ -419,7 +424,114 @@ def pin_dq8ca_linear(o):
     assert np.array_equal(o.linear_dq8ca(x, eight, scales, gs)[0], np.zeros((x.shape[0], N)))
 
 
+def _lora_case(seed, M, N, K, gs, r, act="f32", sdt="f16"):
+    g = torch.Generator().manual_seed(seed)
+    x = draw_activation(g, M, K, act)
+    d_out = draw_activation(g, M, N, act)
+    codes = draw_codes(g, N, K)
+    scales = draw_scales(g, K // gs, N, sdt, 0.005, 0.02)
+    A = (torch.randn(r, K, generator=g) * 0.05).to(torch.float32)
+    B = (torch.randn(N, r, generator=g) * 0.05).to(torch.float32)
+    return x, d_out, codes, scales, A, B
+
+
+def pin_lora_zero_adapter(o):
+    """With B = 0 (or A = 0) the adapter forward is the plain forward and the adapter input
+    gradient the plain input gradient, bit for bit; the vanishing factor's partner gets a zero
+    gradient and the other one the product of the remaining terms."""
+    for act in ACT_DTYPES:
+        x, d, codes, scales, A, B = _lora_case(31, 4, 12, 32, 8, 3, act)
+        y0, r0 = o.linear_fwd(x, codes, scales, 8)
+        dx0, rd0 = o.linear_bwd_input(d, codes, scales, 8)
+        zb = torch.zeros_like(B)
+        y, t, r = o.lora_fwd(x, codes, scales, 8, A, zb, 0.75)
+        assert np.array_equal(y, y0) and np.array_equal(r, r0), act
+        g = o.lora_bwd(x, d, codes, scales, 8, A, zb, 0.75)
+        assert np.array_equal(g["dx"], dx0) and np.array_equal(g["r_dx"], rd0), act
+        assert not np.any(g["dA"]), act                  # u = d_out B = 0
+        za = torch.zeros_like(A)
+        y, t, r = o.lora_fwd(x, codes, scales, 8, za, B, 0.75)
+        assert np.array_equal(y, y0) and not np.any(t), act
+        g = o.lora_bwd(x, d, codes, scales, 8, za, B, 0.75)
+        assert np.array_equal(g["dx"], dx0) and not np.any(g["dB"]), act
+
+
+def pin_lora_numpy(o):
+    """Against numpy fp64 matmuls of the dense matrices: y = x W^T + a (x A^T) B^T,
+    dx = d W + a (d B) A, dA = a (d B)^T x, dB = a d^T (x A^T)."""
+    x, d, codes, scales, A, B = _lora_case(32, 5, 24, 64, 16, 4, "bf16", "f32")
+    a = -1.25
+    W = _dense(codes, scales, 16)
+    X, D = x.double().numpy(), d.double().numpy()
+    An, Bn = A.double().numpy(), B.double().numpy()
+    y, t, r = o.lora_fwd(x, codes, scales, 16, A, B, a)
+    assert np.all(np.abs(y - (X @ W.T + a * (X @ An.T) @ Bn.T)) <= 1e-12 * r + 1e-300)
+    assert np.allclose(t, X @ An.T, rtol=1e-13, atol=1e-300)
+    g = o.lora_bwd(x, d, codes, scales, 16, A, B, a)
+    assert np.all(np.abs(g["dx"] - (D @ W + a * (D @ Bn) @ An)) <= 1e-12 * g["r_dx"] + 1e-300)
+    assert np.all(np.abs(g["dA"] - a * (D @ Bn).T @ X) <= 1e-12 * g["r_dA"] + 1e-300)
+    assert np.all(np.abs(g["dB"] - a * D.T @ (X @ An.T)) <= 1e-12 * g["r_dB"] + 1e-300)
+    assert np.allclose(g["r_dB"], abs(a) * np.abs(D).T @ (np.abs(X) @ np.abs(An).T), rtol=1e-12, atol=0)
+
+
+def pin_lora_adjoint(o):
+    """The three gradients by their definition: y is linear in x, in A and in B, so for the
+    loss <d, y>: <d, y(x)> = <dx, x>, <d, y(A) - y(0)> = <dA, A>, <d, y(B) - y(0)> = <dB, B>."""
+    x, d, codes, scales, A, B = _lora_case(33, 6, 20, 48, 16, 5, "f16", "f16")
+    a = 0.5
+    D, X = d.double().numpy(), x.double().numpy()
+    y, _, r = o.lora_fwd(x, codes, scales, 16, A, B, a)
+    g = o.lora_bwd(x, d, codes, scales, 16, A, B, a)
+    scale = float((np.abs(D) * r).sum())
+    assert abs(float((D * y).sum()) - float((g["dx"] * X).sum())) <= 1e-12 * scale
+    y0, _, _ = o.lora_fwd(x, codes, scales, 16, A, torch.zeros_like(B), a)
+    lhs = float((D * (y - y0)).sum())
+    assert abs(lhs - float((g["dA"] * A.double().numpy()).sum())) <= 1e-12 * scale
+    assert abs(lhs - float((g["dB"] * B.double().numpy()).sum())) <= 1e-12 * scale
+
+
+def pin_adamw_torch(o):
+    """One AdamW step from an fp32 state equals torch.optim.AdamW's on the same state (fp64
+    tensors), at several step counts and hyperparameters."""
+    g = torch.Generator().manual_seed(34)
+    for step, lr, b1, b2, eps, wd in [(1, 1e-3, 0.9, 0.999, 1e-8, 0.01), (7, 3e-2, 0.8, 0.99, 1e-6, 0.1),
+                                     (250, 5e-4, 0.95, 0.9999, 1e-8, 0.0)]:
+        p = torch.randn(64, generator=g).to(torch.float32)
+        gr = (torch.randn(64, generator=g) * 0.1).to(torch.float32)
+        m = (torch.randn(64, generator=g) * 0.05).to(torch.float32) if step > 1 else torch.zeros(64)
+        v = (torch.rand(64, generator=g) * 0.01).to(torch.float32) if step > 1 else torch.zeros(64)
+        pr, mr, vr = o.adamw(p, gr, m, v, lr, b1, b2, eps, wd, step)
+        param = torch.nn.Parameter(p.double().clone())
+        opt = torch.optim.AdamW([param], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+        param.grad = gr.double().clone()
+        opt.state[param] = {"step": torch.tensor(float(step - 1), dtype=torch.float64),
+                            "exp_avg": m.double().clone(), "exp_avg_sq": v.double().clone()}
+        opt.step()
+        st = opt.state[param]
+        assert np.allclose(pr, param.detach().numpy(), rtol=1e-13, atol=1e-15), step
+        assert np.allclose(mr, st["exp_avg"].numpy(), rtol=1e-13, atol=1e-18), step
+        assert np.allclose(vr, st["exp_avg_sq"].numpy(), rtol=1e-13, atol=1e-20), step
+
+
+def pin_adamw_closed_forms(o):
+    """A first step from zero moments without decay moves each parameter by lr g / (|g| + eps)
+    against its gradient; a zero gradient with zero moments only decays: p (1 - lr wd)."""
+    p = torch.tensor([1.0, -2.0, 0.5, 3.0])
+    gr = torch.tensor([0.5, -0.25, 2.0, -1.0])
+    z = torch.zeros(4)
+    lr, eps = 1e-2, 1e-8
+    pr, mr, vr = o.adamw(p, gr, z, z, lr, 0.9, 0.999, eps, 0.0, 1)
+    want = p.double().numpy() - lr * gr.double().numpy() / (np.abs(gr.double().numpy()) + eps)
+    assert np.allclose(pr, want, rtol=1e-14, atol=0)
+    assert np.allclose(mr, 0.1 * gr.double().numpy(), rtol=1e-15, atol=0)
+    assert np.allclose(vr, 0.001 * gr.double().numpy() ** 2, rtol=1e-15, atol=0)
+    pr, mr, vr = o.adamw(p, z, z, z, lr, 0.9, 0.999, eps, 0.25, 3)
+    assert np.array_equal(pr, p.double().numpy() * (1.0 - lr * 0.25))
+    assert not np.any(mr) and not np.any(vr)
+
+
 PINS = [pin_worked_example, pin_code_table, pin_decoders, pin_brute_force, pin_numpy_matmul,
         pin_code8_zero, pin_scale_linearity, pin_adjoint, pin_one_hot, pin_qkv, pin_threads,
         pin_normaliser, pin_embedding, pin_dq8ca_golden, pin_dq8ca_library, pin_dq8ca_properties,
-        pin_dq8ca_linear]
+        pin_dq8ca_linear, pin_lora_zero_adapter, pin_lora_numpy, pin_lora_adjoint, pin_adamw_torch,
+        pin_adamw_closed_forms]

@@ -39,6 +39,21 @@ MUTANTS = {
     "dq8ca_range_without_zero": ("float lo = 0.0f, hi = 0.0f;", "float lo = 1e30f, hi = -1e30f;"),
     "dq8ca_linear_without_zp": ("(double)((int)q[m * K + k] - (int)zp[m])", "(double)((int)q[m * K + k])"),
     "dq8ca_linear_first_row_scale": ("const double sm = (double)scale[m];", "const double sm = (double)scale[0];"),
+    "lora_fwd_alpha_dropped": ("y[row * N + col] += alpha * acc * (double)B[col * rank + j];",
+                               "y[row * N + col] += acc * (double)B[col * rank + j];"),
+    "lora_fwd_B_transposed": ("y[row * N + col] += alpha * acc * (double)B[col * rank + j];",
+                              "y[row * N + col] += alpha * acc * (double)B[j * N + col];"),
+    "lora_bwd_dx_sign": ("dx[row * K + c] += alpha * u * (double)A[j * K + c];",
+                         "dx[row * K + c] -= alpha * u * (double)A[j * K + c];"),
+    "lora_bwd_dA_from_t": ("dA[j * K + c] += alpha * u * a;", "dA[j * K + c] += alpha * tx * a;"),
+    "lora_bwd_dB_from_u": ("dB[col * rank + j] += alpha * g * tx;", "dB[col * rank + j] += alpha * g * u;"),
+    "adamw_no_bias_correction": ("param -= lr * (m1 / bias1) / (sqrt(v1 / bias2) + eps);",
+                                 "param -= lr * m1 / (sqrt(v1) + eps);"),
+    "adamw_coupled_decay": ("        const double grad = (double)g[i];\n        param -= lr * weight_decay * param;",
+                            "        const double grad = (double)g[i] + weight_decay * param;"),
+    "adamw_eps_inside_sqrt": ("(sqrt(v1 / bias2) + eps)", "sqrt(v1 / bias2 + eps)"),
+    "adamw_beta2_in_first_moment": ("const double m1 = beta1 * (double)m[i] + (1.0 - beta1) * grad;",
+                                    "const double m1 = beta1 * (double)m[i] + (1.0 - beta2) * grad;"),
 }
 
 
