@@ -334,6 +334,21 @@ int oracle_linear_dq8ca(const int8_t *q, const float *scale, const int32_t *zp, 
     return ORACLE_OK;
 }
 
+/* codes == NULL in the adapter calls below: the frozen-weight term is left out, so y (or dx)
+ * and its normaliser hold the adapter term alone (for checking the factors at sizes where the
+ * dense term would take too long). */
+static int adapter_only_args(int act_dtype, int64_t M, int64_t N, int64_t K, double *out, double *r)
+{
+    if (M < 0 || N < 0 || K < 0 || act_dtype < ORACLE_F32 || act_dtype > ORACLE_BF16)
+        return ORACLE_E_ARG;
+    for (int64_t i = 0; i < M * N; ++i) {
+        out[i] = 0.0;
+        if (r)
+            r[i] = 0.0;
+    }
+    return ORACLE_OK;
+}
+
 /* The adapter forward (see the header): y and its normaliser r are [M,N], t = x A^T is [M,r].
  * r[m,n] = sum_k |x||dequant(W)| + |alpha| sum_j (sum_k |x[m,k]| |A[j,k]|) |B[n,j]|. */
 int oracle_lora_fwd(const void *x, int act_dtype, int64_t M,
@@ -342,7 +357,9 @@ int oracle_lora_fwd(const void *x, int act_dtype, int64_t M,
                     const float *A, const float *B, int64_t rank, double alpha,
                     double *y, double *t, double *r, int nthreads)
 {
-    int status = oracle_linear_fwd(x, act_dtype, M, codes, scales, scale_dtype, N, K, group_size, y, r, nthreads);
+    int status = codes ? oracle_linear_fwd(x, act_dtype, M, codes, scales, scale_dtype, N, K, group_size, y, r,
+                                           nthreads)
+                       : adapter_only_args(act_dtype, M, N, K, y, r);
     if (status != ORACLE_OK)
         return status;
     if (rank < 0)
@@ -377,8 +394,9 @@ int oracle_lora_bwd(const void *x, const void *d_out, int act_dtype, int64_t M,
                     const float *A, const float *B, int64_t rank, double alpha,
                     double *dx, double *dA, double *dB, double *rdx, double *rdA, double *rdB, int nthreads)
 {
-    int status = oracle_linear_bwd_input(d_out, act_dtype, M, codes, scales, scale_dtype, N, K, group_size,
-                                         dx, rdx, nthreads);
+    int status = codes ? oracle_linear_bwd_input(d_out, act_dtype, M, codes, scales, scale_dtype, N, K, group_size,
+                                                 dx, rdx, nthreads)
+                       : adapter_only_args(act_dtype, M, K, N, dx, rdx);
     if (status != ORACLE_OK)
         return status;
     if (rank < 0)

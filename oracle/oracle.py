@@ -167,18 +167,25 @@ class Oracle:
     def lora_fwd(self, x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, group_size: int,
                  A: torch.Tensor, B: torch.Tensor, alpha: float, threads: int = 0):
         """The adapter forward: (y [M,N], t = x A^T [M,r], R_y [M,N]) as float64 arrays.
-        A is fp32 [r,K], B fp32 [N,r]."""
-        x, codes, scales = x.contiguous(), codes.contiguous(), scales.contiguous()
+        A is fp32 [r,K], B fp32 [N,r].  codes (and scales) None: the frozen-weight term is left
+        out and y, R_y hold the adapter term alone."""
         A = A.to(torch.float32).contiguous()
         B = B.to(torch.float32).contiguous()
-        N, K = codes.shape
+        x = x.contiguous()
+        if codes is None:
+            codes_p, scales_p, sdt = None, None, 0
+            N, K = B.shape[0], A.shape[1]
+        else:
+            codes, scales = codes.contiguous(), scales.contiguous()
+            codes_p, scales_p, sdt = _ptr(codes), _ptr(scales), _DTYPE_CODE[scales.dtype]
+            N, K = codes.shape
         r = A.shape[0]
         if x.dim() != 2 or x.shape[1] != K or A.shape != (r, K) or B.shape != (N, r):
             raise OracleError("x [M,K], A [r,K], B [N,r]")
         M = x.shape[0]
         y = np.zeros((M, N)); t = np.zeros((M, r)); norm = np.zeros((M, N))
-        st = self.lib.oracle_lora_fwd(_ptr(x), _DTYPE_CODE[x.dtype], M, _ptr(codes), _ptr(scales),
-                                      _DTYPE_CODE[scales.dtype], N, K, group_size, _ptr(A), _ptr(B), r,
+        st = self.lib.oracle_lora_fwd(_ptr(x), _DTYPE_CODE[x.dtype], M, codes_p, scales_p,
+                                      sdt, N, K, group_size, _ptr(A), _ptr(B), r,
                                       float(alpha), y.ctypes.data, t.ctypes.data, norm.ctypes.data, threads)
         if st != 0:
             raise OracleError(f"oracle_lora_fwd returned {st}")
@@ -187,12 +194,18 @@ class Oracle:
     def lora_bwd(self, x: torch.Tensor, d_out: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                  group_size: int, A: torch.Tensor, B: torch.Tensor, alpha: float, threads: int = 0):
         """The adapter backward: dict of float64 arrays dx [M,K], dA [r,K], dB [N,r] and their
-        normalisers r_dx, r_dA, r_dB.  x and d_out share one dtype."""
+        normalisers r_dx, r_dA, r_dB.  x and d_out share one dtype.  codes (and scales) None: the
+        frozen-weight term of dx is left out (dA and dB do not depend on it)."""
         x, d_out = x.contiguous(), d_out.contiguous()
-        codes, scales = codes.contiguous(), scales.contiguous()
         A = A.to(torch.float32).contiguous()
         B = B.to(torch.float32).contiguous()
-        N, K = codes.shape
+        if codes is None:
+            codes_p, scales_p, sdt = None, None, 0
+            N, K = B.shape[0], A.shape[1]
+        else:
+            codes, scales = codes.contiguous(), scales.contiguous()
+            codes_p, scales_p, sdt = _ptr(codes), _ptr(scales), _DTYPE_CODE[scales.dtype]
+            N, K = codes.shape
         r = A.shape[0]
         M = x.shape[0]
         if x.dtype != d_out.dtype or x.shape != (M, K) or d_out.shape != (M, N) or A.shape != (r, K) \
@@ -200,8 +213,8 @@ class Oracle:
             raise OracleError("x [M,K] and d_out [M,N] of one dtype, A [r,K], B [N,r]")
         out = {k: np.zeros(sh) for k, sh in (("dx", (M, K)), ("dA", (r, K)), ("dB", (N, r)),
                                              ("r_dx", (M, K)), ("r_dA", (r, K)), ("r_dB", (N, r)))}
-        st = self.lib.oracle_lora_bwd(_ptr(x), _ptr(d_out), _DTYPE_CODE[x.dtype], M, _ptr(codes), _ptr(scales),
-                                      _DTYPE_CODE[scales.dtype], N, K, group_size, _ptr(A), _ptr(B), r,
+        st = self.lib.oracle_lora_bwd(_ptr(x), _ptr(d_out), _DTYPE_CODE[x.dtype], M, codes_p, scales_p,
+                                      sdt, N, K, group_size, _ptr(A), _ptr(B), r,
                                       float(alpha), out["dx"].ctypes.data, out["dA"].ctypes.data,
                                       out["dB"].ctypes.data, out["r_dx"].ctypes.data, out["r_dA"].ctypes.data,
                                       out["r_dB"].ctypes.data, threads)

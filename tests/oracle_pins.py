@@ -490,6 +490,27 @@ def pin_lora_adjoint(o):
     assert abs(lhs - float((g["dB"] * B.double().numpy()).sum())) <= 1e-12 * scale
 
 
+def pin_lora_adapter_only(o):
+    """Leaving the frozen weight out (codes None) leaves the adapter term alone: against numpy
+    fp64 matmuls y = a (x A^T) B^T and dx = a (d B) A, t unchanged, and dA, dB (which do not
+    involve the weight) bit for bit those of the full call."""
+    x, d, codes, scales, A, B = _lora_case(35, 7, 20, 48, 16, 6, "bf16", "f16")
+    a = 1.5
+    X, D = x.double().numpy(), d.double().numpy()
+    An, Bn = A.double().numpy(), B.double().numpy()
+    y, t, r = o.lora_fwd(x, None, None, 16, A, B, a)
+    _, t_full, _ = o.lora_fwd(x, codes, scales, 16, A, B, a)
+    assert np.all(np.abs(y - a * (X @ An.T) @ Bn.T) <= 1e-12 * r + 1e-300)
+    assert np.allclose(r, abs(a) * (np.abs(X) @ np.abs(An).T) @ np.abs(Bn).T, rtol=1e-12, atol=0)
+    assert np.array_equal(t, t_full)
+    g = o.lora_bwd(x, d, None, None, 16, A, B, a)
+    full = o.lora_bwd(x, d, codes, scales, 16, A, B, a)
+    assert np.all(np.abs(g["dx"] - a * (D @ Bn) @ An) <= 1e-12 * g["r_dx"] + 1e-300)
+    assert np.allclose(g["r_dx"], abs(a) * (np.abs(D) @ np.abs(Bn)) @ np.abs(An), rtol=1e-12, atol=0)
+    for k in ("dA", "dB", "r_dA", "r_dB"):
+        assert np.array_equal(g[k], full[k]), k
+
+
 def pin_adamw_torch(o):
     """One AdamW step from an fp32 state equals torch.optim.AdamW's on the same state (fp64
     tensors), at several step counts and hyperparameters."""
@@ -533,5 +554,5 @@ def pin_adamw_closed_forms(o):
 PINS = [pin_worked_example, pin_code_table, pin_decoders, pin_brute_force, pin_numpy_matmul,
         pin_code8_zero, pin_scale_linearity, pin_adjoint, pin_one_hot, pin_qkv, pin_threads,
         pin_normaliser, pin_embedding, pin_dq8ca_golden, pin_dq8ca_library, pin_dq8ca_properties,
-        pin_dq8ca_linear, pin_lora_zero_adapter, pin_lora_numpy, pin_lora_adjoint, pin_adamw_torch,
+        pin_dq8ca_linear, pin_lora_zero_adapter, pin_lora_numpy, pin_lora_adjoint, pin_lora_adapter_only, pin_adamw_torch,
         pin_adamw_closed_forms]
