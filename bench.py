@@ -40,9 +40,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--ops", default="decode,prefill,qkv,bwd,bwd_h,bwd_gs32,embedding,dq8ca",
-                   help="comma-separated ops (embedding, dq8ca, bwd_h, bwd_gs32 and the decode-shaped QKV are "
-                        "timed outside the step)")
+    p.add_argument("--ops", default="decode,prefill,qkv,bwd,bwd_h,bwd_gs32,embedding,dq8ca,adapter",
+                   help="comma-separated ops (embedding, dq8ca, adapter (its forward, backward and AdamW), "
+                        "bwd_h, bwd_gs32 and the decode-shaped QKV are timed outside the step)")
     p.add_argument("--rotate", type=int, default=0, help="input sets rotated (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows per M=512 op in the oracle sample")
@@ -141,6 +141,74 @@ class EmbOp:
         q.embedding(pw, ids, out=out)
 
 
+class AdapterOp:
+    """The adapter step around the frozen MLP up projection (outside the step): the adapter
+    forward (y = x W^T + alpha (x A^T) B^T and t), its backward (d_x, d_A, d_B) or the AdamW
+    update of the factors A [r, K] and B [N, r].  Algorithmic bytes are each call's inputs read
+    once and outputs written once: forward W + x + A + B + y + t; backward W + d_out + x + A +
+    B + t + d_x + d_A + d_B; AdamW 4 reads and 3 writes of the r (K + N) fp32 factor values."""
+
+    def __init__(self, name, kind, case, q, sets):
+        import torch
+        from synthetic_inputs import ADAPTER_ALPHA
+        self.name, self.kind, self.case = name, kind, case
+        self.in_step = False
+        self.alpha = ADAPTER_ALPHA
+        w = case.w
+        M, N, K, r = case.M, w.N, w.K, case.A.shape[0]
+        self.M = M
+        ab = case.x.element_size()
+        wb = w.N * w.K / 2 + w.scales.numel() * w.scales.element_size()
+        fac = 4.0 * r * (K + N)
+        if kind == "adapter_fwd":
+            self.flops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
+            self.weight_bytes = wb
+            self.bytes = wb + M * K * ab + fac + 4.0 * M * N + 4.0 * M * r
+        elif kind == "adapter_bwd":
+            self.flops = 2.0 * M * N * K + 4.0 * M * r * (K + N)
+            self.weight_bytes = wb
+            self.bytes = wb + M * (N + K) * ab + fac + 4.0 * M * r + 4.0 * M * K + fac
+        else:
+            self.flops = 0.0
+            self.weight_bytes = 0.0
+            self.bytes = 7 * fac
+        self.sets = []
+        for s in range(sets):
+            pw = q.pack(w.codes.cuda(), w.scales.cuda(), w.group_size)
+            st = {"pw": pw, "x": case.x.cuda(), "d": case.d_out.cuda(), "A": case.A.cuda(), "B": case.B.cuda()}
+            st["y"] = torch.empty(M, N, dtype=torch.float32, device="cuda")
+            st["t"] = torch.empty(M, r, dtype=torch.float32, device="cuda")
+            st["dx"] = torch.empty(M, K, dtype=torch.float32, device="cuda")
+            st["dA"] = torch.empty(r, K, dtype=torch.float32, device="cuda")
+            st["dB"] = torch.empty(N, r, dtype=torch.float32, device="cuda")
+            # the optimizer state of both factors in one flat buffer each (A's values, then B's)
+            n = r * (K + N)
+            st["p"] = torch.cat([case.A.reshape(-1), case.B.reshape(-1)]).cuda()
+            st["g"] = torch.randn(n, generator=torch.Generator().manual_seed(s)).mul_(1e-3).cuda()
+            st["m"] = torch.zeros(n, device="cuda")
+            st["v"] = torch.zeros(n, device="cuda")
+            self.sets.append(st)
+        op = q.OP_FWD if kind == "adapter_fwd" else q.OP_BWD_INPUT
+        need = q.adapter_workspace_bytes(op, self.sets[0]["pw"], M, case.x.dtype, r)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.route = "adamw" if kind == "adamw" else q.route(op, self.sets[0]["pw"], M, case.x.dtype)
+        self.peak = MFMA_PEAK_TFLOPS
+        self.bound = "hbm" if kind == "adamw" or self.flops / self.bytes < self.peak * 1e12 / (
+            HBM_PEAK_GBS * 1e9) else "mfma"
+        self.steps_done = 0
+
+    def run(self, q, i):
+        st = self.sets[i % len(self.sets)]
+        if self.kind == "adapter_fwd":
+            q.adapter_fwd(st["pw"], st["x"], st["A"], st["B"], self.alpha, out=st["y"], t=st["t"], workspace=self.ws)
+        elif self.kind == "adapter_bwd":
+            q.adapter_bwd(st["pw"], st["x"], st["d"], st["A"], st["B"], self.alpha, st["t"], d_x=st["dx"],
+                          d_A=st["dA"], d_B=st["dB"], workspace=self.ws)
+        else:
+            # the step count only sets the bias corrections; a fixed one keeps captured replays alike
+            q.adamw_step(st["p"], st["g"], st["m"], st["v"], 10, 1e-4, 0.9, 0.999, 1e-8, 0.01)
+
+
 def torch_dtype(name):
     from synthetic_inputs import DTYPES
     return DTYPES[name]
@@ -178,6 +246,12 @@ def build_ops(q, names, rotate):
         elif n == "dq8ca":
             # the prefill workload with its activation rows quantised to int8 per row, outside the step
             specs.append(("dq8ca", "dq8ca", make_workload("prefill")))
+        elif n in ("adapter", "adapter_fwd", "adapter_bwd", "adamw"):
+            # the adapter step around the frozen MLP up projection (M=512, rank 16), outside the step
+            ad = make_workload("adapter")
+            for k in ("adapter_fwd", "adapter_bwd", "adamw"):
+                if n in ("adapter", k):
+                    specs.append((k, k, ad))
         elif n in ("embedding", "emb_t512", "emb_t1"):
             # the row gather from the tied embedding table, outside the step: 512 ids and one id
             emb = make_workload("embedding")
@@ -190,12 +264,16 @@ def build_ops(q, names, rotate):
         else:
             raise SystemExit(f"unknown op {n}")
     def set_bytes(case):
+        if case.A is not None:
+            return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + \
+                (case.x.numel() + case.d_out.numel()) * case.x.element_size()
         if case.ids is not None:
             return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights)
         act = case.x if case.x is not None else case.d_out
         return sum(w.N * w.K / 2 + w.scales.numel() * 2 for w in case.weights) + act.numel() * act.element_size()
 
-    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1", "bwd_h", "bwd_gs32", "dq8ca"}
+    extra = {"qkv_m1", "qkv_m4", "emb_t512", "emb_t1", "bwd_h", "bwd_gs32", "dq8ca", "adapter_fwd", "adapter_bwd",
+             "adamw"}
     if rotate <= 0:
         # the step rotates enough sets of every op to exceed the MALL; each op also gets enough
         # copies of its own to exceed it alone, for its per-op timing
@@ -205,8 +283,14 @@ def build_ops(q, names, rotate):
         per_op = [max(rotate, int(MALL_BYTES * 1.5 // set_bytes(c)) + 1) for _, _, c in specs]
     else:
         per_op = [rotate] * len(specs)
-    ops = [EmbOp(n, c, q, sets) if k == "embedding" else Op(n, k, c, q, sets)
-           for (n, k, c), sets in zip(specs, per_op)]
+    def make(n, k, c, sets):
+        if k == "embedding":
+            return EmbOp(n, c, q, sets)
+        if k in ("adapter_fwd", "adapter_bwd", "adamw"):
+            return AdapterOp(n, k, c, q, sets)
+        return Op(n, k, c, q, sets)
+
+    ops = [make(n, k, c, sets) for (n, k, c), sets in zip(specs, per_op)]
     for op in ops:
         op.in_step = op.name not in extra
     if not any(op.in_step for op in ops):
@@ -224,7 +308,9 @@ _OP_SRC = {"decode": ("gemv.hip",), "qkv_m1": ("gemv.hip",), "qkv_m4": ("gemv.hi
            "qkv_m508": ("gemm_fwd.hip", "gemv.hip"), "qkv_m512": ("gemm_fwd.hip", "gemv.hip"),
            "bwd": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "bwd_h": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"),
            "bwd_gs32": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "emb_t512": ("embedding.hip",),
-           "emb_t1": ("embedding.hip",), "dq8ca": ("dq8ca.hip", "gemv.hip")}
+           "emb_t1": ("embedding.hip",), "dq8ca": ("dq8ca.hip", "gemv.hip"),
+           "adapter_fwd": ("adapter.hip", "gemm_fwd.hip", "gemv.hip"),
+           "adapter_bwd": ("adapter.hip", "gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "adamw": ("adapter.hip",)}
 
 
 def source_hash(op_name=None):
@@ -260,7 +346,10 @@ OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_"),
               "qkv_m512": ("gemm_fwd", "reduce_"), "bwd": ("gemm_bwd", "reduce_"),
               "bwd_h": ("gemm_bwd", "reduce_"), "bwd_gs32": ("gemm_bwd", "reduce_", "split_planes"),
               "emb_t512": ("embedding_kernel",), "emb_t1": ("embedding_kernel",),
-              "dq8ca": ("dq8ca_", "reduce_")}
+              "dq8ca": ("dq8ca_", "reduce_"),
+              "adapter_fwd": ("gemm_fwd", "reduce_", "rank_contract", "rank_expand"),
+              "adapter_bwd": ("gemm_bwd", "reduce_", "rank_contract", "rank_expand", "column_"),
+              "adamw": ("adamw_kernel",)}
 
 
 def _counter_means(d, counter):

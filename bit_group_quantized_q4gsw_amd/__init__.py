@@ -11,7 +11,7 @@ if it has not been built.
 """
 from .binding import (  # noqa: F401
     BF16, F16, F32, OP_BWD_INPUT, OP_DQ8CA, OP_FWD, OP_QKV, ROUTES, PackedWeight, Q4gswError, WeightDesc,
-    build_info, dq8ca_quantize, embedding, linear_dq8ca, forced_plan, forced_route, lib, linear_bwd_input, linear_fwd, linear_fwd_noalloc, pack, packed_bytes, qkv_fused,
+    adamw_step, adapter_bwd, adapter_fwd, adapter_workspace_bytes, build_info, dq8ca_quantize, embedding, linear_dq8ca, forced_plan, forced_route, lib, linear_bwd_input, linear_fwd, linear_fwd_noalloc, pack, packed_bytes, qkv_fused,
     plan, qkv_workspace_bytes, route, route_name, status_str, unpack, workspace_bytes,
 )
 

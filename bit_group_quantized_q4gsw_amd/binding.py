@@ -56,6 +56,12 @@ class Options(ctypes.Structure):
     _fields_ = [("route", ctypes.c_int32), ("tile_rows", ctypes.c_int32), ("splits", ctypes.c_int32)]
 
 
+class AdamwParams(ctypes.Structure):
+    """q4gsw_adamw_params of include/q4gsw.h."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
 # Choices made by forced_route / forced_plan, held per Python thread and handed to each call
 # (the library itself keeps no routing state).
 _local = threading.local()
@@ -104,6 +110,10 @@ def lib() -> ctypes.CDLL:
             "q4gsw_dq8ca_quantize": [vp, i32, i64, i64, vp, vp, vp, vp],
             "q4gsw_linear_dq8ca": [pw, vp, i32, i64, vp, vp, u64, vp],
             "q4gsw_linear_dq8ca_ex": [pw, vp, i32, i64, vp, vp, u64, po, vp],
+            "q4gsw_adapter_workspace_bytes": [i32, pw, i64, i32, i32, ctypes.POINTER(u64)],
+            "q4gsw_adapter_fwd": [pw, vp, i32, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, u64, vp],
+            "q4gsw_adapter_bwd": [pw, vp, vp, i32, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, u64, vp],
+            "q4gsw_adamw_step": [vp, vp, vp, vp, i64, ctypes.POINTER(AdamwParams), i64, vp],
         }
         for name, args in sigs.items():
             fn = getattr(h, name)
@@ -314,6 +324,80 @@ def linear_dq8ca(w: PackedWeight, x: torch.Tensor, out: Optional[torch.Tensor] =
     _check(lib().q4gsw_linear_dq8ca_ex(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, y.data_ptr(), wp, wb,
                                        _opts(), _stream()), "q4gsw_linear_dq8ca")
     return y
+
+
+def adapter_workspace_bytes(op: int, w: PackedWeight, M: int, dtype: torch.dtype, rank: int) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().q4gsw_adapter_workspace_bytes(op, w.ref(), M, _TORCH_DTYPE[dtype], rank, ctypes.byref(out)),
+           "q4gsw_adapter_workspace_bytes")
+    return out.value
+
+
+def _factor(t: torch.Tensor, shape: Tuple[int, int], device, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError(f"{name} must be an fp32 tensor of shape {list(shape)} on {device}")
+    return t.contiguous()
+
+
+def adapter_fwd(w: PackedWeight, x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, alpha: float,
+                out: Optional[torch.Tensor] = None, t: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(y [M, N], t [M, r]) = (x . dequant(W)^T + alpha (x A^T) B^T, x A^T) for the low-rank
+    adapter A [r, K], B [N, r] (fp32) beside the frozen weight."""
+    x = _dev(x, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError("x must be [M, K]")
+    M, r = x.shape[0], A.shape[0]
+    A = _factor(A, (r, w.K), x.device, "A")
+    B = _factor(B, (w.N, r), x.device, "B")
+    y = _out(out, (M, w.N), x.device, "out")
+    t = _out(t, (M, r), x.device, "t")
+    need = adapter_workspace_bytes(OP_FWD, w, M, x.dtype, r)
+    ws, wp, wb = _ws_args(need, workspace, x.device)
+    _check(lib().q4gsw_adapter_fwd(w.ref(), x.data_ptr(), _TORCH_DTYPE[x.dtype], M, A.data_ptr(), B.data_ptr(), r,
+                                   float(alpha), y.data_ptr(), t.data_ptr(), wp, wb, _stream()), "q4gsw_adapter_fwd")
+    return y, t
+
+
+def adapter_bwd(w: PackedWeight, x: torch.Tensor, d_out: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                alpha: float, t: torch.Tensor, d_x: Optional[torch.Tensor] = None,
+                d_A: Optional[torch.Tensor] = None, d_B: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """(d_x [M, K], d_A [r, K], d_B [N, r]): the gradients of <d_out, y> for the adapter forward of
+    the same x (t is its x A^T)."""
+    x = _dev(x, "x")
+    d_out = _dev(d_out, "d_out")
+    if x.dim() != 2 or x.shape[1] != w.K or d_out.shape != (x.shape[0], w.N) or d_out.dtype != x.dtype:
+        raise ValueError("x must be [M, K] and d_out [M, N] of x's dtype")
+    M, r = x.shape[0], A.shape[0]
+    A = _factor(A, (r, w.K), x.device, "A")
+    B = _factor(B, (w.N, r), x.device, "B")
+    t = _factor(t, (M, r), x.device, "t")
+    dx = _out(d_x, (M, w.K), x.device, "d_x")
+    dA = _out(d_A, (r, w.K), x.device, "d_A")
+    dB = _out(d_B, (w.N, r), x.device, "d_B")
+    need = adapter_workspace_bytes(OP_BWD_INPUT, w, M, x.dtype, r)
+    ws, wp, wb = _ws_args(need, workspace, x.device)
+    _check(lib().q4gsw_adapter_bwd(w.ref(), x.data_ptr(), d_out.data_ptr(), _TORCH_DTYPE[x.dtype], M, A.data_ptr(),
+                                   B.data_ptr(), r, float(alpha), t.data_ptr(), dx.data_ptr(), dA.data_ptr(),
+                                   dB.data_ptr(), wp, wb, _stream()), "q4gsw_adapter_bwd")
+    return dx, dA, dB
+
+
+def adamw_step(param: torch.Tensor, grad: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+               step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+               weight_decay: float = 0.01) -> None:
+    """One AdamW step in place on contiguous fp32 GPU tensors of one size (param, exp_avg and
+    exp_avg_sq are updated)."""
+    ts = [param, grad, exp_avg, exp_avg_sq]
+    n = param.numel()
+    for name, tt in zip(("param", "grad", "exp_avg", "exp_avg_sq"), ts):
+        if tt.dtype != torch.float32 or not tt.is_contiguous() or tt.numel() != n or tt.device != param.device \
+                or not tt.is_cuda:
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor of {n} elements on {param.device}")
+    hp = AdamwParams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().q4gsw_adamw_step(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), n,
+                                  ctypes.byref(hp), int(step), _stream()), "q4gsw_adamw_step")
 
 
 def embedding(w: PackedWeight, ids: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -229,6 +229,26 @@ q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M
     }
 }
 
+q4gsw_status run_bwd(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M, float* d_x, void* ws,
+                     int32_t route, const Opts& o, hipStream_t s) {
+    const WView v = view_of(w);
+    switch (route) {
+        case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_bwd(v, d_out, g_dtype, M, d_x, s));
+        case Q4GSW_ROUTE_BWD_GEMV: {
+            const int splits = gemv_bwd_splits(v, M);
+            if (splits == 1) return hip_status(launch_gemv_bwd(v, d_out, g_dtype, M, d_x, 1, s));
+            float* part = static_cast<float*>(ws);
+            hipError_t e = launch_gemv_bwd(v, d_out, g_dtype, M, part, splits, s);
+            if (e == hipSuccess) e = launch_reduce_splits(part, splits, M, v.K, v.k_pad, d_x, v.K, s);
+            return hip_status(e);
+        }
+        default: {
+            const BwdPlan plan = plan_gemm_bwd(v, g_dtype, fold_ok(w), M, o.splits);
+            return hip_status(launch_gemm_bwd(v, d_out, g_dtype, M, d_x, plan, static_cast<float*>(ws), s));
+        }
+    }
+}
+
 bool ws_ok(const void* ws, uint64_t ws_bytes, uint64_t need) {
     return need == 0 || (ws && ws_bytes >= need && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0);
 }
@@ -461,23 +481,7 @@ q4gsw_status q4gsw_linear_bwd_input_ex(const q4gsw_weight* w, const void* d_out,
         (need > 0 && (overlap(xr, range_of(ws, need)) || overlap(range_of(ws, need), gr) ||
                       overlap(range_of(ws, need), range_of(w->data, w->bytes)))))
         return Q4GSW_E_ALIAS;
-    const WView v = view_of(w);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (route) {
-        case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_bwd(v, d_out, g_dtype, M, d_x, s));
-        case Q4GSW_ROUTE_BWD_GEMV: {
-            const int splits = gemv_bwd_splits(v, M);
-            if (splits == 1) return hip_status(launch_gemv_bwd(v, d_out, g_dtype, M, d_x, 1, s));
-            float* part = static_cast<float*>(ws);
-            hipError_t e = launch_gemv_bwd(v, d_out, g_dtype, M, part, splits, s);
-            if (e == hipSuccess) e = launch_reduce_splits(part, splits, M, v.K, v.k_pad, d_x, v.K, s);
-            return hip_status(e);
-        }
-        default: {
-            const BwdPlan plan = plan_gemm_bwd(v, g_dtype, fold_ok(w), M, o.splits);
-            return hip_status(launch_gemm_bwd(v, d_out, g_dtype, M, d_x, plan, static_cast<float*>(ws), s));
-        }
-    }
+    return run_bwd(w, d_out, g_dtype, M, d_x, ws, route, o, static_cast<hipStream_t>(stream));
 }
 
 q4gsw_status q4gsw_linear_bwd_input(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M, float* d_x,
@@ -581,6 +585,114 @@ q4gsw_status q4gsw_qkv_fused(const q4gsw_weight* wq, const q4gsw_weight* wk, con
                              int32_t x_dtype, int64_t M, float* q, float* k, float* v, void* ws, uint64_t ws_bytes,
                              void* stream) {
     return q4gsw_qkv_fused_ex(wq, wk, wv, x, x_dtype, M, q, k, v, ws, ws_bytes, nullptr, stream);
+}
+
+// ---- the adapter step around the frozen base ----------------------------------------------------
+static bool finite_f(double v) { return v == v && v - v == 0.0; }
+
+q4gsw_status q4gsw_adapter_workspace_bytes(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype,
+                                           int32_t rank, uint64_t* bytes) {
+    if (!bytes) return Q4GSW_E_NULL;
+    *bytes = 0;
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (M < 1 || M > kMaxM || rank < 1 || rank > adapter_rank_max()) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(act_dtype)) return Q4GSW_E_DTYPE;
+    const Opts o;
+    if (op == Q4GSW_OP_FWD) {
+        const int32_t route = pick_fwd(w, M, act_dtype, false, o.route, &st);
+        if (st != Q4GSW_OK) return st;
+        *bytes = fwd_ws_bytes(w, M, act_dtype, route, o);
+        return Q4GSW_OK;
+    }
+    if (op == Q4GSW_OP_BWD_INPUT) {
+        const int32_t route = pick_bwd(w, M, act_dtype, o.route, &st);
+        if (st != Q4GSW_OK) return st;
+        *bytes = round_up((int64_t)bwd_ws_bytes(w, M, act_dtype, route, o), 256) +
+                 adapter_bwd_terms_ws_bytes(M, w->N, w->K, rank);
+        return Q4GSW_OK;
+    }
+    return Q4GSW_E_SHAPE;
+}
+
+q4gsw_status q4gsw_adapter_fwd(const q4gsw_weight* w, const void* x, int32_t x_dtype, int64_t M, const float* A,
+                               const float* B, int32_t rank, float alpha, float* y, float* t, void* ws,
+                               uint64_t ws_bytes, void* stream) {
+    const Opts o;
+    int32_t route = Q4GSW_ROUTE_NONE;
+    uint64_t need = 0;
+    q4gsw_status st = prepare_fwd(w, x, x_dtype, M, y, o, &route, &need);
+    if (st != Q4GSW_OK) return st;
+    if (!A || !B || !t) return Q4GSW_E_NULL;
+    if (rank < 1 || rank > adapter_rank_max()) return Q4GSW_E_SHAPE;
+    if (!finite_f(alpha)) return Q4GSW_E_SHAPE;
+    if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
+    if ((st = fwd_alias(w, x, x_dtype, M, y, ws, need)) != Q4GSW_OK) return st;
+    // the outputs y and t against every input and each other; the workspace against t and the factors
+    const Range yr = range_of(y, (uint64_t)M * w->N * 4), tr = range_of(t, (uint64_t)M * rank * 4);
+    const Range ar = range_of(A, (uint64_t)rank * w->K * 4), br = range_of(B, (uint64_t)w->N * rank * 4);
+    const Range xr = range_of(x, (uint64_t)M * w->K * esize(x_dtype)), wr = range_of(w->data, w->bytes);
+    const Range sr = range_of(ws, need);
+    if (overlap(yr, ar) || overlap(yr, br) || overlap(yr, tr) || overlap(tr, xr) || overlap(tr, ar) ||
+        overlap(tr, br) || overlap(tr, wr) || overlap(sr, tr) || overlap(sr, ar) || overlap(sr, br))
+        return Q4GSW_E_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = run_fwd(w, x, x_dtype, M, y, ws, route, o, s)) != Q4GSW_OK) return st;
+    return hip_status(launch_adapter_fwd_terms(x, x_dtype, M, w->N, w->K, A, B, rank, alpha, y, t, s));
+}
+
+q4gsw_status q4gsw_adapter_bwd(const q4gsw_weight* w, const void* x, const void* d_out, int32_t dtype, int64_t M,
+                               const float* A, const float* B, int32_t rank, float alpha, const float* t, float* d_x,
+                               float* d_A, float* d_B, void* ws, uint64_t ws_bytes, void* stream) {
+    q4gsw_status st = check_desc(w);
+    if (st != Q4GSW_OK) return st;
+    if (!x || !d_out || !A || !B || !t || !d_x || !d_A || !d_B) return Q4GSW_E_NULL;
+    if (M < 1 || M > kMaxM || rank < 1 || rank > adapter_rank_max() || !finite_f(alpha)) return Q4GSW_E_SHAPE;
+    if (!act_dtype_ok(dtype)) return Q4GSW_E_DTYPE;
+    const Opts o;
+    const int32_t route = pick_bwd(w, M, dtype, o.route, &st);
+    if (st != Q4GSW_OK) return st;
+    const uint64_t base = round_up((int64_t)bwd_ws_bytes(w, M, dtype, route, o), 256);
+    const uint64_t need = base + adapter_bwd_terms_ws_bytes(M, w->N, w->K, rank);
+    if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
+    const int64_t N = w->N, K = w->K;
+    const Range outs[3] = {range_of(d_x, (uint64_t)M * K * 4), range_of(d_A, (uint64_t)rank * K * 4),
+                           range_of(d_B, (uint64_t)N * rank * 4)};
+    const Range ins[6] = {range_of(x, (uint64_t)M * K * esize(dtype)), range_of(d_out, (uint64_t)M * N * esize(dtype)),
+                          range_of(A, (uint64_t)rank * K * 4), range_of(B, (uint64_t)N * rank * 4),
+                          range_of(t, (uint64_t)M * rank * 4), range_of(w->data, w->bytes)};
+    const Range sr = range_of(ws, need);
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], ins[j])) return Q4GSW_E_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return Q4GSW_E_ALIAS;
+        if (overlap(outs[i], sr)) return Q4GSW_E_ALIAS;
+    }
+    for (int j = 0; j < 6; ++j)
+        if (overlap(sr, ins[j])) return Q4GSW_E_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = run_bwd(w, d_out, dtype, M, d_x, ws, route, o, s)) != Q4GSW_OK) return st;
+    return hip_status(launch_adapter_bwd_terms(x, d_out, dtype, M, N, K, A, B, rank, alpha, t, d_x, d_A, d_B,
+                                               static_cast<uint8_t*>(ws) + base, s));
+}
+
+q4gsw_status q4gsw_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq, int64_t n,
+                              const q4gsw_adamw_params* hp, int64_t step, void* stream) {
+    if (!hp) return Q4GSW_E_NULL;
+    if (n < 0 || step < 1) return Q4GSW_E_SHAPE;
+    if (!(finite_f(hp->lr) && hp->lr >= 0 && finite_f(hp->weight_decay) && hp->weight_decay >= 0 &&
+          hp->beta1 >= 0 && hp->beta1 < 1 && hp->beta2 >= 0 && hp->beta2 < 1 && finite_f(hp->eps) && hp->eps > 0))
+        return Q4GSW_E_SHAPE;
+    if (n == 0) return Q4GSW_OK;
+    if (!param || !grad || !exp_avg || !exp_avg_sq) return Q4GSW_E_NULL;
+    const uint64_t b = (uint64_t)n * 4;
+    const Range r[4] = {range_of(param, b), range_of(grad, b), range_of(exp_avg, b), range_of(exp_avg_sq, b)};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(r[i], r[j])) return Q4GSW_E_ALIAS;
+    return hip_status(launch_adamw(param, grad, exp_avg, exp_avg_sq, n, hp->lr, hp->beta1, hp->beta2, hp->eps,
+                                   hp->weight_decay, step, static_cast<hipStream_t>(stream)));
 }
 
 int32_t q4gsw_route(int32_t op, const q4gsw_weight* w, int64_t M, int32_t act_dtype) {

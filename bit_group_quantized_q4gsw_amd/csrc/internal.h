@@ -126,4 +126,18 @@ hipError_t launch_dq8ca_quantize(const void* x, int x_dtype, int64_t M, int64_t 
 hipError_t launch_dq8ca(const WView& w, const void* x, int x_dtype, int64_t M, float* y, const Dq8caPlan& plan,
                         void* ws, hipStream_t s);
 
+// adapter.hip: the low-rank adapter terms beside the frozen weight (rank 1..adapter_rank_max())
+// and the AdamW update.  t = x A^T [M, r] is written, then y += alpha t B^T.  The backward writes
+// u = d_out B [M, r] (workspace), then d_x += alpha u A, d_A = alpha u^T x, d_B = alpha d_out^T t;
+// its workspace (u, then the row-slab partials of d_A and d_B) is adapter_bwd_terms_ws_bytes.
+int adapter_rank_max();
+uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank);
+hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
+                                    const float* B, int rank, float alpha, float* y, float* t, hipStream_t s);
+hipError_t launch_adapter_bwd_terms(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
+                                    const float* A, const float* B, int rank, float alpha, const float* t,
+                                    float* d_x, float* d_A, float* d_B, void* ws, hipStream_t s);
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, double lr, double beta1,
+                        double beta2, double eps, double weight_decay, int64_t step, hipStream_t s);
+
 }  // namespace q4gsw

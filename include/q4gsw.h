@@ -284,6 +284,67 @@ q4gsw_status q4gsw_linear_dq8ca_ex(const q4gsw_weight *w, const void *x, int32_t
                                    void *ws, uint64_t ws_bytes, const q4gsw_options *opts, void *stream);
 
 /*
+ * The adapter step around the frozen base.  The Vulkan pull request "[ExecuTorch][Vulkan] Add
+ * et_vk.linear_q4gsw_backward kernel (4-bit input-grad)" says (opening summary) that the input
+ * gradient serves on-device adapter training around the frozen 4-bit base, and its stack lists an
+ * on-GPU AdamW optimizer step (et_vk.adamw_step); the pages give no adapter mathematics.
+ * Reading: a rank-r low-rank adapter beside the packed weight, factors A [r, K] and B [N, r] in
+ * fp32 row-major, scaled by alpha:
+ *   t = x A^T [M, r],    y = x . dequant(W)^T + alpha t B^T
+ * and, for the loss <d_out, y>,
+ *   u = d_out B,  d_x = d_out . dequant(W) + alpha u A,  d_A = alpha u^T x,  d_B = alpha d_out^T t.
+ * Both calls run the library's forward / input gradient for the W term (its routes and precision)
+ * and fp32 kernels for the low-rank terms, every sum in a fixed order (results do not depend on
+ * the launch).  rank: 1..64.
+ *
+ * q4gsw_adapter_workspace_bytes: workspace of q4gsw_adapter_fwd (op Q4GSW_OP_FWD) or
+ * q4gsw_adapter_bwd (op Q4GSW_OP_BWD_INPUT) for M rows of act_dtype at this rank.
+ * E_NULL, E_DESC, E_SHAPE (M, rank or op out of range), E_DTYPE.
+ */
+q4gsw_status q4gsw_adapter_workspace_bytes(int32_t op, const q4gsw_weight *w, int64_t M, int32_t act_dtype,
+                                           int32_t rank, uint64_t *bytes);
+/*
+ *   x  device [M, K] in x_dtype;  A device fp32 [rank, K];  B device fp32 [N, rank]
+ *   y  device fp32 [M, N] (written);  t device fp32 [M, rank] (written: x A^T, kept for the backward)
+ *   ws device workspace of ws_bytes (256-byte aligned) >= q4gsw_adapter_workspace_bytes(Q4GSW_OP_FWD)
+ * E_NULL, E_SHAPE (rank, M, non-finite alpha), E_DTYPE, E_GROUP, E_WORKSPACE, E_ALIAS (an output
+ * overlaps an input, the other output or the workspace), E_HIP.
+ */
+q4gsw_status q4gsw_adapter_fwd(const q4gsw_weight *w, const void *x, int32_t x_dtype, int64_t M, const float *A,
+                               const float *B, int32_t rank, float alpha, float *y, float *t, void *ws,
+                               uint64_t ws_bytes, void *stream);
+/*
+ *   x, d_out  device [M, K] and [M, N] in dtype (one dtype for both);  A, B, t as above (t from the
+ *             forward of the same x)
+ *   d_x device fp32 [M, K];  d_A device fp32 [rank, K];  d_B device fp32 [N, rank] (all written)
+ *   ws  device workspace (256-byte aligned) >= q4gsw_adapter_workspace_bytes(Q4GSW_OP_BWD_INPUT):
+ *       the input gradient's, then u [M, rank]
+ * Errors as q4gsw_adapter_fwd; outputs may overlap neither each other, any input nor ws.
+ */
+q4gsw_status q4gsw_adapter_bwd(const q4gsw_weight *w, const void *x, const void *d_out, int32_t dtype, int64_t M,
+                               const float *A, const float *B, int32_t rank, float alpha, const float *t, float *d_x,
+                               float *d_A, float *d_B, void *ws, uint64_t ws_bytes, void *stream);
+
+/*
+ * One AdamW step (Loshchilov and Hutter, "Decoupled Weight Decay Regularization": decoupled decay,
+ * bias-corrected moments) on n fp32 values in place, for step >= 1:
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   p <- p - lr / (1 - b1^step) * m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * param, exp_avg (m), exp_avg_sq (v): device fp32 [n], updated;  grad: device fp32 [n].
+ * E_NULL, E_SHAPE (n < 0, step < 1, lr or wd negative or not finite, beta outside [0, 1), eps not
+ * positive and finite), E_ALIAS (any two buffers overlap), E_HIP.  n = 0 launches nothing.
+ */
+typedef struct q4gsw_adamw_params {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+} q4gsw_adamw_params;
+q4gsw_status q4gsw_adamw_step(float *param, const float *grad, float *exp_avg, float *exp_avg_sq, int64_t n,
+                              const q4gsw_adamw_params *hp, int64_t step, void *stream);
+
+/*
  * Embedding row gather: out[t, k] = dequant(W)[ids[t], k], for t < T and k < K.
  * The embedding_q4gsw op of the Gemma 4 ExecuTorch export (maintainer comment on the
  * react-native-executorch issue "Upstream the Gemma 4 Vulkan support we carry on our

@@ -14,7 +14,13 @@ Recipe (the same for every workload):
   * scales: ``rand * (hi - lo) + lo`` in fp32, then rounded to the scale dtype,
     shape [num_groups, N] with num_groups = K / group_size;
   * token ids (embedding gather): ``randint(0, N)`` int64, shape [M];
-  * draw order: activation(s) or ids first, then (codes, scales) per weight.
+  * low-rank adapter factors (fp32): A [r, K] = ``randn / sqrt(K)``,
+    B [N, r] = ``randn * b_std`` (b_std 0.02 by default; B is nonzero so that both
+    factors' gradients are exercised);
+  * AdamW state (fp32, n values): param ``randn``, grad ``randn * 0.1``, first
+    moment ``randn * 0.01``, second moment ``rand * 1e-3`` (zero moments at step 1);
+  * draw order: activation(s) or ids first, then (codes, scales) per weight, then
+    the adapter factors A, B.
 
 Shapes are those of Llama-3.2-1B projections: MLP up/gate [8192, 2048], down
 [2048, 8192], Q [2048, 2048], K and V [512, 2048]; its tied embedding / output
@@ -82,6 +88,8 @@ class Case:
     d_out: Optional[torch.Tensor]        # [M, N] output gradient (backward input)
     weights: List[Weight] = field(default_factory=list)
     ids: Optional[torch.Tensor] = None   # [M] token ids (embedding gather input)
+    A: Optional[torch.Tensor] = None     # [r, K] fp32 adapter factor
+    B: Optional[torch.Tensor] = None     # [N, r] fp32 adapter factor
 
     @property
     def w(self) -> Weight:
@@ -106,6 +114,38 @@ def make_linear(M: int, K: int, N: int, group_size: int, act_dtype: str, scale_d
     d_out = draw_activation(g, M, N, act_dtype, sigma) if bwd else None
     w = make_weight(g, N, K, group_size, scale_dtype, s_lo, s_hi)
     return Case(name, M, x, d_out, [w])
+
+
+def draw_factors(g: torch.Generator, rank: int, n: int, k: int, b_std: float = 0.02):
+    """Low-rank adapter factors A [rank, k] ~ N(0, 1/k) and B [n, rank] ~ N(0, b_std^2), fp32."""
+    A = (torch.randn(rank, k, generator=g, dtype=torch.float32) / float(k) ** 0.5).contiguous()
+    B = (torch.randn(n, rank, generator=g, dtype=torch.float32) * b_std).contiguous()
+    return A, B
+
+
+def make_adapter(M: int, K: int, N: int, group_size: int, act_dtype: str, scale_dtype: str, rank: int,
+                 seed: int = 0, sigma: float = 1.0, s_lo: float = 0.002, s_hi: float = 0.02,
+                 b_std: float = 0.02, name: str = "adapter") -> Case:
+    """The adapter step's inputs: x [M, K] and d_out [M, N] in one dtype, the frozen weight
+    [N, K] and the factors A [rank, K], B [N, rank]."""
+    g = torch.Generator().manual_seed(seed)
+    x = draw_activation(g, M, K, act_dtype, sigma)
+    d_out = draw_activation(g, M, N, act_dtype, sigma)
+    w = make_weight(g, N, K, group_size, scale_dtype, s_lo, s_hi)
+    A, B = draw_factors(g, rank, N, K, b_std)
+    return Case(name, M, x, d_out, [w], A=A, B=B)
+
+
+def make_adamw_state(n: int, step: int, seed: int = 0):
+    """(param, grad, exp_avg, exp_avg_sq), fp32 [n]; the moments are zero at step 1."""
+    g = torch.Generator().manual_seed(seed)
+    p = torch.randn(n, generator=g, dtype=torch.float32)
+    gr = torch.randn(n, generator=g, dtype=torch.float32) * 0.1
+    if step <= 1:
+        return p, gr, torch.zeros(n), torch.zeros(n)
+    m = torch.randn(n, generator=g, dtype=torch.float32) * 0.01
+    v = torch.rand(n, generator=g, dtype=torch.float32) * 1e-3
+    return p, gr, m, v
 
 
 def make_qkv(M: int, K: int, Ns: Sequence[int], group_size: int, act_dtype: str, scale_dtype: str,
@@ -135,6 +175,8 @@ def make_embedding(M: int, K: int, N: int, group_size: int, scale_dtype: str, se
 #   bwd     : d_out fp32 N(0, 0.1) [512,8192], W [8192,2048] gs=128, fp16 scales
 # and the row gather of the tied embedding / output projection table:
 #   embedding: M=512 uniform ids, table [128256, 2048] gs=32, fp16 scales
+# and the adapter step around the frozen MLP up projection:
+#   adapter : M=512 K=2048 N=8192 gs=128, bf16 x and d_out, fp16 scales, rank 16, alpha 2
 WORKLOADS: Dict[str, dict] = {
     "tiny": dict(kind="linear", M=4, K=64, N=32, group_size=16, act_dtype="f32", scale_dtype="f32",
                  sigma=1.0, s_lo=0.005, s_hi=0.02, fwd=True, bwd=True),
@@ -148,7 +190,10 @@ WORKLOADS: Dict[str, dict] = {
                 scale_dtype="f16", sigma=0.1, s_lo=0.002, s_hi=0.02, fwd=False, bwd=True),
     "embedding": dict(kind="embedding", M=512, K=2048, N=128256, group_size=32, scale_dtype="f16",
                       s_lo=0.002, s_hi=0.02),
+    "adapter": dict(kind="adapter", M=512, K=2048, N=8192, group_size=128, act_dtype="bf16",
+                    scale_dtype="f16", rank=16, sigma=1.0, s_lo=0.002, s_hi=0.02),
 }
+ADAPTER_ALPHA = 2.0
 
 QKV_MS: Tuple[int, ...] = (128, 508, 512)
 
@@ -165,4 +210,6 @@ def make_workload(name: str, seed: int = 0, M: Optional[int] = None, act_dtype: 
         return make_qkv(seed=seed, name=name, **spec)
     if kind == "embedding":
         return make_embedding(seed=seed, name=name, **spec)
+    if kind == "adapter":
+        return make_adapter(seed=seed, name=name, **spec)
     return make_linear(seed=seed, name=name, **spec)

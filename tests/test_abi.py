@@ -420,6 +420,82 @@ def test_embedding_validation(q):
     assert e(ctypes.byref(wide), ids, 1024, FAKE * 128, None) == E_SHAPE
 
 
+def test_adapter_validation(q):
+    """The adapter calls refuse bad ranks, non-finite alpha, missing factors, a short workspace and
+    every output that overlaps an input, the other outputs or the workspace."""
+    lib = q.lib()
+    d = fake_desc(q, 256, 512, 32, 1, flags=1)
+    x, y, A, B, t = FAKE * 8, FAKE * 16, FAKE * 20, FAKE * 24, FAKE * 28
+    nan, inf = float("nan"), float("inf")
+    need = ctypes.c_uint64()
+    wsb = lib.q4gsw_adapter_workspace_bytes
+    assert wsb(q.OP_FWD, ctypes.byref(d), 4, q.F16, 8, None) == E_NULL
+    assert wsb(q.OP_FWD, ctypes.byref(d), 4, q.F16, 0, ctypes.byref(need)) == E_SHAPE
+    assert wsb(q.OP_FWD, ctypes.byref(d), 4, q.F16, 65, ctypes.byref(need)) == E_SHAPE
+    assert wsb(q.OP_QKV, ctypes.byref(d), 4, q.F16, 8, ctypes.byref(need)) == E_SHAPE
+    assert wsb(q.OP_FWD, ctypes.byref(d), 4, 7, 8, ctypes.byref(need)) == E_DTYPE
+    assert wsb(q.OP_BWD_INPUT, ctypes.byref(d), 4, q.F16, 8, ctypes.byref(need)) == S_OK
+    assert need.value >= 4 * 8 * 4                      # u = d_out B lives in the workspace
+    f = lib.q4gsw_adapter_fwd
+    assert f(ctypes.byref(d), x, q.F16, 4, None, B, 8, 1.0, y, t, None, 0, None) == E_NULL
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, None, None, 0, None) == E_NULL
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 0, 1.0, y, t, None, 0, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 65, 1.0, y, t, None, 0, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, nan, y, t, None, 0, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, inf, y, t, None, 0, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, 7, 4, A, B, 8, 1.0, y, t, None, 0, None) == E_DTYPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, x + 64, None, 0, None) == E_ALIAS   # t inside x
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, y + 64, None, 0, None) == E_ALIAS   # t inside y
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, A + 64, t, None, 0, None) == E_ALIAS   # y inside A
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, B + 4, None, 0, None) == E_ALIAS    # t inside B
+    big = fake_desc(q, 2048, 8192, 128, 1, flags=1)
+    assert wsb(q.OP_FWD, ctypes.byref(big), 512, q.BF16, 16, ctypes.byref(need)) == S_OK
+    assert need.value > 0
+    assert f(ctypes.byref(big), x, q.BF16, 512, A, B, 16, 1.0, y, t, None, 0, None) == E_WS
+    assert f(ctypes.byref(big), x, q.BF16, 512, A, B, 16, 1.0, y, t, t, need.value, None) == E_ALIAS  # ws over t
+    g = lib.q4gsw_adapter_bwd
+    gx, dx, dA, dB = FAKE * 32, FAKE * 36, FAKE * 40, FAKE * 44
+    assert wsb(q.OP_BWD_INPUT, ctypes.byref(d), 4, q.F16, 8, ctypes.byref(need)) == S_OK
+    ws = FAKE * 48
+    args = lambda **k: [k.get(n, v) for n, v in (("w", ctypes.byref(d)), ("x", x), ("g", gx), ("dt", q.F16),
+                                                    ("M", 4), ("A", A), ("B", B), ("r", 8), ("alpha", 1.0),
+                                                    ("t", t), ("dx", dx), ("dA", dA), ("dB", dB), ("ws", ws),
+                                                    ("wsb", need.value), ("s", None))]
+    for k in ("x", "g", "A", "B", "t", "dx", "dA", "dB"):
+        assert g(*args(**{k: None})) == E_NULL, k
+    assert g(*args(r=0)) == E_SHAPE
+    assert g(*args(r=65)) == E_SHAPE
+    assert g(*args(M=0)) == E_SHAPE
+    assert g(*args(alpha=nan)) == E_SHAPE
+    assert g(*args(dt=7)) == E_DTYPE
+    assert g(*args(ws=None, wsb=0)) == E_WS
+    assert g(*args(wsb=need.value - 4)) == E_WS
+    assert g(*args(dA=x + 16)) == E_ALIAS                  # d_A inside x
+    assert g(*args(dB=dx + 16)) == E_ALIAS                 # d_B inside d_x
+    assert g(*args(dx=t)) == E_ALIAS                       # d_x over t
+    assert g(*args(ws=gx)) == E_ALIAS                      # workspace over d_out
+    assert g(*args(dx=ws + 256)) == E_ALIAS                # d_x inside the workspace
+    assert g(*args(dB=FAKE * 4 + 512)) == E_ALIAS          # d_B inside the weight
+
+
+def test_adamw_validation(q):
+    lib = q.lib()
+    p, gr, m, v = FAKE * 8, FAKE * 12, FAKE * 16, FAKE * 20
+    hp = lambda **k: ctypes.byref(q.binding.AdamwParams(k.get("lr", 1e-3), k.get("b1", 0.9), k.get("b2", 0.999),
+                                                         k.get("eps", 1e-8), k.get("wd", 0.01)))
+    f = lib.q4gsw_adamw_step
+    assert f(p, gr, m, v, 64, None, 1, None) == E_NULL
+    assert f(None, gr, m, v, 64, hp(), 1, None) == E_NULL
+    assert f(p, gr, m, None, 64, hp(), 1, None) == E_NULL
+    assert f(p, gr, m, v, 64, hp(), 0, None) == E_SHAPE            # steps count from 1
+    assert f(p, gr, m, v, -1, hp(), 1, None) == E_SHAPE
+    for bad in (dict(lr=-1.0), dict(lr=float("inf")), dict(b1=1.0), dict(b1=-0.1), dict(b2=float("nan")),
+                dict(eps=0.0), dict(wd=-0.5)):
+        assert f(p, gr, m, v, 64, hp(**bad), 1, None) == E_SHAPE, bad
+    assert f(p, p + 128, m, v, 64, hp(), 1, None) == E_ALIAS      # grad overlaps param
+    assert f(p, gr, m, m + 4, 64, hp(), 1, None) == E_ALIAS       # second moment overlaps first
+    assert f(None, None, None, None, 0, hp(), 1, None) == S_OK    # nothing to update: no HIP call
+
 
 def test_bench_refuses_several_gpus():
     """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says why (no GPU touched)."""
