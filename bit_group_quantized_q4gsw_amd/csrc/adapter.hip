@@ -7,18 +7,24 @@
 //   t = x A^T [M, r],  y = x W^T + alpha t B^T,
 //   u = d_out B [M, r],  d_x = d_out W + alpha u A,  d_A = alpha u^T x,  d_B = alpha d_out^T t,
 // and AdamW (decoupled weight decay, bias-corrected moments).  The W terms are the library's
-// forward and input gradient; this file holds the low-rank terms and the optimizer:
+// forward and input gradient; this file holds the low-rank terms and the optimizer.  With
+// r <= 64 they are bound by memory and latency, not arithmetic, so they run on the vector ALUs
+// in fp32, laid out for many loads in flight per lane:
 //
-//   * rank_contract_kernel: out[m, j] = sum_c X[m, c] F(j, c) over one row of X per block (t, u);
-//   * rank_expand_kernel:   Y[m, c] += alpha sum_j T[m, j] G(j, c) (the y and d_x updates);
-//   * column_contract_kernel: O(j, c) = alpha sum_m T[m, j] X[m, c] (d_A, d_B);
+//   * row_partial_kernel: P[s, m, j] = sum over column chunk s of X[m, c] F(j, c) (t, u); the
+//     chunk of F is staged in LDS, each lane sums its column quads, and a butterfly over the
+//     64 lanes leaves output (row, j) in one lane;
+//   * expand_kernel: T[m, j] = sum_s P[s, m, j] (chunks in order; written once as t or u), then
+//     Y[m, c] += alpha sum_j T[m, j] G(j, c) (the y and d_x updates);
+//   * column_partial_kernel, column_reduce_kernel: O(j, c) = alpha sum_m T[m, j] X[m, c]
+//     (d_A, d_B) by row slabs, the slabs added in order;
 //   * adamw_kernel: the elementwise update.
 //
-// F and G are A (row j at A + j K, columns c) or B^T (row j at B + j, stride r); O is written
-// [r, C] (d_A) or [C, r] (d_B).  Every output is summed by one thread (or one block, in a fixed
-// tree), in an order fixed by the shape alone.  Rounding: the row contraction sums C / 256 terms
-// per thread and then a 256-way tree; the column contraction sums runs of kRun rows, the runs of a
-// slab in order and then the slabs in order; the expansion sums the r terms in order and adds once.
+// F and G are A (F(j, c) = A[j C + c]) or B^T (F(j, c) = B[c r + j]).  Every output is summed in
+// an order fixed by the shape alone, so results do not depend on timing.  Rounding chains (fp32):
+// the row contraction adds at most 32 products per lane, 6 tree levels and C / 256 chunks; the
+// expansion r products and one fma; the column contraction a quarter of a slab's rows per wave,
+// 3 wave combines, at most 64 slabs and the scale.
 #include "device.h"
 #include "internal.h"
 
@@ -29,166 +35,416 @@ namespace q4gsw {
 namespace {
 
 constexpr int kRankMax = 64;
-constexpr int kRun = 32;               // rows per partial sum in the column contraction
+constexpr int kExpRows = 32;          // rows per block of the expansion (8 per wave)
+constexpr int kSlabRows = 32;         // rows of a slab piece in the column contraction
+constexpr int64_t kMaxSlabs = 64;
 
-// Rows of X per block in the row contraction: the factor is read once per block, so more rows
-// cut its re-reads; the accumulators (rows x rank bucket) stay within 64 registers.
+// Row contraction tiling for rank bucket R: RW rows per wave (4 waves), chunks of CC columns
+// (the F chunk, R x CC fp32, about 33 KB of LDS up to R = 32), NG column quads per lane.
 template <int R>
-constexpr int contract_rows() { return R >= 64 ? 1 : R >= 32 ? 2 : R >= 16 ? 4 : 8; }
+struct RowTile {
+    static constexpr int RW = R >= 64 ? 1 : R >= 32 ? 2 : 4;
+    static constexpr int ROWS = 4 * RW;
+    static constexpr int CC = R >= 32 ? 256 : 8192 / R;
+    static constexpr int NG = CC / 256;
+    static constexpr int LD = CC + 4;     // LDS row stride: quads stay 16-B aligned, staging spreads banks
+};
 
-// out[m * r + j] = sum_c X[m, c] F(j, c) for X [M, C] (dtype XT); a block (256 threads) takes
-// contract_rows<R>() consecutive rows.  FT = 0: F(j, c) = A[j * C + c]; FT = 1: F(j, c) = B[c * r + j].
-template <int XT, int R, int FT>
-__global__ __launch_bounds__(256) void rank_contract_kernel(const void* __restrict__ X, int64_t M, int64_t C,
-                                                            const float* __restrict__ F, int rank,
-                                                            float* __restrict__ out) {
-    constexpr int RB = contract_rows<R>();
-    __shared__ float red[4][RB * R];
-    const int64_t m0 = (int64_t)blockIdx.x * RB;
-    const int tid = threadIdx.x;
-    const int rows = (int)min((int64_t)RB, M - m0);
-    float acc[RB][R];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < R; ++j) acc[i][j] = 0.0f;
-    for (int64_t c = tid; c < C; c += 256) {
-        float f[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j) f[j] = j < rank ? (FT == 0 ? F[(int64_t)j * C + c] : F[c * rank + j]) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            if (i < rows) {
-                const float xv = load_elem<XT>(X, (m0 + i) * C + c);
-#pragma unroll
-                for (int j = 0; j < R; ++j) acc[i][j] = fmaf(xv, f[j], acc[i][j]);
-            }
+// Columns per lane of the expansion and the column contraction: CQ x R accumulators <= 64.
+template <int R>
+constexpr int cols_per_lane() { return R >= 64 ? 1 : R >= 32 ? 2 : 4; }
+
+// Four consecutive elements of X (dtype XT) widened to fp32; i % 4 == 0 and the address aligned.
+template <int XT>
+__device__ __forceinline__ f4 load_quad(const void* X, int64_t i) {
+    if constexpr (XT == kF32) {
+        return *reinterpret_cast<const f4*>(static_cast<const float*>(X) + i);
+    } else {
+        const u2 w = *reinterpret_cast<const u2*>(static_cast<const uint16_t*>(X) + i);
+        f4 r;
+        if constexpr (XT == kF16) {
+            r[0] = f16_bits_to_f32((uint16_t)(w[0] & 0xffffu));
+            r[1] = f16_bits_to_f32((uint16_t)(w[0] >> 16));
+            r[2] = f16_bits_to_f32((uint16_t)(w[1] & 0xffffu));
+            r[3] = f16_bits_to_f32((uint16_t)(w[1] >> 16));
+        } else {
+            r[0] = bitcast<float>(w[0] << 16);
+            r[1] = bitcast<float>(w[0] & 0xffff0000u);
+            r[2] = bitcast<float>(w[1] << 16);
+            r[3] = bitcast<float>(w[1] & 0xffff0000u);
         }
-    }
-    // fixed tree: the wave's 64 lanes by xor steps, then the 4 waves in order
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            float v = acc[i][j];
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-            acc[i][j] = v;
-        }
-    if ((tid & 63) == 0) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-            for (int j = 0; j < R; ++j) red[tid >> 6][i * R + j] = acc[i][j];
-    }
-    __syncthreads();
-    for (int e = tid; e < RB * R; e += 256) {
-        const int i = e / R, j = e % R;
-        if (i < rows && j < rank)
-            out[(m0 + i) * rank + j] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+        return r;
     }
 }
 
-// Y [M, C] (row-major, fp32) += alpha * T [M, r] . G, G(j, c) = A[j * C + c] (GT = 0) or
-// B[c * r + j] (GT = 1).  Block: 8 rows x 256 columns; thread = one column, 8 rows.
-template <int R, int GT>
-__global__ __launch_bounds__(256) void rank_expand_kernel(float* __restrict__ Y, int64_t M, int64_t C,
-                                                          const float* __restrict__ T, const float* __restrict__ G,
-                                                          int rank, float alpha) {
-    __shared__ float ts[8][R];
-    const int tid = threadIdx.x;
-    const int64_t c = (int64_t)blockIdx.x * 256 + tid;
-    const bool live = c < C;
-    float g[R];
+// X[row_base + c .. + 4) with zeros past C or when !row_ok; VEC: rows hold whole aligned quads
+// (C % 4 == 0).  Every load is issued unconditionally (from element 0 when out of range) and
+// the zeros are selected afterwards, so no branch forces a wait between a lane's loads.
+template <int XT, bool VEC>
+__device__ __forceinline__ f4 load_quad_sel(const void* X, int64_t row_base, int64_t c, int64_t C, bool row_ok) {
+    if constexpr (VEC) {
+        const bool ok = row_ok && c < C;
+        const f4 v = load_quad<XT>(X, ok ? row_base + c : 0);
+        return ok ? v : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
+        f4 r;
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-        g[j] = (live && j < rank) ? (GT == 0 ? G[(int64_t)j * C + c] : G[c * rank + j]) : 0.0f;
-    for (int64_t m0 = (int64_t)blockIdx.y * 8; m0 < M; m0 += (int64_t)gridDim.y * 8) {
-        __syncthreads();
-        for (int i = tid; i < 8 * R; i += 256) {
-            const int r = i / R, j = i % R;
-            ts[r][j] = (m0 + r < M && j < rank) ? T[(m0 + r) * rank + j] : 0.0f;
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = row_ok && c + q < C;
+            const float e = load_elem<XT>(X, ok ? row_base + c + q : 0);
+            r[q] = ok ? e : 0.0f;
+        }
+        return r;
+    }
+}
+
+// p[i] when ok, else 0, from an unconditional load (index 0 stands in when !ok).
+__device__ __forceinline__ float load_sel(const float* __restrict__ p, int64_t i, bool ok) {
+    const float v = p[ok ? i : 0];
+    return ok ? v : 0.0f;
+}
+
+// Sum over the 64 lanes of each of the N values v[i] (N a power of two, <= 64); lane l returns
+// the total of value l % N.  Offsets 32 .. N add whole vectors; below N each level keeps the
+// half of the values named by the lane's bit and adds the partner's copy of that half.
+template <int N>
+__device__ __forceinline__ float lanes_spread(const float* v, int lane) {
+    if constexpr (N == 1) {
+        return v[0];
+    } else {
+        constexpr int H = N / 2;
+        const bool hi = (lane & H) != 0;
+        float w[H];
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+            const float keep = hi ? v[H + i] : v[i];
+            const float send = hi ? v[i] : v[H + i];
+            w[i] = keep + __shfl_xor(send, H);
+        }
+        return lanes_spread<H>(w, lane);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ float wave_sum_spread(float (&v)[N], int lane) {
+#pragma unroll
+    for (int off = 32; off >= N; off >>= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], off);
+    return lanes_spread<N>(v, lane);
+}
+
+// P[s, m, j] = sum_{c in chunk s} X[m, c] F(j, c) for X [M, C] (dtype XT); FT = 0: F(j, c) =
+// A[j C + c], FT = 1: F(j, c) = B[c r + j].  Block b: rows (b / chunks) ROWS .. (wave w: RW of
+// them), chunk b % chunks (lane l: column quads 4 l + 256 g).
+template <int XT, int R, int FT, bool VEC>
+__global__ __launch_bounds__(256) void row_partial_kernel(const void* __restrict__ X, int64_t M, int64_t C,
+                                                          const float* __restrict__ F, int rank, int64_t chunks,
+                                                          float* __restrict__ P) {
+    using T = RowTile<R>;
+    __shared__ __align__(16) float Fl[R * T::LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rb = blockIdx.x / chunks, s = blockIdx.x % chunks;
+    const int64_t c0 = s * T::CC;
+    const int64_t m0 = rb * T::ROWS + wave * T::RW;
+    // every load is issued before the first wait: this lane's X quads, then its share of F
+    f4 xv[T::NG][T::RW];
+#pragma unroll
+    for (int g = 0; g < T::NG; ++g)
+#pragma unroll
+        for (int r = 0; r < T::RW; ++r)
+            xv[g][r] = load_quad_sel<XT, VEC>(X, (m0 + r) * C, c0 + 256 * g + 4 * lane, C, m0 + r < M);
+    constexpr int PER = R * T::CC / 256;
+    float fv[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid + 256 * k;
+        const int j = FT == 0 ? i / T::CC : i % R;
+        const int64_t c = c0 + (FT == 0 ? i % T::CC : i / R);
+        fv[k] = load_sel(F, FT == 0 ? (int64_t)j * C + c : c * rank + j, j < rank && c < C);
+    }
+    __builtin_amdgcn_sched_barrier(0);      // keep every load above ahead of the first wait
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = tid + 256 * k;
+        const int j = FT == 0 ? i / T::CC : i % R;
+        const int cc = FT == 0 ? i % T::CC : i / R;
+        Fl[j * T::LD + cc] = fv[k];
+    }
+    __syncthreads();
+    float acc[T::RW * R];
+#pragma unroll
+    for (int i = 0; i < T::RW * R; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < T::NG; ++g) {
+        const int cc = 256 * g + 4 * lane;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const f4 f = *reinterpret_cast<const f4*>(&Fl[j * T::LD + cc]);
+#pragma unroll
+            for (int r = 0; r < T::RW; ++r) {
+                float a = acc[r * R + j];
+                a = fmaf(xv[g][r][0], f[0], a);
+                a = fmaf(xv[g][r][1], f[1], a);
+                a = fmaf(xv[g][r][2], f[2], a);
+                a = fmaf(xv[g][r][3], f[3], a);
+                acc[r * R + j] = a;
+            }
+        }
+    }
+    const float mine = wave_sum_spread<T::RW * R>(acc, lane);
+    const int r = lane / R, j = lane % R;
+    const int64_t m = m0 + r;
+    if (lane < T::RW * R && j < rank && m < M) P[(s * M + m) * rank + j] = mine;
+}
+
+// Sum of the partials P[s, m, j] (stride apart), s ascending, loads issued NB at a time.
+template <int NB>
+__device__ __forceinline__ float chunk_sum(const float* __restrict__ P, int64_t chunks, int64_t stride, int64_t off) {
+    float v = 0.0f;
+    for (int64_t s0 = 0; s0 < chunks; s0 += NB) {
+        float p[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) p[k] = load_sel(P, (s0 + k) * stride + off, s0 + k < chunks);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) v += p[k];       // past the last partial: + 0, exact
+    }
+    return v;
+}
+
+// T[m, j] = sum_s P[s, m, j] (s ascending; written to Tout by the blocks of column block 0),
+// then Y [M, C] (fp32) += alpha T G with G(j, c) = A[j C + c] (GT = 0) or B[c r + j] (GT = 1).
+// Block: 64 CQ columns (lane l: columns CQ l ..) x 32 rows (wave w: rows 8w .. 8w + 7), over row
+// blocks blockIdx.y, blockIdx.y + gridDim.y, ...  Every global load of a row block (its rows of
+// Y, the chunk partials of its rows of T and, for B, the block's chunk of B, which is contiguous)
+// is issued before the first wait; B then goes to LDS j-major, A is read by the lanes directly.
+// VEC: rows of Y (and of A) hold whole aligned groups of CQ values.
+template <int R, int GT, bool VEC>
+__global__ __launch_bounds__(256) void expand_kernel(float* __restrict__ Y, int64_t M, int64_t C,
+                                                     const float* __restrict__ P, int64_t chunks,
+                                                     const float* __restrict__ G, int rank, float alpha,
+                                                     float* __restrict__ Tout) {
+    constexpr int CQ = cols_per_lane<R>();
+    constexpr int SPAN = 64 * CQ;                  // columns per block
+    constexpr int LDG = SPAN + 4;
+    constexpr int kG = GT == 1 ? R * LDG : 0;
+    constexpr int RPW = kExpRows / 4;              // rows per wave
+    constexpr int TPT = (kExpRows * R + 255) / 256;  // values of T per thread
+    __shared__ __align__(16) float smem[kExpRows * R + kG];
+    float* Tl = smem;
+    float* Gl = smem + kExpRows * R;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t cb = (int64_t)blockIdx.x * SPAN;
+    const int64_t c = cb + (int64_t)lane * CQ;
+    const bool live = c < C;
+    const int64_t nrb = (M + kExpRows - 1) / kExpRows;
+    for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+        const int64_t m0 = rb * kExpRows;
+        // ---- issue: rows of Y, the factor, the chunk partials of T
+        float yv[RPW][CQ];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int64_t m = m0 + RPW * wave + i;
+            const bool ok = live && m < M;
+            const float* yp = Y + (ok ? m * C + c : 0);      // element 0 stands in for rows past M
+            if constexpr (VEC && CQ == 4) {
+                const f4 v = *reinterpret_cast<const f4*>(yp);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) yv[i][q] = v[q];
+            } else if constexpr (VEC && CQ == 2) {
+                const float2 v = *reinterpret_cast<const float2*>(yp);
+                yv[i][0] = v.x;
+                yv[i][1] = v.y;
+            } else {
+#pragma unroll
+                for (int q = 0; q < CQ; ++q) yv[i][q] = load_sel(Y, m * C + c + q, ok && c + q < C);
+            }
+        }
+        float g[CQ][R];
+        constexpr int PER = GT == 1 ? SPAN * R / 256 : 1;
+        float gv[PER];
+        const int64_t avail = min((int64_t)SPAN, C - cb) * rank;   // B[cb r ..) holds the block's columns
+        if constexpr (GT == 1) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) gv[k] = load_sel(G, cb * rank + tid + 256 * k, tid + 256 * k < avail);
+        } else {
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const bool okj = j < rank && live;
+                if constexpr (VEC && CQ == 4) {
+                    const f4 v = *reinterpret_cast<const f4*>(G + (okj ? (int64_t)j * C + c : 0));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) g[q][j] = okj ? v[q] : 0.0f;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < CQ; ++q) g[q][j] = load_sel(G, (int64_t)j * C + c + q, okj && c + q < C);
+                }
+            }
+        }
+        float tv[TPT];
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + 256 * k, r = i / R, j = i % R;
+            const int64_t m = m0 + r;
+            tv[k] = (i < kExpRows * R && m < M && j < rank) ? chunk_sum<8>(P, chunks, M * rank, m * rank + j) : 0.0f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- stage: T (and B) into LDS
+        __syncthreads();                                   // the previous row block's readers are done
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + 256 * k, r = i / R, j = i % R;
+            if (i < kExpRows * R) {
+                Tl[i] = tv[k];
+                if (Tout && blockIdx.x == 0 && m0 + r < M && j < rank) Tout[(m0 + r) * rank + j] = tv[k];
+            }
+        }
+        if constexpr (GT == 1) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = tid + 256 * k;
+                if (i < avail) {
+                    const int cc = i / rank, j = i - cc * rank;
+                    Gl[j * LDG + cc] = gv[k];
+                }
+            }
+            for (int i = tid; i < R * LDG; i += 256) {   // the rank bucket's padding and columns past C
+                if (i / LDG >= rank || i % LDG >= SPAN || cb + i % LDG >= C) Gl[i] = 0.0f;
+            }
         }
         __syncthreads();
         if (!live) continue;
+        if constexpr (GT == 1) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t m = m0 + r;
+            for (int q = 0; q < CQ; ++q)
+#pragma unroll
+                for (int j = 0; j < R; ++j) g[q][j] = Gl[j * LDG + lane * CQ + q];
+        }
+        // ---- the rows
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rr = RPW * wave + i;
+            const int64_t m = m0 + rr;
             if (m >= M) break;
-            float s = 0.0f;
 #pragma unroll
-            for (int j = 0; j < R; ++j) s = fmaf(ts[r][j], g[j], s);
-            Y[m * C + c] = fmaf(alpha, s, Y[m * C + c]);
-        }
-    }
-}
-
-// O(j, c) = alpha * sum_m T[m, j] X[m, c] for X [M, C] (dtype XT) and T [M, r] (fp32); thread = one
-// column c of a 256-column block, all j.  Rows are cut into slabs of `slab` rows (a multiple of
-// kRun), one slab per blockIdx.y; within a slab, runs of kRun rows are summed apart and then in
-// order.  One slab: O is written directly, OT = 0: O[j * C + c] (d_A, [r, C]), OT = 1:
-// O[c * r + j] (d_B, [C, r]).  Several: the slab sums go to P [slabs, r, C] unscaled, and
-// column_reduce_kernel adds them in slab order.
-template <int XT, int R, int OT>
-__global__ __launch_bounds__(256) void column_contract_kernel(const void* __restrict__ X, int64_t M, int64_t C,
-                                                              const float* __restrict__ T, int rank, float alpha,
-                                                              int64_t slab, float* __restrict__ O,
-                                                              float* __restrict__ P) {
-    __shared__ float ts[kRun][R];
-    const int tid = threadIdx.x;
-    const int64_t c = (int64_t)blockIdx.x * 256 + tid;
-    const bool live = c < C;
-    const int64_t lo = (int64_t)blockIdx.y * slab, hi = min(M, lo + slab);
-    float tot[R];
+            for (int q = 0; q < CQ; ++q) {
+                float sum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < R; ++j) tot[j] = 0.0f;
-    for (int64_t r0 = lo; r0 < hi; r0 += kRun) {
-        __syncthreads();
-        for (int i = tid; i < kRun * R; i += 256) {
-            const int r = i / R, j = i % R;
-            ts[r][j] = (r0 + r < hi && j < rank) ? T[(r0 + r) * rank + j] : 0.0f;
-        }
-        __syncthreads();
-        float run[R];
+                for (int j = 0; j < R; ++j) sum = fmaf(Tl[rr * R + j], g[q][j], sum);
+                yv[i][q] = fmaf(alpha, sum, yv[i][q]);
+            }
+            float* yp = Y + m * C + c;
+            if constexpr (VEC && CQ == 4) {
+                *reinterpret_cast<f4*>(yp) = f4{yv[i][0], yv[i][1], yv[i][2], yv[i][3]};
+            } else if constexpr (VEC && CQ == 2) {
+                *reinterpret_cast<float2*>(yp) = make_float2(yv[i][0], yv[i][1]);
+            } else {
 #pragma unroll
-        for (int j = 0; j < R; ++j) run[j] = 0.0f;
-        const int rows = (int)min((int64_t)kRun, hi - r0);
-        if (live) {
-            for (int r = 0; r < rows; ++r) {
-                const float xv = load_elem<XT>(X, (r0 + r) * C + c);
-#pragma unroll
-                for (int j = 0; j < R; ++j) run[j] = fmaf(ts[r][j], xv, run[j]);
+                for (int q = 0; q < CQ; ++q)
+                    if (c + q < C) yp[q] = yv[i][q];
             }
         }
-#pragma unroll
-        for (int j = 0; j < R; ++j) tot[j] += run[j];
-    }
-    if (!live) return;
-    if (P) {
-        float* ps = P + (int64_t)blockIdx.y * rank * C;
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            if (j < rank) ps[(int64_t)j * C + c] = tot[j];
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        if (j < rank) {
-            if (OT == 0) O[(int64_t)j * C + c] = alpha * tot[j];
-            else O[c * rank + j] = alpha * tot[j];
-        }
     }
 }
 
-// O(j, c) = alpha * (P[0, j, c] + P[1, j, c] + ... ) in slab order; one thread per (j, c) of
-// r x C, c fastest; O laid out as in column_contract_kernel.
+// Slab sums of O(j, c) = alpha sum_m T[m, j] X[m, c] for X [M, C] (dtype XT), T [M, r] fp32.
+// Block: 64 CQ columns (lane l: columns CQ l ..) x one slab of `slab` rows (blockIdx.y), taken
+// in pieces of 32 rows staged in LDS; wave w adds rows w, w + 4, ... of each piece in order,
+// then the four waves' sums are added in wave order.  One slab: O is written with alpha
+// applied, OT = 0: O[j C + c] ([r, C], d_A), OT = 1: O[c r + j] ([C, r], d_B).  Several: the
+// unscaled slab sums go to Pc [slabs, r, C].
+template <int XT, int R, int OT, bool VEC>
+__global__ __launch_bounds__(256) void column_partial_kernel(const void* __restrict__ X, int64_t M, int64_t C,
+                                                             const float* __restrict__ T, int rank, int64_t slab,
+                                                             float alpha, float* __restrict__ O,
+                                                             float* __restrict__ Pc) {
+    constexpr int CQ = cols_per_lane<R>();
+    constexpr int kT = kSlabRows * R;
+    // one LDS array: the T piece [32][R], then the wave-combine buffer [CQ R][64]
+    __shared__ __align__(16) float smem[kT + CQ * R * 64];
+    float* Ts = smem;
+    float* red = smem + kT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * CQ;
+    const int64_t lo = (int64_t)blockIdx.y * slab, hi = min(M, lo + slab);
+    float acc[CQ][R];
+#pragma unroll
+    for (int q = 0; q < CQ; ++q)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[q][j] = 0.0f;
+    for (int64_t p0 = lo; p0 < hi; p0 += kSlabRows) {
+        const int rows = (int)min((int64_t)kSlabRows, hi - p0);
+        // this wave's 8 rows of the piece (rows wave + 4 i), loaded before the T piece is waited for
+        constexpr int RPW = kSlabRows / 4;
+        float xv[RPW][CQ];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int r = wave + 4 * i;
+            const int64_t rbase = (p0 + r) * C;
+            if constexpr (CQ == 4) {
+                const f4 v = load_quad_sel<XT, VEC>(X, rbase, c, C, r < rows);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xv[i][q] = v[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < CQ; ++q) {
+                    const bool ok = r < rows && c + q < C;
+                    const float e = load_elem<XT>(X, ok ? rbase + c + q : 0);
+                    xv[i][q] = ok ? e : 0.0f;
+                }
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < kT; i += 256) {
+            const int r = i / R, j = i % R;
+            Ts[i] = load_sel(T, (p0 + r) * rank + j, p0 + r < hi && j < rank);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int r = wave + 4 * i;
+            if (r >= rows) break;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const float tv = Ts[r * R + j];
+#pragma unroll
+                for (int q = 0; q < CQ; ++q) acc[q][j] = fmaf(tv, xv[i][q], acc[q][j]);
+            }
+        }
+    }
+    // the four waves' sums, in wave order
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        __syncthreads();
+        if (wave == w) {
+#pragma unroll
+            for (int q = 0; q < CQ; ++q)
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    float& d = red[(q * R + j) * 64 + lane];
+                    d = w == 0 ? acc[q][j] : d + acc[q][j];
+                }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < CQ * R * 64; i += 256) {
+        const int l = i % 64, qj = i / 64, q = qj / R, j = qj % R;
+        const int64_t cc = ((int64_t)blockIdx.x * 64 + l) * CQ + q;
+        if (j >= rank || cc >= C) continue;
+        const float v = red[i];
+        if (Pc) Pc[((int64_t)blockIdx.y * rank + j) * C + cc] = v;
+        else if (OT == 0) O[(int64_t)j * C + cc] = alpha * v;
+        else O[cc * rank + j] = alpha * v;
+    }
+}
+
+// O(j, c) = alpha * (Pc[0, j, c] + Pc[1, j, c] + ...) in slab order; one thread per (j, c).
 template <int OT>
-__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ P, int slabs, int64_t C,
+__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ Pc, int slabs, int64_t C,
                                                             int rank, float alpha, float* __restrict__ O) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= (int64_t)rank * C) return;
-    const int64_t stride = (int64_t)rank * C;
-    float s = 0.0f;
-    for (int i = 0; i < slabs; ++i) s += P[i * stride + e];
+    const float s = chunk_sum<16>(Pc, slabs, (int64_t)rank * C, e);
     const int64_t j = e / C, c = e % C;
     if (OT == 0) O[e] = alpha * s;
     else O[c * rank + j] = alpha * s;
@@ -259,62 +515,114 @@ void with_rank(int rank, F&& f) {
     else f(std::integral_constant<int, 64>{});
 }
 
+template <typename F>
+void with_bool(bool b, F&& f) {
+    if (b) f(std::true_type{});
+    else f(std::false_type{});
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int es_of(int xt) { return xt == kF32 ? 4 : 2; }
+
+// rows of X (element size es) hold whole quads that start aligned
+bool quads_ok(const void* X, int64_t C, int es) { return C % 4 == 0 && aligned(X, 4 * (uintptr_t)es); }
+
+int64_t row_chunks(int64_t C, int rank) {
+    int64_t cc = 0;
+    with_rank(rank, [&](auto rc) { cc = RowTile<decltype(rc)::value>::CC; });
+    return (C + cc - 1) / cc;
+}
+
+int64_t row_blocks(int64_t M, int64_t C, int rank) {
+    int64_t rows = 0;
+    with_rank(rank, [&](auto rc) { rows = RowTile<decltype(rc)::value>::ROWS; });
+    return (M + rows - 1) / rows * row_chunks(C, rank);
+}
+
+int64_t lane_cols(int rank) {
+    int64_t cq = 0;
+    with_rank(rank, [&](auto rc) { cq = cols_per_lane<decltype(rc)::value>(); });
+    return cq;
+}
+
+// Row slabs of the column contraction: about 512 blocks (column blocks x slabs), at most
+// kMaxSlabs, each a whole number of 32-row pieces.  A function of (M, C, rank) alone.
+struct Slabs {
+    int64_t count, rows;
+};
+
+Slabs column_slabs(int64_t M, int64_t C, int rank) {
+    const int64_t span = 64 * lane_cols(rank);
+    const int64_t pieces = (M + kSlabRows - 1) / kSlabRows, gx = (C + span - 1) / span;
+    const int64_t want = min(pieces, max((int64_t)1, min(kMaxSlabs, 512 / gx)));
+    const int64_t per = (pieces + want - 1) / want;
+    return Slabs{(pieces + per - 1) / per, per * kSlabRows};
+}
+
+uint64_t up256(uint64_t b) { return (b + 255) / 256 * 256; }
+
+uint64_t row_partial_bytes(int64_t M, int64_t C, int rank) {
+    return up256((uint64_t)row_chunks(C, rank) * M * rank * 4);
+}
+
+uint64_t column_partial_bytes(int64_t M, int64_t C, int rank) {
+    const Slabs sl = column_slabs(M, C, rank);
+    return sl.count > 1 ? up256((uint64_t)sl.count * rank * C * 4) : 0;
+}
+
 template <int FT>
-hipError_t launch_rank_contract(const void* X, int xt, int64_t M, int64_t C, const float* F, int rank, float* out,
-                                hipStream_t s) {
+hipError_t launch_row_partial(const void* X, int xt, int64_t M, int64_t C, const float* F, int rank, float* P,
+                              hipStream_t s) {
+    const int64_t chunks = row_chunks(C, rank), blocks = row_blocks(M, C, rank);
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     with_rank(rank, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        constexpr int RB = contract_rows<R>();
         with_xt(xt, [&](auto xc) {
             constexpr int XT = decltype(xc)::value;
-            hipLaunchKernelGGL((rank_contract_kernel<XT, R, FT>), dim3((unsigned)((M + RB - 1) / RB)), dim3(256), 0, s,
-                               X, M, C, F, rank, out);
+            with_bool(quads_ok(X, C, es_of(XT)), [&](auto vc) {
+                hipLaunchKernelGGL((row_partial_kernel<XT, R, FT, decltype(vc)::value>), dim3((unsigned)blocks),
+                                   dim3(256), 0, s, X, M, C, F, rank, chunks, P);
+            });
         });
     });
     return hipGetLastError();
 }
 
 template <int GT>
-hipError_t launch_rank_expand(float* Y, int64_t M, int64_t C, const float* T, const float* G, int rank, float alpha,
-                              hipStream_t s) {
-    const int64_t gx = (C + 255) / 256, gy = min((M + 7) / 8, (int64_t)4096);
+hipError_t launch_expand(float* Y, int64_t M, int64_t C, const float* P, int64_t chunks, const float* G, int rank,
+                         float alpha, float* Tout, hipStream_t s) {
+    const int64_t cq = lane_cols(rank);
+    const int64_t gx = (C + 64 * cq - 1) / (64 * cq), gy = min((M + kExpRows - 1) / kExpRows, (int64_t)8192);
     if (gx > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool vec = C % cq == 0 && aligned(Y, 4 * (uintptr_t)cq) && (GT == 1 || aligned(G, 4 * (uintptr_t)cq));
     with_rank(rank, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        hipLaunchKernelGGL((rank_expand_kernel<R, GT>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, Y, M, C,
-                           T, G, rank, alpha);
+        with_bool(vec, [&](auto vc) {
+            hipLaunchKernelGGL((expand_kernel<R, GT, decltype(vc)::value>), dim3((unsigned)gx, (unsigned)gy),
+                               dim3(256), 0, s, Y, M, C, P, chunks, G, rank, alpha, Tout);
+        });
     });
     return hipGetLastError();
 }
 
-// Row slabs of the column contraction: enough blocks (columns / 256 x slabs) to reach about 512,
-// at most kMaxSlabs, each slab a whole number of kRun-row runs.  A function of (M, C) alone.
-constexpr int64_t kMaxSlabs = 64;
-
-struct Slabs {
-    int64_t count, rows;
-};
-
-Slabs column_slabs(int64_t M, int64_t C) {
-    const int64_t runs = (M + kRun - 1) / kRun, gx = (C + 255) / 256;
-    const int64_t want = max((int64_t)1, min(kMaxSlabs, 512 / gx));
-    const int64_t per = (runs + min(runs, want) - 1) / min(runs, want);   // runs per slab
-    return Slabs{(runs + per - 1) / per, per * kRun};
-}
-
 template <int OT>
-hipError_t launch_column_contract(const void* X, int xt, int64_t M, int64_t C, const float* T, int rank, float alpha,
-                                  float* O, float* P, hipStream_t s) {
-    const int64_t gx = (C + 255) / 256;
+hipError_t launch_column(const void* X, int xt, int64_t M, int64_t C, const float* T, int rank, float alpha,
+                         float* O, float* Pc, hipStream_t s) {
+    const int64_t cq = lane_cols(rank);
+    const int64_t gx = (C + 64 * cq - 1) / (64 * cq);
     if (gx > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const Slabs sl = column_slabs(M, C);
-    float* part = sl.count > 1 ? P : nullptr;
+    const Slabs sl = column_slabs(M, C, rank);
+    float* part = sl.count > 1 ? Pc : nullptr;
     with_rank(rank, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
         with_xt(xt, [&](auto xc) {
             constexpr int XT = decltype(xc)::value;
-            hipLaunchKernelGGL((column_contract_kernel<XT, R, OT>), dim3((unsigned)gx, (unsigned)sl.count), dim3(256),
-                               0, s, X, M, C, T, rank, alpha, sl.rows, O, part);
+            with_bool(quads_ok(X, C, es_of(XT)), [&](auto vc) {
+                hipLaunchKernelGGL((column_partial_kernel<XT, R, OT, decltype(vc)::value>),
+                                   dim3((unsigned)gx, (unsigned)sl.count), dim3(256), 0, s, X, M, C, T, rank,
+                                   sl.rows, alpha, O, part);
+            });
         });
     });
     if (part) {
@@ -330,31 +638,45 @@ hipError_t launch_column_contract(const void* X, int xt, int64_t M, int64_t C, c
 
 int adapter_rank_max() { return kRankMax; }
 
+bool adapter_shape_ok(int64_t M, int64_t N, int64_t K, int rank) {
+    const int64_t lim = 0x7fffffff;
+    if (row_blocks(M, K, rank) > lim || row_blocks(M, N, rank) > lim) return false;
+    if (((int64_t)rank * N + 255) / 256 > lim || ((int64_t)rank * K + 255) / 256 > lim) return false;
+    return (N + 63) / 64 <= lim && (K + 63) / 64 <= lim;
+}
+
+uint64_t adapter_fwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank) {
+    (void)N;
+    return row_partial_bytes(M, K, rank);     // the chunk sums of t
+}
+
 uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank) {
-    // u [M, r], then the slab partials of d_A and of d_B (one region, used one after the other)
-    auto up = [](uint64_t b) { return (b + 255) / 256 * 256; };
-    const Slabs a = column_slabs(M, K), b = column_slabs(M, N);
-    const uint64_t pa = a.count > 1 ? (uint64_t)a.count * rank * K * 4 : 0;
-    const uint64_t pb = b.count > 1 ? (uint64_t)b.count * rank * N * 4 : 0;
-    return up((uint64_t)M * rank * 4) + up(max(pa, pb));
+    // the chunk sums of u, u [M, r], then the slab sums of d_A and of d_B (one region, used in turn)
+    return row_partial_bytes(M, N, rank) + up256((uint64_t)M * rank * 4) +
+           max(column_partial_bytes(M, K, rank), column_partial_bytes(M, N, rank));
 }
 
 hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
-                                    const float* B, int rank, float alpha, float* y, float* t, hipStream_t s) {
-    hipError_t e = launch_rank_contract<0>(x, x_dtype, M, K, A, rank, t, s);
+                                    const float* B, int rank, float alpha, float* y, float* t, void* ws,
+                                    hipStream_t s) {
+    float* P = static_cast<float*>(ws);
+    hipError_t e = launch_row_partial<0>(x, x_dtype, M, K, A, rank, P, s);
     if (e != hipSuccess) return e;
-    return launch_rank_expand<1>(y, M, N, t, B, rank, alpha, s);
+    return launch_expand<1>(y, M, N, P, row_chunks(K, rank), B, rank, alpha, t, s);
 }
 
 hipError_t launch_adapter_bwd_terms(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
                                     const float* A, const float* B, int rank, float alpha, const float* t,
                                     float* d_x, float* d_A, float* d_B, void* ws, hipStream_t s) {
-    float* u = static_cast<float*>(ws);
-    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + ((uint64_t)M * rank * 4 + 255) / 256 * 256);
-    hipError_t e = launch_rank_contract<1>(d_out, dtype, M, N, B, rank, u, s);
-    if (e == hipSuccess) e = launch_rank_expand<0>(d_x, M, K, u, A, rank, alpha, s);
-    if (e == hipSuccess) e = launch_column_contract<0>(x, dtype, M, K, u, rank, alpha, d_A, part, s);
-    if (e == hipSuccess) e = launch_column_contract<1>(d_out, dtype, M, N, t, rank, alpha, d_B, part, s);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const uint64_t pb = row_partial_bytes(M, N, rank);
+    float* P = reinterpret_cast<float*>(w);
+    float* u = reinterpret_cast<float*>(w + pb);
+    float* Pc = reinterpret_cast<float*>(w + pb + up256((uint64_t)M * rank * 4));
+    hipError_t e = launch_row_partial<1>(d_out, dtype, M, N, B, rank, P, s);
+    if (e == hipSuccess) e = launch_expand<0>(d_x, M, K, P, row_chunks(N, rank), A, rank, alpha, u, s);
+    if (e == hipSuccess) e = launch_column<0>(x, dtype, M, K, u, rank, alpha, d_A, Pc, s);
+    if (e == hipSuccess) e = launch_column<1>(d_out, dtype, M, N, t, rank, alpha, d_B, Pc, s);
     return e;
 }
 

@@ -596,13 +596,15 @@ q4gsw_status q4gsw_adapter_workspace_bytes(int32_t op, const q4gsw_weight* w, in
     *bytes = 0;
     q4gsw_status st = check_desc(w);
     if (st != Q4GSW_OK) return st;
-    if (M < 1 || M > kMaxM || rank < 1 || rank > adapter_rank_max()) return Q4GSW_E_SHAPE;
+    if (M < 1 || M > kMaxM || rank < 1 || rank > adapter_rank_max() || !adapter_shape_ok(M, w->N, w->K, rank))
+        return Q4GSW_E_SHAPE;
     if (!act_dtype_ok(act_dtype)) return Q4GSW_E_DTYPE;
     const Opts o;
     if (op == Q4GSW_OP_FWD) {
         const int32_t route = pick_fwd(w, M, act_dtype, false, o.route, &st);
         if (st != Q4GSW_OK) return st;
-        *bytes = fwd_ws_bytes(w, M, act_dtype, route, o);
+        *bytes = round_up((int64_t)fwd_ws_bytes(w, M, act_dtype, route, o), 256) +
+                 adapter_fwd_terms_ws_bytes(M, w->N, w->K, rank);
         return Q4GSW_OK;
     }
     if (op == Q4GSW_OP_BWD_INPUT) {
@@ -620,12 +622,15 @@ q4gsw_status q4gsw_adapter_fwd(const q4gsw_weight* w, const void* x, int32_t x_d
                                uint64_t ws_bytes, void* stream) {
     const Opts o;
     int32_t route = Q4GSW_ROUTE_NONE;
-    uint64_t need = 0;
-    q4gsw_status st = prepare_fwd(w, x, x_dtype, M, y, o, &route, &need);
+    uint64_t base = 0;
+    q4gsw_status st = prepare_fwd(w, x, x_dtype, M, y, o, &route, &base);
     if (st != Q4GSW_OK) return st;
     if (!A || !B || !t) return Q4GSW_E_NULL;
-    if (rank < 1 || rank > adapter_rank_max()) return Q4GSW_E_SHAPE;
+    if (rank < 1 || rank > adapter_rank_max() || !adapter_shape_ok(M, w->N, w->K, rank)) return Q4GSW_E_SHAPE;
     if (!finite_f(alpha)) return Q4GSW_E_SHAPE;
+    // the forward's workspace, then the column-chunk sums of t
+    base = round_up((int64_t)base, 256);
+    const uint64_t need = base + adapter_fwd_terms_ws_bytes(M, w->N, w->K, rank);
     if (!ws_ok(ws, ws_bytes, need)) return Q4GSW_E_WORKSPACE;
     if ((st = fwd_alias(w, x, x_dtype, M, y, ws, need)) != Q4GSW_OK) return st;
     // the outputs y and t against every input and each other; the workspace against t and the factors
@@ -638,7 +643,8 @@ q4gsw_status q4gsw_adapter_fwd(const q4gsw_weight* w, const void* x, int32_t x_d
         return Q4GSW_E_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = run_fwd(w, x, x_dtype, M, y, ws, route, o, s)) != Q4GSW_OK) return st;
-    return hip_status(launch_adapter_fwd_terms(x, x_dtype, M, w->N, w->K, A, B, rank, alpha, y, t, s));
+    return hip_status(launch_adapter_fwd_terms(x, x_dtype, M, w->N, w->K, A, B, rank, alpha, y, t,
+                                               static_cast<uint8_t*>(ws) + base, s));
 }
 
 q4gsw_status q4gsw_adapter_bwd(const q4gsw_weight* w, const void* x, const void* d_out, int32_t dtype, int64_t M,
@@ -647,7 +653,9 @@ q4gsw_status q4gsw_adapter_bwd(const q4gsw_weight* w, const void* x, const void*
     q4gsw_status st = check_desc(w);
     if (st != Q4GSW_OK) return st;
     if (!x || !d_out || !A || !B || !t || !d_x || !d_A || !d_B) return Q4GSW_E_NULL;
-    if (M < 1 || M > kMaxM || rank < 1 || rank > adapter_rank_max() || !finite_f(alpha)) return Q4GSW_E_SHAPE;
+    if (M < 1 || M > kMaxM || rank < 1 || rank > adapter_rank_max() || !finite_f(alpha) ||
+        !adapter_shape_ok(M, w->N, w->K, rank))
+        return Q4GSW_E_SHAPE;
     if (!act_dtype_ok(dtype)) return Q4GSW_E_DTYPE;
     const Opts o;
     const int32_t route = pick_bwd(w, M, dtype, o.route, &st);

@@ -127,13 +127,18 @@ hipError_t launch_dq8ca(const WView& w, const void* x, int x_dtype, int64_t M, f
                         void* ws, hipStream_t s);
 
 // adapter.hip: the low-rank adapter terms beside the frozen weight (rank 1..adapter_rank_max())
-// and the AdamW update.  t = x A^T [M, r] is written, then y += alpha t B^T.  The backward writes
+// and the AdamW update.  The forward writes t = x A^T [M, r], then y += alpha t B^T; its
+// workspace (the column-chunk sums of t) is adapter_fwd_terms_ws_bytes.  The backward writes
 // u = d_out B [M, r] (workspace), then d_x += alpha u A, d_A = alpha u^T x, d_B = alpha d_out^T t;
-// its workspace (u, then the row-slab partials of d_A and d_B) is adapter_bwd_terms_ws_bytes.
+// its workspace (the chunk sums of u, u, the row-slab sums of d_A and d_B) is
+// adapter_bwd_terms_ws_bytes.  adapter_shape_ok: every launch of both fits the grid limits.
 int adapter_rank_max();
+bool adapter_shape_ok(int64_t M, int64_t N, int64_t K, int rank);
+uint64_t adapter_fwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank);
 uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank);
 hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
-                                    const float* B, int rank, float alpha, float* y, float* t, hipStream_t s);
+                                    const float* B, int rank, float alpha, float* y, float* t, void* ws,
+                                    hipStream_t s);
 hipError_t launch_adapter_bwd_terms(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
                                     const float* A, const float* B, int rank, float alpha, const float* t,
                                     float* d_x, float* d_A, float* d_B, void* ws, hipStream_t s);

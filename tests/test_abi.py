@@ -437,17 +437,23 @@ def test_adapter_validation(q):
     assert wsb(q.OP_BWD_INPUT, ctypes.byref(d), 4, q.F16, 8, ctypes.byref(need)) == S_OK
     assert need.value >= 4 * 8 * 4                      # u = d_out B lives in the workspace
     f = lib.q4gsw_adapter_fwd
-    assert f(ctypes.byref(d), x, q.F16, 4, None, B, 8, 1.0, y, t, None, 0, None) == E_NULL
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, None, None, 0, None) == E_NULL
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 0, 1.0, y, t, None, 0, None) == E_SHAPE
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 65, 1.0, y, t, None, 0, None) == E_SHAPE
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, nan, y, t, None, 0, None) == E_SHAPE
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, inf, y, t, None, 0, None) == E_SHAPE
-    assert f(ctypes.byref(d), x, 7, 4, A, B, 8, 1.0, y, t, None, 0, None) == E_DTYPE
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, x + 64, None, 0, None) == E_ALIAS   # t inside x
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, y + 64, None, 0, None) == E_ALIAS   # t inside y
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, A + 64, t, None, 0, None) == E_ALIAS   # y inside A
-    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, B + 4, None, 0, None) == E_ALIAS    # t inside B
+    assert wsb(q.OP_FWD, ctypes.byref(d), 4, q.F16, 8, ctypes.byref(need)) == S_OK
+    assert need.value >= 4 * 8 * 4                      # and the column-chunk sums of t
+    fw, fn = FAKE * 52, need.value
+    assert f(ctypes.byref(d), x, q.F16, 4, None, B, 8, 1.0, y, t, fw, fn, None) == E_NULL
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, None, fw, fn, None) == E_NULL
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 0, 1.0, y, t, fw, fn, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 65, 1.0, y, t, fw, fn, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, nan, y, t, fw, fn, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, inf, y, t, fw, fn, None) == E_SHAPE
+    assert f(ctypes.byref(d), x, 7, 4, A, B, 8, 1.0, y, t, fw, fn, None) == E_DTYPE
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, t, None, 0, None) == E_WS
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, t, fw, fn - 4, None) == E_WS
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, x + 64, fw, fn, None) == E_ALIAS   # t inside x
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, y + 64, fw, fn, None) == E_ALIAS   # t inside y
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, A + 64, t, fw, fn, None) == E_ALIAS   # y inside A
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, B + 4, fw, fn, None) == E_ALIAS    # t inside B
+    assert f(ctypes.byref(d), x, q.F16, 4, A, B, 8, 1.0, y, t, A, fn, None) == E_ALIAS         # ws over A
     big = fake_desc(q, 2048, 8192, 128, 1, flags=1)
     assert wsb(q.OP_FWD, ctypes.byref(big), 512, q.BF16, 16, ctypes.byref(need)) == S_OK
     assert need.value > 0
