@@ -98,11 +98,6 @@ __device__ __forceinline__ f4 load_quad_sel(const void* X, int64_t row_base, int
     }
 }
 
-// p[i] when ok, else 0, from an unconditional load (index 0 stands in when !ok).
-__device__ __forceinline__ float load_sel(const float* __restrict__ p, int64_t i, bool ok) {
-    const float v = p[ok ? i : 0];
-    return ok ? v : 0.0f;
-}
 
 // Sum over the 64 lanes of each of the N values v[i] (N a power of two, <= 64); lane l returns
 // the total of value l % N.  Offsets 32 .. N add whole vectors; below N each level keeps the
@@ -198,19 +193,6 @@ __global__ __launch_bounds__(256) void row_partial_kernel(const void* __restrict
     if (lane < T::RW * R && j < rank && m < M) P[(s * M + m) * rank + j] = mine;
 }
 
-// Sum of the partials P[s, m, j] (stride apart), s ascending, loads issued NB at a time.
-template <int NB>
-__device__ __forceinline__ float chunk_sum(const float* __restrict__ P, int64_t chunks, int64_t stride, int64_t off) {
-    float v = 0.0f;
-    for (int64_t s0 = 0; s0 < chunks; s0 += NB) {
-        float p[NB];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) p[k] = load_sel(P, (s0 + k) * stride + off, s0 + k < chunks);
-#pragma unroll
-        for (int k = 0; k < NB; ++k) v += p[k];       // past the last partial: + 0, exact
-    }
-    return v;
-}
 
 // T[m, j] = sum_s P[s, m, j] (s ascending; written to Tout by the blocks of column block 0),
 // then Y [M, C] (fp32) += alpha T G with G(j, c) = A[j C + c] (GT = 0) or B[c r + j] (GT = 1).
@@ -347,17 +329,26 @@ __global__ __launch_bounds__(256) void expand_kernel(float* __restrict__ Y, int6
     }
 }
 
-// Slab sums of O(j, c) = alpha sum_m T[m, j] X[m, c] for X [M, C] (dtype XT), T [M, r] fp32.
-// Block: 64 CQ columns (lane l: columns CQ l ..) x one slab of `slab` rows (blockIdx.y), taken
-// in pieces of 32 rows staged in LDS; wave w adds rows w, w + 4, ... of each piece in order,
-// then the four waves' sums are added in wave order.  One slab: O is written with alpha
-// applied, OT = 0: O[j C + c] ([r, C], d_A), OT = 1: O[c r + j] ([C, r], d_B).  Several: the
-// unscaled slab sums go to Pc [slabs, r, C].
-template <int XT, int R, int OT, bool VEC>
-__global__ __launch_bounds__(256) void column_partial_kernel(const void* __restrict__ X, int64_t M, int64_t C,
-                                                             const float* __restrict__ T, int rank, int64_t slab,
-                                                             float alpha, float* __restrict__ O,
-                                                             float* __restrict__ Pc) {
+// One output of the column contraction: O(j, c) = alpha sum_m T[m, j] X[m, c] for X [M, C],
+// T [M, r] fp32, cut into gx column blocks x `slabs` row slabs of `slab` rows; ot = 0: O[j C + c]
+// ([r, C], d_A), ot = 1: O[c r + j] ([C, r], d_B); Pc [slabs, r, C] holds unscaled slab sums when
+// slabs > 1.
+struct ColSeg {
+    const void* X;
+    const float* T;
+    float* O;
+    float* Pc;
+    int64_t C, gx, slabs, slab;
+    int ot;
+};
+
+// Slab sums of both column contractions of the backward in one launch: blocks [0, a.gx a.slabs)
+// take a (d_A), the rest b (d_B).  Block: 64 CQ columns (lane l: columns CQ l ..) x one slab,
+// taken in pieces of 32 rows staged in LDS; wave w adds rows w, w + 4, ... of each piece in
+// order, then the four waves' sums are added in wave order.  One slab: O is written with alpha
+// applied; several: the unscaled slab sums go to Pc.
+template <int XT, int R, bool VEC>
+__global__ __launch_bounds__(256) void column_partial_kernel(ColSeg a, ColSeg b, int64_t M, int rank, float alpha) {
     constexpr int CQ = cols_per_lane<R>();
     constexpr int kT = kSlabRows * R;
     // one LDS array: the T piece [32][R], then the wave-combine buffer [CQ R][64]
@@ -365,8 +356,16 @@ __global__ __launch_bounds__(256) void column_partial_kernel(const void* __restr
     float* Ts = smem;
     float* red = smem + kT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * CQ;
-    const int64_t lo = (int64_t)blockIdx.y * slab, hi = min(M, lo + slab);
+    const int64_t na = a.gx * a.slabs;
+    const bool second = (int64_t)blockIdx.x >= na;
+    const ColSeg sg = second ? b : a;
+    const int64_t bi = second ? (int64_t)blockIdx.x - na : (int64_t)blockIdx.x;
+    const int64_t bx = bi % sg.gx, by = bi / sg.gx;
+    const int64_t C = sg.C;
+    const void* X = sg.X;
+    const float* T = sg.T;
+    const int64_t c = (bx * 64 + lane) * CQ;
+    const int64_t lo = by * sg.slab, hi = min(M, lo + sg.slab);
     float acc[CQ][R];
 #pragma unroll
     for (int q = 0; q < CQ; ++q)
@@ -429,25 +428,28 @@ __global__ __launch_bounds__(256) void column_partial_kernel(const void* __restr
     __syncthreads();
     for (int i = tid; i < CQ * R * 64; i += 256) {
         const int l = i % 64, qj = i / 64, q = qj / R, j = qj % R;
-        const int64_t cc = ((int64_t)blockIdx.x * 64 + l) * CQ + q;
+        const int64_t cc = (bx * 64 + l) * CQ + q;
         if (j >= rank || cc >= C) continue;
         const float v = red[i];
-        if (Pc) Pc[((int64_t)blockIdx.y * rank + j) * C + cc] = v;
-        else if (OT == 0) O[(int64_t)j * C + cc] = alpha * v;
-        else O[cc * rank + j] = alpha * v;
+        if (sg.slabs > 1) sg.Pc[(by * rank + j) * C + cc] = v;
+        else if (sg.ot == 0) sg.O[(int64_t)j * C + cc] = alpha * v;
+        else sg.O[cc * rank + j] = alpha * v;
     }
 }
 
-// O(j, c) = alpha * (Pc[0, j, c] + Pc[1, j, c] + ...) in slab order; one thread per (j, c).
-template <int OT>
-__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ Pc, int slabs, int64_t C,
-                                                            int rank, float alpha, float* __restrict__ O) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)rank * C) return;
-    const float s = chunk_sum<16>(Pc, slabs, (int64_t)rank * C, e);
-    const int64_t j = e / C, c = e % C;
-    if (OT == 0) O[e] = alpha * s;
-    else O[c * rank + j] = alpha * s;
+// O(j, c) = alpha * (Pc[0, j, c] + Pc[1, j, c] + ...) in slab order for the outputs of a and b
+// that have several slabs; one thread per (j, c), a's first.
+__global__ __launch_bounds__(256) void column_reduce_kernel(ColSeg a, ColSeg b, int rank, float alpha) {
+    const int64_t ea = a.slabs > 1 ? (int64_t)rank * a.C : 0, eb = b.slabs > 1 ? (int64_t)rank * b.C : 0;
+    int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= ea + eb) return;
+    const bool second = e >= ea;
+    const ColSeg sg = second ? b : a;
+    if (second) e -= ea;
+    const float s = chunk_sum<16>(sg.Pc, sg.slabs, (int64_t)rank * sg.C, e);
+    const int64_t j = e / sg.C, c = e % sg.C;
+    if (sg.ot == 0) sg.O[e] = alpha * s;
+    else sg.O[c * rank + j] = alpha * s;
 }
 
 // AdamW on n fp32 values: p *= decay; m = b1 m + (1 - b1) g; v = b2 v + (1 - b2) g^2;
@@ -606,32 +608,49 @@ hipError_t launch_expand(float* Y, int64_t M, int64_t C, const float* P, int64_t
     return hipGetLastError();
 }
 
-template <int OT>
-hipError_t launch_column(const void* X, int xt, int64_t M, int64_t C, const float* T, int rank, float alpha,
-                         float* O, float* Pc, hipStream_t s) {
-    const int64_t cq = lane_cols(rank);
-    const int64_t gx = (C + 64 * cq - 1) / (64 * cq);
-    if (gx > 0x7fffffff) return hipErrorInvalidConfiguration;
+ColSeg column_seg(const void* X, int64_t M, int64_t C, const float* T, int rank, float* O, float* Pc, int ot) {
     const Slabs sl = column_slabs(M, C, rank);
-    float* part = sl.count > 1 ? Pc : nullptr;
+    const int64_t cq = lane_cols(rank);
+    return ColSeg{X, T, O, Pc, C, (C + 64 * cq - 1) / (64 * cq), sl.count, sl.rows, ot};
+}
+
+// d_A (a) and d_B (b) in one launch of column_partial_kernel and, for the outputs with several
+// slabs, one of column_reduce_kernel.
+hipError_t launch_columns(const ColSeg& a, const ColSeg& b, int xt, int64_t M, int rank, float alpha, bool vec,
+                          hipStream_t s) {
+    const int64_t blocks = a.gx * a.slabs + b.gx * b.slabs;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     with_rank(rank, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
         with_xt(xt, [&](auto xc) {
             constexpr int XT = decltype(xc)::value;
-            with_bool(quads_ok(X, C, es_of(XT)), [&](auto vc) {
-                hipLaunchKernelGGL((column_partial_kernel<XT, R, OT, decltype(vc)::value>),
-                                   dim3((unsigned)gx, (unsigned)sl.count), dim3(256), 0, s, X, M, C, T, rank,
-                                   sl.rows, alpha, O, part);
+            with_bool(vec, [&](auto vc) {
+                hipLaunchKernelGGL((column_partial_kernel<XT, R, decltype(vc)::value>), dim3((unsigned)blocks),
+                                   dim3(256), 0, s, a, b, M, rank, alpha);
             });
         });
     });
-    if (part) {
-        const int64_t blocks = ((int64_t)rank * C + 255) / 256;
-        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((column_reduce_kernel<OT>), dim3((unsigned)blocks), dim3(256), 0, s, part, (int)sl.count,
-                           C, rank, alpha, O);
+    const int64_t elems = (a.slabs > 1 ? (int64_t)rank * a.C : 0) + (b.slabs > 1 ? (int64_t)rank * b.C : 0);
+    if (elems > 0) {
+        const int64_t rblocks = (elems + 255) / 256;
+        if (rblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, s, a, b, rank, alpha);
     }
     return hipGetLastError();
+}
+
+// Backward workspace: the chunk sums of u, u [M, r], then the slab sums of d_A and of d_B.
+struct BwdWs {
+    float *P, *u, *PcA, *PcB;
+    uint64_t bytes;
+};
+
+BwdWs bwd_ws(void* ws, int64_t M, int64_t N, int64_t K, int rank) {
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const uint64_t pb = row_partial_bytes(M, N, rank), ub = up256((uint64_t)M * rank * 4);
+    const uint64_t ab = column_partial_bytes(M, K, rank), bb = column_partial_bytes(M, N, rank);
+    return BwdWs{reinterpret_cast<float*>(w), reinterpret_cast<float*>(w + pb), reinterpret_cast<float*>(w + pb + ub),
+                 reinterpret_cast<float*>(w + pb + ub + ab), pb + ub + ab + bb};
 }
 
 }  // namespace
@@ -651,9 +670,7 @@ uint64_t adapter_fwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank) {
 }
 
 uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank) {
-    // the chunk sums of u, u [M, r], then the slab sums of d_A and of d_B (one region, used in turn)
-    return row_partial_bytes(M, N, rank) + up256((uint64_t)M * rank * 4) +
-           max(column_partial_bytes(M, K, rank), column_partial_bytes(M, N, rank));
+    return bwd_ws(nullptr, M, N, K, rank).bytes;
 }
 
 hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
@@ -665,19 +682,27 @@ hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64
     return launch_expand<1>(y, M, N, P, row_chunks(K, rank), B, rank, alpha, t, s);
 }
 
-hipError_t launch_adapter_bwd_terms(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
-                                    const float* A, const float* B, int rank, float alpha, const float* t,
-                                    float* d_x, float* d_A, float* d_B, void* ws, hipStream_t s) {
-    uint8_t* w = static_cast<uint8_t*>(ws);
-    const uint64_t pb = row_partial_bytes(M, N, rank);
-    float* P = reinterpret_cast<float*>(w);
-    float* u = reinterpret_cast<float*>(w + pb);
-    float* Pc = reinterpret_cast<float*>(w + pb + up256((uint64_t)M * rank * 4));
-    hipError_t e = launch_row_partial<1>(d_out, dtype, M, N, B, rank, P, s);
-    if (e == hipSuccess) e = launch_expand<0>(d_x, M, K, P, row_chunks(N, rank), A, rank, alpha, u, s);
-    if (e == hipSuccess) e = launch_column<0>(x, dtype, M, K, u, rank, alpha, d_A, Pc, s);
-    if (e == hipSuccess) e = launch_column<1>(d_out, dtype, M, N, t, rank, alpha, d_B, Pc, s);
-    return e;
+hipError_t launch_adapter_bwd_u(const void* d_out, int dtype, int64_t M, int64_t N, int64_t K, const float* B,
+                                int rank, void* ws, hipStream_t s) {
+    return launch_row_partial<1>(d_out, dtype, M, N, B, rank, bwd_ws(ws, M, N, K, rank).P, s);
+}
+
+LowRankEpi adapter_bwd_epi(int64_t M, int64_t N, int64_t K, const float* A, int rank, float alpha, void* ws) {
+    const BwdWs w = bwd_ws(ws, M, N, K, rank);
+    return LowRankEpi{w.P, row_chunks(N, rank), A, w.u, alpha, rank, 0};
+}
+
+hipError_t launch_adapter_bwd_rest(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
+                                   const float* A, int rank, float alpha, const float* t, float* d_x, bool dx_done,
+                                   float* d_A, float* d_B, void* ws, hipStream_t s) {
+    const BwdWs w = bwd_ws(ws, M, N, K, rank);
+    hipError_t e = hipSuccess;
+    if (!dx_done) e = launch_expand<0>(d_x, M, K, w.P, row_chunks(N, rank), A, rank, alpha, w.u, s);
+    if (e != hipSuccess) return e;
+    const int es = es_of(dtype);
+    const ColSeg a = column_seg(x, M, K, w.u, rank, d_A, w.PcA, 0);
+    const ColSeg b = column_seg(d_out, M, N, t, rank, d_B, w.PcB, 1);
+    return launch_columns(a, b, dtype, M, rank, alpha, quads_ok(x, K, es) && quads_ok(d_out, N, es), s);
 }
 
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, double lr, double beta1,

@@ -229,8 +229,12 @@ q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M
     }
 }
 
+// epi: a low-rank term for the split reduction of the MFMA routes; *epi_done tells whether this
+// call applied it (routes and plans without that reduction leave it to the caller).
 q4gsw_status run_bwd(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, int64_t M, float* d_x, void* ws,
-                     int32_t route, const Opts& o, hipStream_t s) {
+                     int32_t route, const Opts& o, hipStream_t s, const LowRankEpi* epi = nullptr,
+                     bool* epi_done = nullptr) {
+    if (epi_done) *epi_done = false;
     const WView v = view_of(w);
     switch (route) {
         case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_bwd(v, d_out, g_dtype, M, d_x, s));
@@ -244,7 +248,10 @@ q4gsw_status run_bwd(const q4gsw_weight* w, const void* d_out, int32_t g_dtype, 
         }
         default: {
             const BwdPlan plan = plan_gemm_bwd(v, g_dtype, fold_ok(w), M, o.splits);
-            return hip_status(launch_gemm_bwd(v, d_out, g_dtype, M, d_x, plan, static_cast<float*>(ws), s));
+            const bool fuse = epi && !plan.v1 && plan.splits > 1;
+            if (fuse && epi_done) *epi_done = true;
+            return hip_status(launch_gemm_bwd(v, d_out, g_dtype, M, d_x, plan, static_cast<float*>(ws), s,
+                                              fuse ? epi : nullptr));
         }
     }
 }
@@ -680,9 +687,14 @@ q4gsw_status q4gsw_adapter_bwd(const q4gsw_weight* w, const void* x, const void*
     for (int j = 0; j < 6; ++j)
         if (overlap(sr, ins[j])) return Q4GSW_E_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = run_bwd(w, d_out, dtype, M, d_x, ws, route, o, s)) != Q4GSW_OK) return st;
-    return hip_status(launch_adapter_bwd_terms(x, d_out, dtype, M, N, K, A, B, rank, alpha, t, d_x, d_A, d_B,
-                                               static_cast<uint8_t*>(ws) + base, s));
+    // the chunk sums of u first, so that the input gradient's split reduction can add alpha u A
+    void* terms = static_cast<uint8_t*>(ws) + base;
+    if ((st = hip_status(launch_adapter_bwd_u(d_out, dtype, M, N, K, B, rank, terms, s))) != Q4GSW_OK) return st;
+    const LowRankEpi epi = adapter_bwd_epi(M, N, K, A, rank, alpha, terms);
+    bool dx_done = false;
+    if ((st = run_bwd(w, d_out, dtype, M, d_x, ws, route, o, s, &epi, &dx_done)) != Q4GSW_OK) return st;
+    return hip_status(launch_adapter_bwd_rest(x, d_out, dtype, M, N, K, A, rank, alpha, t, d_x, dx_done, d_A, d_B,
+                                              terms, s));
 }
 
 q4gsw_status q4gsw_adamw_step(float* param, const float* grad, float* exp_avg, float* exp_avg_sq, int64_t n,

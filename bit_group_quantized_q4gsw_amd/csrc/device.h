@@ -162,4 +162,26 @@ __device__ __forceinline__ float wave_sum_same_parity(float v) {
     return wave_sum_rows(v);
 }
 
+// p[i] when ok, else 0, from an unconditional load (index 0 stands in when !ok): no branch
+// around the load, so a lane's loads can all be in flight before the first wait.
+__device__ __forceinline__ float load_sel(const float* __restrict__ p, int64_t i, bool ok) {
+    const float v = p[ok ? i : 0];
+    return ok ? v : 0.0f;
+}
+
+// Sum of the partials P[s * stride + off], s = 0 .. count - 1 ascending (starting from 0 + P[0]),
+// loads issued NB at a time.
+template <int NB>
+__device__ __forceinline__ float chunk_sum(const float* __restrict__ P, int64_t count, int64_t stride, int64_t off) {
+    float v = 0.0f;
+    for (int64_t s0 = 0; s0 < count; s0 += NB) {
+        float p[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) p[k] = load_sel(P, (s0 + k) * stride + off, s0 + k < count);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) v += p[k];       // past the last partial: + 0, exact
+    }
+    return v;
+}
+
 }  // namespace q4gsw

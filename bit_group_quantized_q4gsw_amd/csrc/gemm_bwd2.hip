@@ -778,7 +778,7 @@ BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M, int f
 }
 
 hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
-                           const BwdPlan& plan, float* ws, hipStream_t s) {
+                           const BwdPlan& plan, float* ws, hipStream_t s, const LowRankEpi* lr) {
     if (plan.v1) return launch_gemm_bwd_v1(w, d_out, g_dtype, M, d_x, plan, ws, s);
     const int64_t n_chunks = (w.N + kCN - 1) / kCN;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);
@@ -849,7 +849,8 @@ hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64
     if (e != hipSuccess || plan.splits == 1) return e;
     const float* ys[1] = {d_x};
     const int64_t yld[1] = {w.K}, off[1] = {0}, cols[1] = {w.K};
-    return launch_reduce_frags(ws, plan.splits, M, w.k_pad, ys, yld, off, cols, 1, plan.mode == kModeSplit ? 1 : 0, s);
+    return launch_reduce_frags(ws, plan.splits, M, w.k_pad, ys, yld, off, cols, 1, plan.mode == kModeSplit ? 1 : 0, s,
+                               lr);
 }
 
 }  // namespace q4gsw

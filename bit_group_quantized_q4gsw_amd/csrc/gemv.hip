@@ -545,16 +545,43 @@ hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_
 // L = t % 64: rows 8 r4 + 4 (L / 32) + q, column j = L % 32, or its octet permutation when perm
 // is set) with one streaming 16-byte load per split, in split order, so the result does not
 // depend on the launch.  The tile is transposed through LDS so that each thread stores 4 consecutive columns
-// of one row.
+// of one row.  R > 0 (rank bucket): the low-rank term of LowRankEpi is added to each sum, from the
+// tile's rows of T and columns of G staged in the same LDS array (one segment only).
+template <int R>
 __global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restrict__ ws, int splits, int64_t M,
                                                            int64_t ntn, int64_t plane, ReduceSegs seg, int perm,
-                                                           int vec_ok) {
-    __shared__ float tile_s[32][33];
+                                                           int vec_ok, LowRankEpi lr) {
+    constexpr int kLR = R > 0 ? 32 * R + R * 33 : 0;
+    __shared__ float sm[32 * 33 + kLR];
+    float (*tile_s)[33] = reinterpret_cast<float (*)[33]>(sm);
     const int64_t tile = blockIdx.x;
     const int t = threadIdx.x;
     const int64_t tm = tile / ntn, tn = tile - tm * ntn;
     const float* src = ws + tile * 1024 + 4 * t;
     f4 acc = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src));
+    // R > 0: this thread's values of the tile's rows of T (their first NB chunk partials) and
+    // columns of G are loaded next, in flight with the split partials
+    constexpr int TPT = R > 0 ? (32 * R + 255) / 256 : 1;     // values of T (and of G) per thread
+    constexpr int NB = TPT <= 2 ? 16 : 32 / TPT;
+    float tp[TPT][NB];
+    float gv[TPT];
+    if constexpr (R > 0) {
+        const int64_t C = seg.cols[0];
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = t + 256 * k, r = i / R, j = i % R;
+            const int64_t m = 32 * tm + r;
+            const bool ok = i < 32 * R && m < M && j < lr.rank;
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                tp[k][c] = load_sel(lr.P, (c * M + m) * lr.rank + j, ok && c < lr.chunks);
+            const int jg = i / 32, cc = i % 32;
+            const int64_t col = 32 * tn + cc;
+            gv[k] = load_sel(lr.G, lr.gt == 0 ? (int64_t)jg * C + col : col * lr.rank + jg,
+                             i < 32 * R && jg < lr.rank && col < C);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int s = 1; s < splits; ++s) acc += __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + s * plane));
     {
         const int L = t & 63, j = L & 31;
@@ -562,6 +589,33 @@ __global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restri
         const int r0 = 8 * (t >> 6) + 4 * (L >> 5);
 #pragma unroll
         for (int q = 0; q < 4; ++q) tile_s[r0 + q][jc] = acc[q];
+    }
+    if constexpr (R > 0) {
+        // T: chunk sums in chunk order (the first NB from the registers); G as loaded
+        float* t_s = sm + 32 * 33;       // [32][R]
+        float* g_s = t_s + 32 * R;       // [R][33]
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = t + 256 * k, r = i / R, j = i % R;
+            const int64_t m = 32 * tm + r;
+            if (i < 32 * R) {
+                float v = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NB; ++c) v += tp[k][c];          // past the last partial: + 0, exact
+                const bool ok = m < M && j < lr.rank;
+                for (int64_t c0 = NB; c0 < lr.chunks; c0 += 16) {        // the rest, continuing the order
+                    float p[16];
+#pragma unroll
+                    for (int c = 0; c < 16; ++c)
+                        p[c] = load_sel(lr.P, ((c0 + c) * M + m) * lr.rank + j, ok && c0 + c < lr.chunks);
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) v += p[c];
+                }
+                if (lr.Tout && tn == 0 && m < M && j < lr.rank) lr.Tout[m * lr.rank + j] = v;
+                t_s[i] = v;
+                g_s[(i / 32) * 33 + i % 32] = gv[k];
+            }
+        }
     }
     __syncthreads();
     const int row = t >> 3, c4 = 4 * (t & 7);
@@ -573,7 +627,18 @@ __global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restri
     const int64_t cs = col - seg.off[sg];
     if (cs >= seg.cols[sg]) return;
     float* dst = seg.y[sg] + m * seg.y_ld[sg] + cs;
-    const f4 v = {tile_s[row][c4], tile_s[row][c4 + 1], tile_s[row][c4 + 2], tile_s[row][c4 + 3]};
+    f4 v = {tile_s[row][c4], tile_s[row][c4 + 1], tile_s[row][c4 + 2], tile_s[row][c4 + 3]};
+    if constexpr (R > 0) {
+        const float* t_s = sm + 32 * 33;
+        const float* g_s = t_s + 32 * R;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < R; ++j) sum = fmaf(t_s[row * R + j], g_s[j * 33 + c4 + q], sum);
+            v[q] = fmaf(lr.alpha, sum, v[q]);
+        }
+    }
     if (vec_ok && cs + 4 <= seg.cols[sg]) {
         *reinterpret_cast<f4*>(dst) = v;
     } else {
@@ -585,8 +650,9 @@ __global__ __launch_bounds__(256) void reduce_frags_kernel(const float* __restri
 
 hipError_t launch_reduce_frags(const float* ws, int splits, int64_t M, int64_t width, const float* const* y,
                                const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg, int perm,
-                               hipStream_t s) {
+                               hipStream_t s, const LowRankEpi* lr) {
     if (width % 32 != 0 || (reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return hipErrorInvalidValue;
+    if (lr && (nseg != 1 || lr->rank < 1 || lr->rank > 64)) return hipErrorInvalidValue;
     ReduceSegs seg{};
     seg.nseg = nseg;
     int vec_ok = 1;
@@ -601,8 +667,28 @@ hipError_t launch_reduce_frags(const float* ws, int splits, int64_t M, int64_t w
     const int64_t mt = (M + 31) / 32, ntn = width / 32;
     const int64_t tiles = mt * ntn;
     if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(reduce_frags_kernel, dim3((unsigned)tiles), dim3(256), 0, s, ws, splits, M, ntn, mt * 32 * width,
-                       seg, perm, vec_ok);
+    const dim3 grid((unsigned)tiles);
+    const int64_t plane = mt * 32 * width;
+    const LowRankEpi none{};
+    if (!lr) {
+        hipLaunchKernelGGL(reduce_frags_kernel<0>, grid, dim3(256), 0, s, ws, splits, M, ntn, plane, seg, perm, vec_ok,
+                           none);
+    } else if (lr->rank <= 4) {
+        hipLaunchKernelGGL(reduce_frags_kernel<4>, grid, dim3(256), 0, s, ws, splits, M, ntn, plane, seg, perm, vec_ok,
+                           *lr);
+    } else if (lr->rank <= 8) {
+        hipLaunchKernelGGL(reduce_frags_kernel<8>, grid, dim3(256), 0, s, ws, splits, M, ntn, plane, seg, perm, vec_ok,
+                           *lr);
+    } else if (lr->rank <= 16) {
+        hipLaunchKernelGGL(reduce_frags_kernel<16>, grid, dim3(256), 0, s, ws, splits, M, ntn, plane, seg, perm, vec_ok,
+                           *lr);
+    } else if (lr->rank <= 32) {
+        hipLaunchKernelGGL(reduce_frags_kernel<32>, grid, dim3(256), 0, s, ws, splits, M, ntn, plane, seg, perm, vec_ok,
+                           *lr);
+    } else {
+        hipLaunchKernelGGL(reduce_frags_kernel<64>, grid, dim3(256), 0, s, ws, splits, M, ntn, plane, seg, perm, vec_ok,
+                           *lr);
+    }
     return hipGetLastError();
 }
 

@@ -59,9 +59,24 @@ hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_
 // 4 (64 r4 + L) + q, so a wave stores a tile with four 16-byte-per-lane writes.  The reduction
 // writes y[i][m][c] = sum_s for the tile columns of segment i (off[i] multiples of 32).
 inline int64_t frag_plane_floats(int64_t M, int64_t width) { return (M + 31) / 32 * 32 * width; }
+// Optional low-rank term of a one-segment reduction (the adapter's input gradient):
+// y[m, c] = (sum of the splits) then += alpha sum_j T[m, j] G(j, c), with T[m, j] = sum_s
+// P[(s M + m) r + j] over `chunks` partials in order (written to Tout once when Tout is set) and
+// G(j, c) = G[j C + c] (gt 0) or G[c r + j] (gt 1), C the segment's columns; the same fp32
+// operations, in the same order, as the separate expansion kernel, so the results match it bit
+// for bit.
+struct LowRankEpi {
+    const float* P;
+    int64_t chunks;
+    const float* G;
+    float* Tout;
+    float alpha;
+    int rank;
+    int gt;
+};
 hipError_t launch_reduce_frags(const float* ws, int splits, int64_t M, int64_t width, const float* const* y,
                                const int64_t* y_ld, const int64_t* off, const int64_t* cols, int nseg, int perm,
-                               hipStream_t s);
+                               hipStream_t s, const LowRankEpi* lr = nullptr);
 
 // generic.hip: any shape, any group size.
 hipError_t launch_generic_fwd(const WView& w, const void* x, int x_dtype, int64_t M, float* y,
@@ -106,8 +121,10 @@ struct BwdPlan {
 bool gemm_bwd_supported(const WView& w, int g_dtype, int fold_ok);
 // force_splits > 0 pins the contraction splits of the 32x32 routes (0: chosen per shape).
 BwdPlan plan_gemm_bwd(const WView& w, int g_dtype, int fold_ok, int64_t M, int force_splits = 0);
+// lr (the adapter's low-rank term) is applied by the split reduction: only with !plan.v1 and
+// plan.splits > 1 (the caller checks).
 hipError_t launch_gemm_bwd(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
-                           const BwdPlan& plan, float* ws, hipStream_t s);
+                           const BwdPlan& plan, float* ws, hipStream_t s, const LowRankEpi* lr = nullptr);
 bool gemm_bwd_v1_supported(const WView& w, int g_dtype, int fold_ok);
 BwdPlan plan_gemm_bwd_v1(const WView& w, int g_dtype, int fold_ok, int64_t M);
 hipError_t launch_gemm_bwd_v1(const WView& w, const void* d_out, int g_dtype, int64_t M, float* d_x,
@@ -128,9 +145,11 @@ hipError_t launch_dq8ca(const WView& w, const void* x, int x_dtype, int64_t M, f
 
 // adapter.hip: the low-rank adapter terms beside the frozen weight (rank 1..adapter_rank_max())
 // and the AdamW update.  The forward writes t = x A^T [M, r], then y += alpha t B^T; its
-// workspace (the column-chunk sums of t) is adapter_fwd_terms_ws_bytes.  The backward writes
-// u = d_out B [M, r] (workspace), then d_x += alpha u A, d_A = alpha u^T x, d_B = alpha d_out^T t;
-// its workspace (the chunk sums of u, u, the row-slab sums of d_A and d_B) is
+// workspace (the column-chunk sums of t) is adapter_fwd_terms_ws_bytes.  The backward, in order:
+// launch_adapter_bwd_u (the chunk sums of u = d_out B, before the input gradient), the input
+// gradient, which takes adapter_bwd_epi (d_x += alpha u A, u written) into its split reduction
+// when it has one, then launch_adapter_bwd_rest (d_x += alpha u A unless done, d_A = alpha u^T x,
+// d_B = alpha d_out^T t).  Its workspace (chunk sums of u, u, slab sums of d_A and d_B) is
 // adapter_bwd_terms_ws_bytes.  adapter_shape_ok: every launch of both fits the grid limits.
 int adapter_rank_max();
 bool adapter_shape_ok(int64_t M, int64_t N, int64_t K, int rank);
@@ -139,9 +158,12 @@ uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank);
 hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
                                     const float* B, int rank, float alpha, float* y, float* t, void* ws,
                                     hipStream_t s);
-hipError_t launch_adapter_bwd_terms(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
-                                    const float* A, const float* B, int rank, float alpha, const float* t,
-                                    float* d_x, float* d_A, float* d_B, void* ws, hipStream_t s);
+hipError_t launch_adapter_bwd_u(const void* d_out, int dtype, int64_t M, int64_t N, int64_t K, const float* B,
+                                int rank, void* ws, hipStream_t s);
+LowRankEpi adapter_bwd_epi(int64_t M, int64_t N, int64_t K, const float* A, int rank, float alpha, void* ws);
+hipError_t launch_adapter_bwd_rest(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
+                                   const float* A, int rank, float alpha, const float* t, float* d_x, bool dx_done,
+                                   float* d_A, float* d_B, void* ws, hipStream_t s);
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, double lr, double beta1,
                         double beta2, double eps, double weight_decay, int64_t step, hipStream_t s);
 

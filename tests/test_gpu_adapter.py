@@ -98,6 +98,19 @@ def test_adapter_parity(M, N, K, gs, act, sdt, r, alpha):
     assert_within(dB, g["dB"], g["r_dB"], tol_dB(case), "d_B")
 
 
+def test_cases_cover_both_backward_paths():
+    """When the input gradient of the frozen term ends in a split reduction (MFMA routes with K
+    splits), that launch also adds alpha u A; otherwise (small M, one split) a separate launch
+    does.  The parity cases above run both."""
+    q = lib()
+    fused = set()
+    for M, N, K, gs, act, sdt, r, alpha in CASES:
+        case = make_adapter(M, K, N, gs, act, sdt, r, seed=0)
+        pl = q.plan(q.OP_BWD_INPUT, pack(q, case.w), M, case.x.dtype)
+        fused.add(pl["route"] in ("bwd_split", "bwd_bsplit", "bwd_fold") and pl["splits"] > 1)
+    assert fused == {True, False}
+
+
 @pytest.mark.parametrize("act", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("M,N,K,r", [(3, 128, 256, 8), (77, 320, 640, 16), (260, 192, 1088, 64)])
 def test_adapter_terms_alone(act, M, N, K, r):
