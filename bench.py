@@ -347,8 +347,8 @@ OP_KERNELS = {"decode": ("gemv_fwd",), "prefill": ("gemm_fwd", "reduce_"),
               "bwd_h": ("gemm_bwd", "reduce_"), "bwd_gs32": ("gemm_bwd", "reduce_", "split_planes"),
               "emb_t512": ("embedding_kernel",), "emb_t1": ("embedding_kernel",),
               "dq8ca": ("dq8ca_", "reduce_"),
-              "adapter_fwd": ("gemm_fwd", "reduce_", "rank_contract", "rank_expand"),
-              "adapter_bwd": ("gemm_bwd", "reduce_", "rank_contract", "rank_expand", "column_"),
+              "adapter_fwd": ("gemm_fwd", "reduce_", "row_partial", "expand_kernel"),
+              "adapter_bwd": ("gemm_bwd", "reduce_", "row_partial", "expand_kernel", "column_"),
               "adamw": ("adamw_kernel",)}
 
 
