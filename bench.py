@@ -303,14 +303,14 @@ def build_ops(q, names, rotate):
 # the sources an op's kernels are built from: the shared headers and the entry points (which
 # plan the launch), plus the files holding its kernels
 _COMMON_SRC = ("api.hip", "device.h", "internal.h", "layout.h")
-_OP_SRC = {"decode": ("gemv.hip",), "qkv_m1": ("gemv.hip",), "qkv_m4": ("gemv.hip",),
-           "prefill": ("gemm_fwd.hip", "gemv.hip"), "qkv_m128": ("gemm_fwd.hip", "gemv.hip"),
-           "qkv_m508": ("gemm_fwd.hip", "gemv.hip"), "qkv_m512": ("gemm_fwd.hip", "gemv.hip"),
-           "bwd": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "bwd_h": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"),
-           "bwd_gs32": ("gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "emb_t512": ("embedding.hip",),
-           "emb_t1": ("embedding.hip",), "dq8ca": ("dq8ca.hip", "gemv.hip"),
-           "adapter_fwd": ("adapter.hip", "gemm_fwd.hip", "gemv.hip"),
-           "adapter_bwd": ("adapter.hip", "gemm_bwd2.hip", "gemm_bwd.hip", "gemv.hip"), "adamw": ("adapter.hip",)}
+_OP_SRC = {"decode": ("gemv.hip",), "qkv_m1": ("gemv.hip", "reduce.hip"), "qkv_m4": ("gemv.hip", "reduce.hip"),
+           "prefill": ("gemm_fwd.hip", "reduce.hip"), "qkv_m128": ("gemm_fwd.hip", "reduce.hip"),
+           "qkv_m508": ("gemm_fwd.hip", "reduce.hip"), "qkv_m512": ("gemm_fwd.hip", "reduce.hip"),
+           "bwd": ("gemm_bwd2.hip", "gemm_bwd.hip", "reduce.hip"), "bwd_h": ("gemm_bwd2.hip", "gemm_bwd.hip", "reduce.hip"),
+           "bwd_gs32": ("gemm_bwd2.hip", "gemm_bwd.hip", "reduce.hip"), "emb_t512": ("embedding.hip",),
+           "emb_t1": ("embedding.hip",), "dq8ca": ("dq8ca.hip", "reduce.hip"),
+           "adapter_fwd": ("adapter.hip", "gemm_fwd.hip", "reduce.hip"),
+           "adapter_bwd": ("adapter.hip", "gemm_bwd2.hip", "gemm_bwd.hip", "reduce.hip"), "adamw": ("adapter.hip",)}
 
 
 def source_hash(op_name=None):
