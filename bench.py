@@ -655,7 +655,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16/f16",
+        "dtype": "bf16/f16/f32",
         "data": "synthetic",
         "config": {"workload": "llama-3.2-1b q4gsw step: " + ", ".join(
             f"{o.name} M{o.M} route={o.route}" for o in step_ops), "ops": names, "rotated_sets": rotate,

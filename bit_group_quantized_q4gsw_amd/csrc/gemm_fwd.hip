@@ -629,7 +629,12 @@ static void with_spc(int spc, F&& f) {
 }
 template <int XT, int MODE, int SF, typename F>
 static void with_mi(int mi, int spc, bool rg, F&& f) {
-    if (rg) {
+    if constexpr (MODE == kModeSplit) {
+        // 64-row tiles only (see plan_gemm_fwd)
+        (void)mi;
+        if (rg) with_spc<XT, MODE, SF, 2, true>(spc, f);
+        else with_spc<XT, MODE, SF, 2, false>(spc, f);
+    } else if (rg) {
         if (mi == 4) with_spc<XT, MODE, SF, 4, true>(spc, f);
         else with_spc<XT, MODE, SF, 2, true>(spc, f);
     } else {
@@ -689,11 +694,10 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
     double best = 1e300;
     const int forced = force_rows;
     for (int mi : {4, 2}) {
-        if (forced == 64 || forced == 128) {
-            if (32 * mi != forced) continue;
-        } else if (mi == 4 && p.mode == kModeSplit) {
-            continue;                                  // hi + lo planes: the 128-row tile spills
-        }
+        // fp32 x (hi + lo planes) has no 128-row tile: that instance spilled 250-580 bytes per
+        // lane and ran 3-6x slower, so a forced 128 plans 64-row tiles (q4gsw_plan reports it)
+        if (mi == 4 && p.mode == kModeSplit) continue;
+        if (p.mode != kModeSplit && (forced == 64 || forced == 128) && 32 * mi != forced) continue;
         const int64_t bm = 32 * mi;
         const int64_t blocks = tiles * ((M + bm - 1) / bm);
         const int64_t slots = 256 * (int64_t)fwd_blocks_per_cu(p.mode, x_dtype, w0.scale_f16, spc, mi);
@@ -745,7 +749,7 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     const int mode = plan.mode;
     const int spc = fwd_spc(w0.gs);
     if (spc == 4 && mode != kModeFold) return hipErrorInvalidValue;
-    if (plan.mi != 4 && plan.mi != 2) return hipErrorInvalidValue;
+    if ((plan.mi != 4 && plan.mi != 2) || (plan.mi == 4 && mode == kModeSplit)) return hipErrorInvalidValue;
     const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);
     const int64_t bm = 32 * plan.mi;

@@ -104,7 +104,8 @@ typedef enum q4gsw_route_id {
  *              the library picks the precision route inside the family).  A call
  *              the family cannot serve returns Q4GSW_E_ROUTE; a value outside the
  *              enum returns Q4GSW_E_ROUTE too.
- *   tile_rows  forward / QKV MFMA block rows: 0 (per shape), 64 or 128
+ *   tile_rows  forward / QKV MFMA block rows: 0 (per shape), 64 or 128 (fp32 activations always
+ *              take 64: their mode has no 128-row tile)
  *              (Q4GSW_E_SHAPE otherwise).
  *   splits     contraction splits of the 32x32 MFMA GEMMs (forward, QKV and the
  *              input-gradient routes BWD_FOLD, BWD_SPLIT and BWD_BSPLIT): 0 (per shape) or

@@ -213,7 +213,8 @@ def test_forward_tiles(M, N, K, gs, act, sdt, rows):
     x = dev(case.x)
     ref, norm = oracle_fwd(case.x, case.w)
     with q.forced_plan(tile_rows=rows):
-        assert q.plan(q.OP_FWD, pw, M, case.x.dtype)["tile_rows"] == rows
+        # fp32 activations have no 128-row tile: a forced 128 plans 64
+        assert q.plan(q.OP_FWD, pw, M, case.x.dtype)["tile_rows"] == (64 if act == "f32" else rows)
         y = q.linear_fwd(pw, x)
         torch.cuda.synchronize()
     assert_within(y, ref, norm, TOL[case.x.dtype], f"fwd tile {rows} route={q.route(q.OP_FWD, pw, M, case.x.dtype)}")
