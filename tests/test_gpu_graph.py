@@ -7,7 +7,7 @@ replays, must reproduce the eager output exactly.  The benchmark times its step 
 import pytest
 import torch
 
-from synthetic_inputs import make_embedding, make_linear, make_qkv
+from synthetic_inputs import make_adamw_state, make_adapter, make_embedding, make_linear, make_qkv
 from tests.gpu_helpers import dev, lib, pack
 
 pytestmark = pytest.mark.gpu
@@ -92,3 +92,66 @@ def test_graph_replay_matches_eager(kind, M, N, K, gs, act, sdt):
         _call(q, kind, pw, a, eager, ws)
         other.mul_(1.0001)
         torch.cuda.synchronize()
+
+
+def test_graph_replay_adapter_step():
+    """The adapter forward and backward captured once and replayed: every replay gives the eager
+    t, y, d_x, d_A and d_B bit for bit, with eager calls that reuse the workspaces in between.
+    AdamW captured for one step and replayed from a restored state gives the eager step."""
+    q = lib()
+    M, N, K, r, alpha = 300, 1024, 512, 16, 0.5
+    case = make_adapter(M, K, N, 64, "bf16", "f16", r, seed=11)
+    pw = pack(q, case.w)
+    x, d, A, B = dev(case.x), dev(case.d_out), dev(case.A), dev(case.B)
+    wsf = torch.empty(max(q.adapter_workspace_bytes(q.OP_FWD, pw, M, x.dtype, r), 1), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(max(q.adapter_workspace_bytes(q.OP_BWD_INPUT, pw, M, x.dtype, r), 1), dtype=torch.uint8,
+                      device="cuda")
+
+    def step(y, t, dx, dA, dB):
+        q.adapter_fwd(pw, x, A, B, alpha, out=y, t=t, workspace=wsf)
+        q.adapter_bwd(pw, x, d, A, B, alpha, t, d_x=dx, d_A=dA, d_B=dB, workspace=wsb)
+
+    shapes = [(M, N), (M, r), (M, K), (r, K), (N, r)]
+    eager = [torch.empty(s, device="cuda") for s in shapes]
+    step(*eager)
+    torch.cuda.synchronize()
+    outs = [torch.full(s, float("nan"), device="cuda") for s in shapes]
+    step(*outs)                                     # warm the stream before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(*outs)
+    torch.cuda.synchronize()
+    scratch = [torch.empty(s, device="cuda") for s in shapes]
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, o, e in zip(("y", "t", "d_x", "d_A", "d_B"), outs, eager):
+            assert torch.equal(o, e), f"adapter {name}: replay {rep} differs from the eager result"
+        step(*scratch)                              # eager work on the same workspaces
+        torch.cuda.synchronize()
+
+    # AdamW: one captured step, replayed from the same starting state each time
+    p0, g0, m0, v0 = (dev(t) for t in make_adamw_state(4099, 3, seed=2))
+    P, G, Mm, V = (t.clone() for t in (p0, g0, m0, v0))
+    q.adamw_step(P, G, Mm, V, 3, 1e-3, 0.9, 0.999, 1e-8, 0.01)
+    torch.cuda.synchronize()
+    want = (P.clone(), Mm.clone(), V.clone())
+    for t, s in zip((P, Mm, V), (p0, m0, v0)):
+        t.copy_(s)
+    torch.cuda.synchronize()
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        q.adamw_step(P, G, Mm, V, 3, 1e-3, 0.9, 0.999, 1e-8, 0.01)
+    for rep in range(3):
+        for t, s in zip((P, Mm, V), (p0, m0, v0)):
+            t.copy_(s)
+        torch.cuda.synchronize()
+        ga.replay()
+        torch.cuda.synchronize()
+        for name, t, w in zip(("param", "exp_avg", "exp_avg_sq"), (P, Mm, V), want):
+            assert torch.equal(t, w), f"adamw {name}: replay {rep} differs from the eager step"
