@@ -79,6 +79,7 @@ CASES = [
     (200, 264, 384, 64, "f16", "f16", 64, 0.125),    # the largest rank
     (1000, 256, 512, 32, "bf16", "f16", 8, 1.0),     # d_A and d_B over several row slabs
     (9, 96, 2048, 32, "f32", "f32", 17, 3.0),
+    (33, 257, 256, 32, "f16", "f16", 3, 1.0),       # odd N: rows of y, d_out and B^T without whole quads
 ]
 
 
@@ -93,6 +94,38 @@ def test_adapter_parity(M, N, K, gs, act, sdt, r, alpha):
     assert_within(y, oy, ry, tol_y(case, r), "y")
     assert_within(t, ot, t_norm(case.x, case.A), contract_chain(K) * U, "t")
     g = O.lora_bwd(case.x, case.d_out, w.codes, w.scales, gs, case.A, case.B, alpha, threads=THREADS)
+    assert_within(dx, g["dx"], g["r_dx"], tol_dx(case, r), "d_x")
+    assert_within(dA, g["dA"], g["r_dA"], tol_dA(case), "d_A")
+    assert_within(dB, g["dB"], g["r_dB"], tol_dB(case), "d_B")
+
+
+def _offset_copy(t):
+    """t on the GPU, one element past the start of its allocation (misaligned for vector loads)."""
+    big = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    v = big[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_adapter_unaligned_operands(act):
+    """x, d_out, A, B and t one element off their allocations: every low-rank kernel takes its
+    element-wise path, with the same results as the oracle."""
+    q = lib()
+    M, N, K, r, alpha = 70, 320, 512, 12, -1.25
+    case = make_adapter(M, K, N, 64, act, "f16", r, seed=90 + len(act))
+    pw = pack(q, case.w)
+    x, d = _offset_copy(case.x), _offset_copy(case.d_out)
+    A, B = _offset_copy(case.A), _offset_copy(case.B)
+    y, t = q.adapter_fwd(pw, x, A, B, alpha)
+    t_off = _offset_copy(t)
+    dx, dA, dB = q.adapter_bwd(pw, x, d, A, B, alpha, t_off)
+    torch.cuda.synchronize()
+    w = case.w
+    oy, ot, ry = O.lora_fwd(case.x, w.codes, w.scales, 64, case.A, case.B, alpha, threads=THREADS)
+    assert_within(y, oy, ry, tol_y(case, r), "y")
+    assert_within(t, ot, t_norm(case.x, case.A), contract_chain(K) * U, "t")
+    g = O.lora_bwd(case.x, case.d_out, w.codes, w.scales, 64, case.A, case.B, alpha, threads=THREADS)
     assert_within(dx, g["dx"], g["r_dx"], tol_dx(case, r), "d_x")
     assert_within(dA, g["dA"], g["r_dA"], tol_dA(case), "d_A")
     assert_within(dB, g["dB"], g["r_dB"], tol_dB(case), "d_B")
