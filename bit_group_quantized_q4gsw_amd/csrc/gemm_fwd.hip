@@ -8,23 +8,26 @@
 //     feeds 32 MI activation rows;
 //   * block = 8 waves side by side in N (block tile 32 MI x 256), two waves per SIMD, so the
 //     code unpacking of one wave issues while the other wave's MFMAs run;
-//   * every global read is an LDS-DMA (global_load_lds): the 64-column activation chunk
-//     (shared by the 8 waves), each wave's 1 KB of codes and its scales travel straight
+//   * every global read is an LDS-DMA (global_load_lds): the activation chunk (64 columns;
+//     128 in the exact-code group mode with gs == 128, so every chunk opens one group and the
+//     chunk loop is one straight-line path) shared by the 8
+//     waves, each wave's 1 or 2 KB of codes and its scales travel straight
 //     into a ring of KD + 1 LDS stages, KD chunks ahead of the MFMAs, with no VGPR
 //     staging.  Explicit vmcnt waits + s_barrier order the ring; the compiler only sees
 //     LDS reads (fp32 activations are the exception: split into bf16 hi + lo planes in
 //     registers on their way into LDS);
-//   * LDS swizzles: activation k-octet slots of row r sit at slot (octet ^ ((r >> 1) & 7)),
-//     so the 16 lanes of an A-fragment read phase (16 rows of 128 bytes) cover all 64
-//     banks; the 256-byte code run of row-octet R is rotated by 2R 32-byte blocks, so the 64
-//     lanes reading one k-octet pair of the wave's 4 row-octets hit 64 distinct banks;
+//   * LDS swizzles: activation k-octet slots of row r sit at slot (octet ^ ((r >> 1) & 7))
+//     for 128-byte rows and (octet ^ (r & 15)) for 256-byte rows, so the 16 lanes of an
+//     A-fragment read phase (16 rows) cover all 64 banks; each 256-byte code run of
+//     row-octet R is rotated by 2R 32-byte blocks, so the 64 lanes reading one k-octet pair
+//     of the wave's 4 row-octets hit 64 distinct banks;
 //   * the K range is split across blocks when the output tiles cannot fill the GPU; the
 //     split index is the fastest-varying block coordinate, so with 8 splits every XCD owns
 //     one K slice (its activation and code slices stay in that XCD's L2); a reduction
 //     kernel sums the split partials.
 //
-// K order inside a 64-column chunk: MFMA step t contracts k-octets 2t (lanes 0..31) and
-// 2t+1 (lanes 32..63), so a step covers 16 consecutive columns.
+// K order inside a chunk: MFMA step t contracts k-octets 2t (lanes 0..31) and 2t+1 (lanes
+// 32..63), so a step covers 16 consecutive columns.
 //
 // Precision routes (all with fp32 accumulation):
 //   kModeFold  (fp16 x, fp16 scales checked foldable at pack time):
@@ -45,13 +48,12 @@ namespace q4gsw {
 constexpr int kWaves = 8;           // waves per block, two per SIMD
 constexpr int kWN = 32;             // wave columns (N)
 constexpr int kBN = kWaves * kWN;   // block columns (N)
-constexpr int kCK = 64;             // K columns per chunk
+constexpr int kCK = 64;             // K columns per chunk (kCKWide in the wide group instances)
+constexpr int kCKWide = 128;
 #ifndef Q4GSW_FWD_DEPTH
 #define Q4GSW_FWD_DEPTH 2
 #endif
 constexpr int kDepth16 = Q4GSW_FWD_DEPTH;   // chunks in flight ahead of the one multiplied (16-bit x)
-constexpr int kRowBytes = 128;      // one 16-bit activation row of a chunk in LDS
-constexpr int kCodeBytes = 1024;    // one wave's codes for one chunk: 32 rows x 64 columns x 4 bits
 
 struct FwdSegArgs {
     const uint8_t* nib[3];
@@ -113,16 +115,32 @@ __device__ __forceinline__ void wait_chunks_barrier(int64_t n) {
     }
 }
 
-// RG: the activation may be ragged (K % 64 != 0) or not 16-byte aligned, so chunks can take the
+// LDS slot swizzle of activation row r: 128-byte rows (64 columns) pair rows across the two
+// 32-bank halves, 256-byte rows (128 columns) give 16 rows 16 distinct slots.
+template <int CW>
+__device__ __forceinline__ int a_swizzle(int r) {
+    if constexpr (CW == kCK) return (r >> 1) & 7;
+    else return r & 15;
+}
+
+// RG: the activation may be ragged (K % CW != 0) or not 16-byte aligned, so chunks can take the
 // synchronous fallback; the aligned instance carries no fallback code (and none of its live
-// values across the chunk loop).
-template <int XT, int MODE, int SPC, int SF, int MI, int KD, bool RG>
+// values across the chunk loop).  CW: K columns per chunk, 64, or 128 for the exact-code group
+// mode with gs == 128.
+template <int XT, int MODE, int SPC, int SF, int MI, int KD, bool RG, int CW>
 __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const void* __restrict__ x, int64_t M,
                                                           int64_t K, int64_t k_pad, int64_t gs, int x_fast,
                                                           int chunks_per_split, int splits, int mtiles,
                                                           int64_t split_stride) {
     static_assert(MI == 2 || MI == 4, "32-row MFMA tiles per wave");
     static_assert(KD >= 2 && KD <= 6 && (XT != kF32 || KD == 2), "chunks in flight");
+    static_assert(CW == kCK || (CW == kCKWide && XT != kF32 && MODE == kModeGroup && SPC == 1),
+                  "128-column chunks: exact-code group mode with one group per chunk (gs == 128)");
+    constexpr int kSteps = CW / 16;                       // MFMA steps per chunk
+    constexpr int kRowBytes = 2 * CW;                     // one activation row (or bf16 plane row) of a chunk
+    constexpr int kSlots = CW / 8;                        // 16-byte k-octet slots per row
+    constexpr int kCodeBytes = 16 * CW;                   // one wave's codes of a chunk: 32 rows x CW x 4 bits
+    constexpr int kCDma = CW / 64;                        // 1 KB code DMAs per wave per chunk
     constexpr int kStages = KD + 1;                       // LDS stages in the ring
     constexpr int kBM = 32 * MI;                          // block rows (M)
     constexpr int kRowsPerWave = kBM / kWaves;            // activation rows each wave stages
@@ -130,14 +148,15 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     constexpr int kAUnits = kBM * 16 / (64 * kWaves);     // fp32 float4 units per thread per chunk
     constexpr bool kX16 = XT != kF32;
     constexpr int kPlanes = kX16 ? 1 : 2;
-    constexpr int kADma = kX16 ? kRowsPerWave / 8 : 0;    // activation DMAs per wave per chunk
+    constexpr int kRowsPerDma = 1024 / kRowBytes;         // activation rows of one 16-bit DMA
+    constexpr int kADma = kX16 ? kRowsPerWave / kRowsPerDma : 0;   // activation DMAs per wave per chunk
     // Scales: with one or two groups per chunk (SPC <= 2) wave 0 fetches the block's 256 rows
     // in kSDma0 16-byte-per-lane DMAs; with a group per k-octet pair (SPC == 4) every wave
     // fetches its own rows, 4 bytes per lane.
     constexpr bool kBlockScales = SPC <= 2;
     constexpr int kSDma0 = SF ? 1 : SPC;                  // block scale DMAs of wave 0 per chunk
     constexpr int kSDma = kBlockScales ? 0 : SPC;         // scale DMAs of every wave per chunk
-    constexpr int kDmaPerChunk = kADma + 1 + kSDma;
+    constexpr int kDmaPerChunk = kADma + kCDma + kSDma;
     constexpr int kDmaPerChunk0 = kDmaPerChunk + (kBlockScales ? kSDma0 : 0);   // wave 0
     constexpr int kAOff = 0;
     constexpr int kBOff = kPlanes * kPlaneBytes;
@@ -172,16 +191,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     const int64_t nw = wave_active ? n0 : 0;   // an idle wave streams valid rows it never uses
     const int64_t m0 = mb * kBM;
     const int64_t kocts = k_pad >> 3;
-    const int64_t n_chunks = (K + kCK - 1) / kCK;
+    const int64_t n_chunks = (K + CW - 1) / CW;
     const int64_t c_begin = (int64_t)z * chunks_per_split;
     const int64_t c_end = min(c_begin + (int64_t)chunks_per_split, n_chunks);
 
     lds_u8* const sm_l = (lds_u8*)smem;
 
     // ---------------- DMA source addresses ----------------
-    // Codes: one DMA per wave and chunk covers the wave's 4 row-octets; lane l fills LDS bytes
-    // 16 l = row-octet R = l >> 4, rotated block slot p = (l & 15) >> 1, half l & 1, which
-    // holds k-octet (p - 2R) & 7 of the chunk.
+    // Codes: one DMA per wave and 64 chunk columns covers the wave's 4 row-octets; lane l fills
+    // LDS bytes 16 l = row-octet R = l >> 4, rotated block slot p = (l & 15) >> 1, half l & 1,
+    // which holds k-octet (p - 2R) & 7 of those 64 columns.
     const uint8_t* csrc;
     {
         const int R = lane >> 4;
@@ -197,15 +216,15 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     const uint8_t* sptr = static_cast<const uint8_t*>(seg.scales[sg]);
     const int64_t boct = (tile - seg.tile_start[sg]) * (kBN / 8);
     const int64_t n_octs = seg.n_pad[sg] / 8;
-    // Activations (16-bit): DMA q of wave w covers rows kRowsPerWave w + 8q .. +7; lane i fills
-    // slot i & 7 of row (i >> 3), which holds k-octet (i & 7) ^ ((row >> 1) & 7).
+    // Activations (16-bit): DMA q of wave w covers rows kRowsPerWave w + kRowsPerDma q onwards;
+    // lane i fills slot i % kSlots of row i / kSlots, which holds k-octet slot ^ swz(row).
     const uint16_t* xa[kADma > 0 ? kADma : 1];
     int xoct[kADma > 0 ? kADma : 1];
     if constexpr (kX16) {
 #pragma unroll
         for (int q = 0; q < kADma; ++q) {
-            const int row = kRowsPerWave * wave + 8 * q + (lane >> 3);
-            xoct[q] = (lane & 7) ^ ((row >> 1) & 7);
+            const int row = kRowsPerWave * wave + kRowsPerDma * q + lane / kSlots;
+            xoct[q] = (lane % kSlots) ^ a_swizzle<CW>(row);
             const int64_t m = min(m0 + row, M - 1);     // rows past M only feed discarded outputs
             xa[q] = static_cast<const uint16_t*>(x) + m * K + 8 * xoct[q];
         }
@@ -213,8 +232,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
 
     auto issue_codes_scales = [&](int64_t c, int st) {
         lds_u8* base = sm_l + st * kStageBytes;
-        dma16(csrc + 256 * c, base + kBOff + wave * kCodeBytes);
-        const uint32_t kc = (uint32_t)(c * kCK);
+#pragma unroll
+        for (int d = 0; d < kCDma; ++d) dma16(csrc + 256 * (kCDma * c + d), base + kBOff + wave * kCodeBytes + 1024 * d);
+        const uint32_t kc = (uint32_t)(c * CW);
         const uint32_t ug = (uint32_t)gs;
         if constexpr (kBlockScales) {
             if (wave == 0) {
@@ -256,23 +276,23 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     auto fill_a16_slow = [&](int64_t kc, int st) {
 #pragma unroll
         for (int q = 0; q < kADma; ++q) {
-            const int row = kRowsPerWave * wave + 8 * q + (lane >> 3);
+            const int row = kRowsPerWave * wave + kRowsPerDma * q + lane / kSlots;
             const int64_t m = m0 + row;
             const int64_t k = kc + 8 * xoct[q];
             uint32_t e[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 e[i] = (m < M && k + i < K) ? static_cast<const uint16_t*>(x)[m * K + k + i] : 0u;
-            *reinterpret_cast<u4*>(smem + st * kStageBytes + kAOff + row * kRowBytes + 16 * (lane & 7)) =
+            *reinterpret_cast<u4*>(smem + st * kStageBytes + kAOff + row * kRowBytes + 16 * (lane % kSlots)) =
                 u4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
         }
     };
     auto issue_a16 = [&](int64_t c, int st) {
-        const int64_t kc = c * kCK;
-        if (!RG || (x_fast && kc + kCK <= K)) {
+        const int64_t kc = c * CW;
+        if (!RG || (x_fast && kc + CW <= K)) {
 #pragma unroll
             for (int q = 0; q < kADma; ++q)
-                dma16(xa[q] + kc, sm_l + st * kStageBytes + kAOff + (kRowsPerWave * wave + 8 * q) * kRowBytes);
+                dma16(xa[q] + kc, sm_l + st * kStageBytes + kAOff + (kRowsPerWave * wave + kRowsPerDma * q) * kRowBytes);
         } else if constexpr (RG) {
             fill_a16_slow(kc, st);
         }
@@ -281,8 +301,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     // fp32 activations: kAUnits float4 units per thread, split into bf16 hi / lo planes at store time.
     f4 areg[kAUnits];
     auto load_a32 = [&](int64_t c) {
-        const int64_t kc = c * kCK;
-        const bool fast = !RG || (x_fast && kc + kCK <= K);
+        const int64_t kc = c * CW;
+        const bool fast = !RG || (x_fast && kc + CW <= K);
 #pragma unroll
         for (int i = 0; i < kAUnits; ++i) {
             const int unit = tid + 64 * kWaves * i;
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     // ---------------- one chunk of MFMAs ----------------
-    const int swz = (j >> 1) & 7;     // ((row >> 1) & 7) of every A row this lane reads
+    const int swz = a_swizzle<CW>(j);   // the swizzle of every A row (32 mi + j) this lane reads
     const int Rj = j >> 3;            // this lane's row-octet inside the wave
     // LDS byte of this lane's scale (row r = 32 wave + j) in slot q: block form, run
     // SPC (r >> 3) + q of 8 scales; per-wave form, half of a pair word (fp16) or a word (fp32)
@@ -425,10 +445,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
                 for (int r = 0; r < 16; ++r) acc[mi][r] = fmaf(part[mi][r], gopen, acc[mi][r]);
         }
     };
-    // One chunk, software-pipelined: the code words of all four steps are read first; while
-    // the MFMAs of step t run, the A fragments of step t + 1 are read and its codes unpacked.
-    // K0 / K2: kinds of steps 0 and 2 (steps 1 and 3 always accumulate); fixed at compile
-    // time so the chunk body is straight-line code.  Idle waves multiply the valid rows they
+    // One chunk, software-pipelined: the code words of all steps are read first; while the
+    // MFMAs of step t run, the A fragments of step t + 1 are read and its codes unpacked.
+    // K0 / K2: kinds of steps 0 and 2 (every other step accumulates; K2 is a group boundary
+    // only for gs == 32 in 64-column chunks); fixed at compile time so the chunk body is
+    // straight-line code.  Idle waves multiply the valid rows they
     // stream too (their results are never stored): a per-wave branch here would make the
     // accumulators exec-masked.
     auto compute = [&](int st, auto k0, auto k2) {
@@ -436,10 +457,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         const uint8_t* Ab = smem + st * kStageBytes + kAOff;
         const uint8_t* Bb = smem + st * kStageBytes + kBOff + wave * kCodeBytes;
         const uint8_t* S = smem + st * kStageBytes + kSOff + (kBlockScales ? 0 : wave * (SPC * 256));
-        uint32_t bw[4];
+        uint32_t bw[kSteps];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            bw[t] = *reinterpret_cast<const uint32_t*>(Bb + 256 * Rj + 32 * ((2 * t + h + 2 * Rj) & 7) + 4 * (j & 7));
+        for (int t = 0; t < kSteps; ++t)
+            bw[t] = *reinterpret_cast<const uint32_t*>(Bb + 1024 * (t >> 2) + 256 * Rj +
+                                                       32 * ((2 * (t & 3) + h + 2 * Rj) & 7) + 4 * (j & 7));
         u4 a[2][MI], alo[2][MI], b[2];
         read_a(Ab, 0, a[0], alo[0]);
         dequant(bw[0], S, 0, b[0]);
@@ -447,22 +469,29 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         // step's unpacking pieces between them (two pieces per MFMA for MI = 2).
         auto one = [&](auto tc, auto kc) {
             constexpr int t = decltype(tc)::value, KIND = decltype(kc)::value;
-            if constexpr (t < 3) read_a(Ab, t + 1, a[(t + 1) & 1], alo[(t + 1) & 1]);
+            if constexpr (t < kSteps - 1) read_a(Ab, t + 1, a[(t + 1) & 1], alo[(t + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
             uint32_t wpre[2] = {0u, 0u};
             constexpr int kPer = 4 / MI;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if (e % kPer == 0) mma_tile(a[t & 1][e / kPer], alo[t & 1][e / kPer], b[t & 1], e / kPer, kc);
-                if constexpr (t < 3) dequant_piece(bw[t + 1], S, t + 1, b[(t + 1) & 1], e, wpre);
+                if constexpr (t < kSteps - 1) dequant_piece(bw[t + 1], S, t + 1, b[(t + 1) & 1], e, wpre);
                 if (e % kPer == kPer - 1) __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (KIND != 0) gopen = group_scale(S, SPC == 2 ? (t >> 1) : 0);
         };
+        typedef std::integral_constant<int, 0> A0;
         one(std::integral_constant<int, 0>{}, k0);
-        one(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+        one(std::integral_constant<int, 1>{}, A0{});
         one(std::integral_constant<int, 2>{}, k2);
-        one(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{});
+        one(std::integral_constant<int, 3>{}, A0{});
+        if constexpr (kSteps == 8) {
+            one(std::integral_constant<int, 4>{}, A0{});
+            one(std::integral_constant<int, 5>{}, A0{});
+            one(std::integral_constant<int, 6>{}, A0{});
+            one(std::integral_constant<int, 7>{}, A0{});
+        }
     };
 
     // ---------------- pipeline ----------------
@@ -522,15 +551,22 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         // its partial sums are scaled into acc by the first step of the next group, the last
         // group's after the loop
         if (c_begin < c_end) {
-            const int64_t cpg = gs / kCK;
-            int64_t left = cpg - c_begin % cpg;       // chunks of the open group from c_begin on
-            chunk(c_begin, Open{}, Acc{});
-            for (int64_t c = c_begin + 1; c < c_end; ++c) {
-                if (--left == 0) {
-                    left = cpg;
-                    chunk(c, Reopen{}, Acc{});
-                } else {
-                    chunk(c, Acc{}, Acc{});
+            if constexpr (CW == kCKWide) {
+                // gs == 128: every chunk opens a group, so the loop is one path (two chunk kinds
+                // meeting at the loop head made the compiler copy all partial sums there)
+                chunk(c_begin, Open{}, Acc{});
+                for (int64_t c = c_begin + 1; c < c_end; ++c) chunk(c, Reopen{}, Acc{});
+            } else {
+                const int64_t cpg = gs / CW;
+                int64_t left = cpg - c_begin % cpg;       // chunks of the open group from c_begin on
+                chunk(c_begin, Open{}, Acc{});
+                for (int64_t c = c_begin + 1; c < c_end; ++c) {
+                    if (--left == 0) {
+                        left = cpg;
+                        chunk(c, Reopen{}, Acc{});
+                    } else {
+                        chunk(c, Acc{}, Acc{});
+                    }
                 }
             }
             flush_open_group();
@@ -588,13 +624,19 @@ static int fwd_spc(int64_t gs) {
     return 4;
 }
 
+// K columns per chunk: 128 for the exact-code group mode with gs == 128, where every 128-column
+// chunk is one group (measured on a replica of the chunk loop: 1849 against 2383 cycles per 64
+// columns, the 64-column loop paying a copy of every partial sum where its two chunk kinds
+// meet), else 64.
+static int fwd_chunk_cols(int mode, int64_t gs) { return (mode == kModeGroup && gs == kCKWide) ? kCKWide : kCK; }
+
 // Split count minimising a time model (microseconds): rounds of blocks over the CU slots times
-// (chunks per split + 2 for pipeline fill and epilogue) at chunk_us per chunk, plus, with splits,
+// (chunks per split + fill for pipeline fill and epilogue) at chunk_us per chunk, plus, with splits,
 // a reduction launch (~3 us) and the partial buffer written and read back (splits x M x width
 // x 8 bytes at ~5 TB/s).  Ties go to fewer splits.  force_splits > 0 takes that count instead
 // (clamped to the chunks and rounded to a count without an empty split).
 int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width, int64_t slots, double chunk_us,
-                     double* cost_out, int force_splits) {
+                     double* cost_out, int force_splits, double fill) {
     int best = 1;
     double best_cost = 1e300;
     int64_t want = 0;
@@ -608,7 +650,7 @@ int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width,
         if ((n_chunks + per - 1) / per != s) continue;      // some split would be empty
         if (want > 0 && s != want) continue;
         const int64_t rounds = (blocks * s + slots - 1) / slots;
-        double cost = chunk_us * (double)rounds * (double)(per + 2);
+        double cost = chunk_us * (double)rounds * ((double)per + fill);
         if (s > 1) cost += 3.0 + (double)s * (double)M * (double)width * 8.0 / 5e6;
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
@@ -619,56 +661,63 @@ int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width,
     return best;
 }
 
-// Kernel instance for (activation type, mode, scale slots, scale type, row tiles, fallback), handed to f.
+// Kernel instance for (activation type, mode, scale slots, scale type, row tiles, fallback, chunk
+// columns), handed to f; a combination without an instance hands nothing.
 template <int XT, int MODE, int SF, int MI, bool RG, typename F>
-static void with_spc(int spc, F&& f) {
+static void with_spc(int spc, int cw, F&& f) {
     constexpr int KD = XT == kF32 ? 2 : kDepth16;
-    if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG>);
-    else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD, RG>);
-    else if constexpr (MODE == kModeFold) f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD, RG>);
+    if (cw == kCKWide) {
+        if constexpr (MODE == kModeGroup) {
+            if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide>);
+        }
+        return;
+    }
+    if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCK>);
+    else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD, RG, kCK>);
+    else if constexpr (MODE == kModeFold) f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD, RG, kCK>);
 }
 template <int XT, int MODE, int SF, typename F>
-static void with_mi(int mi, int spc, bool rg, F&& f) {
+static void with_mi(int mi, int spc, bool rg, int cw, F&& f) {
     if constexpr (MODE == kModeSplit) {
         // 64-row tiles only (see plan_gemm_fwd)
         (void)mi;
-        if (rg) with_spc<XT, MODE, SF, 2, true>(spc, f);
-        else with_spc<XT, MODE, SF, 2, false>(spc, f);
+        if (rg) with_spc<XT, MODE, SF, 2, true>(spc, cw, f);
+        else with_spc<XT, MODE, SF, 2, false>(spc, cw, f);
     } else if (rg) {
-        if (mi == 4) with_spc<XT, MODE, SF, 4, true>(spc, f);
-        else with_spc<XT, MODE, SF, 2, true>(spc, f);
+        if (mi == 4) with_spc<XT, MODE, SF, 4, true>(spc, cw, f);
+        else with_spc<XT, MODE, SF, 2, true>(spc, cw, f);
     } else {
-        if (mi == 4) with_spc<XT, MODE, SF, 4, false>(spc, f);
-        else with_spc<XT, MODE, SF, 2, false>(spc, f);
+        if (mi == 4) with_spc<XT, MODE, SF, 4, false>(spc, cw, f);
+        else with_spc<XT, MODE, SF, 2, false>(spc, cw, f);
     }
 }
 template <typename F>
-static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, bool rg, F&& f) {
+static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, bool rg, int cw, F&& f) {
     if (mode == kModeFold) {
-        with_mi<kF16, kModeFold, 1>(mi, spc, rg, f);
+        with_mi<kF16, kModeFold, 1>(mi, spc, rg, cw, f);
     } else if (mode == kModeSplit) {
-        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, rg, f);
-        else with_mi<kF32, kModeSplit, 0>(mi, spc, rg, f);
+        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, rg, cw, f);
+        else with_mi<kF32, kModeSplit, 0>(mi, spc, rg, cw, f);
     } else if (x_dtype == kF16) {
-        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, rg, f);
-        else with_mi<kF16, kModeGroup, 0>(mi, spc, rg, f);
+        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, rg, cw, f);
+        else with_mi<kF16, kModeGroup, 0>(mi, spc, rg, cw, f);
     } else {
-        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, rg, f);
-        else with_mi<kBF16, kModeGroup, 0>(mi, spc, rg, f);
+        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, rg, cw, f);
+        else with_mi<kBF16, kModeGroup, 0>(mi, spc, rg, cw, f);
     }
 }
 
 // Blocks of one kernel instance resident per CU (registers and LDS decide), cached per instance.
 // Planning may run on several host threads: the cache entries are atomics, and a race only
 // repeats the same query.
-static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int mi) {
-    static std::atomic<int> cache[3][3][2][5][5];
+static int fwd_blocks_per_cu(int mode, int x_dtype, int scale_f16, int spc, int mi, int cw) {
+    static std::atomic<int> cache[3][3][2][5][5][2];
     // the aligned instance stands for both fallback variants
-    std::atomic<int>& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi];
+    std::atomic<int>& slot = cache[mode][x_dtype][scale_f16 ? 1 : 0][spc][mi][cw == kCKWide ? 1 : 0];
     int n = slot.load(std::memory_order_relaxed);
     if (n == 0) {
         n = 1;
-        dispatch_fwd(mode, x_dtype, scale_f16, spc, mi, false, [&](auto kern) {
+        dispatch_fwd(mode, x_dtype, scale_f16, spc, mi, false, cw, [&](auto kern) {
             int b = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, 64 * kWaves, 0) == hipSuccess && b > 0) n = b;
         });
@@ -689,7 +738,8 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         tiles += (segs[i].w.n_pad + kBN - 1) / kBN;
         npad_total += segs[i].w.n_pad;
     }
-    const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
+    const int cw = fwd_chunk_cols(p.mode, w0.gs);
+    const int64_t n_chunks = (w0.K + cw - 1) / cw;
     const int spc = fwd_spc(w0.gs);
     double best = 1e300;
     const int forced = force_rows;
@@ -700,13 +750,15 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         if (p.mode != kModeSplit && (forced == 64 || forced == 128) && 32 * mi != forced) continue;
         const int64_t bm = 32 * mi;
         const int64_t blocks = tiles * ((M + bm - 1) / bm);
-        const int64_t slots = 256 * (int64_t)fwd_blocks_per_cu(p.mode, x_dtype, w0.scale_f16, spc, mi);
+        const int64_t slots = 256 * (int64_t)fwd_blocks_per_cu(p.mode, x_dtype, w0.scale_f16, spc, mi, cw);
         // a 64-row block does half the MFMA work of a 128-row one per chunk but unpacks as many
         // codes.  Tuned on input sets rotated past the 256 MB Infinity Cache (sweeps on cache-warm
-        // inputs favour other split counts).
-        const double chunk_us = mi == 4 ? 2.0 : 1.3;
+        // inputs favour other split counts).  The model counts 64-column chunks: a 128-column
+        // chunk costs two, and the pipeline fill stays two 64-column chunks.
+        const double chunk_us = (mi == 4 ? 2.0 : 1.3) * (double)(cw / kCK);
         double cost = 0;
-        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost, force_splits);
+        const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost, force_splits,
+                                       2.0 * kCK / cw);
         if (cost < best - 1e-9) {
             best = cost;
             p.mi = mi;
@@ -750,7 +802,8 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     const int spc = fwd_spc(w0.gs);
     if (spc == 4 && mode != kModeFold) return hipErrorInvalidValue;
     if ((plan.mi != 4 && plan.mi != 2) || (plan.mi == 4 && mode == kModeSplit)) return hipErrorInvalidValue;
-    const int64_t n_chunks = (w0.K + kCK - 1) / kCK;
+    const int cw = fwd_chunk_cols(mode, w0.gs);
+    const int64_t n_chunks = (w0.K + cw - 1) / cw;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);
     const int64_t bm = 32 * plan.mi;
     const int64_t mtiles = (M + bm - 1) / bm;
@@ -775,10 +828,13 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
         a.xcd_g = 8;
         a.xcd_cols = npad_total / 2 >= M * esize;
     }
-    const bool rg = !x_fast || (K % kCK) != 0;
-    dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, rg, [&](auto kern) {
+    const bool rg = !x_fast || (K % cw) != 0;
+    bool launched = false;
+    dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, rg, cw, [&](auto kern) {
         hipLaunchKernelGGL(kern, g, dim3(64 * kWaves), 0, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
+        launched = true;
     });
+    if (!launched) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
     const float* ys[3];

@@ -101,11 +101,12 @@ struct FwdPlan {
 FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, int64_t M, int force_rows = 0,
                       int force_splits = 0);
 // Contraction splits for an MFMA GEMM of `blocks` output blocks, `slots` of which run at once,
-// n_chunks 64-wide contraction chunks of ~chunk_us each and an M x width fp32 output; the
-// modelled time (microseconds) goes to *cost when cost is not null; force_splits > 0 pins the
-// split count (clamped to the chunks and rounded to one without empty splits).
+// n_chunks contraction chunks of ~chunk_us each (plus `fill` chunks of pipeline fill and
+// epilogue per block) and an M x width fp32 output; the modelled time (microseconds) goes to
+// *cost when cost is not null; force_splits > 0 pins the split count (clamped to the chunks and
+// rounded to one without empty splits).
 int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width, int64_t slots = 256,
-                     double chunk_us = 2.0, double* cost = nullptr, int force_splits = 0);
+                     double chunk_us = 2.0, double* cost = nullptr, int force_splits = 0, double fill = 2.0);
 bool gemm_fwd_supported(const WView& w, int x_dtype, int fold_ok);
 hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
                            const FwdPlan& plan, float* ws, hipStream_t s);
