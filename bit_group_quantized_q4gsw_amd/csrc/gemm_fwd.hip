@@ -134,8 +134,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
                                                           int64_t split_stride) {
     static_assert(MI == 2 || MI == 4, "32-row MFMA tiles per wave");
     static_assert(KD >= 2 && KD <= 6 && (XT != kF32 || KD == 2), "chunks in flight");
-    static_assert(CW == kCK || (CW == kCKWide && XT != kF32 && MODE == kModeGroup && SPC == 1),
-                  "128-column chunks: exact-code group mode with one group per chunk (gs == 128)");
+    static_assert(CW == kCK || (CW == kCKWide && XT != kF32 &&
+                                ((MODE == kModeGroup && SPC == 1) || (MODE == kModeFold && SF == 1))),
+                  "128-column chunks: exact-code group mode with one group per chunk (gs == 128), or fold mode");
     constexpr int kSteps = CW / 16;                       // MFMA steps per chunk
     constexpr int kRowBytes = 2 * CW;                     // one activation row (or bf16 plane row) of a chunk
     constexpr int kSlots = CW / 8;                        // 16-byte k-octet slots per row
@@ -150,11 +151,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     constexpr int kPlanes = kX16 ? 1 : 2;
     constexpr int kRowsPerDma = 1024 / kRowBytes;         // activation rows of one 16-bit DMA
     constexpr int kADma = kX16 ? kRowsPerWave / kRowsPerDma : 0;   // activation DMAs per wave per chunk
-    // Scales: with one or two groups per chunk (SPC <= 2) wave 0 fetches the block's 256 rows
-    // in kSDma0 16-byte-per-lane DMAs; with a group per k-octet pair (SPC == 4) every wave
-    // fetches its own rows, 4 bytes per lane.
-    constexpr bool kBlockScales = SPC <= 2;
-    constexpr int kSDma0 = SF ? 1 : SPC;                  // block scale DMAs of wave 0 per chunk
+    // Scales: a slot covers kSlotCols columns (SPC slots per chunk).  With slots of 32 columns or
+    // more (SPC <= 2, or any SPC in 128-column chunks) wave 0 fetches the block's 256 rows in
+    // kSDma0 16-byte-per-lane DMAs; with a slot per 16 columns (SPC == 4 in 64-column chunks)
+    // every wave fetches its own rows, 4 bytes per lane.
+    constexpr int kSlotCols = CW / SPC;
+    constexpr bool kBlockScales = kSlotCols >= 32;
+    constexpr int kSDma0 = SF ? (SPC > 2 ? SPC / 2 : 1) : SPC;   // block scale DMAs of wave 0 per chunk
     constexpr int kSDma = kBlockScales ? 0 : SPC;         // scale DMAs of every wave per chunk
     constexpr int kDmaPerChunk = kADma + kCDma + kSDma;
     constexpr int kDmaPerChunk0 = kDmaPerChunk + (kBlockScales ? kSDma0 : 0);   // wave 0
@@ -244,8 +247,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
                     // fp16 with SPC == 1: lanes 32..63 repeat lanes 0..31
                     int o, q, half;
                     if constexpr (SF) {
-                        o = (lane / SPC) & 31;
-                        q = lane % SPC;
+                        const int P = 64 * i + lane;
+                        o = (P / SPC) & 31;
+                        q = P % SPC;
                         half = 0;
                     } else {
                         const int P = 32 * i + (lane >> 1);
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
                         q = P % SPC;
                         half = lane & 1;
                     }
-                    const int64_t g = (int64_t)((kc + 32u * (uint32_t)q) / ug);
+                    const int64_t g = (int64_t)((kc + (uint32_t)kSlotCols * (uint32_t)q) / ug);
                     const int64_t oct = min(boct + o, n_octs - 1);   // rows past n_pad: a valid octet
                     const int64_t idx = (oct * seg.g_pad + g) * 8;
                     const uint8_t* src = SF ? sptr + 2 * idx : sptr + 4 * idx + 16 * half;
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     // B fragment of step t from the lane's code word (row n0 + j).
     auto dequant = [&](uint32_t bw, const uint8_t* S, int t, u4& b) {
         if constexpr (MODE == kModeFold) {
-            const h2 sc = bitcast<h2>(fold_scale(S, (t * SPC) / 4));
+            const h2 sc = bitcast<h2>(fold_scale(S, (t * SPC) / kSteps));
             uint32_t p[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) p[s] = bitcast<uint32_t>(codes_minus8_f16(bw, s) * sc);
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     // carries per-word values from piece 0 to the later pieces.
     auto dequant_piece = [&](uint32_t w, const uint8_t* S, int t, u4& b, int e, uint32_t (&wpre)[2]) {
         if constexpr (MODE == kModeFold) {
-            if (e == 0) wpre[0] = fold_scale(S, (t * SPC) / 4);
+            if (e == 0) wpre[0] = fold_scale(S, (t * SPC) / kSteps);
             b[e] = bitcast<uint32_t>(codes_minus8_f16(w, e) * bitcast<h2>(wpre[0]));
         } else if constexpr (XT == kF16) {
             b[e] = bitcast<uint32_t>(codes_minus8_f16(w, e));
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
                 if constexpr (t < kSteps - 1) dequant_piece(bw[t + 1], S, t + 1, b[(t + 1) & 1], e, wpre);
                 if (e % kPer == kPer - 1) __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (KIND != 0) gopen = group_scale(S, SPC == 2 ? (t >> 1) : 0);
+            if constexpr (KIND != 0) gopen = group_scale(S, (t * SPC) / kSteps);
         };
         typedef std::integral_constant<int, 0> A0;
         one(std::integral_constant<int, 0>{}, k0);
@@ -618,7 +622,10 @@ bool gemm_fwd_supported(const WView& w, int x_dtype, int fold_ok) {
     return w.gs % 64 == 0 || w.gs == 32;
 }
 
-static int fwd_spc(int64_t gs) {
+// Scale slots per chunk of cw columns: one per group that fits a chunk, one per 16 columns for
+// fold-mode groups of 8..24 columns (64-column chunks only).
+static int fwd_spc(int64_t gs, int cw) {
+    if (cw == kCKWide) return gs % 128 == 0 ? 1 : gs % 64 == 0 ? 2 : 4;
     if (gs % 64 == 0) return 1;
     if (gs % 32 == 0) return 2;
     return 4;
@@ -627,8 +634,13 @@ static int fwd_spc(int64_t gs) {
 // K columns per chunk: 128 for the exact-code group mode with gs == 128, where every 128-column
 // chunk is one group (measured on a replica of the chunk loop: 1849 against 2383 cycles per 64
 // columns, the 64-column loop paying a copy of every partial sum where its two chunk kinds
-// meet), else 64.
-static int fwd_chunk_cols(int mode, int64_t gs) { return (mode == kModeGroup && gs == kCKWide) ? kCKWide : kCK; }
+// meet), and for the fold mode with gs % 32 == 0 (half the waits and barriers per column);
+// else 64.
+static int fwd_chunk_cols(int mode, int64_t gs) {
+    if (mode == kModeGroup && gs == kCKWide) return kCKWide;
+    if (mode == kModeFold && gs % 32 == 0) return kCKWide;
+    return kCK;
+}
 
 // Split count minimising a time model (microseconds): rounds of blocks over the CU slots times
 // (chunks per split + fill for pipeline fill and epilogue) at chunk_us per chunk, plus, with splits,
@@ -669,6 +681,10 @@ static void with_spc(int spc, int cw, F&& f) {
     if (cw == kCKWide) {
         if constexpr (MODE == kModeGroup) {
             if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide>);
+        } else if constexpr (MODE == kModeFold) {
+            if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide>);
+            else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD, RG, kCKWide>);
+            else f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD, RG, kCKWide>);
         }
         return;
     }
@@ -740,7 +756,7 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
     }
     const int cw = fwd_chunk_cols(p.mode, w0.gs);
     const int64_t n_chunks = (w0.K + cw - 1) / cw;
-    const int spc = fwd_spc(w0.gs);
+    const int spc = fwd_spc(w0.gs, cw);
     double best = 1e300;
     const int forced = force_rows;
     for (int mi : {4, 2}) {
@@ -799,10 +815,10 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
     a.g_pad = w0.g_pad;
     a.ntn = npad_total / 32;
     const int mode = plan.mode;
-    const int spc = fwd_spc(w0.gs);
+    const int cw = fwd_chunk_cols(mode, w0.gs);
+    const int spc = fwd_spc(w0.gs, cw);
     if (spc == 4 && mode != kModeFold) return hipErrorInvalidValue;
     if ((plan.mi != 4 && plan.mi != 2) || (plan.mi == 4 && mode == kModeSplit)) return hipErrorInvalidValue;
-    const int cw = fwd_chunk_cols(mode, w0.gs);
     const int64_t n_chunks = (w0.K + cw - 1) / cw;
     const int per = (int)((n_chunks + plan.splits - 1) / plan.splits);
     const int64_t bm = 32 * plan.mi;
