@@ -363,7 +363,7 @@ def test_noalloc_forward_validation(q):
     assert f(ctypes.byref(d), x, q.F16, 0, y, None) == E_SHAPE
     assert f(ctypes.byref(d), x, 7, 4, y, None) == E_DTYPE
     assert f(ctypes.byref(d), x, q.F16, 4, x + 64, None) == E_ALIAS
-    pre = fake_desc(q, 2048, 8192, 128, 1, flags=1)
+    pre = fake_desc(q, 2048, 8192, 64, 1, flags=1)    # a prefill-like weight the planner splits K for
     need = ctypes.c_uint64()
     assert lib.q4gsw_workspace_bytes(q.OP_FWD, ctypes.byref(pre), 1536, q.BF16, ctypes.byref(need)) == S_OK
     assert need.value > 32 << 20
