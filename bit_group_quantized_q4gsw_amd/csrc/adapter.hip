@@ -673,13 +673,19 @@ uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank) {
     return bwd_ws(nullptr, M, N, K, rank).bytes;
 }
 
-hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
-                                    const float* B, int rank, float alpha, float* y, float* t, void* ws,
-                                    hipStream_t s) {
-    float* P = static_cast<float*>(ws);
-    hipError_t e = launch_row_partial<0>(x, x_dtype, M, K, A, rank, P, s);
-    if (e != hipSuccess) return e;
-    return launch_expand<1>(y, M, N, P, row_chunks(K, rank), B, rank, alpha, t, s);
+hipError_t launch_adapter_fwd_t(const void* x, int x_dtype, int64_t M, int64_t K, const float* A, int rank, void* ws,
+                                hipStream_t s) {
+    return launch_row_partial<0>(x, x_dtype, M, K, A, rank, static_cast<float*>(ws), s);
+}
+
+LowRankEpi adapter_fwd_epi(int64_t M, int64_t K, const float* B, int rank, float alpha, float* t, void* ws) {
+    (void)M;
+    return LowRankEpi{static_cast<const float*>(ws), row_chunks(K, rank), B, t, alpha, rank, 1};
+}
+
+hipError_t launch_adapter_fwd_expand(float* y, int64_t M, int64_t N, int64_t K, const float* B, int rank, float alpha,
+                                     float* t, void* ws, hipStream_t s) {
+    return launch_expand<1>(y, M, N, static_cast<const float*>(ws), row_chunks(K, rank), B, rank, alpha, t, s);
 }
 
 hipError_t launch_adapter_bwd_u(const void* d_out, int dtype, int64_t M, int64_t N, int64_t K, const float* B,

@@ -208,8 +208,12 @@ uint64_t qkv_ws_bytes(const q4gsw_weight* const w[3], int64_t M, int32_t dt, int
 
 q4gsw_status hip_status(hipError_t e) { return e == hipSuccess ? Q4GSW_OK : Q4GSW_E_HIP; }
 
+// epi: a low-rank term the MFMA route adds in its reduction or epilogue; *epi_done tells whether
+// this call applied it (the other routes leave it to the caller).
 q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M, float* y, void* ws,
-                     int32_t route, const Opts& o, hipStream_t s) {
+                     int32_t route, const Opts& o, hipStream_t s, const LowRankEpi* epi = nullptr,
+                     bool* epi_done = nullptr) {
+    if (epi_done) *epi_done = false;
     const WView v = view_of(w);
     switch (route) {
         case Q4GSW_ROUTE_GENERIC: return hip_status(launch_generic_fwd(v, x, dt, M, y, s));
@@ -224,7 +228,7 @@ q4gsw_status run_fwd(const q4gsw_weight* w, const void* x, int32_t dt, int64_t M
         default: {
             FwdSeg seg{v, y};
             const FwdPlan plan = plan_gemm_fwd(&seg, 1, dt, fold_ok(w), M, o.rows, o.splits);
-            return hip_status(launch_gemm_fwd(&seg, 1, x, dt, M, plan, static_cast<float*>(ws), s));
+            return hip_status(launch_gemm_fwd(&seg, 1, x, dt, M, plan, static_cast<float*>(ws), s, epi, epi_done));
         }
     }
 }
@@ -649,9 +653,13 @@ q4gsw_status q4gsw_adapter_fwd(const q4gsw_weight* w, const void* x, int32_t x_d
         overlap(tr, br) || overlap(tr, wr) || overlap(sr, tr) || overlap(sr, ar) || overlap(sr, br))
         return Q4GSW_E_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = run_fwd(w, x, x_dtype, M, y, ws, route, o, s)) != Q4GSW_OK) return st;
-    return hip_status(launch_adapter_fwd_terms(x, x_dtype, M, w->N, w->K, A, B, rank, alpha, y, t,
-                                               static_cast<uint8_t*>(ws) + base, s));
+    void* tws = static_cast<uint8_t*>(ws) + base;
+    if ((st = hip_status(launch_adapter_fwd_t(x, x_dtype, M, w->K, A, rank, tws, s))) != Q4GSW_OK) return st;
+    const LowRankEpi epi = adapter_fwd_epi(M, w->K, B, rank, alpha, t, tws);
+    bool done = false;
+    if ((st = run_fwd(w, x, x_dtype, M, y, ws, route, o, s, &epi, &done)) != Q4GSW_OK) return st;
+    if (done) return Q4GSW_OK;
+    return hip_status(launch_adapter_fwd_expand(y, M, w->N, w->K, B, rank, alpha, t, tws, s));
 }
 
 q4gsw_status q4gsw_adapter_bwd(const q4gsw_weight* w, const void* x, const void* d_out, int32_t dtype, int64_t M,

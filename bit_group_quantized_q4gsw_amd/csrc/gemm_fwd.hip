@@ -73,6 +73,9 @@ struct FwdSegArgs {
     // row tiles.  xcd_g = 1: row tile, then column tile, after the split index.
     int xcd_g;
     int xcd_cols;
+    // low-rank term of a one-split, one-segment launch (P == nullptr: none): y += alpha t G^T with
+    // G = lr.G [N, rank] and t from its column-chunk partials, as the adapter's expansion does it
+    LowRankEpi lr;
 };
 
 // bf16 pair (16 (c_lo - 8), 16 (c_hi - 8)) for the four MFMA dwords of a code word.  H holds
@@ -126,8 +129,8 @@ __device__ __forceinline__ int a_swizzle(int r) {
 // RG: the activation may be ragged (K % CW != 0) or not 16-byte aligned, so chunks can take the
 // synchronous fallback; the aligned instance carries no fallback code (and none of its live
 // values across the chunk loop).  CW: K columns per chunk, 64, or 128 for the exact-code group
-// mode with gs == 128.
-template <int XT, int MODE, int SPC, int SF, int MI, int KD, bool RG, int CW>
+// mode with gs == 128.  LR: the one-split epilogue adds the low-rank term seg.lr.
+template <int XT, int MODE, int SPC, int SF, int MI, int KD, bool RG, int CW, bool LR = false>
 __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const void* __restrict__ x, int64_t M,
                                                           int64_t K, int64_t k_pad, int64_t gs, int x_fast,
                                                           int chunks_per_split, int splits, int mtiles,
@@ -583,6 +586,27 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     }
 
     // ---------------- epilogue: lane holds D[8 (r/4) + 4 h + r%4][j] of each 32x32 tile ----------------
+    // Low-rank term (one split): every wave, idle ones too, stages the block's rows of alpha t, with
+    // t[m, j] = sum_s P[(s M + m) rank + j] (chunks in order, zero past M and rank), in the ring's
+    // LDS in rows of RP = rank rounded up to 2; the first column tile writes t out.
+    const int RP = LR ? (seg.lr.rank + 1) & ~1 : 0;
+    const float* Tl = reinterpret_cast<const float*>(smem);
+    if constexpr (LR) {
+        __syncthreads();                                   // every wave is done with the ring
+        float* Tw = reinterpret_cast<float*>(smem);
+        const int rank = seg.lr.rank;
+        for (int i = tid; i < kBM * RP; i += 64 * kWaves) {
+            const int r = i / RP, jj = i - r * RP;
+            const int64_t m = m0 + r;
+            float v = 0.0f;
+            if (m < M && jj < rank) {
+                v = chunk_sum<8>(seg.lr.P, seg.lr.chunks, M * rank, m * rank + jj);
+                if (seg.lr.Tout && tile == 0) seg.lr.Tout[m * rank + jj] = v;
+            }
+            Tw[i] = seg.lr.alpha * v;
+        }
+        __syncthreads();
+    }
     if (!wave_active) return;
     if (split_stride) {
         // split partials in the fragment layout: four 16-byte stores per lane and tile, streamed
@@ -605,6 +629,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
     const int64_t brow = n0 + j;
     float* out = seg.out[sg];
     const int64_t ld = seg.out_ld[sg];
+    if constexpr (LR) {
+        // acc += (alpha t) G^T on the matrix cores, two ranks per v_mfma_f32_32x32x2_f32: lane l
+        // holds A[l % 32][l / 32] (row 32 mi + j of alpha t, rank 2 jp + h) and B[l / 32][l % 32]
+        // (G[brow, 2 jp + h]); the result lands in the accumulator layout.  Every lane takes part.
+        const int rank = seg.lr.rank;
+        const bool col_ok = brow < seg.N[sg];
+        for (int jp = 0; jp < RP / 2; ++jp) {
+            const int jr = 2 * jp + h;
+            const float b = load_sel(seg.lr.G, brow * rank + jr, col_ok && jr < rank);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                acc[mi] = __builtin_amdgcn_mfma_f32_32x32x2f32(Tl[(32 * mi + j) * RP + jr], b, acc[mi], 0, 0, 0);
+        }
+    }
     if (brow >= seg.N[sg]) return;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -676,50 +714,58 @@ int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width,
 // Kernel instance for (activation type, mode, scale slots, scale type, row tiles, fallback, chunk
 // columns), handed to f; a combination without an instance hands nothing.
 template <int XT, int MODE, int SF, int MI, bool RG, typename F>
-static void with_spc(int spc, int cw, F&& f) {
+static void with_spc(int spc, int cw, bool lr, F&& f) {
     constexpr int KD = XT == kF32 ? 2 : kDepth16;
     if (cw == kCKWide) {
         if constexpr (MODE == kModeGroup) {
-            if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide>);
+            if (spc == 1) {
+                if (!lr) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide>);
+                else if constexpr (SF == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide, true>);
+            }
         } else if constexpr (MODE == kModeFold) {
+            if (lr) return;
             if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCKWide>);
             else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD, RG, kCKWide>);
             else f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD, RG, kCKWide>);
         }
         return;
     }
+    if (lr) return;
     if (spc == 1) f(gemm_fwd_kernel<XT, MODE, 1, SF, MI, KD, RG, kCK>);
     else if (spc == 2) f(gemm_fwd_kernel<XT, MODE, 2, SF, MI, KD, RG, kCK>);
     else if constexpr (MODE == kModeFold) f(gemm_fwd_kernel<XT, MODE, 4, SF, MI, KD, RG, kCK>);
 }
 template <int XT, int MODE, int SF, typename F>
-static void with_mi(int mi, int spc, bool rg, int cw, F&& f) {
+static void with_mi(int mi, int spc, bool rg, int cw, bool lr, F&& f) {
     if constexpr (MODE == kModeSplit) {
         // 64-row tiles only (see plan_gemm_fwd)
         (void)mi;
-        if (rg) with_spc<XT, MODE, SF, 2, true>(spc, cw, f);
-        else with_spc<XT, MODE, SF, 2, false>(spc, cw, f);
+        if (rg) with_spc<XT, MODE, SF, 2, true>(spc, cw, lr, f);
+        else with_spc<XT, MODE, SF, 2, false>(spc, cw, lr, f);
     } else if (rg) {
-        if (mi == 4) with_spc<XT, MODE, SF, 4, true>(spc, cw, f);
-        else with_spc<XT, MODE, SF, 2, true>(spc, cw, f);
+        if (mi == 4) with_spc<XT, MODE, SF, 4, true>(spc, cw, lr, f);
+        else with_spc<XT, MODE, SF, 2, true>(spc, cw, lr, f);
     } else {
-        if (mi == 4) with_spc<XT, MODE, SF, 4, false>(spc, cw, f);
-        else with_spc<XT, MODE, SF, 2, false>(spc, cw, f);
+        if (mi == 4) with_spc<XT, MODE, SF, 4, false>(spc, cw, lr, f);
+        else with_spc<XT, MODE, SF, 2, false>(spc, cw, lr, f);
     }
 }
+// lr: the instance with the low-rank epilogue (exact-code group mode, 128-column chunks, fp16
+// scales; any other combination hands nothing)
 template <typename F>
-static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, bool rg, int cw, F&& f) {
+static void dispatch_fwd(int mode, int x_dtype, int scale_f16, int spc, int mi, bool rg, int cw, F&& f,
+                         bool lr = false) {
     if (mode == kModeFold) {
-        with_mi<kF16, kModeFold, 1>(mi, spc, rg, cw, f);
+        with_mi<kF16, kModeFold, 1>(mi, spc, rg, cw, lr, f);
     } else if (mode == kModeSplit) {
-        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, rg, cw, f);
-        else with_mi<kF32, kModeSplit, 0>(mi, spc, rg, cw, f);
+        if (scale_f16) with_mi<kF32, kModeSplit, 1>(mi, spc, rg, cw, lr, f);
+        else with_mi<kF32, kModeSplit, 0>(mi, spc, rg, cw, lr, f);
     } else if (x_dtype == kF16) {
-        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, rg, cw, f);
-        else with_mi<kF16, kModeGroup, 0>(mi, spc, rg, cw, f);
+        if (scale_f16) with_mi<kF16, kModeGroup, 1>(mi, spc, rg, cw, lr, f);
+        else with_mi<kF16, kModeGroup, 0>(mi, spc, rg, cw, lr, f);
     } else {
-        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, rg, cw, f);
-        else with_mi<kBF16, kModeGroup, 0>(mi, spc, rg, cw, f);
+        if (scale_f16) with_mi<kBF16, kModeGroup, 1>(mi, spc, rg, cw, lr, f);
+        else with_mi<kBF16, kModeGroup, 0>(mi, spc, rg, cw, lr, f);
     }
 }
 
@@ -791,7 +837,8 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
 // One launch over every segment.  With K splits the partials go to ws as splits planes in the
 // fragment layout over the columns of all segments (segment i from column sum_{j<i} n_pad_j on).
 hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
-                           const FwdPlan& plan, float* ws, hipStream_t s) {
+                           const FwdPlan& plan, float* ws, hipStream_t s, const LowRankEpi* lr, bool* lr_done) {
+    if (lr_done) *lr_done = false;
     const WView& w0 = segs[0].w;
     FwdSegArgs a{};
     a.nseg = nseg;
@@ -847,15 +894,24 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
         a.xcd_g = 8;
         a.xcd_cols = npad_total / 2 >= M * esize;
     }
+    if (lr && nseg != 1) return hipErrorInvalidValue;
     const bool rg = !x_fast || (K % cw) != 0;
+    // one split: the low-rank term goes into the epilogue where an instance carries it
+    bool in_kernel = false;
+    if (lr && plan.splits == 1) {
+        dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, rg, cw, [&](auto) { in_kernel = true; }, true);
+        if (in_kernel) a.lr = *lr;
+    }
     bool launched = false;
     dispatch_fwd(mode, x_dtype, w0.scale_f16, spc, plan.mi, rg, cw, [&](auto kern) {
         hipLaunchKernelGGL(kern, g, dim3(64 * kWaves), 0, s, a, x, M, K, kp, gs, x_fast, per, sp, mt, st);
         launched = true;
-    });
+    }, in_kernel);
     if (!launched) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && in_kernel && lr_done) *lr_done = true;
     if (e != hipSuccess || plan.splits == 1) return e;
+    if (lr && lr_done) *lr_done = true;
     const float* ys[3];
     int64_t yld[3], off[3], cols[3];
     int64_t o = 0;
@@ -866,7 +922,7 @@ hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dt
         cols[i] = segs[i].w.N;
         o += segs[i].w.n_pad;
     }
-    return launch_reduce_frags(ws, plan.splits, M, npad_total, ys, yld, off, cols, nseg, 0, s);
+    return launch_reduce_frags(ws, plan.splits, M, npad_total, ys, yld, off, cols, nseg, 0, s, lr);
 }
 
 }  // namespace q4gsw

@@ -59,7 +59,7 @@ hipError_t launch_reduce_segments(const float* ws, int splits, int64_t M, int64_
 // 4 (64 r4 + L) + q, so a wave stores a tile with four 16-byte-per-lane writes.  The reduction
 // writes y[i][m][c] = sum_s for the tile columns of segment i (off[i] multiples of 32).
 inline int64_t frag_plane_floats(int64_t M, int64_t width) { return (M + 31) / 32 * 32 * width; }
-// Optional low-rank term of a one-segment reduction (the adapter's input gradient):
+// Optional low-rank term of a one-segment reduction (the adapter's forward and input gradient):
 // y[m, c] = (sum of the splits) then += alpha sum_j T[m, j] G(j, c), with T[m, j] = sum_s
 // P[(s M + m) r + j] over `chunks` partials in order (written to Tout once when Tout is set) and
 // G(j, c) = G[j C + c] (gt 0) or G[c r + j] (gt 1), C the segment's columns; the same fp32
@@ -108,8 +108,13 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
 int pick_gemm_splits(int64_t blocks, int64_t n_chunks, int64_t M, int64_t width, int64_t slots = 256,
                      double chunk_us = 2.0, double* cost = nullptr, int force_splits = 0, double fill = 2.0);
 bool gemm_fwd_supported(const WView& w, int x_dtype, int fold_ok);
+// lr (one segment only): the low-rank term of LowRankEpi, added in the split reduction (the same
+// operations in the same order as the separate expansion) or, with one split, by the exact-code
+// group instances with 128-column chunks and fp16 scales in their epilogue (fp32 MFMAs into the
+// accumulators); *lr_done tells whether this launch applied it.
 hipError_t launch_gemm_fwd(const FwdSeg* segs, int nseg, const void* x, int x_dtype, int64_t M,
-                           const FwdPlan& plan, float* ws, hipStream_t s);
+                           const FwdPlan& plan, float* ws, hipStream_t s, const LowRankEpi* lr = nullptr,
+                           bool* lr_done = nullptr);
 
 // MFMA input gradient: gemm_bwd2.hip (32x32x16) dispatches, gemm_bwd.hip (16x16x32) covers
 // the group sizes the former does not take.
@@ -156,9 +161,14 @@ int adapter_rank_max();
 bool adapter_shape_ok(int64_t M, int64_t N, int64_t K, int rank);
 uint64_t adapter_fwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank);
 uint64_t adapter_bwd_terms_ws_bytes(int64_t M, int64_t N, int64_t K, int rank);
-hipError_t launch_adapter_fwd_terms(const void* x, int x_dtype, int64_t M, int64_t N, int64_t K, const float* A,
-                                    const float* B, int rank, float alpha, float* y, float* t, void* ws,
-                                    hipStream_t s);
+// Forward: launch_adapter_fwd_t (the column-chunk partials of t = x A^T, before the GEMM), the
+// GEMM, which takes adapter_fwd_epi (y += alpha t B^T, t written) when it runs on the MFMA route,
+// else launch_adapter_fwd_expand after it.
+hipError_t launch_adapter_fwd_t(const void* x, int x_dtype, int64_t M, int64_t K, const float* A, int rank, void* ws,
+                                hipStream_t s);
+LowRankEpi adapter_fwd_epi(int64_t M, int64_t K, const float* B, int rank, float alpha, float* t, void* ws);
+hipError_t launch_adapter_fwd_expand(float* y, int64_t M, int64_t N, int64_t K, const float* B, int rank, float alpha,
+                                     float* t, void* ws, hipStream_t s);
 hipError_t launch_adapter_bwd_u(const void* d_out, int dtype, int64_t M, int64_t N, int64_t K, const float* B,
                                 int rank, void* ws, hipStream_t s);
 LowRankEpi adapter_bwd_epi(int64_t M, int64_t N, int64_t K, const float* A, int rank, float alpha, void* ws);
