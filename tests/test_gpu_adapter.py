@@ -7,7 +7,9 @@ The low-rank terms run in fp32 with a fixed summation order:
   * t = x A^T, u = d_out B over C columns: each lane adds at most 32 products in order, a
     64-lane tree adds 6 levels and the column chunks (at most C / 256) are added in order:
     a chain of at most C / 256 + 40 roundings;
-  * y += alpha t B^T, d_x += alpha u A: r products in order, then one fma: r + 2 more;
+  * y += alpha t B^T, d_x += alpha u A: r products in order, then one fma: r + 2 more (the
+    one-split forward adds them in its GEMM epilogue on fp32 MFMAs: alpha t rounded once, then r
+    products onto the accumulator, r + 1);
   * d_A = alpha u^T x, d_B = alpha d_out^T t: each wave adds a quarter of a slab's rows in
     order, the 4 waves are added in order, then at most 64 slabs and alpha: at most
     M / 4 + 70 roundings, on top of the error of u or t.
@@ -97,6 +99,35 @@ def test_adapter_parity(M, N, K, gs, act, sdt, r, alpha):
     assert_within(dx, g["dx"], g["r_dx"], tol_dx(case, r), "d_x")
     assert_within(dA, g["dA"], g["r_dA"], tol_dA(case), "d_A")
     assert_within(dB, g["dB"], g["r_dB"], tol_dB(case), "d_B")
+
+
+# Forward shapes whose GEMM plans one K split (K = 128 is one chunk) on the exact-code group route
+# with 128-column chunks (bf16 x, fp16 scales, gs 128): the low-rank term goes through the GEMM's
+# epilogue.  Rows past M, columns past N (inside a wave and whole idle waves), odd rank, rank 1
+# and the largest rank.
+EPI_CASES = [
+    # M, N, K, rank, alpha
+    (70, 300, 128, 33, 1.0),
+    (130, 520, 128, 64, -0.5),
+    (257, 96, 128, 1, 2.0),
+    (64, 256, 128, 16, 0.25),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha", EPI_CASES)
+def test_adapter_fwd_epilogue(M, N, K, r, alpha):
+    q = lib()
+    case = make_adapter(M, K, N, 128, "bf16", "f16", r, seed=7 * M + N + r)
+    print(f"adapter forward epilogue M={M} N={N} K={K} r={r}", flush=True)
+    pw = pack(q, case.w)
+    pl = q.plan(q.OP_FWD, pw, M, case.x.dtype)
+    assert pl["route"] == "gemm_group" and pl["splits"] == 1, pl
+    y, t = q.adapter_fwd(pw, dev(case.x), dev(case.A), dev(case.B), alpha)
+    torch.cuda.synchronize()
+    w = case.w
+    oy, ot, ry = O.lora_fwd(case.x, w.codes, w.scales, 128, case.A, case.B, alpha, threads=THREADS)
+    assert_within(y, oy, ry, tol_y(case, r), "y")
+    assert_within(t, ot, t_norm(case.x, case.A), contract_chain(K) * U, "t")
 
 
 def _offset_copy(t):
