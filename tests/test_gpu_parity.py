@@ -220,6 +220,35 @@ def test_forward_tiles(M, N, K, gs, act, sdt, rows):
     assert_within(y, ref, norm, TOL[case.x.dtype], f"fwd tile {rows} route={q.route(q.OP_FWD, pw, M, case.x.dtype)}")
 
 
+# fp16 activations with foldable fp16 scales and gs % 32 == 0 run 128-column chunks: a last chunk
+# only partly inside K, two or four scale slots per chunk (gs 64, gs 96 with groups not aligned to
+# chunks) and a group across two chunks (gs 256), at both tile heights and with K splits.
+WIDE_FOLD_CASES = [
+    # M, N, K, gs
+    (70, 264, 320, 32),
+    (130, 300, 448, 64),
+    (64, 256, 576, 96),
+    (96, 520, 768, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K,gs", WIDE_FOLD_CASES)
+@pytest.mark.parametrize("rows,splits", [(64, 1), (128, 1), (64, 3)])
+def test_forward_fold_wide_chunks(M, N, K, gs, rows, splits):
+    q = lib()
+    case = make_linear(M, K, N, gs, "f16", "f16", seed=M * 13 + K + gs)
+    pw = pack(q, case.w)
+    x = dev(case.x)
+    ref, norm = oracle_fwd(case.x, case.w)
+    print(f"fold wide chunks M={M} N={N} K={K} gs={gs} rows={rows} splits={splits}", flush=True)
+    with q.forced_plan(tile_rows=rows, splits=splits):
+        info = q.plan(q.OP_FWD, pw, M, case.x.dtype)
+        assert info["route"] == "gemm_fold" and info["tile_rows"] == rows, info
+        y = q.linear_fwd(pw, x)
+        torch.cuda.synchronize()
+    assert_within(y, ref, norm, TOL[case.x.dtype], f"fwd fold gs={gs} K={K} rows={rows} splits={info['splits']}")
+
+
 @pytest.mark.parametrize("rows", [64, 128])
 def test_qkv_tiles(rows):
     q = lib()
