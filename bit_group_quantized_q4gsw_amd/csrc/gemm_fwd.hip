@@ -815,12 +815,14 @@ FwdPlan plan_gemm_fwd(const FwdSeg* segs, int nseg, int x_dtype, int fold_ok, in
         const int64_t slots = 256 * (int64_t)fwd_blocks_per_cu(p.mode, x_dtype, w0.scale_f16, spc, mi, cw);
         // a 64-row block does half the MFMA work of a 128-row one per chunk but unpacks as many
         // codes.  Tuned on input sets rotated past the 256 MB Infinity Cache (sweeps on cache-warm
-        // inputs favour other split counts).  128-column chunks: fitted to a sweep of row tiles and
-        // split counts on the prefill shape (M = 512, K = 8192, N = 2048, bf16), 1.75 and 1.15 us
-        // per chunk with one chunk of fill; the model then picks the measured best plan for that
-        // shape, the fused QKV at M = 128 and 512 and the MLP up projection.
+        // inputs favour other split counts).  128-column chunks: fitted to sweeps of row tiles and
+        // split counts, 1.75 us per chunk for 128-row tiles (prefill: M = 512, K = 8192, N = 2048,
+        // bf16) and 1.3 for 64-row tiles (prefill 1.10-1.21; the fused QKV at M = 128 runs 6 or 8
+        // splits 0.3-0.6 us faster than 4), with one chunk of fill; the model then picks the
+        // measured best plan for prefill, the fused QKV at M = 128 and 512 and the MLP up
+        // projection.
         const bool wide = cw == kCKWide;
-        const double chunk_us = wide ? (mi == 4 ? 1.75 : 1.15) : (mi == 4 ? 2.0 : 1.3);
+        const double chunk_us = wide ? (mi == 4 ? 1.75 : 1.3) : (mi == 4 ? 2.0 : 1.3);
         double cost = 0;
         const int s = pick_gemm_splits(blocks, n_chunks, M, npad_total, slots, chunk_us, &cost, force_splits,
                                        wide ? 1.0 : 2.0);
