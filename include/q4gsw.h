@@ -30,10 +30,12 @@
  *   - Outputs are fp32.  Activations may be fp32, fp16 or bf16; scales fp16 or
  *     fp32.  Accumulation is fp32.
  *   - No C++ exception crosses this interface.  Calls are independent: route and
- *     plan choices are per call (q4gsw_options), never process-wide.  The only
- *     state the library keeps is a cache of resident blocks per CU for each kernel
+ *     plan choices are per call (q4gsw_options), never process-wide.  The state
+ *     the library keeps: a cache of resident blocks per CU for each kernel
  *     instance (filled on first use from the HIP occupancy query, then read-only;
- *     a race between threads only repeats the same query).
+ *     a race between threads only repeats the same query), and, for
+ *     q4gsw_linear_fwd_noalloc, one scratch array per device with its address
+ *     (shared by every call of that entry point on the device; see there).
  */
 #ifndef Q4GSW_H
 #define Q4GSW_H
