@@ -426,11 +426,13 @@ __global__ __launch_bounds__(256) void column_partial_kernel(ColSeg a, ColSeg b,
         }
     }
     __syncthreads();
+    // thread i takes column (i % (64 CQ)) of the block and rank i / (64 CQ): consecutive threads
+    // store consecutive columns of the slab sums (d_A's rows likewise)
     for (int i = tid; i < CQ * R * 64; i += 256) {
-        const int l = i % 64, qj = i / 64, q = qj / R, j = qj % R;
+        const int cl = i % (64 * CQ), j = i / (64 * CQ), l = cl / CQ, q = cl % CQ;
         const int64_t cc = (bx * 64 + l) * CQ + q;
         if (j >= rank || cc >= C) continue;
-        const float v = red[i];
+        const float v = red[(q * R + j) * 64 + l];
         if (sg.slabs > 1) sg.Pc[(by * rank + j) * C + cc] = v;
         else if (sg.ot == 0) sg.O[(int64_t)j * C + cc] = alpha * v;
         else sg.O[cc * rank + j] = alpha * v;
