@@ -41,11 +41,16 @@ constexpr int64_t kMaxSlabs = 64;
 
 // Row contraction tiling for rank bucket R: RW rows per wave (4 waves), chunks of CC columns
 // (the F chunk, R x CC fp32, about 33 KB of LDS up to R = 32), NG column quads per lane.
-template <int R>
+// NARROW: 256-column chunks at every rank, for launches that the wide chunks would leave under
+// 256 blocks (t = x A^T at M = 512, K = 2048, r = 16: 128 blocks and 7.7 us wide; narrow, 256
+// blocks, the adapter forward is 2.3 us faster).  Launches of 256 blocks or more keep the wide
+// chunks: narrowing u = d_out B at N = 8192 (512 -> 1024 blocks, twice the partials to sum) made
+// the adapter backward 1.5 us slower.
+template <int R, bool NARROW = false>
 struct RowTile {
     static constexpr int RW = R >= 64 ? 1 : R >= 32 ? 2 : 4;
     static constexpr int ROWS = 4 * RW;
-    static constexpr int CC = R >= 32 ? 256 : 8192 / R;
+    static constexpr int CC = (NARROW || R >= 32) ? 256 : 8192 / R;
     static constexpr int NG = CC / 256;
     static constexpr int LD = CC + 4;     // LDS row stride: quads stay 16-B aligned, staging spreads banks
 };
@@ -132,11 +137,11 @@ __device__ __forceinline__ float wave_sum_spread(float (&v)[N], int lane) {
 // P[s, m, j] = sum_{c in chunk s} X[m, c] F(j, c) for X [M, C] (dtype XT); FT = 0: F(j, c) =
 // A[j C + c], FT = 1: F(j, c) = B[c r + j].  Block b: rows (b / chunks) ROWS .. (wave w: RW of
 // them), chunk b % chunks (lane l: column quads 4 l + 256 g).
-template <int XT, int R, int FT, bool VEC>
+template <int XT, int R, int FT, bool VEC, bool NARROW>
 __global__ __launch_bounds__(256) void row_partial_kernel(const void* __restrict__ X, int64_t M, int64_t C,
                                                           const float* __restrict__ F, int rank, int64_t chunks,
                                                           float* __restrict__ P) {
-    using T = RowTile<R>;
+    using T = RowTile<R, NARROW>;
     __shared__ __align__(16) float Fl[R * T::LD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t rb = blockIdx.x / chunks, s = blockIdx.x % chunks;
@@ -532,16 +537,27 @@ int es_of(int xt) { return xt == kF32 ? 4 : 2; }
 // rows of X (element size es) hold whole quads that start aligned
 bool quads_ok(const void* X, int64_t C, int es) { return C % 4 == 0 && aligned(X, 4 * (uintptr_t)es); }
 
-int64_t row_chunks(int64_t C, int rank) {
+// the narrow chunks when the wide ones leave the row contraction under 256 blocks
+bool row_narrow(int64_t M, int64_t C, int rank) {
+    int64_t rows = 0, cc = 0;
+    with_rank(rank, [&](auto rc) {
+        rows = RowTile<decltype(rc)::value>::ROWS;
+        cc = RowTile<decltype(rc)::value>::CC;
+    });
+    return cc > 256 && (M + rows - 1) / rows * ((C + cc - 1) / cc) < 256;
+}
+
+int64_t row_chunks(int64_t M, int64_t C, int rank) {
     int64_t cc = 0;
     with_rank(rank, [&](auto rc) { cc = RowTile<decltype(rc)::value>::CC; });
+    if (row_narrow(M, C, rank)) cc = 256;
     return (C + cc - 1) / cc;
 }
 
 int64_t row_blocks(int64_t M, int64_t C, int rank) {
     int64_t rows = 0;
     with_rank(rank, [&](auto rc) { rows = RowTile<decltype(rc)::value>::ROWS; });
-    return (M + rows - 1) / rows * row_chunks(C, rank);
+    return (M + rows - 1) / rows * row_chunks(M, C, rank);
 }
 
 int64_t lane_cols(int rank) {
@@ -567,7 +583,7 @@ Slabs column_slabs(int64_t M, int64_t C, int rank) {
 uint64_t up256(uint64_t b) { return (b + 255) / 256 * 256; }
 
 uint64_t row_partial_bytes(int64_t M, int64_t C, int rank) {
-    return up256((uint64_t)row_chunks(C, rank) * M * rank * 4);
+    return up256((uint64_t)row_chunks(M, C, rank) * M * rank * 4);
 }
 
 uint64_t column_partial_bytes(int64_t M, int64_t C, int rank) {
@@ -578,15 +594,17 @@ uint64_t column_partial_bytes(int64_t M, int64_t C, int rank) {
 template <int FT>
 hipError_t launch_row_partial(const void* X, int xt, int64_t M, int64_t C, const float* F, int rank, float* P,
                               hipStream_t s) {
-    const int64_t chunks = row_chunks(C, rank), blocks = row_blocks(M, C, rank);
+    const int64_t chunks = row_chunks(M, C, rank), blocks = row_blocks(M, C, rank);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     with_rank(rank, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
         with_xt(xt, [&](auto xc) {
             constexpr int XT = decltype(xc)::value;
             with_bool(quads_ok(X, C, es_of(XT)), [&](auto vc) {
-                hipLaunchKernelGGL((row_partial_kernel<XT, R, FT, decltype(vc)::value>), dim3((unsigned)blocks),
-                                   dim3(256), 0, s, X, M, C, F, rank, chunks, P);
+                with_bool(row_narrow(M, C, rank), [&](auto nc) {
+                    hipLaunchKernelGGL((row_partial_kernel<XT, R, FT, decltype(vc)::value, decltype(nc)::value>),
+                                       dim3((unsigned)blocks), dim3(256), 0, s, X, M, C, F, rank, chunks, P);
+                });
             });
         });
     });
@@ -681,13 +699,12 @@ hipError_t launch_adapter_fwd_t(const void* x, int x_dtype, int64_t M, int64_t K
 }
 
 LowRankEpi adapter_fwd_epi(int64_t M, int64_t K, const float* B, int rank, float alpha, float* t, void* ws) {
-    (void)M;
-    return LowRankEpi{static_cast<const float*>(ws), row_chunks(K, rank), B, t, alpha, rank, 1};
+    return LowRankEpi{static_cast<const float*>(ws), row_chunks(M, K, rank), B, t, alpha, rank, 1};
 }
 
 hipError_t launch_adapter_fwd_expand(float* y, int64_t M, int64_t N, int64_t K, const float* B, int rank, float alpha,
                                      float* t, void* ws, hipStream_t s) {
-    return launch_expand<1>(y, M, N, static_cast<const float*>(ws), row_chunks(K, rank), B, rank, alpha, t, s);
+    return launch_expand<1>(y, M, N, static_cast<const float*>(ws), row_chunks(M, K, rank), B, rank, alpha, t, s);
 }
 
 hipError_t launch_adapter_bwd_u(const void* d_out, int dtype, int64_t M, int64_t N, int64_t K, const float* B,
@@ -697,7 +714,7 @@ hipError_t launch_adapter_bwd_u(const void* d_out, int dtype, int64_t M, int64_t
 
 LowRankEpi adapter_bwd_epi(int64_t M, int64_t N, int64_t K, const float* A, int rank, float alpha, void* ws) {
     const BwdWs w = bwd_ws(ws, M, N, K, rank);
-    return LowRankEpi{w.P, row_chunks(N, rank), A, w.u, alpha, rank, 0};
+    return LowRankEpi{w.P, row_chunks(M, N, rank), A, w.u, alpha, rank, 0};
 }
 
 hipError_t launch_adapter_bwd_rest(const void* x, const void* d_out, int dtype, int64_t M, int64_t N, int64_t K,
@@ -705,7 +722,7 @@ hipError_t launch_adapter_bwd_rest(const void* x, const void* d_out, int dtype, 
                                    float* d_A, float* d_B, void* ws, hipStream_t s) {
     const BwdWs w = bwd_ws(ws, M, N, K, rank);
     hipError_t e = hipSuccess;
-    if (!dx_done) e = launch_expand<0>(d_x, M, K, w.P, row_chunks(N, rank), A, rank, alpha, w.u, s);
+    if (!dx_done) e = launch_expand<0>(d_x, M, K, w.P, row_chunks(M, N, rank), A, rank, alpha, w.u, s);
     if (e != hipSuccess) return e;
     const int es = es_of(dtype);
     const ColSeg a = column_seg(x, M, K, w.u, rank, d_A, w.PcA, 0);
