@@ -32,7 +32,7 @@
 // Precision routes (all with fp32 accumulation):
 //   kModeFold  (fp16 x, fp16 scales checked foldable at pack time):
 //       B = fp16((code - 8) * scale), one rounding, |err| <= 2^-11 |w|.
-//   kModeGroup (fp16 or bf16 x): B = code - 8 held exactly (fp16, or bf16 of 16 (code - 8))
+//   kModeGroup (fp16 or bf16 x): B = code - 8 held exactly (fp16, or bf16 of (code - 8) / 16)
 //       and the scale multiplies the fp32 partial sum of each scale group, which the MFMAs
 //       build in a separate set of accumulators.
 //   kModeSplit (fp32 x): x = hi + lo in bf16 (|err| <= 2^-18 |x|), two MFMA passes
@@ -78,29 +78,18 @@ struct FwdSegArgs {
     LowRankEpi lr;
 };
 
-// bf16 pair (16 (c_lo - 8), 16 (c_hi - 8)) for the four MFMA dwords of a code word.  H holds
-// 16 x the odd nibble positions and L 16 x the even ones as signed bytes; byte b of H is
-// position 2b + 1, byte b of L position 2b.  Dword e needs positions e and e + 4.
-__device__ __forceinline__ u4 codes16_bf16(uint32_t w) {
-    const uint32_t wx = w ^ 0x88888888u;
-    uint32_t H = wx & 0xF0F0F0F0u;
-    uint32_t L = (wx << 4) & 0xF0F0F0F0u;
-    // opaque to the optimiser, so each value below stays one byte-select (SDWA) conversion
-    asm volatile("" : "+v"(H), "+v"(L));
-    const float p0 = (float)(int8_t)(L & 0xFFu), p4 = (float)(int8_t)((L >> 16) & 0xFFu);
-    const float p1 = (float)(int8_t)(H & 0xFFu), p5 = (float)(int8_t)((H >> 16) & 0xFFu);
-    const float p2 = (float)(int8_t)((L >> 8) & 0xFFu), p6 = (float)(int8_t)(L >> 24);
-    const float p3 = (float)(int8_t)((H >> 8) & 0xFFu), p7 = (float)(int8_t)(H >> 24);
-    const uint32_t sel = 0x07060302u;     // upper halves: small integers are exact in bf16
-    return u4{__builtin_amdgcn_perm(bitcast<uint32_t>(p4), bitcast<uint32_t>(p0), sel),
-              __builtin_amdgcn_perm(bitcast<uint32_t>(p5), bitcast<uint32_t>(p1), sel),
-              __builtin_amdgcn_perm(bitcast<uint32_t>(p6), bitcast<uint32_t>(p2), sel),
-              __builtin_amdgcn_perm(bitcast<uint32_t>(p7), bitcast<uint32_t>(p3), sel)};
-}
-
-__device__ __forceinline__ u4 codes_f16(uint32_t w) {
-    return u4{bitcast<uint32_t>(codes_minus8_f16(w, 0)), bitcast<uint32_t>(codes_minus8_f16(w, 1)),
-              bitcast<uint32_t>(codes_minus8_f16(w, 2)), bitcast<uint32_t>(codes_minus8_f16(w, 3))};
+// bf16 pair ((c_lo - 8) / 16, (c_hi - 8) / 16) of dword e of a code word's MFMA fragment: nibble
+// positions e (low half) and e + 4 (high half).  With X = w ^ 0x88888888 (every nibble the
+// two's-complement 4-bit c - 8) and Xs = X >> 4, position 2b sits in the low nibble of byte b of
+// X and position 2b + 1 in the low nibble of byte b of Xs.  v_cvt_off_f32_i4 reads the low
+// nibble of a byte select (SDWA) and gives (c - 8) / 16 exactly; its upper half is the exact
+// bf16.  Seven VALU per two codes fewer than widening signed bytes: no masks per word.
+__device__ __forceinline__ uint32_t code_pair_bf16(uint32_t X, uint32_t Xs, int e) {
+    const uint32_t src = (e & 1) ? Xs : X;
+    const int by = e >> 1;
+    const float lo = __builtin_amdgcn_cvt_off_f32_i4((int)((src >> (8 * by)) & 0xFFu));
+    const float hi = __builtin_amdgcn_cvt_off_f32_i4((int)((src >> (8 * (by + 2))) & 0xFFu));
+    return __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
 }
 
 // SPC: scale slots per chunk (1: gs % 64 == 0; 2: gs % 32 == 0, one slot per 32 columns, which
@@ -364,10 +353,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         if constexpr (kBlockScales) return (SF ? 16 : 32) * (SPC * (srl >> 3) + q) + (SF ? 2 : 4) * (srl & 7);
         else return 256 * q + (SF ? 4 * (32 * h + (j >> 1)) + 2 * (j & 1) : 4 * (32 * h + j));
     };
-    // fp32 group scale of slot q for row n0 + j; bf16 codes carry a factor 16 that the scale
+    // fp32 group scale of slot q for row n0 + j; bf16 codes carry a factor 1/16 that the scale
     // removes exactly.
     auto group_scale = [&](const uint8_t* S, int q) -> float {
-        constexpr float kUnit = (XT == kF16) ? 1.0f : 0.0625f;
+        constexpr float kUnit = (XT == kF16) ? 1.0f : 16.0f;
         if constexpr (SF) return (float)bitcast<_Float16>(*reinterpret_cast<const uint16_t*>(S + soff(q))) * kUnit;
         else return *reinterpret_cast<const float*>(S + soff(q)) * kUnit;
     };
@@ -386,42 +375,57 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         const uint32_t s16 = *reinterpret_cast<const uint16_t*>(S + soff(q));
         return s16 | (s16 << 16);
     };
+    // The chunk's fold scales (slot q), read once per chunk: steps 2q' and 2q' + 1 share a slot
+    // when SPC < kSteps.
+    uint32_t fsc[MODE == kModeFold ? SPC : 1];
+    // fp16 c - 8 of nibble pair s (k-offsets 2s, 2s + 1 of the word's octet): (1024 + c) - 1032,
+    // both exact.  The pair mask and the fp16 1024 pair sit in registers the compiler cannot see
+    // through, so each pair is one v_and_or_b32 (gfx9 VOP3 operands take no literals: with both
+    // as literals every pair cost an AND and an OR).  Not in the 128-row exact-code instances,
+    // which are at 256 VGPRs already.
+    constexpr bool kRegUnpack = MODE == kModeFold || MI == 2;
+    uint32_t nib_mask = 0x000F000Fu, f16_1024 = 0x64006400u;
+    if constexpr (kRegUnpack) {
+        asm volatile("" : "+s"(nib_mask));
+        asm volatile("" : "+v"(f16_1024));
+    }
+    auto code_pair = [&](uint32_t w, int s) -> h2 {
+        const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+        if constexpr (kRegUnpack) return bitcast<h2>(((w >> (4 * s)) & nib_mask) | f16_1024) - off;
+        else return codes_minus8_f16(w, s);
+    };
     // B fragment of step t from the lane's code word (row n0 + j).
     auto dequant = [&](uint32_t bw, const uint8_t* S, int t, u4& b) {
         if constexpr (MODE == kModeFold) {
-            const h2 sc = bitcast<h2>(fold_scale(S, (t * SPC) / kSteps));
+            const h2 sc = bitcast<h2>(fsc[(t * SPC) / kSteps]);
             uint32_t p[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) p[s] = bitcast<uint32_t>(codes_minus8_f16(bw, s) * sc);
+            for (int s = 0; s < 4; ++s) p[s] = bitcast<uint32_t>(code_pair(bw, s) * sc);
             b = u4{p[0], p[1], p[2], p[3]};
         } else if constexpr (XT == kF16) {
-            b = codes_f16(bw);
+            b = u4{bitcast<uint32_t>(code_pair(bw, 0)), bitcast<uint32_t>(code_pair(bw, 1)),
+                   bitcast<uint32_t>(code_pair(bw, 2)), bitcast<uint32_t>(code_pair(bw, 3))};
         } else {
-            b = codes16_bf16(bw);
+            uint32_t X = bw ^ 0x88888888u, Xs = X >> 4;
+            asm volatile("" : "+v"(X), "+v"(Xs));   // keeps each conversion one byte select (SDWA)
+            b = u4{code_pair_bf16(X, Xs, 0), code_pair_bf16(X, Xs, 1), code_pair_bf16(X, Xs, 2),
+                   code_pair_bf16(X, Xs, 3)};
         }
     };
     // Dword e of the B fragment of step t, for interleaving pieces with the MFMAs.  wpre
     // carries per-word values from piece 0 to the later pieces.
     auto dequant_piece = [&](uint32_t w, const uint8_t* S, int t, u4& b, int e, uint32_t (&wpre)[2]) {
         if constexpr (MODE == kModeFold) {
-            if (e == 0) wpre[0] = fold_scale(S, (t * SPC) / kSteps);
-            b[e] = bitcast<uint32_t>(codes_minus8_f16(w, e) * bitcast<h2>(wpre[0]));
+            b[e] = bitcast<uint32_t>(code_pair(w, e) * bitcast<h2>(fsc[(t * SPC) / kSteps]));
         } else if constexpr (XT == kF16) {
-            b[e] = bitcast<uint32_t>(codes_minus8_f16(w, e));
+            b[e] = bitcast<uint32_t>(code_pair(w, e));
         } else {
             if (e == 0) {
-                const uint32_t wx = w ^ 0x88888888u;
-                wpre[0] = wx & 0xF0F0F0F0u;
-                wpre[1] = (wx << 4) & 0xF0F0F0F0u;
-                asm volatile("" : "+v"(wpre[0]), "+v"(wpre[1]));
+                wpre[0] = w ^ 0x88888888u;
+                wpre[1] = wpre[0] >> 4;
+                asm volatile("" : "+v"(wpre[0]), "+v"(wpre[1]));   // each conversion stays one byte select (SDWA)
             }
-            // dword e holds nibble positions e (low half) and e + 4 (high half); even positions
-            // come from L = wpre[1], odd ones from H = wpre[0], byte (position >> 1)
-            const uint32_t src = (e & 1) ? wpre[0] : wpre[1];
-            const int by = e >> 1;
-            const float lo = (float)(int8_t)((src >> (8 * by)) & 0xFFu);
-            const float hi = (float)(int8_t)((src >> (8 * (by + 2))) & 0xFFu);
-            b[e] = __builtin_amdgcn_perm(bitcast<uint32_t>(hi), bitcast<uint32_t>(lo), 0x07060302u);
+            b[e] = code_pair_bf16(wpre[0], wpre[1], e);
         }
     };
     // One MFMA (two for fp32 x) on tile mi; KIND as below.  An opening step that follows a
@@ -469,6 +473,10 @@ __global__ __launch_bounds__(512, 1) void gemm_fwd_kernel(FwdSegArgs seg, const 
         for (int t = 0; t < kSteps; ++t)
             bw[t] = *reinterpret_cast<const uint32_t*>(Bb + 1024 * (t >> 2) + 256 * Rj +
                                                        32 * ((2 * (t & 3) + h + 2 * Rj) & 7) + 4 * (j & 7));
+        if constexpr (MODE == kModeFold) {
+#pragma unroll
+            for (int q = 0; q < SPC; ++q) fsc[q] = fold_scale(S, q);
+        }
         u4 a[2][MI], alo[2][MI], b[2];
         read_a(Ab, 0, a[0], alo[0]);
         dequant(bw[0], S, 0, b[0]);
