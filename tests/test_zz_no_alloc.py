@@ -25,8 +25,8 @@ def _call(q, pw, x, y):
 def test_noalloc_forward_twice_then_smaller():
     q = lib()
     cases = [
-        # the prefill workload: M=512, K=8192, N=2048, gs=128, bf16 x; its plan splits K eight ways,
-        # so the partials fill the whole scratch
+        # the prefill workload: M=512, K=8192, N=2048, gs=128, bf16 x; its plan splits K four ways,
+        # so the partials take half of the scratch
         ("prefill", make_workload("prefill")),
         # a smaller forward whose plan also splits K: it reuses what the first call left behind
         ("small", make_linear(96, 2048, 1024, 64, "f16", "f16", seed=5)),
