@@ -132,10 +132,12 @@ __global__ __launch_bounds__(256) void dq8ca_quant_kernel(const void* __restrict
     const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
     float lo = 0.0f, hi = 0.0f;
+    // a row of at most 256 kOcts octets (K <= 8192) is read once: the min / max pass leaves each
+    // thread's octets in v for the codes
+    float v[kOcts][8];
     if constexpr (VEC) {
         const int64_t octs = K >> 3;
         for (int64_t o0 = 0; o0 < octs; o0 += 256 * kOcts) {
-            float v[kOcts][8];
 #pragma unroll
             for (int i = 0; i < kOcts; ++i) {
                 const int64_t o = o0 + tid + 256 * i;
@@ -153,25 +155,40 @@ __global__ __launch_bounds__(256) void dq8ca_quant_kernel(const void* __restrict
         }
     } else {
         for (int64_t k = tid; k < K; k += 256) {
-            const float v = load_elem<XT>(x, m * K + k);
-            lo = v < lo ? v : lo;
-            hi = v > hi ? v : hi;
+            const float e = load_elem<XT>(x, m * K + k);
+            lo = e < lo ? e : lo;
+            hi = e > hi ? e : hi;
         }
     }
     const RowQuant rq = row_quant(lo, hi, red);
     if constexpr (VEC) {
-        // second pass over the row (now in L2): 8 codes per octet, one 8-byte store
+        // 8 codes per octet, one 8-byte store; longer rows read the row again (now in L2)
         const int64_t octs = K >> 3;
-        for (int64_t o = tid; o < octs; o += 256) {
-            float v[8];
-            load_octet<XT>(x, m * K + 8 * o, v);
-            uint32_t wd[2] = {0u, 0u};
+        if (octs <= 256 * kOcts) {
 #pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const int k = GEMM ? kPerm[p] : p;
-                wd[p >> 2] |= (uint32_t)(rq(v[k]) & 0xFF) << (8 * (p & 3));
+            for (int i = 0; i < kOcts; ++i) {
+                const int64_t o = tid + 256 * i;
+                if (o >= octs) continue;
+                uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int k = GEMM ? kPerm[p] : p;
+                    wd[p >> 2] |= (uint32_t)(rq(v[i][k]) & 0xFF) << (8 * (p & 3));
+                }
+                *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{wd[0], wd[1]};
             }
-            *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{wd[0], wd[1]};
+        } else {
+            for (int64_t o = tid; o < octs; o += 256) {
+                float w[8];
+                load_octet<XT>(x, m * K + 8 * o, w);
+                uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int k = GEMM ? kPerm[p] : p;
+                    wd[p >> 2] |= (uint32_t)(rq(w[k]) & 0xFF) << (8 * (p & 3));
+                }
+                *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{wd[0], wd[1]};
+            }
         }
         if constexpr (GEMM)
             for (int64_t o = octs + tid; o < ld / 8; o += 256) *reinterpret_cast<u2*>(q + m * ld + 8 * o) = u2{0u, 0u};
