@@ -398,11 +398,19 @@ __global__ __launch_bounds__(256) void column_partial_kernel(ColSeg a, ColSeg b,
                 }
             }
         }
-        __syncthreads();
-        for (int i = tid; i < kT; i += 256) {
-            const int r = i / R, j = i % R;
-            Ts[i] = load_sel(T, (p0 + r) * rank + j, p0 + r < hi && j < rank);
+        // the T piece goes into registers in the same round trip as the X rows; the barrier then
+        // frees Ts of the previous piece before it is overwritten
+        constexpr int TPT = (kT + 255) / 256;
+        float tv_pre[TPT];
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + 256 * k, r = i / R, j = i % R;
+            tv_pre[k] = load_sel(T, (p0 + r) * rank + j, i < kT && p0 + r < hi && j < rank);
         }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < TPT; ++k)
+            if (tid + 256 * k < kT) Ts[tid + 256 * k] = tv_pre[k];
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
