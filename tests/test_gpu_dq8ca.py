@@ -27,7 +27,9 @@ QUANT_CASES = [
     (1, 64, "f32", 1.0),
     (7, 1000, "bf16", 3.0),
     (130, 257, "f16", 0.01),
-    (64, 8192, "bf16", 1.0),
+    (64, 8192, "bf16", 1.0),     # the longest row kept in registers between the two passes
+    (3, 8200, "bf16", 2.0),      # longer rows read the row a second time
+    (2, 16384, "f16", 0.5),
     (33, 96, "f32", 1e-3),
 ]
 
@@ -73,6 +75,7 @@ LINEAR_CASES = [
     (200, 264, 384, 64, "bf16", "f32"),
     (1, 2048, 2048, 32, "f16", "f16"),
     (257, 128, 192, 64, "f32", "f16"),      # K = 192: chunks past K hold code 8 and zero activations
+    (5, 64, 8320, 64, "bf16", "f16"),       # rows past 8192 columns: the quantisation reads them twice
 ]
 
 
