@@ -355,13 +355,21 @@ __global__ __launch_bounds__(256) void gemv_fwd_row_kernel(RowSegs segs, const v
         }
         const uint32_t wd[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
         if constexpr (XT == kF16) {
+            // the nibble-pair mask and the fp16 1024 pair in registers: one v_and_or_b32 per pair
+            uint32_t nib_mask = 0x000F000Fu, f16_1024 = 0x64006400u;
+            asm volatile("" : "+s"(nib_mask));
+            asm volatile("" : "+v"(f16_1024));
+            const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+            auto pair = [&](uint32_t w, int e) {
+                return bitcast<h2>(((w >> (4 * e)) & nib_mask) | f16_1024) - off;
+            };
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float t = 0.0f;
-                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 0), bitcast<h2>(xr[i].x), t, false);
-                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 1), bitcast<h2>(xr[i].y), t, false);
-                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 2), bitcast<h2>(xr[i].z), t, false);
-                t = __builtin_amdgcn_fdot2(codes_minus8_f16(wd[r], 3), bitcast<h2>(xr[i].w), t, false);
+                t = __builtin_amdgcn_fdot2(pair(wd[r], 0), bitcast<h2>(xr[i].x), t, false);
+                t = __builtin_amdgcn_fdot2(pair(wd[r], 1), bitcast<h2>(xr[i].y), t, false);
+                t = __builtin_amdgcn_fdot2(pair(wd[r], 2), bitcast<h2>(xr[i].z), t, false);
+                t = __builtin_amdgcn_fdot2(pair(wd[r], 3), bitcast<h2>(xr[i].w), t, false);
                 acc[r] = fmaf(t, sc[r], acc[r]);
             }
         } else {
